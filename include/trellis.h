@@ -1,0 +1,165 @@
+/*
+ * trellis.h -- C ABI of libtrellis: trellis-coded FP4 weights on MI355X (gfx950).
+ *
+ * The weight format and its decoder follow two pages:
+ *  - XOR-Trellis news article (aimodeling.com), bullet "XOR-Trellis FP4
+ *    decoder": each weight comes from a 16-bit sliding state; four masked
+ *    parities (0x1089, 0x2112, 0x0A24, 0x2441) give p0, p1, q0, q1; (p0, p1)
+ *    picks one of the palettes P0=[-6,-1.5,0,2], P1=[-4,-1,0.5,3],
+ *    P2=[-3,-0.5,1,4], P3=[-2,0,1.5,6]; (q0, q1) permutes branch -> entry.
+ *  - HEPH abstract (ICLR 2027 submission page): the decoded value is scaled
+ *    by the checkpoint block's UE8M0 exponent (one per 32 weights), so every
+ *    decoded weight is an MXFP4 element; weights are either decoded inside
+ *    the mixture-of-experts kernel on every forward pass ("fused") or
+ *    expanded once into resident MXFP4 ("expand").
+ *
+ * Storage (what the pages leave open is fixed here):
+ *  - A matrix is [rows = output features][cols = input features]; cols % 32 == 0.
+ *  - Branch symbols: 2 bits each, 16 per uint32, little-endian (symbol j of a
+ *    word in bits 2j..2j+1), rows contiguous: syms[n_mat][rows][cols/16].
+ *  - The state is s = ((s << 2) | b) & 0xFFFF, reset to 0 at each row start;
+ *    palette = p0 | p1 << 1, entry = b XOR (q0 | q1 << 1); P3's zero is -0.
+ *  - UE8M0 bytes: scales[n_mat][rows][cols/32], value 2^(e-127).
+ *  - E2M1 codes per the OCP MX v1.0 spec: sign bit 3, exponent bits 2..1,
+ *    mantissa bit 0.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises. Work is enqueued on `stream`
+ *    (NULL = the default stream) and runs asynchronously.
+ *  - Return 0 on success or a negative TRELLIS_E* code. Argument checks run on
+ *    the host before anything is enqueued; on error nothing is enqueued.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Calls that share a workspace must not overlap in time; otherwise calls
+ *    are independent and reentrant.
+ */
+#ifndef TRELLIS_H_
+#define TRELLIS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+enum {
+  TRELLIS_OK = 0,
+  TRELLIS_EINVAL = -1,      /* bad shape, dtype, flag or count */
+  TRELLIS_ENULL = -2,       /* a required pointer is NULL */
+  TRELLIS_EWORKSPACE = -3,  /* workspace too small or misaligned */
+  TRELLIS_EHIP = -4,        /* a HIP runtime call failed (launch error) */
+  TRELLIS_EDEVICE = -5      /* the current device is not gfx950 */
+};
+
+enum { TRELLIS_F32 = 0, TRELLIS_BF16 = 1 };
+
+/* A stack of n_mat trellis-coded matrices of identical shape. */
+typedef struct {
+  const uint32_t *syms;    /* device, [n_mat][rows][cols/16] */
+  const uint8_t *scales;   /* device, [n_mat][rows][cols/32] */
+  int32_t n_mat;           /* >= 1 */
+  int32_t rows;            /* >= 1; multiple of 16 for the GEMV calls */
+  int32_t cols;            /* >= 32, multiple of 32 */
+} trellis_mat_t;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int trellis_version(void);
+
+/* Static text for an error code. */
+const char *trellis_strerror(int err);
+
+/*
+ * trellis_decode_expand -- HEPH's expand serving mode: decode every weight of
+ * w into resident MXFP4.
+ *   codes_out:  device, [n_mat][rows][cols/2] bytes; byte j of a row holds the
+ *               E2M1 code of column 2j in its low nibble and of column 2j+1
+ *               in its high nibble.
+ *   scales_out: device, [n_mat][rows][cols/32]; a byte-for-byte copy of
+ *               w->scales (the UE8M0 exponents are reused unchanged).
+ * The output is bit-exact: it depends on nothing but the stored symbols.
+ * Errors: ENULL for NULL pointers, EINVAL for n_mat/rows < 1 or cols not a
+ * positive multiple of 32.
+ */
+int trellis_decode_expand(hipStream_t stream, const trellis_mat_t *w, uint8_t *codes_out,
+                          uint8_t *scales_out);
+
+/*
+ * Workspace bytes needed by trellis_moe_gemv for this shape. The workspace is
+ * scratch owned by the caller (256-byte aligned); its contents on entry do
+ * not matter. After the call completes, its first 4 bytes hold an int32: the
+ * number of routing slots skipped because their expert id was >= n_mat.
+ */
+size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
+                                       int32_t k);
+
+/*
+ * trellis_moe_gemv -- routed ("mixture-of-experts") GEMV / small-batch GEMM
+ * with the weights decoded inside the kernel on every call (HEPH's fused
+ * serving mode). Expert e's matrix is w[e] (n_mat experts).
+ *   x:          device activations, dtype x_dtype (TRELLIS_F32 or TRELLIS_BF16),
+ *               [T][cols] when x_per_slot == 0, [T][k][cols] when x_per_slot == 1.
+ *   topk_ids:   device int32 [T][k]; slot (t, j) uses expert topk_ids[t][j].
+ *               A negative id is an empty slot; an id >= n_mat is skipped and
+ *               counted (see the workspace note above). Neither is read from w.
+ *   topk_w:     device float [T][k] gate weights, or NULL.
+ *   y:          device float. With topk_w == NULL: y[T][k][rows],
+ *               y[t][j] = W_e x_(t or t,j) (zero for empty/skipped slots).
+ *               With topk_w: y[T][rows] = sum_j topk_w[t][j] * W_e x.
+ * T in 1..32, k in 1..32, T*k <= 1024; rows % 16 == 0.
+ * Accuracy: activations enter the block-scaled FP4 x FP8 matrix cores as a
+ * two-term FP8 (E4M3) split with UE8M0 scales per 32; sums are fp32; each
+ * output satisfies |y - y_exact| <= 2e-3 * sum |w| |x| (|topk_w| included).
+ */
+int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
+                     int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w, int32_t T,
+                     int32_t k, float *y, void *workspace, size_t workspace_bytes);
+
+/* Workspace bytes needed by trellis_moe_ffn for this layer shape. */
+size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t inter, int32_t T,
+                                      int32_t k);
+
+/*
+ * trellis_moe_ffn -- one whole mixture-of-experts layer in fused mode:
+ * gate_up GEMV per routed slot, SwiGLU, down GEMV and the gate-weighted
+ * combine over the k slots of each token.
+ *   w_gate_up:  n_exp matrices [2*inter][hidden]; rows [0, inter) are the gate
+ *               projection, rows [inter, 2*inter) the up projection.
+ *   w_down:     n_exp matrices [hidden][inter].
+ *   x:          device [T][hidden], dtype x_dtype.
+ *   topk_ids, topk_w: as for trellis_moe_gemv; topk_w NULL means all ones.
+ *   h:          device uint16 (bf16 bits) [T][k][inter], written: for each
+ *               live slot, bf16(silu(gate) * up) with silu(z) = z / (1 + e^-z),
+ *               rounded to nearest even; zero for empty/skipped slots.
+ *   y:          device float [T][hidden], sum over slots of topk_w * W_down h.
+ * hidden and inter: multiples of 32; T, k limits as for trellis_moe_gemv.
+ */
+int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_up, const trellis_mat_t *w_down,
+                    const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,
+                    int32_t T, int32_t k, uint16_t *h, float *y, void *workspace,
+                    size_t workspace_bytes);
+
+/*
+ * trellis_moe_ffn_timed -- trellis_moe_ffn that also records HIP events on
+ * `stream` at its stage boundaries, for timing each kernel in place:
+ *   events[0] before the routing / activation prep kernel,
+ *   events[1] before the gate_up + SwiGLU kernel,
+ *   events[2] before the down + combine kernel,
+ *   events[3] after it.
+ * `events` (caller-created hipEvent_t handles) may be NULL, as may any entry.
+ * Same arguments, results and errors as trellis_moe_ffn otherwise.
+ */
+typedef struct ihipEvent_t *hipEvent_t;
+int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
+                          const trellis_mat_t *w_down, const void *x, int32_t x_dtype,
+                          const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k,
+                          uint16_t *h, float *y, void *workspace, size_t workspace_bytes,
+                          hipEvent_t *events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRELLIS_H_ */

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/trellis.h declares, and rejects bad arguments on the host before
+anything would be enqueued (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import trellis_coded_fp4_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "trellis.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(trellis_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tq.lib()
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert sorted(names) == sorted(tq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"libtrellis.so does not export {n}"
+
+
+def test_version_and_strerror():
+    assert tq.version() >= 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert tq.strerror(code)
+    assert tq.strerror(-99) == "unknown error"
+
+
+def _mat(syms=1, scales=1, n_mat=1, rows=16, cols=64):
+    return tq.Mat(syms, scales, n_mat, rows, cols)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("m,code", [
+    (None, -2),
+    (dict(syms=0), -2),
+    (dict(scales=0), -2),
+    (dict(n_mat=0), -1),
+    (dict(rows=0), -1),
+    (dict(cols=48), -1),
+    (dict(cols=0), -1),
+])
+def test_expand_rejects(m, code):
+    lib = tq.lib()
+    arg = None if m is None else ctypes.byref(_mat(**m))
+    assert lib.trellis_decode_expand(None, arg, FAKE, FAKE) == code
+
+
+def test_expand_rejects_null_outputs():
+    lib = tq.lib()
+    assert lib.trellis_decode_expand(None, ctypes.byref(_mat()), None, FAKE) == -2
+    assert lib.trellis_decode_expand(None, ctypes.byref(_mat()), FAKE, None) == -2
+
+
+def _gemv(lib, m=None, x=FAKE, dtype=0, per_slot=0, ids=FAKE, w=None, T=1, k=1, y=FAKE, ws=0x10000,
+          wsb=1 << 30):
+    m = _mat() if m is None else m
+    return lib.trellis_moe_gemv(None, ctypes.byref(m), x, dtype, per_slot, ids, w, T, k, y, ws, wsb)
+
+
+def test_gemv_argument_checks():
+    lib = tq.lib()
+    assert _gemv(lib, x=None) == -2
+    assert _gemv(lib, ids=None) == -2
+    assert _gemv(lib, y=None) == -2
+    assert _gemv(lib, ws=None) == -2
+    assert _gemv(lib, dtype=7) == -1
+    assert _gemv(lib, per_slot=2) == -1
+    assert _gemv(lib, T=0) == -1
+    assert _gemv(lib, T=33) == -1
+    assert _gemv(lib, k=0) == -1
+    assert _gemv(lib, k=33) == -1
+    assert _gemv(lib, m=_mat(rows=24)) == -1          # rows % 16
+    assert _gemv(lib, m=_mat(n_mat=1025)) == -1
+    assert _gemv(lib, ws=0x10010) == -3               # misaligned workspace
+    assert _gemv(lib, wsb=16) == -3                   # too small
+
+
+def test_ffn_argument_checks():
+    lib = tq.lib()
+    gu, dn = _mat(n_mat=2, rows=128, cols=64), _mat(n_mat=2, rows=64, cols=64)
+
+    def call(gu=gu, dn=dn, x=FAKE, h=FAKE, y=FAKE, T=1, k=1, ws=0x10000, wsb=1 << 30):
+        return lib.trellis_moe_ffn(None, ctypes.byref(gu), ctypes.byref(dn), x, 1, FAKE, None, T, k, h, y,
+                                   ws, wsb)
+    assert call(h=None) == -2
+    assert call(x=None) == -2
+    assert call(dn=_mat(n_mat=3, rows=64, cols=64)) == -1     # expert counts differ
+    assert call(dn=_mat(n_mat=2, rows=32, cols=64)) == -1     # down rows != hidden
+    assert call(dn=_mat(n_mat=2, rows=64, cols=32)) == -1     # down cols != inter
+    assert call(gu=_mat(n_mat=2, rows=96, cols=64)) == -1     # 2*inter % 64
+    assert call(wsb=100) == -3
+
+
+def test_workspace_sizes():
+    lib = tq.lib()
+    a = lib.trellis_moe_gemv_workspace_size(32, 5760, 2880, 1, 4)
+    b = lib.trellis_moe_gemv_workspace_size(32, 5760, 2880, 32, 4)
+    assert 0 < a < b
+    assert lib.trellis_moe_gemv_workspace_size(32, 5760, 2881, 1, 4) == 0
+    assert lib.trellis_moe_gemv_workspace_size(32, 5760, 2880, 0, 4) == 0
+    f = lib.trellis_moe_ffn_workspace_size(128, 4096, 1536, 32, 8)
+    assert f > 0 and f % 256 == 0
+    assert lib.trellis_moe_ffn_workspace_size(128, 4096, 1530, 32, 8) == 0

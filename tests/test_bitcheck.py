@@ -1,0 +1,90 @@
+"""Host build of the device decoder's integer arithmetic vs the oracle.
+
+libtq_bitcheck.so is compiled from the same tq_decode.h the kernels use, so
+these CPU tests check the bit-sliced decode (16 weights per word from funnel
+shifts and XORs) and the activation layout without a GPU."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+
+HERE = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(HERE, "trellis_coded_fp4_amd", "libtq_bitcheck.so")
+
+
+@pytest.fixture(scope="module")
+def bc():
+    if not os.path.exists(LIB):
+        pytest.fail("libtq_bitcheck.so not built (run python -m trellis_coded_fp4_amd.build)")
+    L = ctypes.CDLL(LIB)
+    U = ctypes.c_uint32
+    PU = ctypes.POINTER(U)
+    L.tq_bitcheck_decode_word.argtypes = [U, U, PU, PU]
+    L.tq_bitcheck_natural.argtypes = [U, U, PU, PU]
+    for f in ("tq_bitcheck_nibble_position", "tq_bitcheck_bchunk_offset"):
+        getattr(L, f).argtypes = [ctypes.c_int]
+        getattr(L, f).restype = ctypes.c_int
+    L.tq_bitcheck_canonical_k.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.tq_bitcheck_canonical_k.restype = ctypes.c_int
+    return L
+
+
+def _decode_row(bc, words):
+    """Per-weight codes of one row through the bit-sliced decoder."""
+    out = []
+    prev = 0
+    e, o = ctypes.c_uint32(), ctypes.c_uint32()
+    for w in words:
+        bc.tq_bitcheck_decode_word(int(w), prev, ctypes.byref(e), ctypes.byref(o))
+        for m in range(16):
+            src = e.value if m % 2 == 0 else o.value
+            out.append((src >> (4 * (m // 2))) & 0xF)
+        prev = int(w)
+    return np.array(out, dtype=np.uint8)
+
+
+def test_bitsliced_decode_matches_oracle(bc, orc):
+    g = workloads.rng(77, 0)
+    syms = workloads.symbols(g, 1, 40, 256)[0]
+    syms[0, :] = 0
+    syms[1, :] = 0xFFFFFFFF
+    ref = orc.decode_codes(syms, 256)
+    for r in range(syms.shape[0]):
+        assert (_decode_row(bc, syms[r]) == ref[r]).all(), f"row {r}"
+
+
+def test_natural_order_matches_oracle_expand(bc, orc):
+    g = workloads.rng(77, 1)
+    syms = workloads.symbols(g, 1, 8, 128)
+    sc = workloads.scales(g, 1, 8, 128)
+    packed, _ = orc.expand(syms, sc)
+    lo, hi = ctypes.c_uint32(), ctypes.c_uint32()
+    for r in range(8):
+        prev = 0
+        got = bytearray()
+        for w in syms[0, r]:
+            bc.tq_bitcheck_natural(int(w), prev, ctypes.byref(lo), ctypes.byref(hi))
+            got += int(lo.value).to_bytes(4, "little") + int(hi.value).to_bytes(4, "little")
+            prev = int(w)
+        assert bytes(got) == packed[0, r].tobytes()
+
+
+def test_activation_layout_is_a_bijection(bc):
+    # nibble n of the four decoded registers <-> weight position in the block
+    pos = [bc.tq_bitcheck_nibble_position(n) for n in range(32)]
+    assert sorted(pos) == list(range(32))
+    # canonical K of (block, position) covers 0..127 once, and inverts nibble_position
+    ks = [bc.tq_bitcheck_canonical_k(b, p) for b in range(4) for p in range(32)]
+    assert sorted(ks) == list(range(128))
+    for n in range(32):
+        assert bc.tq_bitcheck_canonical_k(0, pos[n]) == n
+    # byte offset of canonical K inside a 128-byte B chunk: bijective, 32 per lane group
+    offs = [bc.tq_bitcheck_bchunk_offset(k) for k in range(128)]
+    assert sorted(offs) == list(range(128))
+    for k in range(128):
+        lane_group, byte = divmod(offs[k], 32)
+        # bytes 0..15 of lane group g hold k = 16g..16g+15, bytes 16..31 hold k = 64+16g..
+        assert k == (16 * lane_group + byte if byte < 16 else 64 + 16 * lane_group + byte - 16)

@@ -1,0 +1,219 @@
+"""Fused trellis-decode MoE GEMV / FFN on the GPU against the oracle.
+
+Bar: every output within 2e-3 * sum |w| |x| of the oracle's fp64 result. For
+the whole layer each stage is gated on its own: the gate_up/SwiGLU stage by
+h, the down stage by the oracle fed the GPU's own h (so bf16 rounding flips
+in h do not compound); the end-to-end difference is printed, not gated.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from helpers import TOL, announce, check_tol, dev, silu, x_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemv_case(tq, orc, E, rows, cols, T, k, bf16, weighted, per_slot, ids=None, seed=0):
+    g = workloads.rng(601, seed, E * 1000 + rows, cols * 100 + T * 10 + k)
+    syms = workloads.symbols(g, E, rows, cols)
+    sc = workloads.scales(g, E, rows, cols)
+    x = workloads.activations(g, T * (k if per_slot else 1), cols, bf16)
+    x = x.reshape((T, k, cols) if per_slot else (T, cols))
+    if ids is None:
+        ids, gw = workloads.routing_topk(g, T, E, min(k, E))
+        if ids.shape[1] < k:
+            ids = np.concatenate([ids, -np.ones((T, k - ids.shape[1]), np.int32)], axis=1)
+            gw = np.concatenate([gw, np.zeros((T, k - gw.shape[1]), np.float32)], axis=1)
+    else:
+        gw = g.uniform(0.1, 1.0, size=ids.shape).astype(np.float32)
+    y = tq.moe_gemv(dev(syms), dev(sc), x_dev(x, bf16), dev(ids),
+                    dev(gw) if weighted else None, x_per_slot=per_slot).cpu().numpy()
+    y_ref, bound, skipped = orc.moe_gemv(syms, sc, x, ids, gate_w=gw if weighted else None,
+                                        x_per_slot=per_slot)
+    return y, y_ref, bound, skipped
+
+
+def test_single_matrix_fp32(trellis_lib, orc):
+    """The 256 x 1024 single-matrix workload: fp32 x, batch 1, one expert."""
+    announce("gemv single matrix 256x1024 fp32")
+    c = workloads.SINGLE_MATRIX
+    g = workloads.rng(c["config_id"], 0)
+    syms = workloads.symbols(g, 1, c["rows"], c["cols"])
+    sc = workloads.scales(workloads.rng(c["config_id"], 1), 1, c["rows"], c["cols"])
+    x = workloads.activations(workloads.rng(c["config_id"], workloads.T_X), 1, c["cols"], bf16=False)
+    ids = np.zeros((1, 1), np.int32)
+    y = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, False), dev(ids)).cpu().numpy()
+    y_ref, bound, _ = orc.moe_gemv(syms, sc, x, ids)
+    r = check_tol(y, y_ref, bound, "single matrix")
+    print(f"worst err/tol {r:.4f}")
+
+
+@pytest.mark.parametrize("E,rows,cols,T,k,bf16,weighted,per_slot", [
+    (5, 48, 96, 3, 2, True, False, False),      # partial 128-K chunk, 3 row tiles
+    (5, 48, 96, 3, 2, True, True, False),
+    (5, 48, 96, 3, 2, False, True, True),
+    (4, 64, 2880, 1, 4, True, False, False),    # K = 2880: 90 blocks, ragged last chunk
+    (4, 64, 2880, 1, 4, True, True, False),
+    (16, 80, 256, 4, 4, True, True, False),
+    (16, 64, 256, 8, 4, True, True, False),
+    (16, 64, 256, 16, 4, True, False, False),
+    (16, 64, 256, 16, 4, True, True, False),
+    (16, 32, 512, 32, 4, True, True, False),
+    (16, 32, 512, 32, 4, True, False, False),
+    (3, 16, 32, 32, 8, False, True, True),      # one block per row; T*k = 256 slots over 3 experts
+])
+def test_moe_gemv(trellis_lib, orc, E, rows, cols, T, k, bf16, weighted, per_slot):
+    announce(f"gemv E={E} {rows}x{cols} T={T} k={k} bf16={bf16} w={weighted} per_slot={per_slot}")
+    y, y_ref, bound, _ = _gemv_case(trellis_lib, orc, E, rows, cols, T, k, bf16, weighted, per_slot)
+    check_tol(y, y_ref, bound, "moe_gemv")
+
+
+def test_moe_gemv_dead_and_duplicate_slots(trellis_lib, orc):
+    announce("gemv dead and duplicate slots")
+    import torch
+    E, rows, cols = 4, 32, 128
+    ids = np.array([[0, -1, 2], [7, 1, 1], [3, 3, -5]], dtype=np.int32)   # 7 >= E is skipped
+    for weighted in (False, True):
+        for per_slot in (False, True):
+            y, y_ref, bound, skipped = _gemv_case(trellis_lib, orc, E, rows, cols, 3, 3, True, weighted,
+                                                  per_slot, ids=ids, seed=1)
+            assert skipped == 1
+            check_tol(y, y_ref, bound, f"dead/dup weighted={weighted} per_slot={per_slot}")
+            if not weighted:
+                assert (y[0, 1] == 0).all() and (y[1, 0] == 0).all() and (y[2, 2] == 0).all()
+    # the skipped-slot count is reported in the first workspace word
+    g = workloads.rng(602, 0)
+    syms = workloads.symbols(g, E, rows, cols)
+    sc = workloads.scales(g, E, rows, cols)
+    ws = trellis_lib.gemv_workspace(E, rows, cols, 3, 3)
+    trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(workloads.activations(g, 3, cols, True), True), dev(ids),
+                         workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0]) == 1
+
+
+def test_moe_gemv_repeat_is_deterministic(trellis_lib, orc):
+    announce("gemv determinism")
+    import torch
+    g = workloads.rng(603, 0)
+    E, rows, cols, T, k = 8, 64, 1024, 4, 4
+    syms, sc = dev(workloads.symbols(g, E, rows, cols)), dev(workloads.scales(g, E, rows, cols))
+    x = x_dev(workloads.activations(g, T, cols, True), True)
+    ids, gw = workloads.routing_topk(g, T, E, k)
+    a = trellis_lib.moe_gemv(syms, sc, x, dev(ids), dev(gw))
+    b = trellis_lib.moe_gemv(syms, sc, x, dev(ids), dev(gw))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _h_tolerance(g_ref, u_ref, bg, bu):
+    """Bound on |h_gpu - silu(g)u| from the per-row GEMV bounds plus bf16 rounding."""
+    sig = 1.0 / (1.0 + np.exp(-g_ref))
+    dsilu = np.abs(sig * (1.0 + g_ref * (1.0 - sig)))
+    tg, tu = TOL * bg, TOL * bu
+    h = silu(g_ref) * u_ref
+    return (dsilu + 0.6 * tg) * (np.abs(u_ref) + tu) * tg + (np.abs(silu(g_ref)) + tg) * tu \
+        + np.abs(h) * 2.0 ** -7 + 1e-30
+
+
+def _check_layer(tq, orc, layer, rows_gu=None, rows_dn=None):
+    """Run the layer on the GPU; check h on sampled (slot, i) and y on sampled rows."""
+    import torch
+    cfg = layer.cfg
+    E = layer.gu_syms.shape[0]
+    I, H = cfg.inter, cfg.hidden
+    T, k = layer.ids.shape
+    y, h = tq.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales),
+                      x_dev(layer.x, cfg.x_bf16), dev(layer.ids), dev(layer.gate_w))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    h = h.float().cpu().numpy()
+    ii = np.arange(I) if rows_gu is None else rows_gu
+    x64 = layer.x.astype(np.float64)
+    worst = 0.0
+    for t in range(T):
+        for j in range(k):
+            e = int(layer.ids[t, j])
+            sel = np.concatenate([ii, I + ii])
+            yg, bg = orc.gemv(layer.gu_syms[e][sel], layer.gu_scales[e][sel], x64[t])
+            g_ref, u_ref = yg[0, :len(ii)], yg[0, len(ii):]
+            bgg, bgu = bg[0, :len(ii)], bg[0, len(ii):]
+            lim = _h_tolerance(g_ref, u_ref, bgg, bgu)
+            err = np.abs(h[t, j, ii] - silu(g_ref) * u_ref)
+            assert (err <= lim).all(), f"h slot ({t},{j}) worst {(err / lim).max():.3f}"
+            worst = max(worst, float((err / lim).max()))
+    # down stage fed the GPU's own h
+    rr = np.arange(H) if rows_dn is None else rows_dn
+    y_ref = np.zeros((T, len(rr)))
+    bound = np.zeros((T, len(rr)))
+    for t in range(T):
+        for j in range(k):
+            e = int(layer.ids[t, j])
+            yd, bd = orc.gemv(layer.dn_syms[e][rr], layer.dn_scales[e][rr], h[t, j].astype(np.float64))
+            y_ref[t] += layer.gate_w[t, j] * yd[0]
+            bound[t] += abs(layer.gate_w[t, j]) * bd[0]
+    r = check_tol(y[:, rr], y_ref, bound, "down + combine")
+    print(f"h worst err/tol {worst:.4f}; y worst err/tol {r:.4f}")
+    return y, h
+
+
+def test_ffn_small_with_edge_routing(trellis_lib, orc):
+    announce("ffn small, dead and duplicate slots")
+    import torch
+    cfg = workloads.MoEConfig(90, "small", 4, 96, 64, 3, 3, True)
+    layer = workloads.moe_layer(cfg)
+    layer.ids[:] = np.array([[0, 2, -1], [1, 1, 3], [9, 0, 0]], np.int32)
+    layer.gate_w[:] = np.array([[0.5, 0.3, 0.2], [0.25, 0.25, 0.5], [0.1, 0.6, 0.3]], np.float32)
+    y, h = trellis_lib.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms),
+                               dev(layer.dn_scales), x_dev(layer.x, True), dev(layer.ids), dev(layer.gate_w))
+    torch.cuda.synchronize()
+    y, h = y.cpu().numpy(), h.float().cpu().numpy()
+    assert (h[0, 2] == 0).all() and (h[2, 0] == 0).all()
+    y_ref, bound, h_ref, skipped = orc.moe_ffn(layer.gu_syms, layer.gu_scales, layer.dn_syms, layer.dn_scales,
+                                              layer.x, layer.ids, layer.gate_w)
+    assert skipped == 1
+    # the oracle's chain fed the GPU's h reproduces y within tolerance
+    yg = np.zeros_like(y_ref)
+    bg = np.zeros_like(y_ref)
+    for t in range(3):
+        for j in range(3):
+            e = int(layer.ids[t, j])
+            if e < 0 or e >= 4:
+                continue
+            yd, bd = orc.gemv(layer.dn_syms[e], layer.dn_scales[e], h[t, j].astype(np.float64))
+            yg[t] += layer.gate_w[t, j] * yd[0]
+            bg[t] += abs(layer.gate_w[t, j]) * bd[0]
+    check_tol(y, yg, bg, "ffn small")
+    print("end-to-end max |y - y_oracle| / bound:", float((np.abs(y - y_ref) / (bound + 1e-30)).max()))
+
+
+def test_ffn_expert_ffn_full(trellis_lib, orc):
+    """One expert FFN, batch 1: gate_up 5760 x 2880 and down 2880 x 2880, all rows."""
+    announce("ffn one expert 5760x2880 + 2880x2880")
+    layer = workloads.moe_layer(workloads.EXPERT_FFN)
+    layer.ids[:] = 0
+    layer.gate_w[:] = 1.0
+    _check_layer(trellis_lib, orc, layer)
+
+
+def test_ffn_32_experts_sampled(trellis_lib, orc):
+    """Full MoE layer, 32 experts, top-4, batch 1 (sampled rows of both stages)."""
+    announce("ffn 32 experts top-4 batch 1")
+    layer = workloads.moe_layer(workloads.MOE_32E)
+    rs = np.random.default_rng(0)
+    _check_layer(trellis_lib, orc, layer, rows_gu=np.sort(rs.choice(2880, 160, replace=False)),
+                 rows_dn=np.sort(rs.choice(2880, 160, replace=False)))
+
+
+@pytest.mark.parametrize("T", [1, 4, 8, 16, 32])
+def test_ffn_128_experts_sweep_sampled(trellis_lib, orc, T):
+    """128 experts, hidden 4096, intermediate 1536, top-8, Zipf(1.1) routing."""
+    announce(f"ffn 128 experts top-8 T={T}")
+    layer = workloads.moe_layer(workloads.moe_128e(T))
+    rs = np.random.default_rng(T)
+    n_gu = 48 if T <= 8 else 16
+    _check_layer(trellis_lib, orc, layer, rows_gu=np.sort(rs.choice(1536, n_gu, replace=False)),
+                 rows_dn=np.sort(rs.choice(4096, 64, replace=False)))

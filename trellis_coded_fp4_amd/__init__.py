@@ -1,0 +1,226 @@
+"""trellis_coded_fp4_amd -- trellis-coded FP4 (MXFP4-grid) weights on MI355X.
+
+Thin ctypes binding of libtrellis.so (HIP kernels for gfx950 behind the C ABI
+declared in include/trellis.h). This module only marshals arguments: every
+step of decoding and multiplication runs in the library's kernels. PyTorch
+supplies device memory and the current HIP stream.
+
+If the library has not been built, importing works but every call raises:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtrellis.so")
+
+TRELLIS_F32 = 0
+TRELLIS_BF16 = 1
+
+ERRORS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_ENULL", -3: "TRELLIS_EWORKSPACE",
+          -4: "TRELLIS_EHIP", -5: "TRELLIS_EDEVICE"}
+
+# Every symbol include/trellis.h declares.
+EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
+           "trellis_moe_gemv_workspace_size", "trellis_moe_gemv",
+           "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed"]
+
+
+class TrellisError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({strerror(code)})")
+
+
+class Mat(ctypes.Structure):
+    """trellis_mat_t"""
+    _fields_ = [("syms", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n_mat", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtrellis.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libtrellis.so not built at {LIB_PATH}; run "
+                               "`python -m trellis_coded_fp4_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        MP = ctypes.POINTER(Mat)
+        L.trellis_version.argtypes = []
+        L.trellis_version.restype = ctypes.c_int
+        L.trellis_strerror.argtypes = [ctypes.c_int]
+        L.trellis_strerror.restype = ctypes.c_char_p
+        L.trellis_decode_expand.argtypes = [P, MP, P, P]
+        L.trellis_decode_expand.restype = ctypes.c_int
+        L.trellis_moe_gemv_workspace_size.argtypes = [I32] * 5
+        L.trellis_moe_gemv_workspace_size.restype = SZ
+        L.trellis_moe_gemv.argtypes = [P, MP, P, I32, I32, P, P, I32, I32, P, P, SZ]
+        L.trellis_moe_gemv.restype = ctypes.c_int
+        L.trellis_moe_ffn_workspace_size.argtypes = [I32] * 5
+        L.trellis_moe_ffn_workspace_size.restype = SZ
+        L.trellis_moe_ffn.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P, P, SZ]
+        L.trellis_moe_ffn.restype = ctypes.c_int
+        L.trellis_moe_ffn_timed.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P, P, SZ, P]
+        L.trellis_moe_ffn_timed.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().trellis_version()
+
+
+def strerror(code: int) -> str:
+    return lib().trellis_strerror(int(code)).decode()
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(t, dtype, name, shape=None):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def mat(syms, scales) -> Mat:
+    """trellis_mat_t for syms [n_mat, rows, cols/16] int32/uint32 and scales [n_mat, rows, cols/32] uint8."""
+    torch = _torch()
+    if syms.dim() == 2:
+        syms = syms.unsqueeze(0)
+    if scales.dim() == 2:
+        scales = scales.unsqueeze(0)
+    if syms.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("syms must be int32/uint32 words")
+    _check(syms, syms.dtype, "syms")
+    n_mat, rows, wpr = syms.shape
+    _check(scales, torch.uint8, "scales", (n_mat, rows, wpr // 2))
+    return Mat(syms.data_ptr(), scales.data_ptr(), n_mat, rows, wpr * 16)
+
+
+def decode_expand(syms, scales, codes_out=None, scales_out=None, stream=None):
+    """Expand to resident MXFP4: returns (codes [n_mat, rows, cols/2] uint8, scales copy)."""
+    torch = _torch()
+    m = mat(syms, scales)
+    if codes_out is None:
+        codes_out = torch.empty((m.n_mat, m.rows, m.cols // 2), dtype=torch.uint8, device=syms.device)
+    if scales_out is None:
+        scales_out = torch.empty((m.n_mat, m.rows, m.cols // 32), dtype=torch.uint8, device=syms.device)
+    _check(codes_out, torch.uint8, "codes_out", (m.n_mat, m.rows, m.cols // 2))
+    _check(scales_out, torch.uint8, "scales_out", (m.n_mat, m.rows, m.cols // 32))
+    rc = lib().trellis_decode_expand(_stream(stream), ctypes.byref(m), codes_out.data_ptr(),
+                                     scales_out.data_ptr())
+    if rc:
+        raise TrellisError(rc, "trellis_decode_expand")
+    return codes_out, scales_out
+
+
+def _x_dtype(x):
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return TRELLIS_F32
+    if x.dtype == torch.bfloat16:
+        return TRELLIS_BF16
+    raise ValueError("x must be float32 or bfloat16")
+
+
+def gemv_workspace(n_mat, rows, cols, T, k, device="cuda"):
+    torch = _torch()
+    n = lib().trellis_moe_gemv_workspace_size(n_mat, rows, cols, T, k)
+    if n == 0:
+        raise TrellisError(-1, "trellis_moe_gemv_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ffn_workspace(n_exp, hidden, inter, T, k, device="cuda"):
+    torch = _torch()
+    n = lib().trellis_moe_ffn_workspace_size(n_exp, hidden, inter, T, k)
+    if n == 0:
+        raise TrellisError(-1, "trellis_moe_ffn_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
+             stream=None):
+    """Routed fused-decode GEMV. y is [T, k, rows] without topk_w, [T, rows] with it."""
+    torch = _torch()
+    m = mat(syms, scales)
+    T, k = topk_ids.shape
+    _check(topk_ids, torch.int32, "topk_ids")
+    if topk_w is not None:
+        _check(topk_w, torch.float32, "topk_w", (T, k))
+    _check(x, x.dtype, "x", (T, k, m.cols) if x_per_slot else (T, m.cols))
+    shape = (T, m.rows) if topk_w is not None else (T, k, m.rows)
+    if y is None:
+        y = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check(y, torch.float32, "y", shape)
+    if workspace is None:
+        workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
+    rc = lib().trellis_moe_gemv(_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x),
+                                int(bool(x_per_slot)), topk_ids.data_ptr(), _ptr(topk_w), T, k,
+                                y.data_ptr(), workspace.data_ptr(), workspace.numel())
+    if rc:
+        raise TrellisError(rc, "trellis_moe_gemv")
+    return y
+
+
+def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
+            workspace=None, stream=None, events=None):
+    """Whole fused MoE layer; returns (y [T, hidden] fp32, h [T, k, inter] bf16).
+
+    ``events``: optional ctypes array of 4 hipEvent_t recorded at the stage
+    boundaries (see trellis_moe_ffn_timed)."""
+    torch = _torch()
+    mg = mat(gu_syms, gu_scales)
+    md = mat(dn_syms, dn_scales)
+    T, k = topk_ids.shape
+    _check(topk_ids, torch.int32, "topk_ids")
+    if topk_w is not None:
+        _check(topk_w, torch.float32, "topk_w", (T, k))
+    hidden, inter = mg.cols, mg.rows // 2
+    _check(x, x.dtype, "x", (T, hidden))
+    if h is None:
+        h = torch.empty((T, k, inter), dtype=torch.bfloat16, device=x.device)
+    _check(h, torch.bfloat16, "h", (T, k, inter))
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+    _check(y, torch.float32, "y", (T, hidden))
+    if workspace is None:
+        workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
+    rc = lib().trellis_moe_ffn_timed(_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(),
+                                     _x_dtype(x), topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(),
+                                     y.data_ptr(), workspace.data_ptr(), workspace.numel(), events)
+    if rc:
+        raise TrellisError(rc, "trellis_moe_ffn")
+    return y, h

@@ -1,0 +1,117 @@
+// tq_decode.h -- bit-sliced decoder for trellis-coded FP4 symbol words.
+//
+// Decoder being implemented (XOR-Trellis news article, aimodeling.com, bullet
+// "XOR-Trellis FP4 decoder"): after shifting symbol b into the 16-bit state s,
+// p0, p1, q0, q1 are the parities of s & 0x1089, 0x2112, 0x0A24, 0x2441;
+// (p0, p1) select the palette and (q0, q1) permute branch -> entry:
+//   P0=[-6,-1.5,0,2] P1=[-4,-1,0.5,3] P2=[-3,-0.5,1,4] P3=[-2,0,1.5,6]
+// with palette = p0 | p1<<1, entry = b ^ (q0 | q1<<1), P3's zero = -0, and
+// the result written as an OCP E2M1 code (sign bit 3, exponent bits 2..1,
+// mantissa bit 0).
+//
+// Why it is a few word-wide XORs: written as E2M1 bits, the 16 palette
+// entries are a bijection onto the 16 codes, and every code bit is affine
+// over GF(2) in the state bits. With e0 = b_lo ^ q0 and e1 = b_hi ^ q1:
+//   mantissa = ~(p0 ^ e1), exp_lo = ~(p1 ^ e1), exp_hi = ~(e0 ^ e1), sign = ~e1.
+// So a whole 32-bit symbol word (16 weights) decodes with funnel shifts of
+// the (current:previous) word pair and XORs, no per-weight work.
+//
+// Lane algebra.  In a symbol word each weight owns a 2-bit slot (bits 2i,
+// 2i+1: "lo" and "hi" lane). Bit 2t+c of weight i's state is bit c of the
+// symbol t places earlier. Shifting the stream left by a bits puts, in slot
+// i, state bit a (even a) or a+2 (odd a) into the lo lane and state bit a+1
+// (even a) or a-1 (odd a) into the hi lane. Reading the masks through that
+// table:
+//   e0 (lo lane): s0 s2 s5 s9 s11  -> shifts {0,2,3,7,9}
+//   e1 (hi lane): s1 s0 s6 s10 s13 -> shifts {0,1,7,11,12}
+//   p0 (lo lane): s0 s3 s7 s12     -> shifts {0,1,5,12}
+//   p1 (hi lane): s1 s4 s8 s13     -> shifts {0,5,9,12}
+// i.e. 8 distinct funnel shifts {1,2,3,5,7,9,11,12} per word. The previous
+// word supplies the 12 history bits (6 symbols); it is 0 at a row start,
+// which is the state reset.
+//
+// Output layout: the 16 codes of a word go into two nibble words, "even"
+// (weights 0,2,..,14 in nibbles 0..7) and "odd" (weights 1,3,..,15). Both
+// consumers handle that order: the matrix-core GEMV permutes activations to
+// match; the expand kernel interleaves to natural order.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+#define TQ_HD __host__ __device__ __forceinline__
+#else
+#define TQ_HD inline
+#endif
+
+namespace tq {
+
+// Low word of ((cur:prev) << n), n in 1..31.
+TQ_HD uint32_t shl_hist(uint32_t cur, uint32_t prev, int n) {
+  return (cur << n) | (prev >> (32 - n));
+}
+
+struct nib2 {
+  uint32_t even;  // nibble m = E2M1 code of weight 2m of the word
+  uint32_t odd;   // nibble m = E2M1 code of weight 2m+1
+};
+
+// Decode one symbol word `g` whose predecessor in the row is `prev`
+// (0 at the row start).
+TQ_HD nib2 decode_word(uint32_t g, uint32_t prev) {
+  const uint32_t LO = 0x55555555u;
+  const uint32_t x1 = shl_hist(g, prev, 1), x2 = shl_hist(g, prev, 2), x3 = shl_hist(g, prev, 3);
+  const uint32_t x5 = shl_hist(g, prev, 5), x7 = shl_hist(g, prev, 7), x9 = shl_hist(g, prev, 9);
+  const uint32_t x11 = shl_hist(g, prev, 11), x12 = shl_hist(g, prev, 12);
+  // E: (e0, e1) in (lo, hi) lanes.  P: (p0, p1).
+  const uint32_t e_lo = x2 ^ x3 ^ x9;
+  const uint32_t e_hi = x1 ^ x11 ^ x12;
+  const uint32_t E = g ^ x7 ^ ((e_lo & LO) | (e_hi & ~LO));
+  const uint32_t P = g ^ x5 ^ x12 ^ ((x1 & LO) | (x9 & ~LO));
+  const uint32_t N = E >> 1;                    // e1 moved into the lo lane
+  const uint32_t R = (N & LO) | (E & ~LO);      // (e1, e1)
+  const uint32_t A = ~(P ^ R);                  // (mantissa, exp_lo)
+  const uint32_t B = ~(E ^ (N & LO));           // (exp_hi, sign)
+  nib2 r;
+  r.even = (A & 0x33333333u) | ((B << 2) & 0xCCCCCCCCu);
+  r.odd = ((A >> 2) & 0x33333333u) | (B & 0xCCCCCCCCu);
+  return r;
+}
+
+// Nibbles 0..3 of v spread to the low nibble of bytes 0..3.
+TQ_HD uint32_t spread_nibbles(uint32_t v) {
+  v &= 0xFFFFu;
+  v = (v | (v << 8)) & 0x00FF00FFu;
+  return (v | (v << 4)) & 0x0F0F0F0Fu;
+}
+
+// Natural-order packed codes of a word: byte j = code(2j) | code(2j+1) << 4.
+// lo covers weights 0..7, hi weights 8..15.
+TQ_HD void natural_order(nib2 n, uint32_t *lo, uint32_t *hi) {
+  *lo = spread_nibbles(n.even) | (spread_nibbles(n.odd) << 4);
+  *hi = spread_nibbles(n.even >> 16) | (spread_nibbles(n.odd >> 16) << 4);
+}
+
+// Position inside a 32-weight block of the code held in nibble n (0..31) of
+// the four decoded registers {even(word0), odd(word0), even(word1), odd(word1)}.
+TQ_HD int nibble_position(int n) {
+  const int r = n >> 3, m = n & 7;
+  return 16 * (r >> 1) + 2 * m + (r & 1);
+}
+
+// ---- activation layout for the matrix cores (see tq_common.h for the operand layout)
+
+// Byte offset, inside one 128-K chunk of a B column (128 bytes laid out as the
+// four lanes' 32-byte operands), of canonical K index k (0..127).
+TQ_HD int bchunk_offset(int k) {
+  return k < 64 ? (k >> 4) * 32 + (k & 15) : ((k - 64) >> 4) * 32 + 16 + (k & 15);
+}
+
+// Canonical K (0..127) of weight `pos` (0..31) of block `beta` (0..3) of a
+// chunk, given the decoder's nibble order (see nibble_position).
+TQ_HD int canonical_k(int beta, int pos) {
+  const int w = pos >> 4, q = pos & 15;
+  const int n = 8 * (2 * w + (q & 1)) + (q >> 1);
+  return 32 * beta + n;
+}
+
+}  // namespace tq

@@ -160,6 +160,18 @@ class MoELayer:
     gate_w: np.ndarray       # float32 [T, k]
 
 
+def moe_batch(cfg: MoEConfig, layer_id: int = 0, rep: int = 0, n_exp: Optional[int] = None):
+    """The routed batch of one step: x [T, hidden], ids [T, k], gate weights [T, k]."""
+    E = cfg.n_exp if n_exp is None else n_exp
+    c = cfg.config_id
+    x = activations(rng(c, T_X, layer_id, rep), cfg.T, cfg.hidden, cfg.x_bf16)
+    if cfg.zipf:
+        ids, w = routing_zipf(rng(c, T_ROUTE, layer_id, rep), cfg.T, E, min(cfg.k, E))
+    else:
+        ids, w = routing_topk(rng(c, T_ROUTE, layer_id, rep), cfg.T, E, min(cfg.k, E))
+    return x, ids, w
+
+
 def moe_layer(cfg: MoEConfig, layer_id: int = 0, rep: int = 0,
               n_exp: Optional[int] = None, route_rep: Optional[int] = None) -> MoELayer:
     """All tensors of one layer instance. ``n_exp`` may shrink the expert
@@ -171,10 +183,6 @@ def moe_layer(cfg: MoEConfig, layer_id: int = 0, rep: int = 0,
     gu_e = scales(rng(c, T_SCALES_GATE_UP, layer_id, rep), E, 2 * cfg.inter, cfg.hidden)
     dn_s = symbols(rng(c, T_SYMS_DOWN, layer_id, rep), E, cfg.hidden, cfg.inter)
     dn_e = scales(rng(c, T_SCALES_DOWN, layer_id, rep), E, cfg.hidden, cfg.inter)
-    x = activations(rng(c, T_X, layer_id, rr), cfg.T, cfg.hidden, cfg.x_bf16)
-    if cfg.zipf:
-        ids, w = routing_zipf(rng(c, T_ROUTE, layer_id, rr), cfg.T, E, min(cfg.k, E))
-    else:
-        ids, w = routing_topk(rng(c, T_ROUTE, layer_id, rr), cfg.T, E, min(cfg.k, E))
+    x, ids, w = moe_batch(cfg, layer_id, rr, n_exp=E)
     return MoELayer(cfg, gu_s, gu_e, dn_s, dn_e, x, ids, w)
 
