@@ -87,10 +87,19 @@ int trellis_decode_expand(hipStream_t stream, const trellis_mat_t *w, uint8_t *c
                           uint8_t *scales_out);
 
 /*
- * Workspace bytes needed by trellis_moe_gemv for this shape. The workspace is
- * scratch owned by the caller (256-byte aligned); its contents on entry do
- * not matter. After the call completes, its first 4 bytes hold an int32: the
- * number of routing slots skipped because their expert id was >= n_mat.
+ * Workspace bytes needed by trellis_moe_gemv for this shape.
+ *
+ * Workspaces (for trellis_moe_gemv and trellis_moe_ffn) are device scratch
+ * owned by the caller, 256-byte aligned, and must be ZERO-FILLED once before
+ * their first use; every call leaves the synchronisation words zero again,
+ * so a workspace can be reused by later calls (of any shape that fits)
+ * without clearing. Each call runs as one persistent kernel whose work items
+ * wait on counters in the workspace; the waits are bounded. After a call
+ * completes:
+ *   int32 at byte 0: routing slots skipped because their expert id >= n_mat;
+ *   int32 at byte 4: nonzero if a wait timed out (results are then invalid;
+ *                    this happens only if other work keeps the kernel's
+ *                    workgroups from being resident at the same time).
  */
 size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
                                        int32_t k);
@@ -143,13 +152,13 @@ int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_up, const tr
 
 /*
  * trellis_moe_ffn_timed -- trellis_moe_ffn that also records HIP events on
- * `stream` at its stage boundaries, for timing each kernel in place:
- *   events[0] before the routing / activation prep kernel,
- *   events[1] before the gate_up + SwiGLU kernel,
- *   events[2] before the down + combine kernel,
- *   events[3] after it.
- * `events` (caller-created hipEvent_t handles) may be NULL, as may any entry.
- * Same arguments, results and errors as trellis_moe_ffn otherwise.
+ * `stream` around its work, for timing the layer kernel in place:
+ *   events[0] just before the layer kernel is enqueued,
+ *   events[1] just after it.
+ * (The whole layer -- routing, activation split, gate_up + SwiGLU, down +
+ * combine -- is one persistent kernel.) `events` (caller-created hipEvent_t
+ * handles) may be NULL, as may either entry. Same arguments, results and
+ * errors as trellis_moe_ffn otherwise.
  */
 typedef struct ihipEvent_t *hipEvent_t;
 int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,

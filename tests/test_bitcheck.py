@@ -88,3 +88,28 @@ def test_activation_layout_is_a_bijection(bc):
         lane_group, byte = divmod(offs[k], 32)
         # bytes 0..15 of lane group g hold k = 16g..16g+15, bytes 16..31 hold k = 64+16g..
         assert k == (16 * lane_group + byte if byte < 16 else 64 + 16 * lane_group + byte - 16)
+
+
+def test_activation_column_layout(bc):
+    """Physical block b of a row feeds matrix-core step 2*(b//8) + b%2 as K-block
+    (b%8)//2, which is what lane-group g reads when it loads blocks 8j+2g, 8j+2g+1.
+    Over a whole column the weight positions map one-to-one onto bytes."""
+    bc.tq_bitcheck_act_offset.argtypes = [ctypes.c_int, ctypes.c_int]
+    bc.tq_bitcheck_act_offset.restype = ctypes.c_int
+    bc.tq_bitcheck_act_scale_index.argtypes = [ctypes.c_int]
+    bc.tq_bitcheck_act_scale_index.restype = ctypes.c_int
+    nb = 96
+    offs = [bc.tq_bitcheck_act_offset(b, p) for b in range(nb) for p in range(32)]
+    assert sorted(offs) == list(range(nb * 32))
+    sidx = [bc.tq_bitcheck_act_scale_index(b) for b in range(nb)]
+    assert sorted(sidx) == list(range(nb))
+    for j in range(nb // 8):
+        for g in range(4):
+            for h in range(2):
+                b = 8 * j + 2 * g + h
+                step = 2 * j + h
+                assert sidx[b] == 4 * step + g
+                # the block's 32 bytes sit in lane-group g's halves of the step's chunk
+                got = sorted(bc.tq_bitcheck_act_offset(b, p) - 128 * step for p in range(32))
+                assert got == list(range(16 * g, 16 * g + 16)) + list(range(64 + 16 * g, 64 + 16 * g + 16)) or \
+                    got == sorted(bc.tq_bitcheck_bchunk_offset(32 * g + n) for n in range(32))

@@ -160,7 +160,7 @@ def gemv_workspace(n_mat, rows, cols, T, k, device="cuda"):
     n = lib().trellis_moe_gemv_workspace_size(n_mat, rows, cols, T, k)
     if n == 0:
         raise TrellisError(-1, "trellis_moe_gemv_workspace_size")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)   # zero-filled before first use
 
 
 def ffn_workspace(n_exp, hidden, inter, T, k, device="cuda"):
@@ -168,7 +168,7 @@ def ffn_workspace(n_exp, hidden, inter, T, k, device="cuda"):
     n = lib().trellis_moe_ffn_workspace_size(n_exp, hidden, inter, T, k)
     if n == 0:
         raise TrellisError(-1, "trellis_moe_ffn_workspace_size")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)   # zero-filled before first use
 
 
 def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,

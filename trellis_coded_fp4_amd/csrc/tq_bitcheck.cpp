@@ -19,3 +19,5 @@ extern "C" void tq_bitcheck_natural(uint32_t g, uint32_t prev, uint32_t *lo, uin
 extern "C" int tq_bitcheck_nibble_position(int n) { return tq::nibble_position(n); }
 extern "C" int tq_bitcheck_canonical_k(int beta, int pos) { return tq::canonical_k(beta, pos); }
 extern "C" int tq_bitcheck_bchunk_offset(int k) { return tq::bchunk_offset(k); }
+extern "C" int tq_bitcheck_act_offset(int b, int pos) { return tq::act_offset(b, pos); }
+extern "C" int tq_bitcheck_act_scale_index(int b) { return tq::act_scale_index(b); }

@@ -114,4 +114,23 @@ TQ_HD int canonical_k(int beta, int pos) {
   return 32 * beta + n;
 }
 
+// Which matrix-core step consumes a 32-weight block of a row, and as which of
+// its four K-blocks. A lane of lane-group g loads 16 bytes = physical blocks
+// 8j+2g and 8j+2g+1 of its row ("piece" j) and feeds them to steps 2j and
+// 2j+1; so physical block b goes to step 2*(b/8) + b%2 as K-block (b%8)/2.
+TQ_HD int block_step(int b) { return 2 * (b >> 3) + (b & 1); }
+TQ_HD int block_beta(int b) { return (b & 7) >> 1; }
+
+// Byte offset of weight `pos` of physical block `b` inside one activation
+// column laid out as consecutive 128-byte step chunks.
+TQ_HD int act_offset(int b, int pos) {
+  return block_step(b) * 128 + bchunk_offset(canonical_k(block_beta(b), pos));
+}
+
+// Index of the UE8M0 byte of physical block `b` in a column's scale array.
+TQ_HD int act_scale_index(int b) { return block_step(b) * 4 + block_beta(b); }
+
+// Matrix-core steps for a row of nb blocks (pieces of 8 blocks, two steps each).
+TQ_HD int steps_for_blocks(int nb) { return 2 * ((nb + 7) >> 3); }
+
 }  // namespace tq
