@@ -17,23 +17,28 @@
 //                  SwiGLU over 32 gate rows and the matching 32 up rows,
 //                  writing h (bf16) and its FP8 hi/lo copy (gate weight
 //                  folded in) for stage 2.
-//   stage-2 items  16 output rows summed over all active experts; columns =
-//                  tokens. Deterministic, no atomics on outputs.
-// Stage-1 items wait (spin on a device counter) for all prep items, stage-2
-// items for all stage-1 items (or prep items when there is no stage 1); each
-// item issues its weight loads before waiting. The grid never exceeds the
-// number of co-resident workgroups, so every wait is for a running
-// workgroup; waits are bounded and set an error flag on timeout. The last
-// workgroup to finish publishes the status words and clears the counters.
+//   stage-2 items  16 output rows summed over all active experts (one expert
+//                  per wave at a time); columns = tokens. Deterministic, no
+//                  atomics on outputs.
+// Stage-1 items wait for all prep items, stage-2 items for all stage-1 items
+// (or prep items when there is no stage 1). Every item issues all of its
+// weight loads before it waits. Cross-workgroup data (activation splits, h)
+// is written with device-coherent stores and read with device-coherent
+// loads, so a dependency costs a store-completion wait and a counter, not a
+// cache writeback or invalidate. The grid never exceeds the co-resident
+// workgroup count, so every wait is for running work; waits are bounded and
+// set an error word on timeout. A workgroup publishes its finished prep and
+// stage-1 items in one count when it moves on; the last workgroup out
+// publishes the status words and clears the counters.
 //
 // Weight streaming: a wave owns one 16-row tile over the full K. Lane
 // (row i, lane-group g) loads "piece" j = 16 bytes = blocks 8j+2g, 8j+2g+1 of
 // its row, and feeds them to matrix-core steps 2j and 2j+1 as K-block g (the
-// activations are laid out to match). A wave instruction therefore reads 16
-// rows x 64 contiguous bytes; all of a tile's pieces (up to 16, K <= 4096 per
-// pass) are in flight before the first decode. The decoder history of a
-// block is the word before it: from the neighbouring lane-group's piece via
-// ds_bpermute, or from the previous piece.
+// activations are laid out to match). A wave instruction reads 16 rows x 64
+// contiguous bytes; all pieces of a tile (up to 16, K <= 4096 per pass) are
+// issued at once. The decoder history of a block is the word before it: from
+// the neighbouring lane-group's piece via ds_bpermute, or the previous piece.
+// Activation columns are staged in LDS before the matrix-core loop.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -49,7 +54,10 @@ constexpr int kMaxT = 32;
 constexpr int kMaxK = 32;
 constexpr int kMaxSlots = 1024;
 constexpr int kMaxExperts = 1024;
-constexpr unsigned kSpinLimit = 1u << 20;   // polls (each a device-coherent load + short sleep)
+constexpr int kPieceMax = 16;               // pieces per pass: 16 x 256 weights
+constexpr unsigned kSpinLimit = 1u << 20;   // polls (device-coherent load + sleep)
+constexpr int kBBytes = 32 * 1024;          // LDS for staged activation columns (codes)
+constexpr int kBScaleBytes = kBBytes / 32;  // and their UE8M0 scales
 
 enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 
@@ -113,42 +121,60 @@ struct Shared {
   int slots[kMaxSlots];
   int wcnt[kWaves];
   int n_active;
-  int n_slots;
-  float red[kWaves * 4 * 256];  // per-wave accumulator dumps (NT <= 4)
+  // Staged activation columns (step-chunk layout: steps x 128 code bytes per
+  // column) and their scales (steps x 4); after the matrix-core loop the code
+  // area is reused for the per-wave accumulator dumps.
+  uint8_t bq[kBBytes] __attribute__((aligned(16)));
+  uint8_t bs[kBScaleBytes] __attribute__((aligned(16)));
 };
+static_assert(kWaves * 4 * 256 * sizeof(float) <= kBBytes, "accumulator dump must fit the column area");
 
-// ---------------------------------------------------------------- small helpers
+// ---------------------------------------------------------------- helpers
 
 __device__ __forceinline__ float load_x(const void *x, int bf16, size_t i) {
   return bf16 ? bf16_to_f32(((const uint16_t *)x)[i]) : ((const float *)x)[i];
 }
 
-__device__ __forceinline__ void signal(int *ctr) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    atomicAdd(ctr, 1);
-  }
+// Device-coherent accesses for data handed between workgroups.
+__device__ __forceinline__ void st_dc(uint8_t *p, uint32_t v) {
+  __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dc64(const uint8_t *p) {
+  return __hip_atomic_load((uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dc32(const uint8_t *p) {
+  return __hip_atomic_load((uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void wait_for(int *ctr, int target, int *err) {
+// Publish `n` finished items: every wave's device-coherent stores complete,
+// then one thread bumps the counter.
+__device__ __forceinline__ void signal_n(int *ctr, int n) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (once per workgroup and counter: `seen` remembers) until the counter
+// reaches `target`. Bounded: on timeout the error word is set.
+__device__ __forceinline__ void wait_for(int *ctr, int target, int *err, bool &seen) {
+  if (seen) return;
   if (threadIdx.x == 0) {
     unsigned spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(4);
       if (++spins > kSpinLimit) {
-        atomicOr(err, 1);
+        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    __threadfence();
   }
   __syncthreads();
+  seen = true;
 }
 
 // Two-term FP8 split of one 32-value block held by the 32 lanes of a
-// half-wave (lane = position in the block); stores codes and scales of
-// physical block `blk` into one column pair.
+// half-wave (lane = position in the block); device-coherent stores of the
+// codes and scales of physical block `blk` into one column pair.
 __device__ __forceinline__ void quantize_block(float v, int pos, int blk, uint8_t *q_hi, uint8_t *q_lo,
                                                uint8_t *s_hi, uint8_t *s_lo, bool store) {
   float amax = fabsf(v);
@@ -164,11 +190,11 @@ __device__ __forceinline__ void quantize_block(float v, int pos, int blk, uint8_
   const uint32_t lo = f32_to_e4m3(ldexpf(r, -El));
   if (store) {
     const int off = act_offset(blk, pos);
-    q_hi[off] = (uint8_t)hi;
-    q_lo[off] = (uint8_t)lo;
+    st_dc(q_hi + off, hi);
+    st_dc(q_lo + off, lo);
     if (pos == 0) {
-      s_hi[act_scale_index(blk)] = (uint8_t)(E + 127);
-      s_lo[act_scale_index(blk)] = (uint8_t)(El + 127);
+      st_dc(s_hi + act_scale_index(blk), (uint32_t)(E + 127));
+      st_dc(s_lo + act_scale_index(blk), (uint32_t)(El + 127));
     }
   }
 }
@@ -188,131 +214,106 @@ __device__ __forceinline__ float folded_gate(const Shared &S, int slot, int k, i
   return g;
 }
 
+// Copy activation columns into LDS: LDS column c <- global column src_col(c)
+// (steps x 128 code bytes, steps x 4 scale bytes), device-coherent loads.
+// `first`/`stride` split the work among the threads that call it.
+template <typename ColMap>
+__device__ __forceinline__ void copy_columns(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
+                                             int steps, int ncols, ColMap src_col, int first, int stride) {
+  const int per_col = steps * 16;   // 8-byte pieces per column
+  for (int idx = first; idx < ncols * per_col; idx += stride) {
+    const int c = idx / per_col, p = idx - c * per_col;
+    const size_t col = (size_t)src_col(c);
+    *(uint64_t *)(lq + ((size_t)c * per_col + p) * 8) = ld_dc64(gq + (col * per_col + p) * 8);
+  }
+  for (int idx = first; idx < ncols * steps; idx += stride) {
+    const int c = idx / steps, p = idx - c * steps;
+    const size_t col = (size_t)src_col(c);
+    *(uint32_t *)(ls + ((size_t)c * steps + p) * 4) = ld_dc32(gs + (col * steps + p) * 4);
+  }
+}
+
 // ---------------------------------------------------------------- weight tiles
 
-constexpr int kRing = 8;   // pieces in flight per wave (8 x 1 KiB per wave instruction stream)
-
-struct Piece {
-  uint4 a;       // words 16j+4g .. 16j+4g+3 of this lane's row
-  uint32_t sc;   // UE8M0 of blocks 8j+2g (byte 0) and 8j+2g+1 (byte 1)
+struct Tile {
+  uint4 a[kPieceMax];       // piece j: words 16j+4g .. 16j+4g+3 of this lane's row
+  uint32_t sc[kPieceMax];   // piece j: UE8M0 of blocks 8j+2g (byte 0) and 8j+2g+1 (byte 1)
 };
 
-// Load piece j of one row (`row` null: an invalid tile, all zeros).
-// ALIGNED: words per row % 4 == 0 (so blocks per row are even): one 16-byte
-// load and one 2-byte scale load per lane, a piece is either whole or past
-// the row end. Otherwise pieces may be half-filled and rows 8-byte aligned.
+// Issue the loads of pieces [p0, p0 + np) of one row into t (`row` null for
+// an invalid tile: zeros). ALIGNED: words per row % 4 == 0, so a piece is one
+// 16-byte load and one 2-byte scale load, whole or past the row end.
 template <bool ALIGNED>
-__device__ __forceinline__ void load_piece(Piece &p, const uint32_t *row, const uint8_t *srow, int wpr, int nb,
-                                           int j, int g) {
-  const int wi = 16 * j + 4 * g;
-  const int b = 8 * j + 2 * g;
-  if (ALIGNED) {
-    const bool ok = row && wi < wpr;
-    p.a = ok ? *(const uint4 *)(row + wi) : make_uint4(0u, 0u, 0u, 0u);
-    p.sc = ok ? (uint32_t)*(const uint16_t *)(srow + b) : 0x7F7Fu;
-  } else {
-    p.a = make_uint4(0u, 0u, 0u, 0u);
-    p.sc = 0x7F7Fu;
-    if (row && wi < wpr) {
-      const uint2 lo = *(const uint2 *)(row + wi);
-      const uint2 hi = wi + 2 < wpr ? *(const uint2 *)(row + wi + 2) : make_uint2(0u, 0u);
-      p.a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      p.sc = (uint32_t)srow[b] | ((b + 1 < nb ? (uint32_t)srow[b + 1] : 0x7Fu) << 8);
+__device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, const uint8_t *srow, int wpr, int nb,
+                                          int p0, int np, int g) {
+#pragma unroll
+  for (int q = 0; q < kPieceMax; ++q) {
+    const int j = p0 + q;
+    const int wi = 16 * j + 4 * g;
+    const int b = 8 * j + 2 * g;
+    const bool ok = q < np && row && wi < wpr;
+    if (ALIGNED) {
+      t.a[q] = ok ? *(const uint4 *)(row + wi) : make_uint4(0u, 0u, 0u, 0u);
+      t.sc[q] = ok ? (uint32_t)*(const uint16_t *)(srow + b) : 0x7F7Fu;
+    } else {
+      t.a[q] = make_uint4(0u, 0u, 0u, 0u);
+      t.sc[q] = 0x7F7Fu;
+      if (ok) {
+        const uint2 lo = *(const uint2 *)(row + wi);
+        const uint2 hi = wi + 2 < wpr ? *(const uint2 *)(row + wi + 2) : make_uint2(0u, 0u);
+        t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        t.sc[q] = (uint32_t)srow[b] | ((b + 1 < nb ? (uint32_t)srow[b + 1] : 0x7Fu) << 8);
+      }
     }
   }
 }
 
-struct BCol {
-  const uint8_t *q;     // this lane's 32-byte operand of step 0 (advance 128 B per step)
-  const uint8_t *s;     // this lane's scale byte of step 0 (advance 4 B per step)
-  bool on;
-};
-
-__device__ __forceinline__ void load_b(v8i &b, uint32_t &s, const BCol &c, int step) {
-  if (c.on) {
-    const uint4 *p = (const uint4 *)(c.q + step * 128);
-    const uint4 u0 = p[0], u1 = p[1];
-    b = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-    s = c.s[step * 4];
-  } else {
-    b = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    s = 127u;
-  }
-}
-
-// A wave's 16-row tile streamed through a ring of kRing pieces: the first
-// kRing pieces are issued by start_tile (before any wait), and each piece
-// consumed refills its slot kRing pieces ahead.
-struct TileStream {
-  const uint32_t *row;
-  const uint8_t *srow;
-  int wpr, nb, J;
-  Piece ring[kRing];
-};
-
-template <bool ALIGNED>
-__device__ __forceinline__ void start_tile(TileStream &ts, const uint32_t *row, const uint8_t *srow, int wpr,
-                                           int nb, int g) {
-  ts.row = row;
-  ts.srow = srow;
-  ts.wpr = wpr;
-  ts.nb = nb;
-  ts.J = (nb + 7) >> 3;
-#pragma unroll
-  for (int r = 0; r < kRing; ++r) {
-    if (r < ts.J) load_piece<ALIGNED>(ts.ring[r], row, srow, wpr, nb, r, g);
-  }
-}
-
-// Decode the tile and accumulate it against the B columns (all of K).
-template <int NT, bool ALIGNED>
-__device__ __forceinline__ void mma_tile(TileStream &ts, const BCol (&bc)[NT], v4f (&acc)[NT], int lane) {
+// Decode pieces [p0, p0 + np) of the tile and accumulate them against NT
+// N-tiles of LDS-staged columns. Lane (column jc = lane & 15, lane-group g):
+// N-tile n reads LDS column col0[n] (or zeros when !on[n]).
+template <int NT>
+__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const uint8_t *lq, const uint8_t *ls,
+                                         int steps, const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
+                                         uint32_t &carry, int lane) {
   const int g = lane >> 4;
   const int src = ((lane - 16) & 63) << 2;   // lane-group g-1 (mod 4), same row
-  v8i bq[NT], bn[NT];
-  uint32_t bs[NT], bsn[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) load_b(bq[n], bs[n], bc[n], 0);
-  uint32_t carry = 0u;
-  for (int base = 0; base < ts.J; base += kRing) {
+  for (int q = 0; q < kPieceMax; ++q) {
+    if (q < np) {
+      const int j = p0 + q;
+      const uint4 a = t.a[q];
+      const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
+      const uint32_t hist = g == 0 ? carry : rot;
+      carry = rot;
 #pragma unroll
-    for (int r = 0; r < kRing; ++r) {
-      const int j = base + r;
-      if (j < ts.J) {
-        const uint4 a = ts.ring[r].a;
-        const uint32_t sc = ts.ring[r].sc;
-        if (j + kRing < ts.J) load_piece<ALIGNED>(ts.ring[r], ts.row, ts.srow, ts.wpr, ts.nb, j + kRing, g);
-        const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
-        const uint32_t hist = g == 0 ? carry : rot;
-        carry = rot;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int step = 2 * j + hh;
+        v8i B[NT];
+        uint32_t sb[NT];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int step = 2 * j + hh;
-          const bool more = hh == 0 || j + 1 < ts.J;
-          if (more) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) load_b(bn[n], bsn[n], bc[n], step + 1);
+        for (int n = 0; n < NT; ++n) {
+          if (on[n]) {
+            const uint4 *p = (const uint4 *)(lq + ((size_t)col[n] * steps + step) * 128 + g * 32);
+            const uint4 u0 = p[0], u1 = p[1];
+            B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+            sb[n] = ls[((size_t)col[n] * steps + step) * 4 + g];
+          } else {
+            B[n] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            sb[n] = 127u;
           }
-          const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
-          const nib2 d0 = decode_word(w0, hw);
-          const nib2 d1 = decode_word(w1, w0);
-          const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        }
+        const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
+        const nib2 d0 = decode_word(w0, hw);
+        const nib2 d1 = decode_word(w1, w0);
+        const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (hh == 0)
-              acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bq[n], acc[n], 4, 0, 0, (int)sc, 0,
-                                                                       (int)bs[n]);
-            else
-              acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bq[n], acc[n], 4, 0, 1, (int)sc, 0,
-                                                                       (int)bs[n]);
-          }
-          if (more) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              bq[n] = bn[n];
-              bs[n] = bsn[n];
-            }
-          }
+        for (int n = 0; n < NT; ++n) {
+          if (hh == 0)
+            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)t.sc[q], 0,
+                                                                     (int)sb[n]);
+          else
+            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 1, (int)t.sc[q], 0,
+                                                                     (int)sb[n]);
         }
       }
     }
@@ -325,12 +326,15 @@ __device__ __forceinline__ int d_index(int wave, int nt, int row, int col) {
   return ((wave * NT + nt) * 64 + lane) * 4 + (row & 3);
 }
 
+// Dump the wave accumulators into the (now free) column area; the caller
+// synchronises before and after.
 template <int NT>
 __device__ __forceinline__ void dump_acc(Shared &S, const v4f (&acc)[NT], int wave, int lane) {
+  float *red = (float *)S.bq;
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S.red[((wave * NT + n) * 64 + lane) * 4 + r] = acc[n][r];
+    for (int r = 0; r < 4; ++r) red[((wave * NT + n) * 64 + lane) * 4 + r] = acc[n][r];
 }
 
 // ---------------------------------------------------------------- work items
@@ -345,7 +349,7 @@ __device__ __forceinline__ void prep_item(const LayerArgs &a, Shared &S, int v) 
   if (tid == 0) {
     int skipped = 0;
     for (int s = s_lo; s < s_hi; ++s) skipped += S.ids[s] >= a.E;
-    if (skipped) atomicAdd(&a.sync[SY_SKIP], skipped);
+    if (skipped) __hip_atomic_fetch_add(&a.sync[SY_SKIP], skipped, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   for (int s = s_lo; s < s_hi; ++s) {
     const int e = S.ids[s];
@@ -356,13 +360,13 @@ __device__ __forceinline__ void prep_item(const LayerArgs &a, Shared &S, int v) 
       for (int c = tid; c < a.inter; c += kThreads) a.h[(size_t)s * a.inter + c] = 0;
     if (a.mode == MODE_FFN) {
       // K padding of the slot's down-projection activations: zero codes, finite scales
-      const int nbh = a.inter / 32;
-      for (int idx = tid; idx < 2 * (4 * a.h_steps - nbh) * 32; idx += kThreads) {
-        const int hl = idx / ((4 * a.h_steps - nbh) * 32), rem = idx % ((4 * a.h_steps - nbh) * 32);
+      const int nbh = a.inter / 32, npad = 4 * a.h_steps - nbh;
+      for (int idx = tid; idx < 2 * npad * 32; idx += kThreads) {
+        const int hl = idx / (npad * 32), rem = idx % (npad * 32);
         const int blk = nbh + rem / 32, pos = rem % 32;
         const size_t col = (size_t)s * 2 + hl;
-        a.hq[col * a.h_steps * 128 + act_offset(blk, pos)] = 0;
-        if (pos == 0) a.hs[col * a.h_steps * 4 + act_scale_index(blk)] = 127;
+        st_dc(a.hq + col * a.h_steps * 128 + act_offset(blk, pos), 0u);
+        if (pos == 0) st_dc(a.hs + col * a.h_steps * 4 + act_scale_index(blk), 127u);
       }
     }
   }
@@ -418,54 +422,63 @@ __device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
 }
 
 template <int NT, bool ALIGNED>
-__device__ __forceinline__ void stage1_item(const LayerArgs &a, Shared &S, int item) {
+__device__ __forceinline__ void stage1_item(const LayerArgs &a, Shared &S, int item, bool &prep_seen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int ai = item / a.n_rg1, rg = item % a.n_rg1;
-  if (ai >= S.n_active) {
-    signal(&a.sync[SY_S1]);
-    return;
-  }
+  if (ai >= S.n_active) return;   // no such active expert: nothing to do
   const int e = S.active[ai];
   const bool ffn = a.mode == MODE_FFN;
   const int r0 = ffn ? (wave < 2 ? 0 : a.inter) + rg * 32 + 16 * (wave & 1) : rg * 64 + 16 * wave;
   const bool tile_ok = r0 < a.rows1;
-  const int wpr = a.cols1 / 16, nb = a.cols1 / 32;
+  const int wpr = a.cols1 / 16, nb = a.cols1 / 32, J = (nb + 7) >> 3;
   const size_t row = (size_t)e * a.rows1 + (tile_ok ? r0 + i16 : 0);
   const uint32_t *rowp = tile_ok ? a.w1 + row * wpr : nullptr;
   const uint8_t *srow = a.s1 + row * nb;
-  TileStream ts;
-  start_tile<ALIGNED>(ts, rowp, srow, wpr, nb, g);   // in flight while we gather slots and wait
+  Tile tl;
+  load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, 0, min(J, kPieceMax), g);   // in flight while we wait
   const int ne = gather_slots(S, e, a.T * a.k);
-  wait_for(&a.sync[SY_PREP], a.n_prep, &a.sync[SY_ERR]);
+  wait_for(&a.sync[SY_PREP], a.n_prep, &a.sync[SY_ERR], prep_seen);
 
-  for (int cg = 0; cg * NT * 8 < ne; ++cg) {
-    BCol bc[NT];
+  // slots per column group: whatever fits the LDS column area (<= NT * 8)
+  const int steps = a.x_steps;
+  const int gsz = min(NT * 8, kBBytes / (2 * steps * 128));
+  for (int c0 = 0; c0 < ne; c0 += gsz) {
+    const int ncol = min(ne - c0, gsz);
+    // LDS column c = slot (c0 + c/2)'s hi (even c) or lo (odd c) term
+    copy_columns(S.bq, S.bs, a.xq, a.xs, steps, 2 * ncol,
+                 [&](int c) {
+                   const int slot = S.slots[c0 + (c >> 1)];
+                   return (a.prep_per_slot ? slot : slot / a.k) * 2 + (c & 1);
+                 },
+                 threadIdx.x, kThreads);
+    __syncthreads();
+    int col[NT];
+    bool on[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const int c = cg * NT * 8 + n * 8 + (i16 >> 1);
-      bc[n].on = c < ne;
-      const int slot = bc[n].on ? S.slots[c] : 0;
-      const int vec = a.prep_per_slot ? slot : slot / a.k;
-      const size_t col = (size_t)vec * 2 + (i16 & 1);
-      bc[n].q = a.xq + col * a.x_steps * 128 + g * 32;
-      bc[n].s = a.xs + col * a.x_steps * 4 + g;
+      col[n] = n * 16 + i16;
+      on[n] = n * 8 + (i16 >> 1) < ncol;
     }
     v4f acc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (cg > 0) start_tile<ALIGNED>(ts, rowp, srow, wpr, nb, g);
-    mma_tile<NT, ALIGNED>(ts, bc, acc, lane);
+    uint32_t carry = 0u;
+    for (int p0 = 0; p0 < J; p0 += kPieceMax) {
+      if (p0 > 0 || c0 > 0) load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, p0, min(J - p0, kPieceMax), g);
+      mma_tile<NT>(tl, p0, min(J - p0, kPieceMax), S.bq, S.bs, steps, col, on, acc, carry, lane);
+    }
+    __syncthreads();   // everyone is done with the staged columns
     dump_acc<NT>(S, acc, wave, lane);
     __syncthreads();
-    const int ncol = min(ne - cg * NT * 8, NT * 8);
+    const float *red = (const float *)S.bq;
     if (!ffn) {
       for (int idx = threadIdx.x; idx < ncol * 64; idx += kThreads) {
         const int c = idx >> 6, rr = idx & 63, w = rr >> 4, ri = rr & 15;
         if (rg * 64 + rr >= a.rows1) continue;
         const int n = c >> 3, cj = 2 * (c & 7);
-        const float v = S.red[d_index<NT>(w, n, ri, cj)] + S.red[d_index<NT>(w, n, ri, cj + 1)];
-        a.y[(size_t)S.slots[cg * NT * 8 + c] * a.rows1 + rg * 64 + rr] = v;
+        const float v = red[d_index<NT>(w, n, ri, cj)] + red[d_index<NT>(w, n, ri, cj + 1)];
+        a.y[(size_t)S.slots[c0 + c] * a.rows1 + rg * 64 + rr] = v;
       }
     } else {
       for (int base = 0; base < ncol; base += kThreads / 32) {
@@ -475,11 +488,11 @@ __device__ __forceinline__ void stage1_item(const LayerArgs &a, Shared &S, int i
         int slot = 0;
         if (live) {
           const int n = c >> 3, cj = 2 * (c & 7), w = i >> 4, ri = i & 15;
-          const float gate = S.red[d_index<NT>(w, n, ri, cj)] + S.red[d_index<NT>(w, n, ri, cj + 1)];
-          const float up = S.red[d_index<NT>(w + 2, n, ri, cj)] + S.red[d_index<NT>(w + 2, n, ri, cj + 1)];
+          const float gate = red[d_index<NT>(w, n, ri, cj)] + red[d_index<NT>(w, n, ri, cj + 1)];
+          const float up = red[d_index<NT>(w + 2, n, ri, cj)] + red[d_index<NT>(w + 2, n, ri, cj + 1)];
           const float silu = gate / (1.0f + expf(-gate));
           const uint16_t hb = f32_to_bf16_rne(silu * up);
-          slot = S.slots[cg * NT * 8 + c];
+          slot = S.slots[c0 + c];
           a.h[(size_t)slot * a.inter + rg * 32 + i] = hb;
           hv = bf16_to_f32(hb) * folded_gate(S, slot, a.k, a.E);
         }
@@ -490,61 +503,83 @@ __device__ __forceinline__ void stage1_item(const LayerArgs &a, Shared &S, int i
     }
     __syncthreads();
   }
-  signal(&a.sync[SY_S1]);
 }
 
+// Stage 2: wave w handles experts w, w+4, ... of the active list. Each wave
+// stages its own expert's columns (the tokens routed to it) in its quarter of
+// the column area, in token groups that fit.
 template <int NT, bool ALIGNED>
-__device__ __forceinline__ void stage2_item(const LayerArgs &a, Shared &S, int rt) {
+__device__ __forceinline__ void stage2_item(const LayerArgs &a, Shared &S, int rt, bool &dep_seen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
-  const int wpr = a.cols2 / 16, nb = a.cols2 / 32;
+  const int wpr = a.cols2 / 16, nb = a.cols2 / 32, J = (nb + 7) >> 3;
   const int n_act = S.n_active;
   const bool ffn = a.mode == MODE_FFN;
-  const uint8_t *bq = ffn ? a.hq : a.xq;
-  const uint8_t *bsc = ffn ? a.hs : a.xs;
-  const int bsteps = ffn ? a.h_steps : a.x_steps;
+  const uint8_t *gq = ffn ? a.hq : a.xq;
+  const uint8_t *gs = ffn ? a.hs : a.xs;
+  const int steps = ffn ? a.h_steps : a.x_steps;
+  uint8_t *lq = S.bq + wave * (kBBytes / kWaves);
+  uint8_t *ls = S.bs + wave * (kBScaleBytes / kWaves);
+  const int tsz = max(1, min(NT * 8, kBBytes / kWaves / (2 * steps * 128)));   // tokens per group
   v4f acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-  TileStream ts;
-  bool waited = false;
-  for (int ai = wave; ai < n_act || !waited; ai += kWaves) {
+  Tile tl;
+  for (int ai = wave; ai < n_act || !dep_seen; ai += kWaves) {
     const bool have = ai < n_act;
     const int e = have ? S.active[ai] : 0;
     const size_t row = (size_t)e * a.rows2 + rt * 16 + i16;
     const uint32_t *rowp = have ? a.w2 + row * wpr : nullptr;
     const uint8_t *srow = a.s2 + row * nb;
-    if (have) start_tile<ALIGNED>(ts, rowp, srow, wpr, nb, g);
-    if (!waited) {
+    if (have) load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, 0, min(J, kPieceMax), g);
+    if (!dep_seen) {
       // every wave reaches this once (block-wide barrier inside)
-      if (ffn) wait_for(&a.sync[SY_S1], a.n_s1, &a.sync[SY_ERR]);
-      else wait_for(&a.sync[SY_PREP], a.n_prep, &a.sync[SY_ERR]);
-      waited = true;
+      if (ffn) wait_for(&a.sync[SY_S1], a.n_s1, &a.sync[SY_ERR], dep_seen);
+      else wait_for(&a.sync[SY_PREP], a.n_prep, &a.sync[SY_ERR], dep_seen);
     }
     if (!have) break;
-    BCol bc[NT];
+    // tokens [t0, t0 + tsz) per group, LDS column 2 * (t - t0) + hilo; the
+    // group's matrix-core steps add into the batch-wide accumulators with
+    // zero activations for tokens outside the group
+    auto slot_of = [&](int t) {   // first slot of (token, e): duplicates were folded into it
+      for (int jj = 0; jj < a.k; ++jj)
+        if (S.ids[t * a.k + jj] == e) return t * a.k + jj;
+      return -1;
+    };
+    for (int t0 = 0; t0 < a.T; t0 += tsz) {
+      const int nt_tok = min(a.T - t0, tsz);
+      copy_columns(lq, ls, gq, gs, steps, 2 * nt_tok,
+                   [&](int c) {
+                     const int s = slot_of(t0 + (c >> 1));
+                     return (s < 0 ? 0 : s) * 2 + (c & 1);
+                   },
+                   lane, 64);
+      int col[NT];
+      bool on[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int t = n * 8 + (i16 >> 1);
-      int slot = -1;
-      if (t < a.T)
-        for (int jj = 0; jj < a.k; ++jj)
-          if (S.ids[t * a.k + jj] == e) { slot = t * a.k + jj; break; }
-      bc[n].on = slot >= 0;
-      const size_t col = (size_t)(slot < 0 ? 0 : slot) * 2 + (i16 & 1);
-      bc[n].q = bq + col * bsteps * 128 + g * 32;
-      bc[n].s = bsc + col * bsteps * 4 + g;
+      for (int n = 0; n < NT; ++n) {
+        const int tok = n * 8 + (i16 >> 1);
+        const bool in = tok >= t0 && tok < t0 + nt_tok;
+        on[n] = in && slot_of(tok) >= 0;
+        col[n] = in ? 2 * (tok - t0) + (i16 & 1) : 0;
+      }
+      uint32_t carry = 0u;
+      for (int p0 = 0; p0 < J; p0 += kPieceMax) {
+        if (p0 > 0 || t0 > 0) load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, p0, min(J - p0, kPieceMax), g);
+        mma_tile<NT>(tl, p0, min(J - p0, kPieceMax), lq, ls, steps, col, on, acc, carry, lane);
+      }
     }
-    mma_tile<NT, ALIGNED>(ts, bc, acc, lane);
   }
+  __syncthreads();   // all waves done with their staged columns
   dump_acc<NT>(S, acc, wave, lane);
   __syncthreads();
+  const float *red = (const float *)S.bq;
   for (int idx = threadIdx.x; idx < a.T * 16; idx += kThreads) {
     const int t = idx >> 4, ri = idx & 15;
     const int n = t >> 3, cj = 2 * (t & 7);
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += S.red[d_index<NT>(w, n, ri, cj)] + S.red[d_index<NT>(w, n, ri, cj + 1)];
+    for (int w = 0; w < kWaves; ++w) v += red[d_index<NT>(w, n, ri, cj)] + red[d_index<NT>(w, n, ri, cj + 1)];
     a.y[(size_t)t * a.rows2 + rt * 16 + ri] = v;
   }
   __syncthreads();
@@ -585,31 +620,40 @@ __global__ void __launch_bounds__(kThreads) k_layer(LayerArgs a) {
   }
   __syncthreads();
 
+  // Items come in index order, so a workgroup's prep items, then its stage-1
+  // items, are contiguous: their completions are published in one signal
+  // when the workgroup moves on (before it can wait on anyone), and each
+  // dependency is waited for at most once per workgroup.
   const int n_items = a.n_prep + a.n_s1 + a.n_s2;
+  int prep_done = 0, s1_done = 0;
+  bool prep_seen = false, dep_seen = false;
   for (int item = blockIdx.x; item < n_items; item += a.grid) {
     if (item < a.n_prep) {
       prep_item(a, S, item);
-      signal(&a.sync[SY_PREP]);
+      ++prep_done;
     } else if (item < a.n_prep + a.n_s1) {
-      stage1_item<NT, ALIGNED>(a, S, item - a.n_prep);
+      if (prep_done) { signal_n(&a.sync[SY_PREP], prep_done); prep_done = 0; }
+      stage1_item<NT, ALIGNED>(a, S, item - a.n_prep, prep_seen);
+      ++s1_done;
     } else {
-      stage2_item<NT, ALIGNED>(a, S, item - a.n_prep - a.n_s1);
+      if (prep_done) { signal_n(&a.sync[SY_PREP], prep_done); prep_done = 0; }
+      if (s1_done) { signal_n(&a.sync[SY_S1], s1_done); s1_done = 0; }
+      stage2_item<NT, ALIGNED>(a, S, item - a.n_prep - a.n_s1, dep_seen);
     }
     __syncthreads();
   }
+  if (prep_done) signal_n(&a.sync[SY_PREP], prep_done);
+  if (s1_done) signal_n(&a.sync[SY_S1], s1_done);
   // the last workgroup out publishes the status and clears the counters
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    if (atomicAdd(&a.sync[SY_EXIT], 1) == a.grid - 1) {
-      __threadfence();
+    if (__hip_atomic_fetch_add(&a.sync[SY_EXIT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.grid - 1) {
       const int skipped = __hip_atomic_load(&a.sync[SY_SKIP], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int err = __hip_atomic_load(&a.sync[SY_ERR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.sync[ST_SKIPPED], skipped, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.sync[ST_ERROR], err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int i = SY_PREP; i <= SY_ERR; ++i)
         __hip_atomic_store(&a.sync[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
     }
   }
 }
