@@ -1,4 +1,4 @@
-// tq_layer.hip -- fused trellis-decode mixture-of-experts layer on gfx950.
+// tq_layer.hip -- fused trellis-decode mixture-of-experts GEMV / small-batch GEMM on gfx950.
 //
 // HEPH abstract (ICLR 2027 submission page): in "fused" serving the
 // compressed streams stay resident and every weight is decoded inside the
@@ -7,38 +7,45 @@
 // UE8M0 exponents as the A scales, at every batch size: the vector ALUs do
 // the decode, the matrix cores the multiply-accumulate.
 //
-// One persistent launch per call. Workgroups take work items round-robin:
-//   prep items     one activation vector each: split into two FP8 E4M3 terms
-//                  (hi + lo, UE8M0 scale per 32) in matrix-core B layout,
-//                  optionally pre-multiplied by the slot's gate weight;
-//                  bookkeeping for dead (empty / out-of-range) slots.
-//   stage-1 items  one active expert x 64 output rows; columns = the slots
-//                  routed to the expert. Epilogue: plain per-slot output, or
-//                  SwiGLU over 32 gate rows and the matching 32 up rows,
-//                  writing h (bf16) and its FP8 hi/lo copy (gate weight
-//                  folded in) for stage 2.
-//   stage-2 items  16 output rows summed over all active experts (one expert
-//                  per wave at a time); columns = tokens. Deterministic, no
-//                  atomics on outputs.
-// Stage-1 items wait for all prep items, stage-2 items for all stage-1 items
-// (or prep items when there is no stage 1). Every item issues all of its
-// weight loads before it waits. Cross-workgroup data (activation splits, h)
-// is written with device-coherent stores and read with device-coherent
-// loads, so a dependency costs a store-completion wait and a counter, not a
-// cache writeback or invalidate. The grid never exceeds the co-resident
-// workgroup count, so every wait is for running work; waits are bounded and
-// set an error word on timeout. A workgroup publishes its finished prep and
-// stage-1 items in one count when it moves on; the last workgroup out
-// publishes the status words and clears the counters.
+// One persistent launch per call; its workgroups take work items
+// round-robin. An item is one active expert x 64 output rows (a 16-row tile
+// per wave) of a grouped GEMM whose columns are the routing slots sent to
+// that expert:
+//   stage-1 items  the first (or only) matrix; the activations are split on
+//                  the spot into two FP8 E4M3 terms (hi + lo, UE8M0 scale per
+//                  32) in matrix-core B layout in LDS. Epilogue: per-slot
+//                  output; or per-slot partial output + combine (below); or,
+//                  in a layer, SwiGLU over 32 gate rows and the matching 32
+//                  up rows, writing h (bf16) and its FP8 hi/lo split, which
+//                  is exactly one K-block of the down projection.
+//   stage-2 items  a layer's down projection; its columns are the h splits
+//                  of the expert's slots, copied into LDS once every
+//                  stage-1 item of that expert has finished.
+// Combine: per-slot partial outputs go to the workspace; the item that
+// arrives last at a 64-row output tile (a counter per tile) sums them with
+// the gate weights, in slot order, into y. No atomics touch outputs and the
+// summation order is fixed, so results are deterministic.
 //
-// Weight streaming: a wave owns one 16-row tile over the full K. Lane
-// (row i, lane-group g) loads "piece" j = 16 bytes = blocks 8j+2g, 8j+2g+1 of
-// its row, and feeds them to matrix-core steps 2j and 2j+1 as K-block g (the
-// activations are laid out to match). A wave instruction reads 16 rows x 64
-// contiguous bytes; all pieces of a tile (up to 16, K <= 4096 per pass) are
-// issued at once. The decoder history of a block is the word before it: from
-// the neighbouring lane-group's piece via ds_bpermute, or the previous piece.
-// Activation columns are staged in LDS before the matrix-core loop.
+// Synchronisation costs no grid-wide barrier: counters live one per
+// 128-byte line (device-scope atomics on one address serialise), each is
+// cleared by the last work item that reads it, so a workspace returns to
+// zero at the end of every call. Cross-workgroup data (h splits, partial
+// outputs) moves through device-coherent stores and loads; a producer waits
+// for its stores to complete before it counts. The grid never exceeds the
+// co-resident workgroup count and items run in index order, so every wait
+// is for running work; waits are bounded and set an error word on timeout.
+//
+// Weight streaming: a wave owns one 16-row tile. Lane (row i, lane-group g)
+// loads "piece" j = 16 bytes = blocks 8j+2g, 8j+2g+1 of its row and feeds
+// them to matrix-core steps 2j and 2j+1 as K-block g (the activations are
+// laid out to match). A wave instruction reads 16 rows x 64 contiguous bytes;
+// up to 16 pieces (K <= 4096) are in flight at once. The tile's UE8M0 bytes
+// are one contiguous run (rows are contiguous): they are fetched with a few
+// 16-byte loads into the wave's LDS slot instead of one 2-byte load per
+// piece. Activation loads are issued before the weight loads, because loads
+// complete in issue order. The decoder history of a block is the word before
+// it: from the neighbouring lane-group's piece via ds_bpermute, or the
+// previous piece.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -54,78 +61,96 @@ constexpr int kMaxT = 32;
 constexpr int kMaxK = 32;
 constexpr int kMaxSlots = 1024;
 constexpr int kMaxExperts = 1024;
-constexpr int kPieceMax = 16;               // pieces per pass: 16 x 256 weights
+constexpr int kPieceMax = 16;               // pieces per register window: 16 x 256 weights
 constexpr unsigned kSpinLimit = 1u << 20;   // polls (device-coherent load + sleep)
-constexpr int kBBytes = 32 * 1024;          // LDS for staged activation columns (codes)
-constexpr int kBScaleBytes = kBBytes / 32;  // and their UE8M0 scales
+constexpr int kBBytes = 32 * 1024;          // LDS for one pass of activation columns (codes)
+constexpr int kBScaleBytes = 1024;          // and their UE8M0 scales
+constexpr int kAScaleBytes = 2048;          // per wave: its tile's UE8M0 bytes (16 rows x <= 128)
+constexpr int kXPre = 16;                   // activation values per lane fetched ahead of the weights
+constexpr int kLineInts = 32;               // one counter per 128-byte line
 
 enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 
-// int words at the start of the workspace
-enum {
-  ST_SKIPPED = 0,   // public: slots skipped (expert id >= n_exp) by the last call
-  ST_ERROR = 1,     // public: nonzero if a wait timed out in the last call
-  SY_PREP = 8,      // working counters, zero between calls
-  SY_S1 = 9,
-  SY_EXIT = 10,
-  SY_SKIP = 11,
-  SY_ERR = 12,
-};
+// int words at the start of the workspace (public)
+enum { ST_SKIPPED = 0, ST_ERROR = 1 };
+
+// Timeline instrumentation, compiled in only with -DTQ_TRACE: per workgroup
+// 32 u64 slots of s_memrealtime stamps (entry, routing done, then six per
+// item: id, start, and four item-specific marks).
+#ifdef TQ_TRACE
+#define TQ_MARK(S, k) do { if (threadIdx.x == 0 && (S).trp) (S).trp[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
+static void *g_trace = nullptr;
+#else
+#define TQ_MARK(S, k) do { } while (0)
+#endif
 
 struct Layout {
-  size_t sync, xq, xs, hq, hs, total;
+  size_t status, cnt1, obs1, cnt2, yslot, hq, hs, total;
 };
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-static Layout make_layout(int x_vecs, int x_cols, int h_vecs, int h_cols) {
+// n_act: first-stage completion counters (layer only); n_rt: 64-row output
+// tiles that combine partial outputs; n_slots x y_rows partial outputs;
+// h_cols: width of the h splits (layer only).
+static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
-  L.sync = take(256);
-  const size_t xs = (size_t)steps_for_blocks(x_cols / 32);
-  L.xq = take((size_t)x_vecs * 2 * xs * 128);
-  L.xs = take((size_t)x_vecs * 2 * xs * 4);
+  L.status = take(256);
+  L.cnt1 = take((size_t)n_act * kLineInts * 4);
+  L.obs1 = take((size_t)n_act * kLineInts * 4);
+  L.cnt2 = take((size_t)n_rt * kLineInts * 4);
+  L.yslot = take((size_t)n_slots * y_rows * 4);
   const size_t hs = h_cols ? (size_t)steps_for_blocks(h_cols / 32) : 0;
-  L.hq = take((size_t)h_vecs * 2 * hs * 128);
-  L.hs = take((size_t)h_vecs * 2 * hs * 4);
+  L.hq = take((size_t)n_slots * 2 * hs * 128);
+  L.hs = take((size_t)n_slots * 2 * hs * 4);
   L.total = o;
   return L;
 }
 
 struct LayerArgs {
   int mode;
-  const uint32_t *w1; const uint8_t *s1; int rows1, cols1;   // stage-1 matrices
-  const uint32_t *w2; const uint8_t *s2; int rows2, cols2;   // stage-2 matrices
+  const uint32_t *w1; const uint8_t *s1; int rows1, cols1, fast1;   // stage-1 matrices
+  const uint32_t *w2; const uint8_t *s2; int rows2, cols2, fast2;   // stage-2 matrices (layer)
   int E, T, k;
   const int32_t *ids;
   const float *gate_w;          // may be null (all ones)
   const void *x; int x_bf16; int x_per_slot;
-  int n_prep, prep_per_slot, fold;
-  int x_steps; uint8_t *xq; uint8_t *xs;
+  int inter;                    // layer: intermediate width
+  uint16_t *h;                  // layer: [T][k][inter]
   int h_steps; uint8_t *hq; uint8_t *hs;
-  int inter;                    // FFN intermediate width
-  uint16_t *h;                  // FFN: [T][k][inter]
-  float *y;                     // FFN / COMBINE: [T][rows2]; SLOTS: [T][k][rows1]
-  int n_s1, n_rg1, n_s2;
-  int *sync;
+  float *yslot;                 // partial outputs [T*k][y_rows]
+  float *y;                     // SLOTS: [T][k][rows1]; COMBINE / layer: [T][y_rows]
+  int y_rows;
+  int *status, *cnt1, *obs1, *cnt2;
+  int n_rg1, n_s1;              // stage-1 row groups per expert, items
+  int n_rt2, n_s2;              // stage-2 row tiles per expert, items
   int grid;
+#ifdef TQ_TRACE
+  unsigned long long *trace;
+#endif
 };
 
 struct Shared {
-  int ids[kMaxSlots];
+  int16_t ids[kMaxSlots];       // expert per slot: -1 empty, >= E skipped (clamped)
+  int16_t slots[kMaxSlots];     // slots of the current expert, in slot order
+  int16_t active[kMaxExperts];  // active experts in id order
   float gw[kMaxSlots];
   unsigned mask[kMaxExperts / 32];
   int wpre[kMaxExperts / 32 + 1];
-  int active[kMaxExperts];
-  int slots[kMaxSlots];
   int wcnt[kWaves];
   int n_active;
-  // Staged activation columns (step-chunk layout: steps x 128 code bytes per
-  // column) and their scales (steps x 4); after the matrix-core loop the code
+  int last;
+#ifdef TQ_TRACE
+  unsigned long long *trp;
+#endif
+  // One pass of activation columns (step-chunk layout: 128 code bytes and 4
+  // scale bytes per column and step); after the matrix-core loop the code
   // area is reused for the per-wave accumulator dumps.
   uint8_t bq[kBBytes] __attribute__((aligned(16)));
   uint8_t bs[kBScaleBytes] __attribute__((aligned(16)));
+  uint8_t as[kWaves][kAScaleBytes] __attribute__((aligned(16)));
 };
 static_assert(kWaves * 4 * 256 * sizeof(float) <= kBBytes, "accumulator dump must fit the column area");
 
@@ -136,146 +161,282 @@ __device__ __forceinline__ float load_x(const void *x, int bf16, size_t i) {
 }
 
 // Device-coherent accesses for data handed between workgroups.
-__device__ __forceinline__ void st_dc(uint8_t *p, uint32_t v) {
+__device__ __forceinline__ void st_dc8(uint8_t *p, uint32_t v) {
   __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ld_dc64(const uint8_t *p) {
-  return __hip_atomic_load((uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_dcf(float *p, float v) {
+  __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t ld_dc32(const uint8_t *p) {
-  return __hip_atomic_load((uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t ld_dc64(const uint8_t *p) {
+  return __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dc32(const void *p) {
+  return __hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_ctr(const int *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_ctr(int *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Publish `n` finished items: every wave's device-coherent stores complete,
-// then one thread bumps the counter.
-__device__ __forceinline__ void signal_n(int *ctr, int n) {
+// Every thread's device-coherent stores have completed (the workgroup's
+// results are visible device-wide); then one thread may count.
+__device__ __forceinline__ void stores_done() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait (once per workgroup and counter: `seen` remembers) until the counter
-// reaches `target`. Bounded: on timeout the error word is set.
-__device__ __forceinline__ void wait_for(int *ctr, int target, int *err, bool &seen) {
-  if (seen) return;
-  if (threadIdx.x == 0) {
-    unsigned spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(4);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
+// Thread 0 waits until the counter reaches `target`; bounded: on timeout
+// the error word is set. The caller synchronises the workgroup after.
+__device__ __forceinline__ void spin_until(const int *ctr, int target, int *status) {
+  unsigned spins = 0;
+  while (ld_ctr(ctr) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_fetch_or(&status[ST_ERROR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
   }
-  __syncthreads();
-  seen = true;
 }
 
 // Two-term FP8 split of one 32-value block held by the 32 lanes of a
-// half-wave (lane = position in the block); device-coherent stores of the
-// codes and scales of physical block `blk` into one column pair.
-__device__ __forceinline__ void quantize_block(float v, int pos, int blk, uint8_t *q_hi, uint8_t *q_lo,
-                                               uint8_t *s_hi, uint8_t *s_lo, bool store) {
+// half-wave (lane = position in the block).
+struct Split {
+  uint32_t hi, lo;
+  int E, El;
+};
+__device__ __forceinline__ Split split_block(float v) {
+  Split s;
   float amax = fabsf(v);
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
-  const int E = block_exponent(amax);
-  const uint32_t hi = f32_to_e4m3(ldexpf(v, -E));
-  const float r = v - ldexpf(e4m3_to_f32(hi), E);
+  s.E = block_exponent(amax);
+  s.hi = f32_to_e4m3(ldexpf(v, -s.E));
+  const float r = v - ldexpf(e4m3_to_f32(s.hi), s.E);
   float rmax = fabsf(r);
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 32));
-  const int El = block_exponent(rmax);
-  const uint32_t lo = f32_to_e4m3(ldexpf(r, -El));
-  if (store) {
-    const int off = act_offset(blk, pos);
-    st_dc(q_hi + off, hi);
-    st_dc(q_lo + off, lo);
-    if (pos == 0) {
-      st_dc(s_hi + act_scale_index(blk), (uint32_t)(E + 127));
-      st_dc(s_lo + act_scale_index(blk), (uint32_t)(El + 127));
+  s.El = block_exponent(rmax);
+  s.lo = f32_to_e4m3(ldexpf(r, -s.El));
+  return s;
+}
+
+// Slot list of expert e into S.slots (slot order); returns the count.
+__device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int total = 0;
+  for (int base = 0; base < n; base += kThreads) {
+    const int i = base + threadIdx.x;
+    const bool p = i < n && S.ids[i] == e;
+    const unsigned long long bal = __ballot(p);
+    if (lane == 0) S.wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += S.wcnt[w];
+    if (p) S.slots[off + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)i;
+    for (int w = 0; w < kWaves; ++w) total += S.wcnt[w];
+    __syncthreads();
+  }
+  return total;
+}
+
+// ---------------------------------------------------------------- activation columns in LDS
+//
+// A pass covers pieces [kp, kp + np) of K: column c holds 2*np step chunks
+// (128 code bytes each, then 4 scale bytes per step in the scale area).
+// Column 2c / 2c+1 is the hi / lo term of column pair c.
+
+// Activation values of the pass, one unit = (column pair, block) per
+// half-wave; the first kXPre units of every half-wave can be fetched ahead.
+struct XPre {
+  float v[kXPre];
+};
+
+template <typename RowMap>
+__device__ __forceinline__ float x_unit(const LayerArgs &a, int K, int nb, int kp, int np, int u, RowMap row_of) {
+  const int nbp = 8 * np;
+  const int c = u / nbp, blk = 8 * kp + u % nbp;
+  const int pos = threadIdx.x & 31;
+  return blk < nb ? load_x(a.x, a.x_bf16, (size_t)row_of(c) * K + (size_t)blk * 32 + pos) : 0.0f;
+}
+
+template <typename RowMap>
+__device__ __forceinline__ void x_prefetch(XPre &xp, const LayerArgs &a, int K, int nb, int kp, int np, int npairs,
+                                           RowMap row_of) {
+  const int hw = threadIdx.x >> 5, total = npairs * 8 * np;
+#pragma unroll
+  for (int m = 0; m < kXPre; ++m) {
+    const int u = hw + m * (kThreads / 32);
+    xp.v[m] = u < total ? x_unit(a, K, nb, kp, np, u, row_of) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v) {
+  const int nbp = 8 * np, psteps = 2 * np;
+  const int c = u / nbp, b = u % nbp, pos = threadIdx.x & 31;
+  const Split s = split_block(v);
+  const int off = act_offset(b, pos);
+  lq[(size_t)(2 * c) * psteps * 128 + off] = (uint8_t)s.hi;
+  lq[(size_t)(2 * c + 1) * psteps * 128 + off] = (uint8_t)s.lo;
+  if (pos == 0) {
+    ls[(size_t)(2 * c) * psteps * 4 + act_scale_index(b)] = (uint8_t)(s.E + 127);
+    ls[(size_t)(2 * c + 1) * psteps * 4 + act_scale_index(b)] = (uint8_t)(s.El + 127);
+  }
+}
+
+// Split the prefetched units, then load and split the rest of the pass.
+template <typename RowMap>
+__device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *ls, const LayerArgs &a, int K, int nb,
+                                         int kp, int np, int npairs, RowMap row_of) {
+  const int hw = threadIdx.x >> 5, total = npairs * 8 * np;
+  constexpr int kStride = kThreads / 32;
+#pragma unroll
+  for (int m = 0; m < kXPre; ++m) {
+    const int u = hw + m * kStride;
+    if (u < total) x_store_unit(lq, ls, np, u, xp.v[m]);   // uniform over the half-wave
+  }
+  for (int base = hw + kXPre * kStride; base < total; base += kXPre * kStride) {
+    float v[kXPre];
+#pragma unroll
+    for (int m = 0; m < kXPre; ++m) {
+      const int u = base + m * kStride;
+      v[m] = u < total ? x_unit(a, K, nb, kp, np, u, row_of) : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < kXPre; ++m) {
+      const int u = base + m * kStride;
+      if (u < total) x_store_unit(lq, ls, np, u, v[m]);
     }
   }
 }
 
-// Gate weight a slot's activation carries when gate weights are folded: the
-// first slot of a (token, expert) pair gets the sum over the token's slots
-// with that expert, later duplicates get 0.
-__device__ __forceinline__ float folded_gate(const Shared &S, int slot, int k, int E) {
-  const int e = S.ids[slot];
-  if (e < 0 || e >= E) return 0.0f;
-  const int t = slot / k, j = slot % k;
-  for (int jj = 0; jj < j; ++jj)
-    if (S.ids[t * k + jj] == e) return 0.0f;
-  float g = 0.0f;
-  for (int jj = 0; jj < k; ++jj)
-    if (S.ids[t * k + jj] == e) g += S.gw[t * k + jj];
-  return g;
+// Physical block (0-based in the pass) held at byte `o` of pass step `st`'s
+// chunk: the chunk's 16-byte halves belong to K-blocks in the order
+// 0, 2, 0, 2, 1, 3, 1, 3.
+__device__ __forceinline__ int chunk_block(int st, int o) {
+  const int beta = 2 * ((o >> 4) & 1) + (o >> 6);
+  return 8 * (st >> 1) + 2 * beta + (st & 1);
 }
 
-// Copy activation columns into LDS: LDS column c <- global column src_col(c)
-// (steps x 128 code bytes, steps x 4 scale bytes), device-coherent loads.
-// `first`/`stride` split the work among the threads that call it.
+// Copy the pass's slice of stored activation columns (global step-chunk
+// layout, gsteps steps per column; LDS column c <- global column src_col(c))
+// with device-coherent loads, issued 8 per thread before any LDS write.
+// Blocks >= nb (the K padding, never written in global memory) become zero
+// codes with scale 127.
 template <typename ColMap>
-__device__ __forceinline__ void copy_columns(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
-                                             int steps, int ncols, ColMap src_col, int first, int stride) {
-  const int per_col = steps * 16;   // 8-byte pieces per column
-  for (int idx = first; idx < ncols * per_col; idx += stride) {
-    const int c = idx / per_col, p = idx - c * per_col;
-    const size_t col = (size_t)src_col(c);
-    *(uint64_t *)(lq + ((size_t)c * per_col + p) * 8) = ld_dc64(gq + (col * per_col + p) * 8);
+__device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
+                                          int gsteps, int kp, int np, int nb, int ncols, ColMap src_col) {
+  constexpr int kBatch = 8;
+  const int psteps = 2 * np, per_col = psteps * 16;   // 8-byte pieces per column
+  const int total = ncols * per_col;
+  for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
+    uint64_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = base + u * kThreads;
+      v[u] = 0;
+      if (idx < total) {
+        const int c = idx / per_col, p = idx - c * per_col;
+        const int st = p >> 4, o = (p & 15) * 8;
+        if (8 * kp + chunk_block(st, o) < nb)
+          v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + 2 * kp + st) * 128 + o);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = base + u * kThreads;
+      if (idx < total) *(uint64_t *)(lq + (size_t)idx * 8) = v[u];
+    }
   }
-  for (int idx = first; idx < ncols * steps; idx += stride) {
-    const int c = idx / steps, p = idx - c * steps;
-    const size_t col = (size_t)src_col(c);
-    *(uint32_t *)(ls + ((size_t)c * steps + p) * 4) = ld_dc32(gs + (col * steps + p) * 4);
+  const int stotal = ncols * psteps;
+  for (int idx = threadIdx.x; idx < stotal; idx += kThreads) {
+    const int c = idx / psteps, st = idx - c * psteps;
+    uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + 2 * kp + st) * 4);
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta)
+      if (8 * kp + 8 * (st >> 1) + 2 * beta + (st & 1) >= nb) w = (w & ~(0xFFu << (8 * beta))) | (127u << (8 * beta));
+    *(uint32_t *)(ls + (size_t)idx * 4) = w;
   }
 }
 
 // ---------------------------------------------------------------- weight tiles
 
 struct Tile {
-  uint4 a[kPieceMax];       // piece j: words 16j+4g .. 16j+4g+3 of this lane's row
-  uint32_t sc[kPieceMax];   // piece j: UE8M0 of blocks 8j+2g (byte 0) and 8j+2g+1 (byte 1)
+  uint4 a[kPieceMax];       // piece q: words 16(p0+q)+4g .. +3 of this lane's row
 };
 
-// Issue the loads of pieces [p0, p0 + np) of one row into t (`row` null for
-// an invalid tile: zeros). ALIGNED: words per row % 4 == 0, so a piece is one
-// 16-byte load and one 2-byte scale load, whole or past the row end.
+// Issue the loads of pieces [p0, p0 + np) of one row (`row` null for a tile
+// past the matrix: zeros). ALIGNED: words per row % 4 == 0, so a piece is one
+// 16-byte load, whole or past the row end.
 template <bool ALIGNED>
-__device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, const uint8_t *srow, int wpr, int nb,
-                                          int p0, int np, int g) {
+__device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, int wpr, int p0, int np, int g) {
 #pragma unroll
   for (int q = 0; q < kPieceMax; ++q) {
-    const int j = p0 + q;
-    const int wi = 16 * j + 4 * g;
-    const int b = 8 * j + 2 * g;
+    const int wi = 16 * (p0 + q) + 4 * g;
     const bool ok = q < np && row && wi < wpr;
     if (ALIGNED) {
       t.a[q] = ok ? *(const uint4 *)(row + wi) : make_uint4(0u, 0u, 0u, 0u);
-      t.sc[q] = ok ? (uint32_t)*(const uint16_t *)(srow + b) : 0x7F7Fu;
     } else {
       t.a[q] = make_uint4(0u, 0u, 0u, 0u);
-      t.sc[q] = 0x7F7Fu;
       if (ok) {
         const uint2 lo = *(const uint2 *)(row + wi);
         const uint2 hi = wi + 2 < wpr ? *(const uint2 *)(row + wi + 2) : make_uint2(0u, 0u);
         t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        t.sc[q] = (uint32_t)srow[b] | ((b + 1 < nb ? (uint32_t)srow[b + 1] : 0x7Fu) << 8);
       }
     }
   }
 }
 
-// Decode pieces [p0, p0 + np) of the tile and accumulate them against NT
-// N-tiles of LDS-staged columns. Lane (column jc = lane & 15, lane-group g):
-// N-tile n reads LDS column col0[n] (or zeros when !on[n]).
+// The tile's UE8M0 bytes in the wave's LDS slot, row i at i * stride:
+//  fast   (16-byte aligned base, whole row in one window): the tile's 16 x nb
+//         bytes are contiguous; two 16-byte loads per lane, stride nb.
+//  generic: per window, each lane fetches its two bytes per piece, stride 128.
+struct AScalePre {
+  uint4 v[2];
+};
+
+__device__ __forceinline__ void ascale_prefetch(AScalePre &sp, const uint8_t *sblk, int nb, bool ok) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = lane + 64 * m;
+    sp.v[m] = ok && idx < nb ? ((const uint4 *)sblk)[idx] : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  }
+}
+
+__device__ __forceinline__ void ascale_store(uint8_t *as_w, const AScalePre &sp, int nb) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = lane + 64 * m;
+    if (idx < nb) ((uint4 *)as_w)[idx] = sp.v[m];
+  }
+}
+
+__device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *srow, int nb, int p0, int np, bool ok) {
+  const int lane = threadIdx.x & 63, i16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < kPieceMax; ++q) {
+    if (q < np) {
+      const int b = 8 * (p0 + q) + 2 * g;
+      const uint32_t lo = ok && b < nb ? srow[b] : 127u;
+      const uint32_t hi = ok && b + 1 < nb ? srow[b + 1] : 127u;
+      *(uint16_t *)(as_w + i16 * 128 + 8 * q + 2 * g) = (uint16_t)(lo | (hi << 8));
+    }
+  }
+}
+
+// Decode window pieces [0, np) (global piece p0 + q) and accumulate them
+// against NT N-tiles of the window's LDS columns. Lane
+// (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
+// (zeros when !on[n]).
 template <int NT>
-__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const uint8_t *lq, const uint8_t *ls,
-                                         int steps, const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
+__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const uint8_t *as_w, int astride,
+                                         int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
+                                         const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
                                          uint32_t &carry, int lane) {
-  const int g = lane >> 4;
+  const int g = lane >> 4, i16 = lane & 15;
   const int src = ((lane - 16) & 63) << 2;   // lane-group g-1 (mod 4), same row
 #pragma unroll
   for (int q = 0; q < kPieceMax; ++q) {
@@ -285,18 +446,20 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const ui
       const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
       const uint32_t hist = g == 0 ? carry : rot;
       carry = rot;
+      const int sb_a = 8 * j + 2 * g;
+      const uint32_t sa = sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * q + 2 * g) : 0x7F7Fu;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int step = 2 * j + hh;
+        const int step = 2 * q + hh;
         v8i B[NT];
         uint32_t sb[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           if (on[n]) {
-            const uint4 *p = (const uint4 *)(lq + ((size_t)col[n] * steps + step) * 128 + g * 32);
+            const uint4 *p = (const uint4 *)(lq + ((size_t)col[n] * psteps + step) * 128 + g * 32);
             const uint4 u0 = p[0], u1 = p[1];
             B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-            sb[n] = ls[((size_t)col[n] * steps + step) * 4 + g];
+            sb[n] = ls[((size_t)col[n] * psteps + step) * 4 + g];
           } else {
             B[n] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             sb[n] = 127u;
@@ -309,10 +472,10 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const ui
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           if (hh == 0)
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)t.sc[q], 0,
+            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)sa, 0,
                                                                      (int)sb[n]);
           else
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 1, (int)t.sc[q], 0,
+            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 1, (int)sa, 0,
                                                                      (int)sb[n]);
         }
       }
@@ -337,122 +500,76 @@ __device__ __forceinline__ void dump_acc(Shared &S, const v4f (&acc)[NT], int wa
     for (int r = 0; r < 4; ++r) red[((wave * NT + n) * 64 + lane) * 4 + r] = acc[n][r];
 }
 
+// hi + lo of column pair (n*8 + i16/2), row 4g + r, summed in the even lane.
+template <int NT, typename Out>
+__device__ __forceinline__ void per_slot_out(const v4f (&acc)[NT], int ncol, int lane, Out out) {
+  const int i16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[n][r] + __shfl_xor(acc[n][r], 1);
+      const int c = n * 8 + (i16 >> 1);
+      if ((i16 & 1) == 0 && c < ncol) out(c, 4 * g + r, v);
+    }
+}
+
+// Sum the partial outputs of rows [rt*64, rt*64 + 64) over each token's live
+// slots, in slot order, weighted by the gate weights.
+__device__ __forceinline__ void combine_rows(const LayerArgs &a, const Shared &S, int rt) {
+  for (int idx = threadIdx.x; idx < a.T * 64; idx += kThreads) {
+    const int t = idx >> 6, r = rt * 64 + (idx & 63);
+    if (r >= a.y_rows) continue;
+    float v = 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+      const int s = t * a.k + j, e = S.ids[s];
+      if (e >= 0 && e < a.E) v += S.gw[s] * __uint_as_float(ld_dc32(a.yslot + (size_t)s * a.y_rows + r));
+    }
+    a.y[(size_t)t * a.y_rows + r] = v;
+  }
+}
+
+// The item's partial outputs are stored; count it at its output tile and,
+// if it is the last of the n_active experts there, combine the tile.
+__device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S, int rt) {
+  stores_done();
+  if (threadIdx.x == 0) {
+    int *ctr = a.cnt2 + (size_t)rt * kLineInts;
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    S.last = old == S.n_active - 1;
+    if (S.last) st_ctr(ctr, 0);   // every arrival is in: clear for the next call
+  }
+  __syncthreads();
+  if (S.last) combine_rows(a, S, rt);
+}
+
 // ---------------------------------------------------------------- work items
 
-__device__ __forceinline__ void prep_item(const LayerArgs &a, Shared &S, int v) {
-  const int tid = threadIdx.x;
-  int t, j0 = 0;
-  if (a.prep_per_slot) { t = v / a.k; j0 = v % a.k; } else { t = v; }
-  // bookkeeping for the slots this item covers
-  const int s_lo = a.prep_per_slot ? v : t * a.k;
-  const int s_hi = a.prep_per_slot ? v + 1 : t * a.k + a.k;
-  if (tid == 0) {
-    int skipped = 0;
-    for (int s = s_lo; s < s_hi; ++s) skipped += S.ids[s] >= a.E;
-    if (skipped) __hip_atomic_fetch_add(&a.sync[SY_SKIP], skipped, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  for (int s = s_lo; s < s_hi; ++s) {
-    const int e = S.ids[s];
-    const bool dead = e < 0 || e >= a.E;
-    if (dead && a.mode == MODE_SLOTS)
-      for (int r = tid; r < a.rows1; r += kThreads) a.y[(size_t)s * a.rows1 + r] = 0.0f;
-    if (dead && a.mode == MODE_FFN)
-      for (int c = tid; c < a.inter; c += kThreads) a.h[(size_t)s * a.inter + c] = 0;
-    if (a.mode == MODE_FFN) {
-      // K padding of the slot's down-projection activations: zero codes, finite scales
-      const int nbh = a.inter / 32, npad = 4 * a.h_steps - nbh;
-      for (int idx = tid; idx < 2 * npad * 32; idx += kThreads) {
-        const int hl = idx / (npad * 32), rem = idx % (npad * 32);
-        const int blk = nbh + rem / 32, pos = rem % 32;
-        const size_t col = (size_t)s * 2 + hl;
-        st_dc(a.hq + col * a.h_steps * 128 + act_offset(blk, pos), 0u);
-        if (pos == 0) st_dc(a.hs + col * a.h_steps * 4 + act_scale_index(blk), 127u);
-      }
-    }
-  }
-  // the activation vector
-  const int K = a.mode == MODE_COMBINE ? a.cols2 : a.cols1;
-  const int nb = K / 32;
-  const int nblk = 4 * a.x_steps;
-  uint8_t *q_hi = a.xq + ((size_t)v * 2 + 0) * a.x_steps * 128;
-  uint8_t *q_lo = a.xq + ((size_t)v * 2 + 1) * a.x_steps * 128;
-  uint8_t *c_hi = a.xs + ((size_t)v * 2 + 0) * a.x_steps * 4;
-  uint8_t *c_lo = a.xs + ((size_t)v * 2 + 1) * a.x_steps * 4;
-  const int pos = tid & 31;
-  for (int blk = tid >> 5; blk < nblk; blk += kThreads / 32) {
-    float xv = 0.0f;
-    if (blk < nb) {
-      const size_t off = (size_t)blk * 32 + pos;
-      if (!a.prep_per_slot) {
-        xv = load_x(a.x, a.x_bf16, (size_t)t * K + off);
-      } else if (!a.fold) {
-        xv = load_x(a.x, a.x_bf16, (size_t)(a.x_per_slot ? v : t) * K + off);
-      } else {
-        // canonical slot of (token, expert): sum over the duplicates
-        const int e = S.ids[v];
-        bool canonical = e >= 0 && e < a.E;
-        for (int jj = 0; jj < j0 && canonical; ++jj) canonical = S.ids[t * a.k + jj] != e;
-        if (canonical)
-          for (int jj = 0; jj < a.k; ++jj)
-            if (S.ids[t * a.k + jj] == e)
-              xv += S.gw[t * a.k + jj] * load_x(a.x, a.x_bf16, (size_t)(a.x_per_slot ? t * a.k + jj : t) * K + off);
-      }
-    }
-    quantize_block(xv, pos, blk, q_hi, q_lo, c_hi, c_lo, true);
-  }
-}
-
-// Slot list of expert e into S.slots (slot order); returns the count.
-__device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int total = 0;
-  for (int base = 0; base < n; base += kThreads) {
-    const int i = base + threadIdx.x;
-    const bool p = i < n && S.ids[i] == e;
-    const unsigned long long bal = __ballot(p);
-    if (lane == 0) S.wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = total;
-    for (int w = 0; w < wave; ++w) off += S.wcnt[w];
-    if (p) S.slots[off + __popcll(bal & ((1ull << lane) - 1ull))] = i;
-    for (int w = 0; w < kWaves; ++w) total += S.wcnt[w];
-    __syncthreads();
-  }
-  return total;
-}
-
-template <int NT, bool ALIGNED>
-__device__ __forceinline__ void stage1_item(const LayerArgs &a, Shared &S, int item, bool &prep_seen) {
+// The grouped GEMM of one item: expert e, 16 rows per wave starting at r0
+// (past the matrix: zeros, no output), columns = the expert's ne slots. K
+// is covered in register windows of up to 16 pieces; the LDS holds one
+// window of activation columns for a group of slots (as many as fit, at
+// most 8*NT). fetch_ahead(c0, ncol, p0, np) runs before the window's weight
+// loads are issued; stage(c0, ncol, p0, np) then fills the LDS;
+// epilogue(c0, ncol, acc) runs per slot group with the LDS free. With one
+// window the weight tile stays in registers across slot groups.
+template <int NT, bool ALIGNED, typename Ahead, typename Stage, typename Epi>
+__device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
+                                          int fast, int e, int r0, int ne, Ahead fetch_ahead, Stage stage,
+                                          Epi epilogue) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
-  const int ai = item / a.n_rg1, rg = item % a.n_rg1;
-  if (ai >= S.n_active) return;   // no such active expert: nothing to do
-  const int e = S.active[ai];
-  const bool ffn = a.mode == MODE_FFN;
-  const int r0 = ffn ? (wave < 2 ? 0 : a.inter) + rg * 32 + 16 * (wave & 1) : rg * 64 + 16 * wave;
-  const bool tile_ok = r0 < a.rows1;
-  const int wpr = a.cols1 / 16, nb = a.cols1 / 32, J = (nb + 7) >> 3;
-  const size_t row = (size_t)e * a.rows1 + (tile_ok ? r0 + i16 : 0);
-  const uint32_t *rowp = tile_ok ? a.w1 + row * wpr : nullptr;
-  const uint8_t *srow = a.s1 + row * nb;
+  const bool tile_ok = r0 < rows;
+  const int wpr = K / 16, nb = K / 32, J = (nb + 7) >> 3;
+  const size_t row0 = (size_t)e * rows + (tile_ok ? r0 : 0);
+  const uint32_t *rowp = tile_ok ? w + (row0 + i16) * wpr : nullptr;
+  const uint8_t *srow = sc + (row0 + i16) * nb;
+  uint8_t *as_w = S.as[wave];
+  const int astride = fast ? nb : 128;
+  const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * 512));
   Tile tl;
-  load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, 0, min(J, kPieceMax), g);   // in flight while we wait
-  const int ne = gather_slots(S, e, a.T * a.k);
-  wait_for(&a.sync[SY_PREP], a.n_prep, &a.sync[SY_ERR], prep_seen);
-
-  // slots per column group: whatever fits the LDS column area (<= NT * 8)
-  const int steps = a.x_steps;
-  const int gsz = min(NT * 8, kBBytes / (2 * steps * 128));
   for (int c0 = 0; c0 < ne; c0 += gsz) {
     const int ncol = min(ne - c0, gsz);
-    // LDS column c = slot (c0 + c/2)'s hi (even c) or lo (odd c) term
-    copy_columns(S.bq, S.bs, a.xq, a.xs, steps, 2 * ncol,
-                 [&](int c) {
-                   const int slot = S.slots[c0 + (c >> 1)];
-                   return (a.prep_per_slot ? slot : slot / a.k) * 2 + (c & 1);
-                 },
-                 threadIdx.x, kThreads);
-    __syncthreads();
     int col[NT];
     bool on[NT];
 #pragma unroll
@@ -465,135 +582,168 @@ __device__ __forceinline__ void stage1_item(const LayerArgs &a, Shared &S, int i
     for (int n = 0; n < NT; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
     uint32_t carry = 0u;
     for (int p0 = 0; p0 < J; p0 += kPieceMax) {
-      if (p0 > 0 || c0 > 0) load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, p0, min(J - p0, kPieceMax), g);
-      mma_tile<NT>(tl, p0, min(J - p0, kPieceMax), S.bq, S.bs, steps, col, on, acc, carry, lane);
+      const int np = min(J - p0, kPieceMax);
+      const bool reload = c0 == 0 || J > kPieceMax;
+      fetch_ahead(c0, ncol, p0, np);
+      AScalePre sp;
+      if (reload && fast) ascale_prefetch(sp, sc + row0 * nb, nb, tile_ok);
+      if (reload) load_tile<ALIGNED>(tl, rowp, wpr, p0, np, g);
+      if (reload && !fast) ascale_generic(as_w, srow, nb, p0, np, tile_ok);
+      stage(c0, ncol, p0, np);
+      if (reload && fast) ascale_store(as_w, sp, nb);
+      __syncthreads();
+      TQ_MARK(S, 3);
+      mma_tile<NT>(tl, p0, np, as_w, astride, nb, S.bq, S.bs, 2 * np, col, on, acc, carry, lane);
+      __syncthreads();   // everyone is done with the window's columns
     }
-    __syncthreads();   // everyone is done with the staged columns
-    dump_acc<NT>(S, acc, wave, lane);
-    __syncthreads();
-    const float *red = (const float *)S.bq;
-    if (!ffn) {
-      for (int idx = threadIdx.x; idx < ncol * 64; idx += kThreads) {
-        const int c = idx >> 6, rr = idx & 63, w = rr >> 4, ri = rr & 15;
-        if (rg * 64 + rr >= a.rows1) continue;
-        const int n = c >> 3, cj = 2 * (c & 7);
-        const float v = red[d_index<NT>(w, n, ri, cj)] + red[d_index<NT>(w, n, ri, cj + 1)];
-        a.y[(size_t)S.slots[c0 + c] * a.rows1 + rg * 64 + rr] = v;
-      }
-    } else {
-      for (int base = 0; base < ncol; base += kThreads / 32) {
-        const int c = base + (threadIdx.x >> 5), i = threadIdx.x & 31;
-        const bool live = c < ncol;
-        float hv = 0.0f;
-        int slot = 0;
-        if (live) {
-          const int n = c >> 3, cj = 2 * (c & 7), w = i >> 4, ri = i & 15;
-          const float gate = red[d_index<NT>(w, n, ri, cj)] + red[d_index<NT>(w, n, ri, cj + 1)];
-          const float up = red[d_index<NT>(w + 2, n, ri, cj)] + red[d_index<NT>(w + 2, n, ri, cj + 1)];
-          const float silu = gate / (1.0f + expf(-gate));
-          const uint16_t hb = f32_to_bf16_rne(silu * up);
-          slot = S.slots[c0 + c];
-          a.h[(size_t)slot * a.inter + rg * 32 + i] = hb;
-          hv = bf16_to_f32(hb) * folded_gate(S, slot, a.k, a.E);
-        }
-        quantize_block(hv, i, rg, a.hq + ((size_t)slot * 2 + 0) * a.h_steps * 128,
-                       a.hq + ((size_t)slot * 2 + 1) * a.h_steps * 128, a.hs + ((size_t)slot * 2 + 0) * a.h_steps * 4,
-                       a.hs + ((size_t)slot * 2 + 1) * a.h_steps * 4, live);
-      }
-    }
-    __syncthreads();
+    TQ_MARK(S, 4);
+    epilogue(c0, ncol, acc);
   }
 }
 
-// Stage 2: wave w handles experts w, w+4, ... of the active list. Each wave
-// stages its own expert's columns (the tokens routed to it) in its quarter of
-// the column area, in token groups that fit.
+// One work item. Stage-1 items (item < n_s1): expert active[item / n_rg1],
+// row group item % n_rg1 of the first matrix; columns from the activations.
+// Stage-2 items: expert active[i / n_rt2], row tile i % n_rt2 of the down
+// projection (i = item - n_s1); columns from the h splits. A single call
+// site of the grouped GEMM serves every kind, so the kernel holds one copy
+// of the matrix-core loop.
 template <int NT, bool ALIGNED>
-__device__ __forceinline__ void stage2_item(const LayerArgs &a, Shared &S, int rt, bool &dep_seen) {
+__device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, g = lane >> 4;
-  const int wpr = a.cols2 / 16, nb = a.cols2 / 32, J = (nb + 7) >> 3;
-  const int n_act = S.n_active;
+  const bool s1 = item < a.n_s1;
+  const int i2 = item - a.n_s1;
+  const int ai = s1 ? item / a.n_rg1 : i2 / a.n_rt2;
+  const int tile = s1 ? item % a.n_rg1 : i2 % a.n_rt2;   // row group (stage 1) / row tile (stage 2)
+  if (ai >= S.n_active) return;   // no such active expert: nothing to do
+  const int e = S.active[ai];
   const bool ffn = a.mode == MODE_FFN;
-  const uint8_t *gq = ffn ? a.hq : a.xq;
-  const uint8_t *gs = ffn ? a.hs : a.xs;
-  const int steps = ffn ? a.h_steps : a.x_steps;
-  uint8_t *lq = S.bq + wave * (kBBytes / kWaves);
-  uint8_t *ls = S.bs + wave * (kBScaleBytes / kWaves);
-  const int tsz = max(1, min(NT * 8, kBBytes / kWaves / (2 * steps * 128)));   // tokens per group
-  v4f acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-  Tile tl;
-  for (int ai = wave; ai < n_act || !dep_seen; ai += kWaves) {
-    const bool have = ai < n_act;
-    const int e = have ? S.active[ai] : 0;
-    const size_t row = (size_t)e * a.rows2 + rt * 16 + i16;
-    const uint32_t *rowp = have ? a.w2 + row * wpr : nullptr;
-    const uint8_t *srow = a.s2 + row * nb;
-    if (have) load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, 0, min(J, kPieceMax), g);
-    if (!dep_seen) {
-      // every wave reaches this once (block-wide barrier inside)
-      if (ffn) wait_for(&a.sync[SY_S1], a.n_s1, &a.sync[SY_ERR], dep_seen);
-      else wait_for(&a.sync[SY_PREP], a.n_prep, &a.sync[SY_ERR], dep_seen);
+  const int r0 = s1 && ffn ? (wave < 2 ? 0 : a.inter) + tile * 32 + 16 * (wave & 1) : tile * 64 + 16 * wave;
+  const uint32_t *w = s1 ? a.w1 : a.w2;
+  const uint8_t *sc = s1 ? a.s1 : a.s2;
+  const int rows = s1 ? a.rows1 : a.rows2, K = s1 ? a.cols1 : a.cols2, fast = s1 ? a.fast1 : a.fast2;
+  const int nb = K / 32;
+  const int ne = gather_slots(S, e, a.T * a.k);
+  TQ_MARK(S, 2);
+  auto row_of = [&](int c) {
+    const int slot = S.slots[c];
+    return a.x_per_slot ? slot : slot / a.k;
+  };
+  XPre xp;
+  int obs_old = 0;
+  bool waited = false;
+  auto ahead = [&](int c0, int ncol, int kp, int np) {
+    if (s1) x_prefetch(xp, a, K, nb, kp, np, ncol, [&](int c) { return row_of(c0 + c); });
+  };
+  auto stage = [&](int c0, int ncol, int kp, int np) {
+    if (s1) {
+      x_finish(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) { return row_of(c0 + c); });
+      return;
     }
-    if (!have) break;
-    // tokens [t0, t0 + tsz) per group, LDS column 2 * (t - t0) + hilo; the
-    // group's matrix-core steps add into the batch-wide accumulators with
-    // zero activations for tokens outside the group
-    auto slot_of = [&](int t) {   // first slot of (token, e): duplicates were folded into it
-      for (int jj = 0; jj < a.k; ++jj)
-        if (S.ids[t * a.k + jj] == e) return t * a.k + jj;
-      return -1;
-    };
-    for (int t0 = 0; t0 < a.T; t0 += tsz) {
-      const int nt_tok = min(a.T - t0, tsz);
-      copy_columns(lq, ls, gq, gs, steps, 2 * nt_tok,
-                   [&](int c) {
-                     const int s = slot_of(t0 + (c >> 1));
-                     return (s < 0 ? 0 : s) * 2 + (c & 1);
-                   },
-                   lane, 64);
-      int col[NT];
-      bool on[NT];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int tok = n * 8 + (i16 >> 1);
-        const bool in = tok >= t0 && tok < t0 + nt_tok;
-        on[n] = in && slot_of(tok) >= 0;
-        col[n] = in ? 2 * (tok - t0) + (i16 & 1) : 0;
+    if (!waited) {
+      // the expert's h is complete once all its stage-1 items have counted;
+      // the first window's weight loads are already in flight
+      if (threadIdx.x == 0) {
+        spin_until(a.cnt1 + (size_t)ai * kLineInts, a.n_rg1, a.status);
+        obs_old = __hip_atomic_fetch_add(a.obs1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
       }
-      uint32_t carry = 0u;
-      for (int p0 = 0; p0 < J; p0 += kPieceMax) {
-        if (p0 > 0 || t0 > 0) load_tile<ALIGNED>(tl, rowp, srow, wpr, nb, p0, min(J - p0, kPieceMax), g);
-        mma_tile<NT>(tl, p0, min(J - p0, kPieceMax), lq, ls, steps, col, on, acc, carry, lane);
-      }
+      __syncthreads();
+      waited = true;
     }
+    copy_pass(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) {
+      return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
+    });
+  };
+  auto epilogue = [&](int c0, int ncol, const v4f (&acc)[NT]) {
+    if (s1 && ffn) {
+      // SwiGLU: gate rows in waves 0, 1, the matching up rows in waves 2, 3
+      dump_acc<NT>(S, acc, wave, lane);
+      __syncthreads();
+      const float *red = (const float *)S.bq;
+      for (int base = 0; base < ncol; base += kThreads / 32) {
+        const int c = base + (threadIdx.x >> 5), i = threadIdx.x & 31;
+        if (c < ncol) {   // uniform over the half-wave
+          const int n = c >> 3, cj = 2 * (c & 7), wv = i >> 4, ri = i & 15;
+          const float gate = red[d_index<NT>(wv, n, ri, cj)] + red[d_index<NT>(wv, n, ri, cj + 1)];
+          const float up = red[d_index<NT>(wv + 2, n, ri, cj)] + red[d_index<NT>(wv + 2, n, ri, cj + 1)];
+          const float silu = gate / (1.0f + expf(-gate));
+          const uint16_t hb = f32_to_bf16_rne(silu * up);
+          const int slot = S.slots[c0 + c];
+          a.h[(size_t)slot * a.inter + tile * 32 + i] = hb;
+          const Split s = split_block(bf16_to_f32(hb));
+          uint8_t *q_hi = a.hq + (size_t)(slot * 2) * a.h_steps * 128;
+          uint8_t *q_lo = a.hq + (size_t)(slot * 2 + 1) * a.h_steps * 128;
+          st_dc8(q_hi + act_offset(tile, i), s.hi);
+          st_dc8(q_lo + act_offset(tile, i), s.lo);
+          if (i == 0) {
+            st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + act_scale_index(tile), (uint32_t)(s.E + 127));
+            st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + act_scale_index(tile), (uint32_t)(s.El + 127));
+          }
+        }
+      }
+      __syncthreads();
+      return;
+    }
+    if (r0 >= rows) return;
+    const bool partial = !s1 || a.mode == MODE_COMBINE;
+    per_slot_out<NT>(acc, ncol, lane, [&](int c, int rr, float v) {
+      const int slot = S.slots[c0 + c];
+      if (partial) st_dcf(a.yslot + (size_t)slot * a.y_rows + r0 + rr, v);
+      else a.y[(size_t)slot * a.rows1 + r0 + rr] = v;
+    });
+  };
+  gemm_item<NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, ahead, stage, epilogue);
+  if (s1 && ffn) {
+    stores_done();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(a.cnt1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  __syncthreads();   // all waves done with their staged columns
-  dump_acc<NT>(S, acc, wave, lane);
-  __syncthreads();
-  const float *red = (const float *)S.bq;
-  for (int idx = threadIdx.x; idx < a.T * 16; idx += kThreads) {
-    const int t = idx >> 4, ri = idx & 15;
-    const int n = t >> 3, cj = 2 * (t & 7);
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[d_index<NT>(w, n, ri, cj)] + red[d_index<NT>(w, n, ri, cj + 1)];
-    a.y[(size_t)t * a.rows2 + rt * 16 + ri] = v;
+  if (!s1 && threadIdx.x == 0 && obs_old == a.n_rt2 - 1) {
+    // the last of the expert's row tiles to see its h clears the expert's counters
+    st_ctr(a.cnt1 + (size_t)ai * kLineInts, 0);
+    st_ctr(a.obs1 + (size_t)ai * kLineInts, 0);
   }
-  __syncthreads();
+  if (!s1 || a.mode == MODE_COMBINE) arrive_and_combine(a, S, tile);
+}
+
+// Work done once per call by workgroup 0: status words and the outputs of
+// dead (empty / out-of-range) slots.
+__device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
+  const int tid = threadIdx.x, n = a.T * a.k;
+  if (tid == 0) {
+    int skipped = 0;
+    for (int s = 0; s < n; ++s) skipped += S.ids[s] >= a.E;
+    st_ctr(&a.status[ST_SKIPPED], skipped);
+    st_ctr(&a.status[ST_ERROR], 0);
+  }
+  for (int s = 0; s < n; ++s) {
+    const int e = S.ids[s];
+    if (e >= 0 && e < a.E) continue;
+    if (a.mode == MODE_SLOTS)
+      for (int r = tid; r < a.rows1; r += kThreads) a.y[(size_t)s * a.rows1 + r] = 0.0f;
+    if (a.mode == MODE_FFN)
+      for (int c = tid; c < a.inter; c += kThreads) a.h[(size_t)s * a.inter + c] = 0;
+  }
+  if (S.n_active == 0 && a.mode != MODE_SLOTS)
+    for (int i = tid; i < a.T * a.y_rows; i += kThreads) a.y[i] = 0.0f;
 }
 
 template <int NT, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads) k_layer(LayerArgs a) {
   __shared__ Shared S;
   const int tid = threadIdx.x;
+#ifdef TQ_TRACE
+  unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 32 : nullptr;
+  if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
+  if (tid == 0) S.trp = nullptr;
+#endif
   // routing, redundantly in every workgroup: active experts in id order
   const int n = a.T * a.k;
   const int nw = (a.E + 31) >> 5;
   for (int i = tid; i < n; i += kThreads) {
-    S.ids[i] = a.ids[i];
+    const int e = a.ids[i];
+    S.ids[i] = (int16_t)(e < 0 ? -1 : (e >= a.E ? kMaxExperts : e));
     S.gw[i] = a.gate_w ? a.gate_w[i] : 1.0f;
   }
   for (int w = tid; w < nw; w += kThreads) S.mask[w] = 0u;
@@ -614,47 +764,31 @@ __global__ void __launch_bounds__(kThreads) k_layer(LayerArgs a) {
     int o = S.wpre[w];
     while (m) {
       const int b = __ffs(m) - 1;
-      S.active[o++] = w * 32 + b;
+      S.active[o++] = (int16_t)(w * 32 + b);
       m &= m - 1u;
     }
   }
   __syncthreads();
+  if (blockIdx.x == 0) bookkeeping(a, S);
 
-  // Items come in index order, so a workgroup's prep items, then its stage-1
-  // items, are contiguous: their completions are published in one signal
-  // when the workgroup moves on (before it can wait on anyone), and each
-  // dependency is waited for at most once per workgroup.
-  const int n_items = a.n_prep + a.n_s1 + a.n_s2;
-  int prep_done = 0, s1_done = 0;
-  bool prep_seen = false, dep_seen = false;
+#ifdef TQ_TRACE
+  if (TR && tid == 0) TR[1] = __builtin_amdgcn_s_memrealtime();
+  int it_no = 0;
+#endif
+  const int n_items = a.n_s1 + a.n_s2;
   for (int item = blockIdx.x; item < n_items; item += a.grid) {
-    if (item < a.n_prep) {
-      prep_item(a, S, item);
-      ++prep_done;
-    } else if (item < a.n_prep + a.n_s1) {
-      if (prep_done) { signal_n(&a.sync[SY_PREP], prep_done); prep_done = 0; }
-      stage1_item<NT, ALIGNED>(a, S, item - a.n_prep, prep_seen);
-      ++s1_done;
-    } else {
-      if (prep_done) { signal_n(&a.sync[SY_PREP], prep_done); prep_done = 0; }
-      if (s1_done) { signal_n(&a.sync[SY_S1], s1_done); s1_done = 0; }
-      stage2_item<NT, ALIGNED>(a, S, item - a.n_prep - a.n_s1, dep_seen);
+#ifdef TQ_TRACE
+    if (tid == 0) {
+      S.trp = (TR && it_no < 5) ? TR + 2 + 6 * it_no : nullptr;
+      if (S.trp) S.trp[0] = (unsigned long long)item;
     }
     __syncthreads();
-  }
-  if (prep_done) signal_n(&a.sync[SY_PREP], prep_done);
-  if (s1_done) signal_n(&a.sync[SY_S1], s1_done);
-  // the last workgroup out publishes the status and clears the counters
-  __syncthreads();
-  if (tid == 0) {
-    if (__hip_atomic_fetch_add(&a.sync[SY_EXIT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.grid - 1) {
-      const int skipped = __hip_atomic_load(&a.sync[SY_SKIP], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int err = __hip_atomic_load(&a.sync[SY_ERR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.sync[ST_SKIPPED], skipped, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.sync[ST_ERROR], err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int i = SY_PREP; i <= SY_ERR; ++i)
-        __hip_atomic_store(&a.sync[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    TQ_MARK(S, 1);
+    ++it_no;
+#endif
+    run_item<NT, ALIGNED>(a, S, item);
+    __syncthreads();
+    TQ_MARK(S, 5);
   }
 }
 
@@ -679,8 +813,7 @@ template <int NT, bool ALIGNED>
 static int resident_blocks() {
   static int cached[64];
   int dev = 0;
-  hipGetDevice(&dev);
-  if (dev < 0 || dev >= 64) return 1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   if (cached[dev] == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_layer<NT, ALIGNED>, kThreads, 0) != hipSuccess ||
@@ -705,7 +838,7 @@ static int check_routing(int T, int k) {
 
 template <int NT, bool ALIGNED>
 static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
-  const int n_items = a.n_prep + a.n_s1 + a.n_s2;
+  const int n_items = a.n_s1 + a.n_s2;
   a.grid = std::max(1, std::min(n_items, cus * resident_blocks<NT, ALIGNED>()));
   hipLaunchKernelGGL((k_layer<NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
@@ -722,11 +855,13 @@ static int launch_al(LayerArgs &a, int cus, hipStream_t s) {
 }
 
 // The aligned instances need every streamed matrix to have cols % 64 == 0
-// (words per row % 4 == 0) and 16-byte aligned symbol / 2-byte aligned
-// scale bases.
+// (words per row % 4 == 0) and a 16-byte aligned symbol base. The fast scale
+// path needs a 16-byte aligned scale base and cols <= 4096.
 static int launch(LayerArgs &a, int cus, hipStream_t s) {
   const bool aligned = a.cols1 % 64 == 0 && a.cols2 % 64 == 0 && ((uintptr_t)a.w1 & 15) == 0 &&
-                       ((uintptr_t)a.w2 & 15) == 0 && ((uintptr_t)a.s1 & 1) == 0 && ((uintptr_t)a.s2 & 1) == 0;
+                       ((uintptr_t)a.w2 & 15) == 0;
+  a.fast1 = aligned && ((uintptr_t)a.s1 & 15) == 0 && a.cols1 / 32 <= kAScaleBytes / 16;
+  a.fast2 = aligned && ((uintptr_t)a.s2 & 15) == 0 && a.cols2 / 32 <= kAScaleBytes / 16;
   return aligned ? launch_al<true>(a, cus, s) : launch_al<false>(a, cus, s);
 }
 
@@ -737,7 +872,7 @@ using namespace tq;
 extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
                                                   int32_t k) {
   if (n_mat < 1 || cols < 32 || cols % 32 || rows < 1 || check_routing(T, k)) return 0;
-  return make_layout(T * k, cols, 0, 0).total;
+  return make_layout(0, (rows + 63) / 64, T * k, rows, 0).total;
 }
 
 extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
@@ -750,8 +885,8 @@ extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, cons
     return TRELLIS_EINVAL;
   if ((rc = check_routing(T, k))) return rc;
   const bool combine = topk_w != nullptr;
-  const bool per_slot = combine || x_per_slot;
-  const Layout L = make_layout(per_slot ? T * k : T, w->cols, 0, 0);
+  const int n_rt = (w->rows + 63) / 64;
+  const Layout L = make_layout(0, n_rt, T * k, w->rows, 0);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -762,24 +897,20 @@ extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, cons
   a.w2 = w->syms; a.s2 = w->scales; a.rows2 = w->rows; a.cols2 = w->cols;
   a.E = w->n_mat; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
   a.x = x; a.x_bf16 = x_dtype == TRELLIS_BF16; a.x_per_slot = x_per_slot;
-  a.n_prep = per_slot ? T * k : T; a.prep_per_slot = per_slot; a.fold = combine;
-  a.x_steps = steps_for_blocks(w->cols / 32);
-  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs);
-  a.y = y;
-  a.sync = (int *)(ws + L.sync);
-  const int max_active = std::min(w->n_mat, T * k);
-  if (combine) {
-    a.n_s1 = 0; a.n_rg1 = 1; a.n_s2 = w->rows / 16;
-  } else {
-    a.n_rg1 = (w->rows + 63) / 64; a.n_s1 = max_active * a.n_rg1; a.n_s2 = 0;
-  }
+  a.y = y; a.y_rows = w->rows;
+  a.status = (int *)(ws + L.status);
+  a.cnt2 = (int *)(ws + L.cnt2);
+  a.yslot = (float *)(ws + L.yslot);
+  a.n_rg1 = n_rt;
+  a.n_s1 = std::min(w->n_mat, T * k) * a.n_rg1;
+  a.n_rt2 = 1; a.n_s2 = 0;
   return launch(a, cus, stream);
 }
 
 extern "C" size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t inter, int32_t T,
                                                  int32_t k) {
   if (n_exp < 1 || hidden < 32 || hidden % 32 || inter < 32 || inter % 32 || check_routing(T, k)) return 0;
-  return make_layout(T, hidden, T * k, inter).total;
+  return make_layout(std::min(n_exp, T * k), (hidden + 63) / 64, T * k, hidden, inter).total;
 }
 
 extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
@@ -795,7 +926,8 @@ extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_
   const int E = w_gate_up->n_mat, hidden = w_gate_up->cols, inter = w_gate_up->rows / 2;
   if (w_gate_up->rows % 64 || w_down->n_mat != E || w_down->rows != hidden || w_down->cols != inter)
     return TRELLIS_EINVAL;
-  const Layout L = make_layout(T, hidden, T * k, inter);
+  const int max_act = std::min(E, T * k);
+  const Layout L = make_layout(max_act, (hidden + 63) / 64, T * k, hidden, inter);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -806,19 +938,23 @@ extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_
   a.w2 = w_down->syms; a.s2 = w_down->scales; a.rows2 = hidden; a.cols2 = inter;
   a.E = E; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
   a.x = x; a.x_bf16 = x_dtype == TRELLIS_BF16; a.x_per_slot = 0;
-  a.n_prep = T; a.prep_per_slot = 0; a.fold = 0;
-  a.x_steps = steps_for_blocks(hidden / 32);
-  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs);
+  a.inter = inter; a.h = h;
   a.h_steps = steps_for_blocks(inter / 32);
   a.hq = (uint8_t *)(ws + L.hq); a.hs = (uint8_t *)(ws + L.hs);
-  a.inter = inter; a.h = h; a.y = y;
-  a.sync = (int *)(ws + L.sync);
+  a.yslot = (float *)(ws + L.yslot);
+  a.y = y; a.y_rows = hidden;
+  a.status = (int *)(ws + L.status);
+  a.cnt1 = (int *)(ws + L.cnt1); a.obs1 = (int *)(ws + L.obs1); a.cnt2 = (int *)(ws + L.cnt2);
+#ifdef TQ_TRACE
+  a.trace = (unsigned long long *)g_trace;
+#endif
   a.n_rg1 = inter / 32;
-  a.n_s1 = std::min(E, T * k) * a.n_rg1;
-  a.n_s2 = hidden / 16;
-  if (events && events[0]) hipEventRecord(events[0], stream);
+  a.n_s1 = max_act * a.n_rg1;
+  a.n_rt2 = (hidden + 63) / 64;
+  a.n_s2 = max_act * a.n_rt2;
+  if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
   rc = launch(a, cus, stream);
-  if (events && events[1]) hipEventRecord(events[1], stream);
+  if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
   return rc;
 }
 
@@ -829,3 +965,7 @@ extern "C" int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_u
   return trellis_moe_ffn_timed(stream, w_gate_up, w_down, x, x_dtype, topk_ids, topk_w, T, k, h, y, workspace,
                                workspace_bytes, nullptr);
 }
+
+#ifdef TQ_TRACE
+extern "C" void tq_set_trace(void *p) { tq::g_trace = p; }
+#endif
