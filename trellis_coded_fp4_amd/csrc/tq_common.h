@@ -30,19 +30,16 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, v8i b, v4f c, int sa, int sb)
 
 // Round a float (|v| < 448) to OCP E4M3, ties to even.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {                 // |v| >= 2^-6: normal E4M3
-    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // keep 3 mantissa bits
-    code = r - ((127u - 7u) << 3);
-    if (code > 0x7Eu) code = 0x7Eu;       // saturate at 448
-  } else {                                // subnormal range: multiples of 2^-9
-    float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
-    code = (uint32_t)q;                   // 0..8; 8 is the smallest normal
-  }
-  return sign | code;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  // |v| >= 2^-6: normal E4M3, keep 3 mantissa bits (round half to even),
+  // saturate at 448. Below: subnormals, multiples of 2^-9 (0..8; 8 is the
+  // smallest normal). Both are computed and selected, without branches.
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  const uint32_t normal = min(r - ((127u - 7u) << 3), 0x7Eu);
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | (a >= 0x3C800000u ? normal : sub);
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {

@@ -74,9 +74,13 @@ enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 // int words at the start of the workspace (public)
 enum { ST_SKIPPED = 0, ST_ERROR = 1 };
 
+// Every device lambda is inlined: a real call would force the argument
+// block and the live registers through scratch memory.
+#define TQ_INLINE __attribute__((always_inline))
+
 // Timeline instrumentation, compiled in only with -DTQ_TRACE: per workgroup
-// 32 u64 slots of s_memrealtime stamps (entry, routing done, then six per
-// item: id, start, and four item-specific marks).
+// 64 u64 slots of s_memrealtime stamps (entry, routing done, then ten per
+// item: id, start, marks 2..8, end).
 #ifdef TQ_TRACE
 #define TQ_MARK(S, k) do { if (threadIdx.x == 0 && (S).trp) (S).trp[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
 static void *g_trace = nullptr;
@@ -85,19 +89,21 @@ static void *g_trace = nullptr;
 #endif
 
 struct Layout {
-  size_t status, cnt1, obs1, cnt2, yslot, hq, hs, total;
+  size_t status, cntp, cnt1, obs1, cnt2, yslot, hq, hs, xq, xs, total;
 };
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // n_act: first-stage completion counters (layer only); n_rt: 64-row output
 // tiles that combine partial outputs; n_slots x y_rows partial outputs;
-// h_cols: width of the h splits (layer only).
-static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols) {
+// h_cols: width of the h splits (layer only); x_cols: width of one token's
+// split (the resident-token case).
+static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int x_cols) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.status = take(256);
+  L.cntp = take(2 * kLineInts * 4);   // resident-token split: done count, readers count
   L.cnt1 = take((size_t)n_act * kLineInts * 4);
   L.obs1 = take((size_t)n_act * kLineInts * 4);
   L.cnt2 = take((size_t)n_rt * kLineInts * 4);
@@ -105,6 +111,9 @@ static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_co
   const size_t hs = h_cols ? (size_t)steps_for_blocks(h_cols / 32) : 0;
   L.hq = take((size_t)n_slots * 2 * hs * 128);
   L.hs = take((size_t)n_slots * 2 * hs * 4);
+  const size_t xs = (size_t)steps_for_blocks(x_cols / 32);
+  L.xq = take(2 * xs * 128);
+  L.xs = take(2 * xs * 4);
   L.total = o;
   return L;
 }
@@ -126,6 +135,10 @@ struct LayerArgs {
   int *status, *cnt1, *obs1, *cnt2;
   int n_rg1, n_s1;              // stage-1 row groups per expert, items
   int n_rt2, n_s2;              // stage-2 row tiles per expert, items
+  int x_resident;               // one token, K <= 4096: split once per call, copied into each workgroup
+  int n_xprep;                  // workgroups that split it (at most; one 32-value block per half-wave)
+  uint8_t *xq; uint8_t *xs;     // the split token: columns 0 (hi), 1 (lo), step-chunk layout
+  int *cntp;                    // [0] split blocks done (x 1 per workgroup), [kLineInts] readers
   int grid;
 #ifdef TQ_TRACE
   unsigned long long *trace;
@@ -142,17 +155,19 @@ struct Shared {
   int wcnt[kWaves];
   int n_active;
   int last;
+  int x_done;                   // the resident token's columns are in place
 #ifdef TQ_TRACE
   unsigned long long *trp;
 #endif
   // One pass of activation columns (step-chunk layout: 128 code bytes and 4
-  // scale bytes per column and step); after the matrix-core loop the code
-  // area is reused for the per-wave accumulator dumps.
+  // scale bytes per column and step); after the matrix-core loop its upper
+  // half is reused for the per-wave accumulator dumps (a resident single
+  // token's columns, in the lower half, stay).
   uint8_t bq[kBBytes] __attribute__((aligned(16)));
   uint8_t bs[kBScaleBytes] __attribute__((aligned(16)));
   uint8_t as[kWaves][kAScaleBytes] __attribute__((aligned(16)));
 };
-static_assert(kWaves * 4 * 256 * sizeof(float) <= kBBytes, "accumulator dump must fit the column area");
+static_assert(kWaves * 4 * 256 * sizeof(float) <= kBBytes / 2, "accumulator dump must fit the column area");
 
 // ---------------------------------------------------------------- helpers
 
@@ -200,6 +215,21 @@ __device__ __forceinline__ void spin_until(const int *ctr, int target, int *stat
   }
 }
 
+// Maximum of a non-negative float over the 32 lanes of a half-wave. On
+// non-negative IEEE floats the bit patterns order like the values, so this
+// is an integer max: four DPP steps (quad xor 1, quad xor 2, half-row
+// mirror, row mirror) give the maximum over each 16-lane row, a swizzle
+// (xor 16) combines the two rows.
+__device__ __forceinline__ float halfwave_max(float v) {
+  int m = __float_as_int(v);
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x141, 0xF, 0xF, false));
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x140, 0xF, 0xF, false));
+  m = max(m, __builtin_amdgcn_ds_swizzle(m, 0x401F));
+  return __int_as_float(m);
+}
+
 // Two-term FP8 split of one 32-value block held by the 32 lanes of a
 // half-wave (lane = position in the block).
 struct Split {
@@ -208,16 +238,10 @@ struct Split {
 };
 __device__ __forceinline__ Split split_block(float v) {
   Split s;
-  float amax = fabsf(v);
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
-  s.E = block_exponent(amax);
+  s.E = block_exponent(halfwave_max(fabsf(v)));
   s.hi = f32_to_e4m3(ldexpf(v, -s.E));
   const float r = v - ldexpf(e4m3_to_f32(s.hi), s.E);
-  float rmax = fabsf(r);
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 32));
-  s.El = block_exponent(rmax);
+  s.El = block_exponent(halfwave_max(fabsf(r)));
   s.lo = f32_to_e4m3(ldexpf(r, -s.El));
   return s;
 }
@@ -249,33 +273,71 @@ __device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
 
 // Activation values of the pass, one unit = (column pair, block) per
 // half-wave; the first kXPre units of every half-wave can be fetched ahead.
+typedef uint32_t u32xp __attribute__((ext_vector_type(kXPre)));
 struct XPre {
-  float v[kXPre];
+  u32xp v;                  // raw 32-bit words holding the values (a vector: stays in registers)
 };
 
+// Register hygiene for the loads below: a load's destination is never
+// written before the load (no "zero, then load if in range"), because that
+// makes the compiler wait for every load in flight. Out-of-range lanes load
+// from a clamped, valid address and the value is discarded at its use.
+
+// Element index of activation unit u (column pair, block) of the pass for
+// this lane's position; ok false past the pass or the row.
 template <typename RowMap>
-__device__ __forceinline__ float x_unit(const LayerArgs &a, int K, int nb, int kp, int np, int u, RowMap row_of) {
-  const int nbp = 8 * np;
-  const int c = u / nbp, blk = 8 * kp + u % nbp;
-  const int pos = threadIdx.x & 31;
-  return blk < nb ? load_x(a.x, a.x_bf16, (size_t)row_of(c) * K + (size_t)blk * 32 + pos) : 0.0f;
+__device__ __forceinline__ size_t x_elem(const LayerArgs &a, int K, int nb, int kp, int np, int npairs, int u,
+                                         RowMap row_of, bool &ok) {
+  const int nbp = 8 * np, c = u / nbp, blk = 8 * kp + u - c * nbp;
+  ok = u < npairs * nbp && blk < nb;
+  return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (threadIdx.x & 31) : 0;
+}
+
+// One dword load per value for either dtype: the aligned word holding it
+// (a bf16 row has an even length, so the word stays inside the buffer).
+__device__ __forceinline__ uint32_t x_word(const LayerArgs &a, size_t elem) {
+  const size_t byte = elem << (a.x_bf16 ? 1 : 2);
+  return *(const uint32_t *)((const uint8_t *)a.x + (byte & ~(size_t)3));
+}
+
+__device__ __forceinline__ float x_value(const LayerArgs &a, size_t elem, uint32_t word) {
+  if (!a.x_bf16) return __uint_as_float(word);
+  return __uint_as_float((elem & 1 ? word >> 16 : word & 0xFFFFu) << 16);
+}
+
+// Raw words of units first, first + 8, ... (kXPre of them) of the pass.
+template <typename RowMap>
+__device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int nb, int kp, int np,
+                                       int npairs, int first, RowMap row_of) {
+  constexpr int kStride = kThreads / 32;
+  const int nbp = 8 * np, total = npairs * nbp;
+  int c = first / nbp, b = first - c * nbp;   // unit (c, b); nbp >= 8, so b wraps at most once a step
+  size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
+#pragma unroll
+  for (int m = 0; m < kXPre; ++m) {
+    const int u = first + m * kStride, blk = 8 * kp + b;
+    const bool ok = u < total && blk < nb;
+    v[m] = x_word(a, ok ? rbase + (size_t)blk * 32 : 0);
+    b += kStride;
+    if (b >= nbp) {
+      b -= nbp;
+      ++c;
+      rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
+    }
+  }
 }
 
 template <typename RowMap>
 __device__ __forceinline__ void x_prefetch(XPre &xp, const LayerArgs &a, int K, int nb, int kp, int np, int npairs,
                                            RowMap row_of) {
-  const int hw = threadIdx.x >> 5, total = npairs * 8 * np;
-#pragma unroll
-  for (int m = 0; m < kXPre; ++m) {
-    const int u = hw + m * (kThreads / 32);
-    xp.v[m] = u < total ? x_unit(a, K, nb, kp, np, u, row_of) : 0.0f;
-  }
+  x_load(xp.v, a, K, nb, kp, np, npairs, threadIdx.x >> 5, row_of);
 }
 
-__device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v) {
+__device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v, bool store) {
   const int nbp = 8 * np, psteps = 2 * np;
   const int c = u / nbp, b = u % nbp, pos = threadIdx.x & 31;
   const Split s = split_block(v);
+  if (!store) return;
   const int off = act_offset(b, pos);
   lq[(size_t)(2 * c) * psteps * 128 + off] = (uint8_t)s.hi;
   lq[(size_t)(2 * c + 1) * psteps * 128 + off] = (uint8_t)s.lo;
@@ -291,22 +353,24 @@ __device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *l
                                          int kp, int np, int npairs, RowMap row_of) {
   const int hw = threadIdx.x >> 5, total = npairs * 8 * np;
   constexpr int kStride = kThreads / 32;
+  // Every half-wave splits all its prefetched units without branches (the
+  // cross-lane steps need the whole half-wave) and stores the real ones.
 #pragma unroll
   for (int m = 0; m < kXPre; ++m) {
     const int u = hw + m * kStride;
-    if (u < total) x_store_unit(lq, ls, np, u, xp.v[m]);   // uniform over the half-wave
+    bool ok;
+    const size_t el = x_elem(a, K, nb, kp, np, npairs, u, row_of, ok);
+    x_store_unit(lq, ls, np, u, ok ? x_value(a, el, xp.v[m]) : 0.0f, u < total);
   }
   for (int base = hw + kXPre * kStride; base < total; base += kXPre * kStride) {
-    float v[kXPre];
+    u32xp v;
+    x_load(v, a, K, nb, kp, np, npairs, base, row_of);
 #pragma unroll
     for (int m = 0; m < kXPre; ++m) {
       const int u = base + m * kStride;
-      v[m] = u < total ? x_unit(a, K, nb, kp, np, u, row_of) : 0.0f;
-    }
-#pragma unroll
-    for (int m = 0; m < kXPre; ++m) {
-      const int u = base + m * kStride;
-      if (u < total) x_store_unit(lq, ls, np, u, v[m]);
+      bool ok;
+      const size_t el = x_elem(a, K, nb, kp, np, npairs, u, row_of, ok);
+      x_store_unit(lq, ls, np, u, ok ? x_value(a, el, v[m]) : 0.0f, u < total);
     }
   }
 }
@@ -334,19 +398,18 @@ __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_
     uint64_t v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int idx = base + u * kThreads;
-      v[u] = 0;
-      if (idx < total) {
-        const int c = idx / per_col, p = idx - c * per_col;
-        const int st = p >> 4, o = (p & 15) * 8;
-        if (8 * kp + chunk_block(st, o) < nb)
-          v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + 2 * kp + st) * 128 + o);
-      }
+      const int idx = min(base + u * kThreads, total - 1);
+      const int c = idx / per_col, p = idx - c * per_col;
+      v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + 2 * kp + (p >> 4)) * 128 + (p & 15) * 8);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int idx = base + u * kThreads;
-      if (idx < total) *(uint64_t *)(lq + (size_t)idx * 8) = v[u];
+      if (idx < total) {
+        const int p = idx % per_col;
+        const bool pad = 8 * kp + chunk_block(p >> 4, (p & 15) * 8) >= nb;   // never written: zero it
+        *(uint64_t *)(lq + (size_t)idx * 8) = pad ? 0ull : v[u];
+      }
     }
   }
   const int stotal = ncols * psteps;
@@ -366,22 +429,32 @@ struct Tile {
   uint4 a[kPieceMax];       // piece q: words 16(p0+q)+4g .. +3 of this lane's row
 };
 
-// Issue the loads of pieces [p0, p0 + np) of one row (`row` null for a tile
-// past the matrix: zeros). ALIGNED: words per row % 4 == 0, so a piece is one
-// 16-byte load, whole or past the row end.
+// Issue the loads of pieces [p0, p0 + np) of one row (`row` is always a
+// valid row; the caller masks tiles past the matrix). Lanes past the row end
+// load a clamped address; mma_tile zeroes those words. ALIGNED: words per
+// row % 4 == 0, so a piece is one 16-byte load.
 template <bool ALIGNED>
 __device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, int wpr, int p0, int np, int g) {
+  // Every piece but the last lies inside the row: one base address plus
+  // immediate offsets. Only the last piece's address is clamped.
+  const uint32_t *base = row + 16 * p0 + 4 * g;
+  const int wl = 16 * (p0 + np - 1) + 4 * g;   // the last piece's first word
 #pragma unroll
   for (int q = 0; q < kPieceMax; ++q) {
-    const int wi = 16 * (p0 + q) + 4 * g;
-    const bool ok = q < np && row && wi < wpr;
-    if (ALIGNED) {
-      t.a[q] = ok ? *(const uint4 *)(row + wi) : make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      t.a[q] = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) {
-        const uint2 lo = *(const uint2 *)(row + wi);
-        const uint2 hi = wi + 2 < wpr ? *(const uint2 *)(row + wi + 2) : make_uint2(0u, 0u);
+    if (q < np - 1) {   // uniform
+      if (ALIGNED) {
+        t.a[q] = *(const uint4 *)(base + 16 * q);
+      } else {
+        const uint2 lo = *(const uint2 *)(base + 16 * q);
+        const uint2 hi = *(const uint2 *)(base + 16 * q + 2);
+        t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    } else if (q == np - 1) {
+      if (ALIGNED) {
+        t.a[q] = *(const uint4 *)(row + min(wl, wpr - 4));
+      } else {
+        const uint2 lo = *(const uint2 *)(row + min(wl, wpr - 2));
+        const uint2 hi = *(const uint2 *)(row + min(wl + 2, wpr - 2));
         t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     }
@@ -393,25 +466,19 @@ __device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, int wpr,
 //         bytes are contiguous; two 16-byte loads per lane, stride nb.
 //  generic: per window, each lane fetches its two bytes per piece, stride 128.
 struct AScalePre {
-  uint4 v[2];
+  uint4 v0, v1;
 };
 
-__device__ __forceinline__ void ascale_prefetch(AScalePre &sp, const uint8_t *sblk, int nb, bool ok) {
+__device__ __forceinline__ void ascale_prefetch(AScalePre &sp, const uint8_t *sblk, int nb) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int idx = lane + 64 * m;
-    sp.v[m] = ok && idx < nb ? ((const uint4 *)sblk)[idx] : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  }
+  sp.v0 = ((const uint4 *)sblk)[min(lane, nb - 1)];
+  sp.v1 = ((const uint4 *)sblk)[min(lane + 64, nb - 1)];
 }
 
 __device__ __forceinline__ void ascale_store(uint8_t *as_w, const AScalePre &sp, int nb) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int idx = lane + 64 * m;
-    if (idx < nb) ((uint4 *)as_w)[idx] = sp.v[m];
-  }
+  if (lane < nb) ((uint4 *)as_w)[lane] = sp.v0;
+  if (lane + 64 < nb) ((uint4 *)as_w)[lane + 64] = sp.v1;
 }
 
 __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *srow, int nb, int p0, int np, bool ok) {
@@ -432,8 +499,8 @@ __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *sro
 // (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
 // (zeros when !on[n]).
 template <int NT>
-__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const uint8_t *as_w, int astride,
-                                         int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
+__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool tile_ok, int wpr, const uint8_t *as_w,
+                                         int astride, int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
                                          const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
                                          uint32_t &carry, int lane) {
   const int g = lane >> 4, i16 = lane & 15;
@@ -442,12 +509,16 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, const ui
   for (int q = 0; q < kPieceMax; ++q) {
     if (q < np) {
       const int j = p0 + q;
-      const uint4 a = t.a[q];
+      const int wi = 16 * j + 4 * g;
+      const bool ok_lo = tile_ok && wi < wpr, ok_hi = tile_ok && wi + 2 < wpr;
+      const uint4 a = make_uint4(ok_lo ? t.a[q].x : 0u, ok_lo ? t.a[q].y : 0u, ok_hi ? t.a[q].z : 0u,
+                                 ok_hi ? t.a[q].w : 0u);
       const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
       const uint32_t hist = g == 0 ? carry : rot;
       carry = rot;
       const int sb_a = 8 * j + 2 * g;
-      const uint32_t sa = sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * q + 2 * g) : 0x7F7Fu;
+      const uint32_t sa =
+          tile_ok && sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * q + 2 * g) : 0x7F7Fu;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int step = 2 * q + hh;
@@ -493,7 +564,7 @@ __device__ __forceinline__ int d_index(int wave, int nt, int row, int col) {
 // synchronises before and after.
 template <int NT>
 __device__ __forceinline__ void dump_acc(Shared &S, const v4f (&acc)[NT], int wave, int lane) {
-  float *red = (float *)S.bq;
+  float *red = (float *)(S.bq + kBBytes / 2);
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -553,28 +624,62 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
 // loads are issued; stage(c0, ncol, p0, np) then fills the LDS;
 // epilogue(c0, ncol, acc) runs per slot group with the LDS free. With one
 // window the weight tile stays in registers across slot groups.
+// shared_cols: every slot reads LDS columns 0 (hi) and 1 (lo).
 template <int NT, bool ALIGNED, typename Ahead, typename Stage, typename Epi>
 __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
-                                          int fast, int e, int r0, int ne, Ahead fetch_ahead, Stage stage,
-                                          Epi epilogue) {
+                                          int fast, int e, int r0, int ne, bool shared_cols, Ahead fetch_ahead,
+                                          Stage stage, Epi epilogue) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const bool tile_ok = r0 < rows;
   const int wpr = K / 16, nb = K / 32, J = (nb + 7) >> 3;
   const size_t row0 = (size_t)e * rows + (tile_ok ? r0 : 0);
-  const uint32_t *rowp = tile_ok ? w + (row0 + i16) * wpr : nullptr;
+  const uint32_t *rowp = w + (row0 + i16) * wpr;
   const uint8_t *srow = sc + (row0 + i16) * nb;
   uint8_t *as_w = S.as[wave];
   const int astride = fast ? nb : 128;
   const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * 512));
   Tile tl;
+  if (J <= kPieceMax && ne <= gsz) {
+    // The common case, one window and one slot group, as straight-line code:
+    // the loads of the activations, the tile's scales and its pieces are
+    // issued in that order and each consumer waits only for its own.
+    int col[NT];
+    bool on[NT];
+    v4f acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      col[n] = shared_cols ? (i16 & 1) : n * 16 + i16;
+      on[n] = n * 8 + (i16 >> 1) < ne;
+      acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    uint32_t carry = 0u;
+    fetch_ahead(0, ne, 0, J);
+    AScalePre sp;
+    if (fast) ascale_prefetch(sp, sc + row0 * nb, nb);
+    load_tile<ALIGNED>(tl, rowp, wpr, 0, J, g);
+    if (!fast) ascale_generic(as_w, srow, nb, 0, J, tile_ok);
+    TQ_MARK(S, 3);
+    stage(0, ne, 0, J);
+    TQ_MARK(S, 4);
+    if (fast) ascale_store(as_w, sp, nb);
+    TQ_MARK(S, 5);
+    __syncthreads();
+    TQ_MARK(S, 6);
+    mma_tile<NT>(tl, 0, J, tile_ok, wpr, as_w, astride, nb, S.bq, S.bs, 2 * J, col, on, acc, carry, lane);
+    TQ_MARK(S, 7);
+    __syncthreads();
+    epilogue(0, ne, acc);
+    TQ_MARK(S, 8);
+    return;
+  }
   for (int c0 = 0; c0 < ne; c0 += gsz) {
     const int ncol = min(ne - c0, gsz);
     int col[NT];
     bool on[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      col[n] = n * 16 + i16;
+      col[n] = shared_cols ? (i16 & 1) : n * 16 + i16;
       on[n] = n * 8 + (i16 >> 1) < ncol;
     }
     v4f acc[NT];
@@ -586,17 +691,15 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       const bool reload = c0 == 0 || J > kPieceMax;
       fetch_ahead(c0, ncol, p0, np);
       AScalePre sp;
-      if (reload && fast) ascale_prefetch(sp, sc + row0 * nb, nb, tile_ok);
+      if (reload && fast) ascale_prefetch(sp, sc + row0 * nb, nb);
       if (reload) load_tile<ALIGNED>(tl, rowp, wpr, p0, np, g);
       if (reload && !fast) ascale_generic(as_w, srow, nb, p0, np, tile_ok);
       stage(c0, ncol, p0, np);
       if (reload && fast) ascale_store(as_w, sp, nb);
       __syncthreads();
-      TQ_MARK(S, 3);
-      mma_tile<NT>(tl, p0, np, as_w, astride, nb, S.bq, S.bs, 2 * np, col, on, acc, carry, lane);
+      mma_tile<NT>(tl, p0, np, tile_ok, wpr, as_w, astride, nb, S.bq, S.bs, 2 * np, col, on, acc, carry, lane);
       __syncthreads();   // everyone is done with the window's columns
     }
-    TQ_MARK(S, 4);
     epilogue(c0, ncol, acc);
   }
 }
@@ -624,19 +727,32 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   const int nb = K / 32;
   const int ne = gather_slots(S, e, a.T * a.k);
   TQ_MARK(S, 2);
-  auto row_of = [&](int c) {
+  auto row_of = [&](int c) TQ_INLINE {
     const int slot = S.slots[c];
     return a.x_per_slot ? slot : slot / a.k;
   };
   XPre xp;
-  int obs_old = 0;
+  const bool resident = s1 && a.x_resident;
+  int obs_old = 0, obsp_old = -1;
   bool waited = false;
-  auto ahead = [&](int c0, int ncol, int kp, int np) {
-    if (s1) x_prefetch(xp, a, K, nb, kp, np, ncol, [&](int c) { return row_of(c0 + c); });
+  auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
+    if (s1 && !resident) x_prefetch(xp, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
   };
-  auto stage = [&](int c0, int ncol, int kp, int np) {
+  auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
+    if (resident) {
+      if (!S.x_done) {   // this workgroup's first stage-1 item: fetch the token's split
+        if (threadIdx.x == 0) {
+          spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
+          obsp_old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        copy_pass(S.bq, S.bs, a.xq, a.xs, 2 * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
+        S.x_done = 1;    // read after the caller's barrier
+      }
+      return;
+    }
     if (s1) {
-      x_finish(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) { return row_of(c0 + c); });
+      x_finish(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
       return;
     }
     if (!waited) {
@@ -650,16 +766,16 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       __syncthreads();
       waited = true;
     }
-    copy_pass(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) {
+    copy_pass(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
       return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
     });
   };
-  auto epilogue = [&](int c0, int ncol, const v4f (&acc)[NT]) {
+  auto epilogue = [&](int c0, int ncol, const v4f (&acc)[NT]) TQ_INLINE {
     if (s1 && ffn) {
       // SwiGLU: gate rows in waves 0, 1, the matching up rows in waves 2, 3
       dump_acc<NT>(S, acc, wave, lane);
       __syncthreads();
-      const float *red = (const float *)S.bq;
+      const float *red = (const float *)(S.bq + kBBytes / 2);
       for (int base = 0; base < ncol; base += kThreads / 32) {
         const int c = base + (threadIdx.x >> 5), i = threadIdx.x & 31;
         if (c < ncol) {   // uniform over the half-wave
@@ -686,13 +802,18 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     }
     if (r0 >= rows) return;
     const bool partial = !s1 || a.mode == MODE_COMBINE;
-    per_slot_out<NT>(acc, ncol, lane, [&](int c, int rr, float v) {
+    per_slot_out<NT>(acc, ncol, lane, [&](int c, int rr, float v) TQ_INLINE {
       const int slot = S.slots[c0 + c];
       if (partial) st_dcf(a.yslot + (size_t)slot * a.y_rows + r0 + rr, v);
       else a.y[(size_t)slot * a.rows1 + r0 + rr] = v;
     });
   };
-  gemm_item<NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, ahead, stage, epilogue);
+  gemm_item<NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, ahead, stage, epilogue);
+  if (obsp_old >= 0 && obsp_old == min(a.grid, S.n_active * a.n_rg1) - 1) {
+    // every workgroup that reads the split has fetched it: clear for the next call
+    st_ctr(a.cntp, 0);
+    st_ctr(a.cntp + kLineInts, 0);
+  }
   if (s1 && ffn) {
     stores_done();
     if (threadIdx.x == 0)
@@ -730,14 +851,38 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
 }
 
 template <int NT, bool ALIGNED>
-__global__ void __launch_bounds__(kThreads) k_layer(LayerArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_layer(LayerArgs a) {
   __shared__ Shared S;
   const int tid = threadIdx.x;
 #ifdef TQ_TRACE
-  unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 32 : nullptr;
+  unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 64 : nullptr;
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) S.trp = nullptr;
 #endif
+  // A single token's activations are split once per call, one 32-value
+  // block per half-wave of the first n_xprep workgroups, into the
+  // workspace; every workgroup copies the split into LDS once.
+  const int n_prep = min(a.n_xprep, a.grid);
+  if (a.x_resident && (int)blockIdx.x < n_prep) {
+    const int nb1 = a.cols1 / 32, steps = steps_for_blocks(nb1), pos = tid & 31;
+    for (int base = blockIdx.x * (kThreads / 32); base < 4 * steps; base += n_prep * (kThreads / 32)) {
+      const int blk = base + (tid >> 5);   // uniform per half-wave
+      const size_t el = blk < nb1 ? (size_t)blk * 32 + pos : 0;
+      const uint32_t word = x_word(a, el);
+      const Split sp = split_block(blk < nb1 ? x_value(a, el, word) : 0.0f);
+      if (blk < 4 * steps) {
+        st_dc8(a.xq + act_offset(blk, pos), sp.hi);
+        st_dc8(a.xq + (size_t)steps * 128 + act_offset(blk, pos), sp.lo);
+        if (pos == 0) {
+          st_dc8(a.xs + act_scale_index(blk), (uint32_t)(sp.E + 127));
+          st_dc8(a.xs + (size_t)steps * 4 + act_scale_index(blk), (uint32_t)(sp.El + 127));
+        }
+      }
+    }
+    stores_done();
+    if (tid == 0) __hip_atomic_fetch_add(a.cntp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) S.x_done = 0;
   // routing, redundantly in every workgroup: active experts in id order
   const int n = a.T * a.k;
   const int nw = (a.E + 31) >> 5;
@@ -779,7 +924,7 @@ __global__ void __launch_bounds__(kThreads) k_layer(LayerArgs a) {
   for (int item = blockIdx.x; item < n_items; item += a.grid) {
 #ifdef TQ_TRACE
     if (tid == 0) {
-      S.trp = (TR && it_no < 5) ? TR + 2 + 6 * it_no : nullptr;
+      S.trp = (TR && it_no < 6) ? TR + 2 + 10 * it_no : nullptr;
       if (S.trp) S.trp[0] = (unsigned long long)item;
     }
     __syncthreads();
@@ -788,7 +933,7 @@ __global__ void __launch_bounds__(kThreads) k_layer(LayerArgs a) {
 #endif
     run_item<NT, ALIGNED>(a, S, item);
     __syncthreads();
-    TQ_MARK(S, 5);
+    TQ_MARK(S, 9);
   }
 }
 
@@ -872,7 +1017,7 @@ using namespace tq;
 extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
                                                   int32_t k) {
   if (n_mat < 1 || cols < 32 || cols % 32 || rows < 1 || check_routing(T, k)) return 0;
-  return make_layout(0, (rows + 63) / 64, T * k, rows, 0).total;
+  return make_layout(0, (rows + 63) / 64, T * k, rows, 0, cols).total;
 }
 
 extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
@@ -886,7 +1031,7 @@ extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, cons
   if ((rc = check_routing(T, k))) return rc;
   const bool combine = topk_w != nullptr;
   const int n_rt = (w->rows + 63) / 64;
-  const Layout L = make_layout(0, n_rt, T * k, w->rows, 0);
+  const Layout L = make_layout(0, n_rt, T * k, w->rows, 0, w->cols);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -904,13 +1049,16 @@ extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, cons
   a.n_rg1 = n_rt;
   a.n_s1 = std::min(w->n_mat, T * k) * a.n_rg1;
   a.n_rt2 = 1; a.n_s2 = 0;
+  a.x_resident = T == 1 && !x_per_slot && steps_for_blocks(w->cols / 32) <= 2 * kPieceMax;
+  a.n_xprep = (4 * steps_for_blocks(w->cols / 32) + kThreads / 32 - 1) / (kThreads / 32);
+  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
   return launch(a, cus, stream);
 }
 
 extern "C" size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t inter, int32_t T,
                                                  int32_t k) {
   if (n_exp < 1 || hidden < 32 || hidden % 32 || inter < 32 || inter % 32 || check_routing(T, k)) return 0;
-  return make_layout(std::min(n_exp, T * k), (hidden + 63) / 64, T * k, hidden, inter).total;
+  return make_layout(std::min(n_exp, T * k), (hidden + 63) / 64, T * k, hidden, inter, hidden).total;
 }
 
 extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
@@ -927,7 +1075,7 @@ extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_
   if (w_gate_up->rows % 64 || w_down->n_mat != E || w_down->rows != hidden || w_down->cols != inter)
     return TRELLIS_EINVAL;
   const int max_act = std::min(E, T * k);
-  const Layout L = make_layout(max_act, (hidden + 63) / 64, T * k, hidden, inter);
+  const Layout L = make_layout(max_act, (hidden + 63) / 64, T * k, hidden, inter, hidden);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -952,6 +1100,9 @@ extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_
   a.n_s1 = max_act * a.n_rg1;
   a.n_rt2 = (hidden + 63) / 64;
   a.n_s2 = max_act * a.n_rt2;
+  a.x_resident = T == 1 && steps_for_blocks(hidden / 32) <= 2 * kPieceMax;
+  a.n_xprep = (4 * steps_for_blocks(hidden / 32) + kThreads / 32 - 1) / (kThreads / 32);
+  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
   if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
   rc = launch(a, cus, stream);
   if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
