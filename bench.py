@@ -49,7 +49,24 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-stage-events", action="store_true",
                    help="time only the whole step (no events between kernels)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB ten times (reference for the HBM "
+                        "byte counters of a profiler) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain torch device-to-device copy of a known size: its profiler byte
+    counters (FETCH_SIZE, WRITE_SIZE) per dispatch give the scale factor
+    between counter readings and bytes moved."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 10}), flush=True)
 
 
 def workload_cfg(name):
@@ -92,6 +109,9 @@ def main():
         print(f"bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU "
               f"mode (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import trellis_coded_fp4_amd as tq
 

@@ -509,10 +509,10 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool til
   for (int q = 0; q < kPieceMax; ++q) {
     if (q < np) {
       const int j = p0 + q;
-      const int wi = 16 * j + 4 * g;
-      const bool ok_lo = tile_ok && wi < wpr, ok_hi = tile_ok && wi + 2 < wpr;
-      const uint4 a = make_uint4(ok_lo ? t.a[q].x : 0u, ok_lo ? t.a[q].y : 0u, ok_hi ? t.a[q].z : 0u,
-                                 ok_hi ? t.a[q].w : 0u);
+      // Words past the row end (clamped loads) decode to finite E2M1 values
+      // that meet the zero codes of the activations' K padding, and rows past
+      // the matrix give outputs that are never stored: no masking needed.
+      const uint4 a = t.a[q];
       const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
       const uint32_t hist = g == 0 ? carry : rot;
       carry = rot;
@@ -524,17 +524,16 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool til
         const int step = 2 * q + hh;
         v8i B[NT];
         uint32_t sb[NT];
+        // Output column c of D depends only on B column c, and the columns
+        // of unused N-tile lanes are never read: those lanes load column 0
+        // or 1 instead of zeros, so the loads need no lane masking.
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          if (on[n]) {
-            const uint4 *p = (const uint4 *)(lq + ((size_t)col[n] * psteps + step) * 128 + g * 32);
-            const uint4 u0 = p[0], u1 = p[1];
-            B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-            sb[n] = ls[((size_t)col[n] * psteps + step) * 4 + g];
-          } else {
-            B[n] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            sb[n] = 127u;
-          }
+          const int c = on[n] ? col[n] : (col[n] & 1);
+          const uint4 *p = (const uint4 *)(lq + ((size_t)c * psteps + step) * 128 + g * 32);
+          const uint4 u0 = p[0], u1 = p[1];
+          B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+          sb[n] = ls[((size_t)c * psteps + step) * 4 + g];
         }
         const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
         const nib2 d0 = decode_word(w0, hw);
@@ -641,9 +640,11 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
   const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * 512));
   Tile tl;
   if (J <= kPieceMax && ne <= gsz) {
-    // The common case, one window and one slot group, as straight-line code:
-    // the loads of the activations, the tile's scales and its pieces are
-    // issued in that order and each consumer waits only for its own.
+    // The common case, one window and one slot group, as straight-line code.
+    // Load order: activations, the tile's pieces, whatever the stage loads,
+    // then the tile's scales (loads complete in issue order; the scales are
+    // needed only once the pieces are, and issuing them late keeps them from
+    // occupying registers across the stage).
     int col[NT];
     bool on[NT];
     v4f acc[NT];
@@ -655,14 +656,17 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
     }
     uint32_t carry = 0u;
     fetch_ahead(0, ne, 0, J);
-    AScalePre sp;
-    if (fast) ascale_prefetch(sp, sc + row0 * nb, nb);
     load_tile<ALIGNED>(tl, rowp, wpr, 0, J, g);
-    if (!fast) ascale_generic(as_w, srow, nb, 0, J, tile_ok);
     TQ_MARK(S, 3);
     stage(0, ne, 0, J);
     TQ_MARK(S, 4);
-    if (fast) ascale_store(as_w, sp, nb);
+    if (fast) {
+      AScalePre sp;
+      ascale_prefetch(sp, sc + row0 * nb, nb);
+      ascale_store(as_w, sp, nb);
+    } else {
+      ascale_generic(as_w, srow, nb, 0, J, tile_ok);
+    }
     TQ_MARK(S, 5);
     __syncthreads();
     TQ_MARK(S, 6);
@@ -690,12 +694,15 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       const int np = min(J - p0, kPieceMax);
       const bool reload = c0 == 0 || J > kPieceMax;
       fetch_ahead(c0, ncol, p0, np);
-      AScalePre sp;
-      if (reload && fast) ascale_prefetch(sp, sc + row0 * nb, nb);
       if (reload) load_tile<ALIGNED>(tl, rowp, wpr, p0, np, g);
-      if (reload && !fast) ascale_generic(as_w, srow, nb, p0, np, tile_ok);
       stage(c0, ncol, p0, np);
-      if (reload && fast) ascale_store(as_w, sp, nb);
+      if (reload && fast) {
+        AScalePre sp;
+        ascale_prefetch(sp, sc + row0 * nb, nb);
+        ascale_store(as_w, sp, nb);
+      } else if (reload) {
+        ascale_generic(as_w, srow, nb, p0, np, tile_ok);
+      }
       __syncthreads();
       mma_tile<NT>(tl, p0, np, tile_ok, wpr, as_w, astride, nb, S.bq, S.bs, 2 * np, col, on, acc, carry, lane);
       __syncthreads();   // everyone is done with the window's columns
