@@ -167,6 +167,43 @@ int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
                           uint16_t *h, float *y, void *workspace, size_t workspace_bytes,
                           hipEvent_t *events);
 
+/*
+ * Expand serving mode, second half (HEPH abstract: the expanded MXFP4 weights
+ * feed a grouped mixture-of-experts kernel): the same routed GEMV / layer as
+ * above, on weights that trellis_decode_expand has already turned into
+ * resident MXFP4.
+ */
+typedef struct {
+  const uint8_t *codes;    /* device, [n_mat][rows][cols/2]: E2M1 codes, column 2j in the low
+                              nibble of byte j, column 2j+1 in its high nibble (the
+                              codes_out of trellis_decode_expand); 16-byte aligned */
+  const uint8_t *scales;   /* device, [n_mat][rows][cols/32] UE8M0; 16-byte aligned */
+  int32_t n_mat;           /* >= 1 */
+  int32_t rows;            /* >= 1, multiple of 16 */
+  int32_t cols;            /* >= 32, multiple of 32 */
+} trellis_mx_t;
+
+/*
+ * trellis_mxfp4_moe_gemv -- trellis_moe_gemv with MXFP4 weights: same
+ * arguments, outputs, accuracy bound, workspace (trellis_moe_gemv_workspace_size
+ * covers it) and errors, plus EINVAL when codes or scales are not 16-byte
+ * aligned.
+ */
+int trellis_mxfp4_moe_gemv(hipStream_t stream, const trellis_mx_t *w, const void *x, int32_t x_dtype,
+                           int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w, int32_t T,
+                           int32_t k, float *y, void *workspace, size_t workspace_bytes);
+
+/*
+ * trellis_mxfp4_moe_ffn -- trellis_moe_ffn with MXFP4 weights (gate_up
+ * [2*inter][hidden] and down [hidden][inter] per expert): same arguments,
+ * outputs, workspace (trellis_moe_ffn_workspace_size) and errors, plus EINVAL
+ * for misaligned codes or scales.
+ */
+int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, const trellis_mx_t *w_down,
+                          const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,
+                          int32_t T, int32_t k, uint16_t *h, float *y, void *workspace,
+                          size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

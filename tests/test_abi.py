@@ -113,3 +113,22 @@ def test_workspace_sizes():
     f = lib.trellis_moe_ffn_workspace_size(128, 4096, 1536, 32, 8)
     assert f > 0 and f % 256 == 0
     assert lib.trellis_moe_ffn_workspace_size(128, 4096, 1530, 32, 8) == 0
+
+
+def test_mxfp4_argument_checks():
+    lib = tq.lib()
+    m = tq.MxMat(0x10000, 0x20000, 1, 16, 64)
+    call = lambda mm, **kw: lib.trellis_mxfp4_moe_gemv(None, ctypes.byref(mm) if mm is not None else None,
+                                                       kw.get("x", FAKE), 0, 0, FAKE, None, 1, 1, FAKE, 0x10000,
+                                                       1 << 30)
+    assert call(None) == -2
+    assert call(tq.MxMat(0, 0x20000, 1, 16, 64)) == -2
+    assert call(tq.MxMat(0x10008, 0x20000, 1, 16, 64)) == -1     # codes not 16-byte aligned
+    assert call(tq.MxMat(0x10000, 0x20004, 1, 16, 64)) == -1     # scales not 16-byte aligned
+    assert call(tq.MxMat(0x10000, 0x20000, 1, 24, 64)) == -1     # rows % 16
+    assert call(m, x=None) == -2
+    gu, dn = tq.MxMat(0x10000, 0x20000, 2, 128, 64), tq.MxMat(0x10000, 0x20000, 2, 64, 64)
+    f = lambda g, d, h=FAKE: lib.trellis_mxfp4_moe_ffn(None, ctypes.byref(g), ctypes.byref(d), FAKE, 1, FAKE,
+                                                       None, 1, 1, h, FAKE, 0x10000, 1 << 30)
+    assert f(gu, dn, h=None) == -2
+    assert f(gu, tq.MxMat(0x10000, 0x20000, 2, 64, 32)) == -1    # down cols != inter

@@ -119,15 +119,19 @@ def _h_tolerance(g_ref, u_ref, bg, bu):
         + np.abs(h) * 2.0 ** -7 + 1e-30
 
 
-def _check_layer(tq, orc, layer, rows_gu=None, rows_dn=None):
-    """Run the layer on the GPU; check h on sampled (slot, i) and y on sampled rows."""
+def _check_layer(tq, orc, layer, rows_gu=None, rows_dn=None, run=None):
+    """Run the layer on the GPU (trellis weights, or run(layer) -> (y, h)); check h
+    on sampled (slot, i) and y on sampled rows."""
     import torch
     cfg = layer.cfg
     E = layer.gu_syms.shape[0]
     I, H = cfg.inter, cfg.hidden
     T, k = layer.ids.shape
-    y, h = tq.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales),
-                      x_dev(layer.x, cfg.x_bf16), dev(layer.ids), dev(layer.gate_w))
+    if run is None:
+        y, h = tq.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales),
+                          x_dev(layer.x, cfg.x_bf16), dev(layer.ids), dev(layer.gate_w))
+    else:
+        y, h = run(layer)
     torch.cuda.synchronize()
     y = y.cpu().numpy()
     h = h.float().cpu().numpy()

@@ -26,7 +26,8 @@ ERRORS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_ENULL", -3: "TRELL
 # Every symbol include/trellis.h declares.
 EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_gemv_workspace_size", "trellis_moe_gemv",
-           "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed"]
+           "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
+           "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn"]
 
 
 class TrellisError(RuntimeError):
@@ -38,6 +39,12 @@ class TrellisError(RuntimeError):
 class Mat(ctypes.Structure):
     """trellis_mat_t"""
     _fields_ = [("syms", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n_mat", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class MxMat(ctypes.Structure):
+    """trellis_mx_t"""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n_mat", ctypes.c_int32),
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
 
 
@@ -70,6 +77,11 @@ def lib():
         L.trellis_moe_ffn.restype = ctypes.c_int
         L.trellis_moe_ffn_timed.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P, P, SZ, P]
         L.trellis_moe_ffn_timed.restype = ctypes.c_int
+        XP = ctypes.POINTER(MxMat)
+        L.trellis_mxfp4_moe_gemv.argtypes = [P, XP, P, I32, I32, P, P, I32, I32, P, P, SZ]
+        L.trellis_mxfp4_moe_gemv.restype = ctypes.c_int
+        L.trellis_mxfp4_moe_ffn.argtypes = [P, XP, XP, P, I32, P, P, I32, I32, P, P, P, SZ]
+        L.trellis_mxfp4_moe_ffn.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -223,4 +235,72 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
                                      y.data_ptr(), workspace.data_ptr(), workspace.numel(), events)
     if rc:
         raise TrellisError(rc, "trellis_moe_ffn")
+    return y, h
+
+
+# ---------------------------------------------------------------- expanded (MXFP4) weights
+
+def mx_mat(codes, scales) -> MxMat:
+    """trellis_mx_t for codes [n_mat, rows, cols/2] uint8 (as trellis_decode_expand writes
+    them) and scales [n_mat, rows, cols/32] uint8; both 16-byte aligned."""
+    torch = _torch()
+    if codes.dim() == 2:
+        codes = codes.unsqueeze(0)
+    if scales.dim() == 2:
+        scales = scales.unsqueeze(0)
+    _check(codes, torch.uint8, "codes")
+    n_mat, rows, half = codes.shape
+    _check(scales, torch.uint8, "scales", (n_mat, rows, half // 16))
+    return MxMat(codes.data_ptr(), scales.data_ptr(), n_mat, rows, half * 2)
+
+
+def mxfp4_moe_gemv(codes, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
+                   stream=None):
+    """moe_gemv on expanded MXFP4 weights (trellis_mxfp4_moe_gemv)."""
+    torch = _torch()
+    m = mx_mat(codes, scales)
+    T, k = topk_ids.shape
+    _check(topk_ids, torch.int32, "topk_ids")
+    if topk_w is not None:
+        _check(topk_w, torch.float32, "topk_w", (T, k))
+    _check(x, x.dtype, "x", (T, k, m.cols) if x_per_slot else (T, m.cols))
+    shape = (T, m.rows) if topk_w is not None else (T, k, m.rows)
+    if y is None:
+        y = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check(y, torch.float32, "y", shape)
+    if workspace is None:
+        workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
+    rc = lib().trellis_mxfp4_moe_gemv(_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x),
+                                      int(bool(x_per_slot)), topk_ids.data_ptr(), _ptr(topk_w), T, k,
+                                      y.data_ptr(), workspace.data_ptr(), workspace.numel())
+    if rc:
+        raise TrellisError(rc, "trellis_mxfp4_moe_gemv")
+    return y
+
+
+def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
+                  workspace=None, stream=None):
+    """moe_ffn on expanded MXFP4 weights (trellis_mxfp4_moe_ffn); returns (y, h)."""
+    torch = _torch()
+    mg = mx_mat(gu_codes, gu_scales)
+    md = mx_mat(dn_codes, dn_scales)
+    T, k = topk_ids.shape
+    _check(topk_ids, torch.int32, "topk_ids")
+    if topk_w is not None:
+        _check(topk_w, torch.float32, "topk_w", (T, k))
+    hidden, inter = mg.cols, mg.rows // 2
+    _check(x, x.dtype, "x", (T, hidden))
+    if h is None:
+        h = torch.empty((T, k, inter), dtype=torch.bfloat16, device=x.device)
+    _check(h, torch.bfloat16, "h", (T, k, inter))
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+    _check(y, torch.float32, "y", (T, hidden))
+    if workspace is None:
+        workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
+    rc = lib().trellis_mxfp4_moe_ffn(_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(),
+                                     _x_dtype(x), topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(),
+                                     y.data_ptr(), workspace.data_ptr(), workspace.numel())
+    if rc:
+        raise TrellisError(rc, "trellis_mxfp4_moe_ffn")
     return y, h

@@ -71,6 +71,32 @@ constexpr int kLineInts = 32;               // one counter per 128-byte line
 
 enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 
+// Weight formats. A "piece" is what a lane loads with one 16-byte load from
+// its row: for trellis-coded weights 8 blocks of 32 (256 two-bit symbols)
+// feeding two matrix-core steps; for expanded MXFP4 weights one step's 4
+// blocks (128 E2M1 nibbles, natural order). Each format has its own
+// activation layout: block b of a column goes to byte offset(b, pos) of the
+// step-chunk layout, its UE8M0 byte to scale_index(b).
+struct FmtTrellis {
+  static constexpr int kSteps = 2;    // matrix-core steps per piece
+  static constexpr int kBlocks = 8;   // 32-weight blocks per piece
+  static constexpr int kWords = 2;    // 32-bit words per block
+  __device__ __host__ static int offset(int b, int pos) { return act_offset(b, pos); }
+  __device__ __host__ static int scale_index(int b) { return act_scale_index(b); }
+  // block of step st (within a pass) whose data is K-block beta of the step
+  __device__ __host__ static int block_of(int st, int beta) { return 8 * (st >> 1) + 2 * beta + (st & 1); }
+};
+struct FmtMx {
+  static constexpr int kSteps = 1;
+  static constexpr int kBlocks = 4;
+  static constexpr int kWords = 4;
+  __device__ __host__ static int offset(int b, int pos) { return (b >> 2) * 128 + bchunk_offset(32 * (b & 3) + pos); }
+  __device__ __host__ static int scale_index(int b) { return b; }
+  __device__ __host__ static int block_of(int st, int beta) { return 4 * st + beta; }
+};
+template <typename F>
+__host__ __device__ inline int fmt_steps(int nb) { return F::kSteps * ((nb + F::kBlocks - 1) / F::kBlocks); }
+
 // int words at the start of the workspace (public)
 enum { ST_SKIPPED = 0, ST_ERROR = 1 };
 
@@ -98,6 +124,7 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // tiles that combine partial outputs; n_slots x y_rows partial outputs;
 // h_cols: width of the h splits (layer only); x_cols: width of one token's
 // split (the resident-token case).
+template <typename F>
 static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int x_cols) {
   Layout L;
   size_t o = 0;
@@ -108,10 +135,10 @@ static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_co
   L.obs1 = take((size_t)n_act * kLineInts * 4);
   L.cnt2 = take((size_t)n_rt * kLineInts * 4);
   L.yslot = take((size_t)n_slots * y_rows * 4);
-  const size_t hs = h_cols ? (size_t)steps_for_blocks(h_cols / 32) : 0;
+  const size_t hs = h_cols ? (size_t)fmt_steps<F>(h_cols / 32) : 0;
   L.hq = take((size_t)n_slots * 2 * hs * 128);
   L.hs = take((size_t)n_slots * 2 * hs * 4);
-  const size_t xs = (size_t)steps_for_blocks(x_cols / 32);
+  const size_t xs = (size_t)fmt_steps<F>(x_cols / 32);
   L.xq = take(2 * xs * 128);
   L.xs = take(2 * xs * 4);
   L.total = o;
@@ -285,10 +312,10 @@ struct XPre {
 
 // Element index of activation unit u (column pair, block) of the pass for
 // this lane's position; ok false past the pass or the row.
-template <typename RowMap>
+template <typename F, typename RowMap>
 __device__ __forceinline__ size_t x_elem(const LayerArgs &a, int K, int nb, int kp, int np, int npairs, int u,
                                          RowMap row_of, bool &ok) {
-  const int nbp = 8 * np, c = u / nbp, blk = 8 * kp + u - c * nbp;
+  const int nbp = F::kBlocks * np, c = u / nbp, blk = F::kBlocks * kp + u - c * nbp;
   ok = u < npairs * nbp && blk < nb;
   return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (threadIdx.x & 31) : 0;
 }
@@ -306,52 +333,57 @@ __device__ __forceinline__ float x_value(const LayerArgs &a, size_t elem, uint32
 }
 
 // Raw words of units first, first + 8, ... (kXPre of them) of the pass.
-template <typename RowMap>
+template <typename F, typename RowMap>
 __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int nb, int kp, int np,
                                        int npairs, int first, RowMap row_of) {
   constexpr int kStride = kThreads / 32;
-  const int nbp = 8 * np, total = npairs * nbp;
-  int c = first / nbp, b = first - c * nbp;   // unit (c, b); nbp >= 8, so b wraps at most once a step
+  const int nbp = F::kBlocks * np, total = npairs * nbp;
+  int c = first / nbp, b = first - c * nbp;   // unit (c, b); nbp >= 4, so b wraps at most twice a step
   size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
 #pragma unroll
   for (int m = 0; m < kXPre; ++m) {
-    const int u = first + m * kStride, blk = 8 * kp + b;
+    const int u = first + m * kStride, blk = F::kBlocks * kp + b;
     const bool ok = u < total && blk < nb;
     v[m] = x_word(a, ok ? rbase + (size_t)blk * 32 : 0);
     b += kStride;
     if (b >= nbp) {
       b -= nbp;
       ++c;
+      if (b >= nbp) {
+        b -= nbp;
+        ++c;
+      }
       rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
     }
   }
 }
 
-template <typename RowMap>
+template <typename F, typename RowMap>
 __device__ __forceinline__ void x_prefetch(XPre &xp, const LayerArgs &a, int K, int nb, int kp, int np, int npairs,
                                            RowMap row_of) {
-  x_load(xp.v, a, K, nb, kp, np, npairs, threadIdx.x >> 5, row_of);
+  x_load<F>(xp.v, a, K, nb, kp, np, npairs, threadIdx.x >> 5, row_of);
 }
 
+template <typename F>
 __device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v, bool store) {
-  const int nbp = 8 * np, psteps = 2 * np;
+  const int nbp = F::kBlocks * np, psteps = F::kSteps * np;
   const int c = u / nbp, b = u % nbp, pos = threadIdx.x & 31;
   const Split s = split_block(v);
   if (!store) return;
-  const int off = act_offset(b, pos);
+  const int off = F::offset(b, pos);
   lq[(size_t)(2 * c) * psteps * 128 + off] = (uint8_t)s.hi;
   lq[(size_t)(2 * c + 1) * psteps * 128 + off] = (uint8_t)s.lo;
   if (pos == 0) {
-    ls[(size_t)(2 * c) * psteps * 4 + act_scale_index(b)] = (uint8_t)(s.E + 127);
-    ls[(size_t)(2 * c + 1) * psteps * 4 + act_scale_index(b)] = (uint8_t)(s.El + 127);
+    ls[(size_t)(2 * c) * psteps * 4 + F::scale_index(b)] = (uint8_t)(s.E + 127);
+    ls[(size_t)(2 * c + 1) * psteps * 4 + F::scale_index(b)] = (uint8_t)(s.El + 127);
   }
 }
 
 // Split the prefetched units, then load and split the rest of the pass.
-template <typename RowMap>
+template <typename F, typename RowMap>
 __device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *ls, const LayerArgs &a, int K, int nb,
                                          int kp, int np, int npairs, RowMap row_of) {
-  const int hw = threadIdx.x >> 5, total = npairs * 8 * np;
+  const int hw = threadIdx.x >> 5, total = npairs * F::kBlocks * np;
   constexpr int kStride = kThreads / 32;
   // Every half-wave splits all its prefetched units without branches (the
   // cross-lane steps need the whole half-wave) and stores the real ones.
@@ -359,28 +391,27 @@ __device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *l
   for (int m = 0; m < kXPre; ++m) {
     const int u = hw + m * kStride;
     bool ok;
-    const size_t el = x_elem(a, K, nb, kp, np, npairs, u, row_of, ok);
-    x_store_unit(lq, ls, np, u, ok ? x_value(a, el, xp.v[m]) : 0.0f, u < total);
+    const size_t el = x_elem<F>(a, K, nb, kp, np, npairs, u, row_of, ok);
+    x_store_unit<F>(lq, ls, np, u, ok ? x_value(a, el, xp.v[m]) : 0.0f, u < total);
   }
   for (int base = hw + kXPre * kStride; base < total; base += kXPre * kStride) {
     u32xp v;
-    x_load(v, a, K, nb, kp, np, npairs, base, row_of);
+    x_load<F>(v, a, K, nb, kp, np, npairs, base, row_of);
 #pragma unroll
     for (int m = 0; m < kXPre; ++m) {
       const int u = base + m * kStride;
       bool ok;
-      const size_t el = x_elem(a, K, nb, kp, np, npairs, u, row_of, ok);
-      x_store_unit(lq, ls, np, u, ok ? x_value(a, el, v[m]) : 0.0f, u < total);
+      const size_t el = x_elem<F>(a, K, nb, kp, np, npairs, u, row_of, ok);
+      x_store_unit<F>(lq, ls, np, u, ok ? x_value(a, el, v[m]) : 0.0f, u < total);
     }
   }
 }
 
-// Physical block (0-based in the pass) held at byte `o` of pass step `st`'s
-// chunk: the chunk's 16-byte halves belong to K-blocks in the order
-// 0, 2, 0, 2, 1, 3, 1, 3.
+// Block (0-based in the pass) held at byte `o` of pass step `st`'s chunk:
+// the chunk's 16-byte halves belong to K-blocks 0, 2, 0, 2, 1, 3, 1, 3.
+template <typename F>
 __device__ __forceinline__ int chunk_block(int st, int o) {
-  const int beta = 2 * ((o >> 4) & 1) + (o >> 6);
-  return 8 * (st >> 1) + 2 * beta + (st & 1);
+  return F::block_of(st, 2 * ((o >> 4) & 1) + (o >> 6));
 }
 
 // Copy the pass's slice of stored activation columns (global step-chunk
@@ -388,11 +419,11 @@ __device__ __forceinline__ int chunk_block(int st, int o) {
 // with device-coherent loads, issued 8 per thread before any LDS write.
 // Blocks >= nb (the K padding, never written in global memory) become zero
 // codes with scale 127.
-template <typename ColMap>
+template <typename F, typename ColMap>
 __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
                                           int gsteps, int kp, int np, int nb, int ncols, ColMap src_col) {
   constexpr int kBatch = 8;
-  const int psteps = 2 * np, per_col = psteps * 16;   // 8-byte pieces per column
+  const int psteps = F::kSteps * np, per_col = psteps * 16;   // 8-byte pieces per column
   const int total = ncols * per_col;
   for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
     uint64_t v[kBatch];
@@ -400,14 +431,14 @@ __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_
     for (int u = 0; u < kBatch; ++u) {
       const int idx = min(base + u * kThreads, total - 1);
       const int c = idx / per_col, p = idx - c * per_col;
-      v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + 2 * kp + (p >> 4)) * 128 + (p & 15) * 8);
+      v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + F::kSteps * kp + (p >> 4)) * 128 + (p & 15) * 8);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int idx = base + u * kThreads;
       if (idx < total) {
         const int p = idx % per_col;
-        const bool pad = 8 * kp + chunk_block(p >> 4, (p & 15) * 8) >= nb;   // never written: zero it
+        const bool pad = F::kBlocks * kp + chunk_block<F>(p >> 4, (p & 15) * 8) >= nb;   // never written: zero it
         *(uint64_t *)(lq + (size_t)idx * 8) = pad ? 0ull : v[u];
       }
     }
@@ -415,10 +446,10 @@ __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_
   const int stotal = ncols * psteps;
   for (int idx = threadIdx.x; idx < stotal; idx += kThreads) {
     const int c = idx / psteps, st = idx - c * psteps;
-    uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + 2 * kp + st) * 4);
+    uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + F::kSteps * kp + st) * 4);
 #pragma unroll
     for (int beta = 0; beta < 4; ++beta)
-      if (8 * kp + 8 * (st >> 1) + 2 * beta + (st & 1) >= nb) w = (w & ~(0xFFu << (8 * beta))) | (127u << (8 * beta));
+      if (F::kBlocks * kp + F::block_of(st, beta) >= nb) w = (w & ~(0xFFu << (8 * beta))) | (127u << (8 * beta));
     *(uint32_t *)(ls + (size_t)idx * 4) = w;
   }
 }
@@ -481,15 +512,18 @@ __device__ __forceinline__ void ascale_store(uint8_t *as_w, const AScalePre &sp,
   if (lane + 64 < nb) ((uint4 *)as_w)[lane + 64] = sp.v1;
 }
 
+// (A lane's blocks of piece j: trellis 8j+2g and 8j+2g+1, MXFP4 4j+g.)
+template <typename F>
 __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *srow, int nb, int p0, int np, bool ok) {
   const int lane = threadIdx.x & 63, i16 = lane & 15, g = lane >> 4;
+  constexpr int kPer = F::kBlocks / 4;   // blocks per lane and piece
 #pragma unroll
   for (int q = 0; q < kPieceMax; ++q) {
     if (q < np) {
-      const int b = 8 * (p0 + q) + 2 * g;
-      const uint32_t lo = ok && b < nb ? srow[b] : 127u;
-      const uint32_t hi = ok && b + 1 < nb ? srow[b + 1] : 127u;
-      *(uint16_t *)(as_w + i16 * 128 + 8 * q + 2 * g) = (uint16_t)(lo | (hi << 8));
+      const int b = F::kBlocks * (p0 + q) + kPer * g;
+#pragma unroll
+      for (int h = 0; h < kPer; ++h)
+        as_w[i16 * 128 + F::kBlocks * q + kPer * g + h] = ok && b + h < nb ? srow[b + h] : (uint8_t)127;
     }
   }
 }
@@ -498,13 +532,40 @@ __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *sro
 // against NT N-tiles of the window's LDS columns. Lane
 // (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
 // (zeros when !on[n]).
-template <int NT>
+template <typename F, int NT>
 __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool tile_ok, int wpr, const uint8_t *as_w,
-                                         int astride, int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
+                                         int astride, int a_p0, int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
                                          const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
                                          uint32_t &carry, int lane) {
   const int g = lane >> 4, i16 = lane & 15;
   const int src = ((lane - 16) & 63) << 2;   // lane-group g-1 (mod 4), same row
+  if (F::kSteps == 1) {
+    // Expanded MXFP4: a piece is one step's A operand as stored, scaled by
+    // the UE8M0 byte of block 4j + g.
+#pragma unroll
+    for (int q = 0; q < kPieceMax; ++q) {
+      if (q < np) {
+        const int j = p0 + q;
+        const uint4 a = t.a[q];
+        const uint32_t sa = tile_ok && 4 * j + g < nb ? (uint32_t)as_w[i16 * astride + 4 * (a_p0 + q) + g] : 0x7Fu;
+        v8i B[NT];
+        uint32_t sb[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const int c = on[n] ? col[n] : (col[n] & 1);
+          const uint4 *p = (const uint4 *)(lq + ((size_t)c * psteps + q) * 128 + g * 32);
+          const uint4 u0 = p[0], u1 = p[1];
+          B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+          sb[n] = ls[((size_t)c * psteps + q) * 4 + g];
+        }
+        const v8i A = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)sa, 0, (int)sb[n]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < kPieceMax; ++q) {
     if (q < np) {
@@ -518,7 +579,7 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool til
       carry = rot;
       const int sb_a = 8 * j + 2 * g;
       const uint32_t sa =
-          tile_ok && sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * q + 2 * g) : 0x7F7Fu;
+          tile_ok && sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * (a_p0 + q) + 2 * g) : 0x7F7Fu;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int step = 2 * q + hh;
@@ -624,20 +685,20 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
 // epilogue(c0, ncol, acc) runs per slot group with the LDS free. With one
 // window the weight tile stays in registers across slot groups.
 // shared_cols: every slot reads LDS columns 0 (hi) and 1 (lo).
-template <int NT, bool ALIGNED, typename Ahead, typename Stage, typename Epi>
+template <typename F, int NT, bool ALIGNED, typename Ahead, typename Stage, typename Epi>
 __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
                                           int fast, int e, int r0, int ne, bool shared_cols, Ahead fetch_ahead,
                                           Stage stage, Epi epilogue) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const bool tile_ok = r0 < rows;
-  const int wpr = K / 16, nb = K / 32, J = (nb + 7) >> 3;
+  const int wpr = K / 32 * F::kWords, nb = K / 32, J = (nb + F::kBlocks - 1) / F::kBlocks;
   const size_t row0 = (size_t)e * rows + (tile_ok ? r0 : 0);
   const uint32_t *rowp = w + (row0 + i16) * wpr;
   const uint8_t *srow = sc + (row0 + i16) * nb;
   uint8_t *as_w = S.as[wave];
   const int astride = fast ? nb : 128;
-  const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * 512));
+  const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * F::kSteps * 256));
   Tile tl;
   if (J <= kPieceMax && ne <= gsz) {
     // The common case, one window and one slot group, as straight-line code.
@@ -665,12 +726,13 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       ascale_prefetch(sp, sc + row0 * nb, nb);
       ascale_store(as_w, sp, nb);
     } else {
-      ascale_generic(as_w, srow, nb, 0, J, tile_ok);
+      ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
     }
     TQ_MARK(S, 5);
     __syncthreads();
     TQ_MARK(S, 6);
-    mma_tile<NT>(tl, 0, J, tile_ok, wpr, as_w, astride, nb, S.bq, S.bs, 2 * J, col, on, acc, carry, lane);
+    mma_tile<F, NT>(tl, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on, acc, carry,
+                    lane);
     TQ_MARK(S, 7);
     __syncthreads();
     epilogue(0, ne, acc);
@@ -701,10 +763,11 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
         ascale_prefetch(sp, sc + row0 * nb, nb);
         ascale_store(as_w, sp, nb);
       } else if (reload) {
-        ascale_generic(as_w, srow, nb, p0, np, tile_ok);
+        ascale_generic<F>(as_w, srow, nb, p0, np, tile_ok);
       }
       __syncthreads();
-      mma_tile<NT>(tl, p0, np, tile_ok, wpr, as_w, astride, nb, S.bq, S.bs, 2 * np, col, on, acc, carry, lane);
+      mma_tile<F, NT>(tl, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np, col,
+                      on, acc, carry, lane);
       __syncthreads();   // everyone is done with the window's columns
     }
     epilogue(c0, ncol, acc);
@@ -717,7 +780,7 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
 // projection (i = item - n_s1); columns from the h splits. A single call
 // site of the grouped GEMM serves every kind, so the kernel holds one copy
 // of the matrix-core loop.
-template <int NT, bool ALIGNED>
+template <typename F, int NT, bool ALIGNED>
 __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool s1 = item < a.n_s1;
@@ -743,7 +806,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   int obs_old = 0, obsp_old = -1;
   bool waited = false;
   auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
-    if (s1 && !resident) x_prefetch(xp, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
+    if (s1 && !resident) x_prefetch<F>(xp, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
   };
   auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
     if (resident) {
@@ -753,13 +816,13 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
           obsp_old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        copy_pass(S.bq, S.bs, a.xq, a.xs, 2 * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
+        copy_pass<F>(S.bq, S.bs, a.xq, a.xs, F::kSteps * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
         S.x_done = 1;    // read after the caller's barrier
       }
       return;
     }
     if (s1) {
-      x_finish(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
+      x_finish<F>(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
       return;
     }
     if (!waited) {
@@ -773,7 +836,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       __syncthreads();
       waited = true;
     }
-    copy_pass(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
+    copy_pass<F>(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
       return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
     });
   };
@@ -796,11 +859,11 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
           const Split s = split_block(bf16_to_f32(hb));
           uint8_t *q_hi = a.hq + (size_t)(slot * 2) * a.h_steps * 128;
           uint8_t *q_lo = a.hq + (size_t)(slot * 2 + 1) * a.h_steps * 128;
-          st_dc8(q_hi + act_offset(tile, i), s.hi);
-          st_dc8(q_lo + act_offset(tile, i), s.lo);
+          st_dc8(q_hi + F::offset(tile, i), s.hi);
+          st_dc8(q_lo + F::offset(tile, i), s.lo);
           if (i == 0) {
-            st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + act_scale_index(tile), (uint32_t)(s.E + 127));
-            st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + act_scale_index(tile), (uint32_t)(s.El + 127));
+            st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + F::scale_index(tile), (uint32_t)(s.E + 127));
+            st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + F::scale_index(tile), (uint32_t)(s.El + 127));
           }
         }
       }
@@ -815,7 +878,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       else a.y[(size_t)slot * a.rows1 + r0 + rr] = v;
     });
   };
-  gemm_item<NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, ahead, stage, epilogue);
+  gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, ahead, stage, epilogue);
   if (obsp_old >= 0 && obsp_old == min(a.grid, S.n_active * a.n_rg1) - 1) {
     // every workgroup that reads the split has fetched it: clear for the next call
     st_ctr(a.cntp, 0);
@@ -857,7 +920,7 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
     for (int i = tid; i < a.T * a.y_rows; i += kThreads) a.y[i] = 0.0f;
 }
 
-template <int NT, bool ALIGNED>
+template <typename F, int NT, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_layer(LayerArgs a) {
   __shared__ Shared S;
   const int tid = threadIdx.x;
@@ -871,18 +934,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   // workspace; every workgroup copies the split into LDS once.
   const int n_prep = min(a.n_xprep, a.grid);
   if (a.x_resident && (int)blockIdx.x < n_prep) {
-    const int nb1 = a.cols1 / 32, steps = steps_for_blocks(nb1), pos = tid & 31;
+    const int nb1 = a.cols1 / 32, steps = fmt_steps<F>(nb1), pos = tid & 31;
     for (int base = blockIdx.x * (kThreads / 32); base < 4 * steps; base += n_prep * (kThreads / 32)) {
       const int blk = base + (tid >> 5);   // uniform per half-wave
       const size_t el = blk < nb1 ? (size_t)blk * 32 + pos : 0;
       const uint32_t word = x_word(a, el);
       const Split sp = split_block(blk < nb1 ? x_value(a, el, word) : 0.0f);
       if (blk < 4 * steps) {
-        st_dc8(a.xq + act_offset(blk, pos), sp.hi);
-        st_dc8(a.xq + (size_t)steps * 128 + act_offset(blk, pos), sp.lo);
+        st_dc8(a.xq + F::offset(blk, pos), sp.hi);
+        st_dc8(a.xq + (size_t)steps * 128 + F::offset(blk, pos), sp.lo);
         if (pos == 0) {
-          st_dc8(a.xs + act_scale_index(blk), (uint32_t)(sp.E + 127));
-          st_dc8(a.xs + (size_t)steps * 4 + act_scale_index(blk), (uint32_t)(sp.El + 127));
+          st_dc8(a.xs + F::scale_index(blk), (uint32_t)(sp.E + 127));
+          st_dc8(a.xs + (size_t)steps * 4 + F::scale_index(blk), (uint32_t)(sp.El + 127));
         }
       }
     }
@@ -938,7 +1001,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     TQ_MARK(S, 1);
     ++it_no;
 #endif
-    run_item<NT, ALIGNED>(a, S, item);
+    run_item<F, NT, ALIGNED>(a, S, item);
     __syncthreads();
     TQ_MARK(S, 9);
   }
@@ -961,14 +1024,14 @@ static int device_check(int *cus) {
   return cached[dev] > 0 ? TRELLIS_OK : TRELLIS_EDEVICE;
 }
 
-template <int NT, bool ALIGNED>
+template <typename F, int NT, bool ALIGNED>
 static int resident_blocks() {
   static int cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   if (cached[dev] == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_layer<NT, ALIGNED>, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_layer<F, NT, ALIGNED>, kThreads, 0) != hipSuccess ||
         nb < 1)
       nb = 1;
     cached[dev] = nb;
@@ -976,10 +1039,17 @@ static int resident_blocks() {
   return cached[dev];
 }
 
-static int check_mat(const trellis_mat_t *w) {
-  if (!w || !w->syms || !w->scales) return TRELLIS_ENULL;
-  if (w->n_mat < 1 || w->rows < 1 || w->cols < 32 || w->cols % 32) return TRELLIS_EINVAL;
-  if (w->rows % 16 || w->n_mat > kMaxExperts) return TRELLIS_EINVAL;
+// A stack of n_mat matrices of either format: base pointers as given.
+struct Mats {
+  const void *w;
+  const uint8_t *scales;
+  int n_mat, rows, cols;
+};
+
+static int check_mats(const Mats &m) {
+  if (!m.w || !m.scales) return TRELLIS_ENULL;
+  if (m.n_mat < 1 || m.rows < 1 || m.cols < 32 || m.cols % 32) return TRELLIS_EINVAL;
+  if (m.rows % 16 || m.n_mat > kMaxExperts) return TRELLIS_EINVAL;
   return TRELLIS_OK;
 }
 
@@ -988,113 +1058,98 @@ static int check_routing(int T, int k) {
   return TRELLIS_OK;
 }
 
-template <int NT, bool ALIGNED>
+template <typename F, int NT, bool ALIGNED>
 static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
   const int n_items = a.n_s1 + a.n_s2;
-  a.grid = std::max(1, std::min(n_items, cus * resident_blocks<NT, ALIGNED>()));
-  hipLaunchKernelGGL((k_layer<NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
+  a.grid = std::max(1, std::min(n_items, cus * resident_blocks<F, NT, ALIGNED>()));
+  hipLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
 }
 
-template <bool ALIGNED>
+template <typename F, bool ALIGNED>
 static int launch_al(LayerArgs &a, int cus, hipStream_t s) {
   switch ((a.T + 7) / 8) {
-    case 1: return launch_nt<1, ALIGNED>(a, cus, s);
-    case 2: return launch_nt<2, ALIGNED>(a, cus, s);
-    case 3: return launch_nt<3, ALIGNED>(a, cus, s);
-    default: return launch_nt<4, ALIGNED>(a, cus, s);
+    case 1: return launch_nt<F, 1, ALIGNED>(a, cus, s);
+    case 2: return launch_nt<F, 2, ALIGNED>(a, cus, s);
+    case 3: return launch_nt<F, 3, ALIGNED>(a, cus, s);
+    default: return launch_nt<F, 4, ALIGNED>(a, cus, s);
   }
 }
 
-// The aligned instances need every streamed matrix to have cols % 64 == 0
-// (words per row % 4 == 0) and a 16-byte aligned symbol base. The fast scale
-// path needs a 16-byte aligned scale base and cols <= 4096.
+// The aligned instances need every streamed matrix to have whole 16-byte
+// pieces per row (words per row % 4 == 0) and a 16-byte aligned base. The
+// fast scale path needs a 16-byte aligned scale base and cols <= 4096.
+template <typename F>
 static int launch(LayerArgs &a, int cus, hipStream_t s) {
-  const bool aligned = a.cols1 % 64 == 0 && a.cols2 % 64 == 0 && ((uintptr_t)a.w1 & 15) == 0 &&
-                       ((uintptr_t)a.w2 & 15) == 0;
+  const bool aligned = (a.cols1 / 32 * F::kWords) % 4 == 0 && (a.cols2 / 32 * F::kWords) % 4 == 0 &&
+                       ((uintptr_t)a.w1 & 15) == 0 && ((uintptr_t)a.w2 & 15) == 0;
   a.fast1 = aligned && ((uintptr_t)a.s1 & 15) == 0 && a.cols1 / 32 <= kAScaleBytes / 16;
   a.fast2 = aligned && ((uintptr_t)a.s2 & 15) == 0 && a.cols2 / 32 <= kAScaleBytes / 16;
-  return aligned ? launch_al<true>(a, cus, s) : launch_al<false>(a, cus, s);
+  return aligned ? launch_al<F, true>(a, cus, s) : launch_al<F, false>(a, cus, s);
 }
 
-}  // namespace tq
-
-using namespace tq;
-
-extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
-                                                  int32_t k) {
-  if (n_mat < 1 || cols < 32 || cols % 32 || rows < 1 || check_routing(T, k)) return 0;
-  return make_layout(0, (rows + 63) / 64, T * k, rows, 0, cols).total;
-}
-
-extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
-                                int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w,
-                                int32_t T, int32_t k, float *y, void *workspace, size_t workspace_bytes) {
-  int rc = check_mat(w);
+template <typename F>
+static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x_dtype, int32_t x_per_slot,
+                     const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k, float *y,
+                     void *workspace, size_t workspace_bytes) {
+  int rc = check_mats(w);
   if (rc) return rc;
   if (!x || !topk_ids || !y || !workspace) return TRELLIS_ENULL;
   if ((x_dtype != TRELLIS_F32 && x_dtype != TRELLIS_BF16) || (x_per_slot != 0 && x_per_slot != 1))
     return TRELLIS_EINVAL;
   if ((rc = check_routing(T, k))) return rc;
   const bool combine = topk_w != nullptr;
-  const int n_rt = (w->rows + 63) / 64;
-  const Layout L = make_layout(0, n_rt, T * k, w->rows, 0, w->cols);
+  const int n_rt = (w.rows + 63) / 64;
+  const Layout L = make_layout<F>(0, n_rt, T * k, w.rows, 0, w.cols);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
   char *ws = (char *)workspace;
   LayerArgs a{};
   a.mode = combine ? MODE_COMBINE : MODE_SLOTS;
-  a.w1 = w->syms; a.s1 = w->scales; a.rows1 = w->rows; a.cols1 = w->cols;
-  a.w2 = w->syms; a.s2 = w->scales; a.rows2 = w->rows; a.cols2 = w->cols;
-  a.E = w->n_mat; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
+  a.w1 = (const uint32_t *)w.w; a.s1 = w.scales; a.rows1 = w.rows; a.cols1 = w.cols;
+  a.w2 = (const uint32_t *)w.w; a.s2 = w.scales; a.rows2 = w.rows; a.cols2 = w.cols;
+  a.E = w.n_mat; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
   a.x = x; a.x_bf16 = x_dtype == TRELLIS_BF16; a.x_per_slot = x_per_slot;
-  a.y = y; a.y_rows = w->rows;
+  a.y = y; a.y_rows = w.rows;
   a.status = (int *)(ws + L.status);
   a.cnt2 = (int *)(ws + L.cnt2);
   a.yslot = (float *)(ws + L.yslot);
   a.n_rg1 = n_rt;
-  a.n_s1 = std::min(w->n_mat, T * k) * a.n_rg1;
+  a.n_s1 = std::min(w.n_mat, T * k) * a.n_rg1;
   a.n_rt2 = 1; a.n_s2 = 0;
-  a.x_resident = T == 1 && !x_per_slot && steps_for_blocks(w->cols / 32) <= 2 * kPieceMax;
-  a.n_xprep = (4 * steps_for_blocks(w->cols / 32) + kThreads / 32 - 1) / (kThreads / 32);
+  const int J = (w.cols / 32 + F::kBlocks - 1) / F::kBlocks;
+  a.x_resident = T == 1 && !x_per_slot && J <= kPieceMax;
+  a.n_xprep = (4 * fmt_steps<F>(w.cols / 32) + kThreads / 32 - 1) / (kThreads / 32);
   a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
-  return launch(a, cus, stream);
+  return launch<F>(a, cus, stream);
 }
 
-extern "C" size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t inter, int32_t T,
-                                                 int32_t k) {
-  if (n_exp < 1 || hidden < 32 || hidden % 32 || inter < 32 || inter % 32 || check_routing(T, k)) return 0;
-  return make_layout(std::min(n_exp, T * k), (hidden + 63) / 64, T * k, hidden, inter, hidden).total;
-}
-
-extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
-                                     const trellis_mat_t *w_down, const void *x, int32_t x_dtype,
-                                     const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k,
-                                     uint16_t *h, float *y, void *workspace, size_t workspace_bytes,
-                                     hipEvent_t *events) {
+template <typename F>
+static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const void *x, int32_t x_dtype,
+                    const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k, uint16_t *h, float *y,
+                    void *workspace, size_t workspace_bytes, hipEvent_t *events) {
   int rc;
-  if ((rc = check_mat(w_gate_up)) || (rc = check_mat(w_down))) return rc;
+  if ((rc = check_mats(gu)) || (rc = check_mats(dn))) return rc;
   if (!x || !topk_ids || !h || !y || !workspace) return TRELLIS_ENULL;
   if (x_dtype != TRELLIS_F32 && x_dtype != TRELLIS_BF16) return TRELLIS_EINVAL;
   if ((rc = check_routing(T, k))) return rc;
-  const int E = w_gate_up->n_mat, hidden = w_gate_up->cols, inter = w_gate_up->rows / 2;
-  if (w_gate_up->rows % 64 || w_down->n_mat != E || w_down->rows != hidden || w_down->cols != inter)
-    return TRELLIS_EINVAL;
+  const int E = gu.n_mat, hidden = gu.cols, inter = gu.rows / 2;
+  if (gu.rows % 64 || dn.n_mat != E || dn.rows != hidden || dn.cols != inter) return TRELLIS_EINVAL;
   const int max_act = std::min(E, T * k);
-  const Layout L = make_layout(max_act, (hidden + 63) / 64, T * k, hidden, inter, hidden);
+  const Layout L = make_layout<F>(max_act, (hidden + 63) / 64, T * k, hidden, inter, hidden);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
   char *ws = (char *)workspace;
   LayerArgs a{};
   a.mode = MODE_FFN;
-  a.w1 = w_gate_up->syms; a.s1 = w_gate_up->scales; a.rows1 = w_gate_up->rows; a.cols1 = hidden;
-  a.w2 = w_down->syms; a.s2 = w_down->scales; a.rows2 = hidden; a.cols2 = inter;
+  a.w1 = (const uint32_t *)gu.w; a.s1 = gu.scales; a.rows1 = gu.rows; a.cols1 = hidden;
+  a.w2 = (const uint32_t *)dn.w; a.s2 = dn.scales; a.rows2 = hidden; a.cols2 = inter;
   a.E = E; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
   a.x = x; a.x_bf16 = x_dtype == TRELLIS_BF16; a.x_per_slot = 0;
   a.inter = inter; a.h = h;
-  a.h_steps = steps_for_blocks(inter / 32);
+  a.h_steps = fmt_steps<F>(inter / 32);
   a.hq = (uint8_t *)(ws + L.hq); a.hs = (uint8_t *)(ws + L.hs);
   a.yslot = (float *)(ws + L.yslot);
   a.y = y; a.y_rows = hidden;
@@ -1107,13 +1162,55 @@ extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_
   a.n_s1 = max_act * a.n_rg1;
   a.n_rt2 = (hidden + 63) / 64;
   a.n_s2 = max_act * a.n_rt2;
-  a.x_resident = T == 1 && steps_for_blocks(hidden / 32) <= 2 * kPieceMax;
-  a.n_xprep = (4 * steps_for_blocks(hidden / 32) + kThreads / 32 - 1) / (kThreads / 32);
+  const int J = (hidden / 32 + F::kBlocks - 1) / F::kBlocks;
+  a.x_resident = T == 1 && J <= kPieceMax;
+  a.n_xprep = (4 * fmt_steps<F>(hidden / 32) + kThreads / 32 - 1) / (kThreads / 32);
   a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
   if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
-  rc = launch(a, cus, stream);
+  rc = launch<F>(a, cus, stream);
   if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
   return rc;
+}
+
+static Mats trellis_mats(const trellis_mat_t *w) {
+  return w ? Mats{w->syms, w->scales, w->n_mat, w->rows, w->cols} : Mats{nullptr, nullptr, 0, 0, 0};
+}
+static Mats mx_mats(const trellis_mx_t *w) {
+  return w ? Mats{w->codes, w->scales, w->n_mat, w->rows, w->cols} : Mats{nullptr, nullptr, 0, 0, 0};
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
+                                                  int32_t k) {
+  if (n_mat < 1 || cols < 32 || cols % 32 || rows < 1 || check_routing(T, k)) return 0;
+  return make_layout<FmtTrellis>(0, (rows + 63) / 64, T * k, rows, 0, cols).total;
+}
+
+extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
+                                int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w,
+                                int32_t T, int32_t k, float *y, void *workspace, size_t workspace_bytes) {
+  if (!w) return TRELLIS_ENULL;
+  return gemv_impl<FmtTrellis>(stream, trellis_mats(w), x, x_dtype, x_per_slot, topk_ids, topk_w, T, k, y,
+                               workspace, workspace_bytes);
+}
+
+extern "C" size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t inter, int32_t T,
+                                                 int32_t k) {
+  if (n_exp < 1 || hidden < 32 || hidden % 32 || inter < 32 || inter % 32 || check_routing(T, k)) return 0;
+  return make_layout<FmtTrellis>(std::min(n_exp, T * k), (hidden + 63) / 64, T * k, hidden, inter, hidden).total;
+}
+
+extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
+                                     const trellis_mat_t *w_down, const void *x, int32_t x_dtype,
+                                     const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k,
+                                     uint16_t *h, float *y, void *workspace, size_t workspace_bytes,
+                                     hipEvent_t *events) {
+  if (!w_gate_up || !w_down) return TRELLIS_ENULL;
+  return ffn_impl<FmtTrellis>(stream, trellis_mats(w_gate_up), trellis_mats(w_down), x, x_dtype, topk_ids, topk_w,
+                              T, k, h, y, workspace, workspace_bytes, events);
 }
 
 extern "C" int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_up, const trellis_mat_t *w_down,
@@ -1122,6 +1219,34 @@ extern "C" int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_u
                                size_t workspace_bytes) {
   return trellis_moe_ffn_timed(stream, w_gate_up, w_down, x, x_dtype, topk_ids, topk_w, T, k, h, y, workspace,
                                workspace_bytes, nullptr);
+}
+
+// Expanded MXFP4 weights: the same kernels with the weights' nibbles fed to
+// the matrix cores as stored. MXFP4 steps never outnumber trellis steps for
+// a width, so the trellis workspace sizes cover both.
+static int check_mx_align(const trellis_mx_t *w) {
+  if (!w) return TRELLIS_ENULL;
+  if (((uintptr_t)w->codes & 15) || ((uintptr_t)w->scales & 15)) return TRELLIS_EINVAL;
+  return TRELLIS_OK;
+}
+
+extern "C" int trellis_mxfp4_moe_gemv(hipStream_t stream, const trellis_mx_t *w, const void *x, int32_t x_dtype,
+                                      int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w,
+                                      int32_t T, int32_t k, float *y, void *workspace, size_t workspace_bytes) {
+  int rc = check_mx_align(w);
+  if (rc) return rc;
+  return gemv_impl<FmtMx>(stream, mx_mats(w), x, x_dtype, x_per_slot, topk_ids, topk_w, T, k, y, workspace,
+                          workspace_bytes);
+}
+
+extern "C" int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, const trellis_mx_t *w_down,
+                                     const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,
+                                     int32_t T, int32_t k, uint16_t *h, float *y, void *workspace,
+                                     size_t workspace_bytes) {
+  int rc;
+  if ((rc = check_mx_align(w_gate_up)) || (rc = check_mx_align(w_down))) return rc;
+  return ffn_impl<FmtMx>(stream, mx_mats(w_gate_up), mx_mats(w_down), x, x_dtype, topk_ids, topk_w, T, k, h, y,
+                         workspace, workspace_bytes, nullptr);
 }
 
 #ifdef TQ_TRACE
