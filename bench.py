@@ -1,25 +1,37 @@
-"""Benchmark: compressed-weight GB/s of the fused trellis-decode MoE layer at batch 1.
+"""Benchmark of the trellis-coded FP4 hot path on one MI355X.
 
-One step = one whole MoE layer through the C ABI (trellis_moe_ffn): routing
-and activation prep, the fused decode + FP4 matrix-core gate_up GEMV with the
-SwiGLU epilogue, and the fused down GEMV with the gate-weighted combine.
+Default (the headline): compressed-weight GB/s of the fused trellis-decode
+MoE layer at batch 1 -- 32 experts, top-4, hidden = intermediate = 2880, one
+token (gpt-oss-class layer shape) -- through the C ABI (trellis_moe_ffn):
+routing, the activation split, the fused decode + FP4 matrix-core gate_up
+GEMV with the SwiGLU epilogue, and the fused down GEMV with the gate-weighted
+combine, all in one kernel launch. A step is one layer for one routed token.
 
-Default workload: 32 experts, top-4, hidden = intermediate = 2880, one token
-(gpt-oss-class layer shape; synthetic symbols, scales, activations and
-routing from workloads.py). Weights are resident in HBM before timing. To
-keep the 256 MB Infinity Cache from serving repeated weights, the steps walk
-a ring of distinct layer instances totalling >= --ring-gb GiB.
+Other workloads (--workload):
+  ffn1      one expert FFN, gate_up 5760x2880 + down 2880x2880, batch 1
+  gemv1     one 256x1024 matrix, fp32 x, batch 1 (trellis_moe_gemv)
+  moe128:T  128 experts, top-8, hidden 4096, intermediate 1536, Zipf(1.1)
+            routing, T tokens (batch sweep; T >= 16 is the matrix-core path)
+  expand    expand mode: decode all 128 experts x 3 matrices (4096x1536)
+            into resident MXFP4 (trellis_decode_expand)
+  mx128:T   expand mode, second half: the 128-expert layer on the expanded
+            MXFP4 weights (trellis_mxfp4_moe_ffn)
+  mx32      the default layer shape on expanded MXFP4 weights
 
-Printed: one JSON line with the throughput (algorithmic compressed bytes of
-the experts each step touches / wall time), a roofline entry for the
-dominant kernel (its average duration from HIP events recorded around it in
-the timed region, on the stream it runs on), and the CPU oracle's rate on a
-bounded sample as a reported baseline.
+All data is synthetic (workloads.py) and resident in HBM before timing. To
+keep the 256 MB Infinity Cache from serving repeated weights, steps walk a
+ring of distinct copies of the weights totalling >= --ring-gb GiB.
+
+Printed: one JSON line with the whole-job throughput, a roofline entry for
+the kernel (its average duration from HIP events recorded around each launch
+in the timed region, on the stream it runs on), and the CPU oracle's rate on
+a bounded sample as a reported baseline.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -32,8 +44,11 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
-BYTES_PER_WEIGHT = 0.25 + 1.0 / 32.0      # 2-bit symbol + one UE8M0 byte per 32 weights
+TRELLIS_BPW = 0.25 + 1.0 / 32.0           # 2-bit symbol + one UE8M0 byte per 32 weights
+MX_BPW = 0.5 + 1.0 / 32.0                 # E2M1 nibble + UE8M0 byte per 32 weights
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
+FP4_PEAK_TFLOPS = 10100.0                 # MI355X dense FP4 matrix cores, published
+METRIC = "compressed-weight GB/s of fused trellis-decode MoE GEMV (batch 1) + % HBM peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -43,12 +58,12 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="moe32",
-                   help="moe32 (default) | ffn1 | moe128:T")
+                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32")
     p.add_argument("--ring-gb", type=float, default=1.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-stage-events", action="store_true",
-                   help="time only the whole step (no events between kernels)")
+                   help="no events around each launch (time only the whole timed region)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB ten times (reference for the HBM "
                         "byte counters of a profiler) and exit")
@@ -69,38 +84,232 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 10}), flush=True)
 
 
-def workload_cfg(name):
-    if name == "moe32":
-        return workloads.MOE_32E
-    if name == "ffn1":
-        return workloads.EXPERT_FFN
-    if name.startswith("moe128:"):
-        return workloads.moe_128e(int(name.split(":")[1]))
-    raise SystemExit(f"unknown workload {name}")
+# ---------------------------------------------------------------- HIP events on the launch stream
+
+class Hip:
+    def __init__(self):
+        L = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
+        L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L = L
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.L.hipEventCreate(ctypes.byref(e))
+        assert rc == 0, rc
+        return e.value
+
+    def record(self, ev, stream):
+        rc = self.L.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        assert rc == 0, rc
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        assert rc == 0, rc
+        return ms.value
 
 
-def hip():
-    L = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
-    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    return L
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).cuda()
 
 
-def new_event(H):
-    e = ctypes.c_void_p()
-    rc = H.hipEventCreate(ctypes.byref(e))
-    assert rc == 0, rc
-    return e.value
+def ring_copies(tensors, bytes_per_copy, ring_gb):
+    """Distinct device copies of `tensors`, enough to total >= ring_gb GiB."""
+    n = max(1, int(np.ceil(ring_gb * (1 << 30) / bytes_per_copy)))
+    return [tensors] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
 
 
-def elapsed_ms(H, a, b):
-    ms = ctypes.c_float()
-    rc = H.hipEventElapsedTime(ctypes.byref(ms), a, b)
-    assert rc == 0, rc
-    return ms.value
+# ---------------------------------------------------------------- workloads
+#
+# Each returns a dict: name/config, step(s, events) that enqueues one step
+# (recording events[0] / events[1] around the launch when given), per-step
+# algorithmic bytes, and optionally flops and a CPU-oracle sample.
+
+def layer_workload(args, cfg, mx=False):
+    import torch
+    import trellis_coded_fp4_amd as tq
+    E, H, I = cfg.n_exp, cfg.hidden, cfg.inter
+    L0 = workloads.moe_layer(cfg)
+    w0 = (dev(L0.gu_syms), dev(L0.gu_scales), dev(L0.dn_syms), dev(L0.dn_scales))
+    bpw = MX_BPW if mx else TRELLIS_BPW
+    if mx:
+        gc, gs = tq.decode_expand(w0[0], w0[1])
+        dc, ds = tq.decode_expand(w0[2], w0[3])
+        torch.cuda.synchronize()
+        w0 = (gc, gs, dc, ds)
+    expert_weights = 3 * H * I
+    ring = ring_copies(w0, E * expert_weights * bpw, args.ring_gb)
+    routes, uniq, slots = [], [], []
+    for s in range(args.warmup + args.steps):
+        x, ids, gw = (L0.x, L0.ids, L0.gate_w) if s == 0 else workloads.moe_batch(cfg, 0, 1000 + s)
+        xs = dev(x).to(torch.bfloat16) if cfg.x_bf16 else dev(x)
+        routes.append((xs, dev(ids), dev(gw)))
+        live = ids[(ids >= 0) & (ids < E)]
+        uniq.append(len(np.unique(live)))
+        slots.append(len(live))
+    T, k = cfg.T, cfg.k
+    ws = tq.ffn_workspace(E, H, I, T, k)
+    h = torch.empty((T, k, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(s, events=None):
+        a, b, c, d = ring[s % len(ring)]
+        xs, ids, gw = routes[s]
+        if mx:
+            if events:
+                hip.record(events[0], stream)
+            tq.mxfp4_moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws)
+            if events:
+                hip.record(events[1], stream)
+        else:
+            tq.moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws,
+                       events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
+
+    def cpu_sample(seconds):
+        import oracle
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.moe_ffn(L0.gu_syms, L0.gu_scales, L0.dn_syms, L0.dn_scales, L0.x, L0.ids, L0.gate_w)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return done * uniq[0] * expert_weights * TRELLIS_BPW / dt / 1e9, \
+            f"{done} full layer step(s) of the same workload (routing of step 0), single-threaded C oracle, {dt:.1f} s"
+
+    kernel = ("k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)" if mx else
+              "k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 matrix-core "
+              "gate_up + SwiGLU, down + combine)")
+    return dict(
+        name=cfg.name + (" [expanded MXFP4]" if mx else ""), step=step, hip=hip, stream=stream,
+        bytes=lambda s: uniq[s] * expert_weights * bpw,
+        flops=lambda s: 2.0 * slots[s] * expert_weights,
+        tokens=T, kernel=kernel, cpu=cpu_sample,
+        config={"n_experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
+                "bytes_per_weight": bpw, "weights": "expanded MXFP4" if mx else "trellis-coded",
+                "ring_copies": len(ring)})
+
+
+def gemv_workload(args):
+    import torch
+    import trellis_coded_fp4_amd as tq
+    c = workloads.SINGLE_MATRIX
+    rows, cols = c["rows"], c["cols"]
+    syms = workloads.symbols(workloads.rng(c["config_id"], 0), 1, rows, cols)
+    sc = workloads.scales(workloads.rng(c["config_id"], 1), 1, rows, cols)
+    x = workloads.activations(workloads.rng(c["config_id"], workloads.T_X), 1, cols, bf16=False)
+    w0 = (dev(syms), dev(sc))
+    ring = ring_copies(w0, rows * cols * TRELLIS_BPW, args.ring_gb)
+    xs, ids = dev(x), dev(np.zeros((1, 1), np.int32))
+    ws = tq.gemv_workspace(1, rows, cols, 1, 1)
+    y = torch.empty((1, 1, rows), dtype=torch.float32, device="cuda")
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(s, events=None):
+        a, b = ring[s % len(ring)]
+        if events:
+            hip.record(events[0], stream)
+        tq.moe_gemv(a, b, xs, ids, y=y, workspace=ws)
+        if events:
+            hip.record(events[1], stream)
+
+    def cpu_sample(seconds):
+        import oracle
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.moe_gemv(syms, sc, x, np.zeros((1, 1), np.int32))
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return done * rows * cols * TRELLIS_BPW / dt / 1e9, f"{done} GEMV(s), single-threaded C oracle, {dt:.1f} s"
+
+    return dict(name=c["name"], step=step, hip=hip, stream=stream, bytes=lambda s: rows * cols * TRELLIS_BPW,
+                flops=lambda s: 2.0 * rows * cols, tokens=1, cpu=cpu_sample,
+                kernel="k_layer<FmtTrellis> (routed GEMV, one slot)",
+                config={"rows": rows, "cols": cols, "tokens": 1, "x": "fp32", "ring_copies": len(ring)})
+
+
+def expand_workload(args):
+    import torch
+    import trellis_coded_fp4_amd as tq
+    c = workloads.EXPAND_128E
+    n, rows, cols = 3 * c["n_exp"], c["rows"], c["cols"]
+    # 384 matrices of uniform symbols and scales in 124..130, drawn on the device
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(c["config_id"])
+    syms = torch.randint(-2**31, 2**31 - 1, (n, rows, cols // 16), dtype=torch.int32, device="cuda", generator=gen)
+    sc = torch.randint(workloads.SCALE_LO, workloads.SCALE_HI + 1, (n, rows, cols // 32), dtype=torch.uint8,
+                       device="cuda", generator=gen)
+    codes = torch.empty((n, rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales_out = torch.empty((n, rows, cols // 32), dtype=torch.uint8, device="cuda")
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    weights = n * rows * cols
+
+    def step(s, events=None):
+        if events:
+            hip.record(events[0], stream)
+        tq.decode_expand(syms, sc, codes_out=codes, scales_out=scales_out)
+        if events:
+            hip.record(events[1], stream)
+
+    g = workloads.rng(c["config_id"], 0)
+    small = (workloads.symbols(g, 1, 64, cols), workloads.scales(g, 1, 64, cols))
+
+    def cpu_sample(seconds):
+        import oracle
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.expand(*small)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return done * 64 * cols * TRELLIS_BPW / dt / 1e9, \
+            f"{done} expand(s) of a 64x{cols} matrix, single-threaded C oracle, {dt:.1f} s"
+
+    return dict(name=c["name"], step=step, hip=hip, stream=stream, bytes=lambda s: weights * TRELLIS_BPW,
+                flops=None, tokens=None, cpu=cpu_sample, traffic_bytes=weights * (TRELLIS_BPW + MX_BPW),
+                kernel="k_expand_quads (decode to packed E2M1 + scale copy)",
+                config={"matrices": n, "rows": rows, "cols": cols, "read_bytes": weights * TRELLIS_BPW,
+                        "write_bytes": weights * MX_BPW})
+
+
+def pick(args):
+    w = args.workload
+    if w == "moe32":
+        return layer_workload(args, workloads.MOE_32E)
+    if w == "mx32":
+        return layer_workload(args, workloads.MOE_32E, mx=True)
+    if w == "ffn1":
+        return layer_workload(args, workloads.EXPERT_FFN)
+    if w == "gemv1":
+        return gemv_workload(args)
+    if w == "expand":
+        return expand_workload(args)
+    if w.startswith("moe128:"):
+        return layer_workload(args, workloads.moe_128e(int(w.split(":")[1])))
+    if w.startswith("mx128:"):
+        return layer_workload(args, workloads.moe_128e(int(w.split(":")[1])), mx=True)
+    raise SystemExit(f"unknown workload {w}")
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "trellis_coded_fp4_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def main():
@@ -113,119 +322,69 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     import torch
-    import trellis_coded_fp4_amd as tq
-
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    cfg = workload_cfg(args.workload)
-    E, H_, I = cfg.n_exp, cfg.hidden, cfg.inter
-    layer_weights = E * (2 * I * H_ + H_ * I)
-    layer_bytes = layer_weights * BYTES_PER_WEIGHT
-    n_layers = max(1, int(np.ceil(args.ring_gb * (1 << 30) / layer_bytes)))
-
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).cuda()
-
-    ring = []
-    for li in range(n_layers):
-        L = workloads.moe_layer(cfg, layer_id=li)
-        ring.append((dev(L.gu_syms), dev(L.gu_scales), dev(L.dn_syms), dev(L.dn_scales)))
-        if li == 0:
-            layer0 = L
-    # one routed batch per step, drawn up front and resident on the device
-    n_route = args.warmup + args.steps
-    routes = []
-    uniq = []
-    for s in range(n_route):
-        if s:
-            x_np, ids_np, gw_np = workloads.moe_batch(cfg, layer_id=0, rep=1000 + s)
-        else:
-            x_np, ids_np, gw_np = layer0.x, layer0.ids, layer0.gate_w
-        xs = dev(x_np).to(torch.bfloat16) if cfg.x_bf16 else dev(x_np)
-        routes.append((xs, dev(ids_np), dev(gw_np)))
-        uniq.append(len(np.unique(ids_np[(ids_np >= 0) & (ids_np < E)])))
-    T, k = cfg.T, cfg.k
-    ws = tq.ffn_workspace(E, H_, I, T, k)
-    h = torch.empty((T, k, I), dtype=torch.bfloat16, device="cuda")
-    y = torch.empty((T, H_), dtype=torch.float32, device="cuda")
-    Hl = hip()
-    stream = torch.cuda.current_stream()
-    ev_arrays = []
-    for s in range(args.steps):
-        arr = (ctypes.c_void_p * 4)()
-        if not args.no_stage_events:
-            for i in range(2):
-                arr[i] = new_event(Hl)
-        ev_arrays.append(arr)
-    t0e, t1e = new_event(Hl), new_event(Hl)
-
-    def step(s, events=None):
-        gs, ge, ds, de = ring[s % n_layers]
-        xs, ids, gw = routes[s]
-        tq.moe_ffn(gs, ge, ds, de, xs, ids, gw, h=h, y=y, workspace=ws, events=events)
+    W = pick(args)
+    hip, stream = W["hip"], W["stream"]
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)] if not args.no_stage_events else None
+    t0e, t1e = hip.event(), hip.event()
 
     for s in range(args.warmup):
-        step(s)
+        W["step"](s)
     torch.cuda.synchronize()
-    Hl.hipEventRecord(t0e, ctypes.c_void_p(stream.cuda_stream))
+    hip.record(t0e, stream)
     w0 = time.perf_counter()
     for s in range(args.steps):
-        step(args.warmup + s, None if args.no_stage_events else ev_arrays[s])
-    Hl.hipEventRecord(t1e, ctypes.c_void_p(stream.cuda_stream))
+        W["step"](args.warmup + s, evs[s] if evs else None)
+    hip.record(t1e, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    total_ms = elapsed_ms(Hl, t0e, t1e)
+    total_ms = hip.elapsed_ms(t0e, t1e)
     ms_per_step = total_ms / args.steps
-
-    expert_bytes = (2 * I * H_ + H_ * I) * BYTES_PER_WEIGHT
-    timed_uniq = uniq[args.warmup:]
-    total_bytes = sum(u * expert_bytes for u in timed_uniq)
+    timed = range(args.warmup, args.warmup + args.steps)
+    total_bytes = sum(W["bytes"](s) for s in timed)
     value = total_bytes / (total_ms * 1e-3) / 1e9
 
-    roofline = None
-    stages = None
-    if not args.no_stage_events:
-        d = np.array([elapsed_ms(Hl, ev[0], ev[1]) for ev in ev_arrays])
-        stages = {"layer_kernel_us": float(d.mean() * 1e3), "layer_kernel_us_min": float(d.min() * 1e3),
+    roofline, launch = None, None
+    if evs:
+        d = np.array([hip.elapsed_ms(a, b) for a, b in evs])
+        launch = {"kernel_us_mean": float(d.mean() * 1e3), "kernel_us_min": float(d.min() * 1e3),
                   "step_us": float(ms_per_step * 1e3)}
-        launch_bytes = float(np.mean([u * expert_bytes for u in timed_uniq]))
-        achieved = launch_bytes / (d.mean() * 1e-3) / 1e9
+        per_launch = float(np.mean([W["bytes"](s) for s in timed]))
+        achieved = per_launch / (d.mean() * 1e-3) / 1e9
         traffic = None
         if os.path.exists(PROFILE_TRAFFIC):
             try:
-                tr = json.load(open(PROFILE_TRAFFIC))
-                if tr.get("workload") == args.workload and tr.get("kernel_source_sha") == _kernel_sha():
+                tr = json.load(open(PROFILE_TRAFFIC)).get(args.workload, {})
+                if tr.get("kernel_source_sha") == kernel_sha():
                     traffic = tr.get("bytes_per_launch")
-            except Exception:
+            except (OSError, ValueError):
                 traffic = None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": "k_layer (whole MoE layer: routing, activation split, fused decode + FP4 MFMA "
-                              "gate_up + SwiGLU, down + combine)",
-                    "bytes_per_launch": launch_bytes}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": W["kernel"],
+                    "bytes_per_launch": per_launch}
+        if W.get("traffic_bytes"):
+            roofline["read_plus_write_GBs"] = round(W["traffic_bytes"] / (d.mean() * 1e-3) / 1e9, 1)
+        if W.get("flops"):
+            fl = float(np.mean([W["flops"](s) for s in timed]))
+            tf = fl / (d.mean() * 1e-3) / 1e12
+            roofline["matrix_core"] = {"useful_tflops": round(tf, 3), "fp4_dense_peak_tflops": FP4_PEAK_TFLOPS,
+                                       "frac": round(tf / FP4_PEAK_TFLOPS, 6), "flops_per_launch": fl}
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        L0 = layer0
-        done = 0
-        bytes_done = 0.0
-        c0 = time.perf_counter()
-        while True:
-            oracle.moe_ffn(L0.gu_syms, L0.gu_scales, L0.dn_syms, L0.dn_scales, L0.x, L0.ids, L0.gate_w)
-            done += 1
-            bytes_done += uniq[0] * expert_bytes
-            if time.perf_counter() - c0 >= args.cpu_seconds:
-                break
-        cdt = time.perf_counter() - c0
-        cpu = {"value": round(bytes_done / cdt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} full layer step(s) of the same workload (routing of step 0), "
-                         f"single-threaded C oracle, {cdt:.1f} s"}
+        v, sample = W["cpu"](args.cpu_seconds)
+        cpu = {"value": round(v, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
 
+    if args.workload == "moe32":
+        metric = METRIC
+    elif args.workload == "expand":
+        metric = "decode GB/s (compressed bytes read) of expand to MXFP4"
+    else:
+        metric = f"compressed-weight GB/s, {W['name']}"
     out = {
-        "metric": "compressed-weight GB/s of fused trellis-decode MoE GEMV (batch 1) + % HBM peak",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -235,29 +394,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32 decode, e2m1 x e4m3(hi+lo) -> f32",
+        "dtype": "u32 decode, e2m1 x e4m3(hi+lo) -> f32" if args.workload != "expand" else "u32 -> u8",
         "data": "synthetic",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
-        "config": {"workload": cfg.name, "n_experts": E, "top_k": k, "hidden": H_, "intermediate": I,
-                   "tokens": T, "bytes_per_weight": BYTES_PER_WEIGHT, "ring_layers": n_layers,
-                   "ring_gib": round(n_layers * layer_bytes / (1 << 30), 3),
-                   "stage_events": not args.no_stage_events, "wall_s": round(wall, 4)},
-        "stages": stages,
+        "tokens_per_s": round(W["tokens"] / (ms_per_step * 1e-3), 1) if W.get("tokens") else None,
+        "config": dict({"workload": W["name"]}, **W["config"],
+                       **{"stage_events": bool(evs), "wall_s": round(wall, 4)}),
+        "launch": launch,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-
-
-def _kernel_sha():
-    import hashlib
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "trellis_coded_fp4_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(d, f), "rb").read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":
