@@ -55,25 +55,42 @@ struct nib2 {
   uint32_t odd;   // nibble m = E2M1 code of weight 2m+1
 };
 
+// Three-input bitwise function with truth table IMM: output bit =
+// IMM bit ((a << 2) | (b << 1) | c), the v_bitop3_b32 form (IMM for f is
+// f(0xF0, 0xCC, 0xAA)). The host version serves the CPU check of this file.
+template <uint32_t IMM>
+TQ_HD uint32_t bop3(uint32_t a, uint32_t b, uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_bitop3_b32(a, b, c, IMM);
+#else
+  uint32_t r = 0;
+  for (int i = 0; i < 8; ++i)
+    if ((IMM >> i) & 1u) r |= ((i & 4) ? a : ~a) & ((i & 2) ? b : ~b) & ((i & 1) ? c : ~c);
+  return r;
+#endif
+}
+constexpr uint32_t kXor3 = 0x96;   // a ^ b ^ c
+constexpr uint32_t kSel = 0xCA;    // (a & b) | (~a & c): bits of b where a is set, else c
+constexpr uint32_t kXnorAnd = 0x87;   // ~(a ^ (b & c))
+
 // Decode one symbol word `g` whose predecessor in the row is `prev`
-// (0 at the row start).
+// (0 at the row start). 8 funnel shifts and 15 three-input operations.
 TQ_HD nib2 decode_word(uint32_t g, uint32_t prev) {
-  const uint32_t LO = 0x55555555u;
+  const uint32_t LO = 0x55555555u, M33 = 0x33333333u;
   const uint32_t x1 = shl_hist(g, prev, 1), x2 = shl_hist(g, prev, 2), x3 = shl_hist(g, prev, 3);
   const uint32_t x5 = shl_hist(g, prev, 5), x7 = shl_hist(g, prev, 7), x9 = shl_hist(g, prev, 9);
   const uint32_t x11 = shl_hist(g, prev, 11), x12 = shl_hist(g, prev, 12);
   // E: (e0, e1) in (lo, hi) lanes.  P: (p0, p1).
-  const uint32_t e_lo = x2 ^ x3 ^ x9;
-  const uint32_t e_hi = x1 ^ x11 ^ x12;
-  const uint32_t E = g ^ x7 ^ ((e_lo & LO) | (e_hi & ~LO));
-  const uint32_t P = g ^ x5 ^ x12 ^ ((x1 & LO) | (x9 & ~LO));
+  const uint32_t e_lo = bop3<kXor3>(x2, x3, x9);
+  const uint32_t e_hi = bop3<kXor3>(x1, x11, x12);
+  const uint32_t E = bop3<kXor3>(g, x7, bop3<kSel>(LO, e_lo, e_hi));
+  const uint32_t P = bop3<kXor3>(bop3<kXor3>(g, x5, x12), bop3<kSel>(LO, x1, x9), 0u);
   const uint32_t N = E >> 1;                    // e1 moved into the lo lane
-  const uint32_t R = (N & LO) | (E & ~LO);      // (e1, e1)
-  const uint32_t A = ~(P ^ R);                  // (mantissa, exp_lo)
-  const uint32_t B = ~(E ^ (N & LO));           // (exp_hi, sign)
+  const uint32_t A = ~(P ^ bop3<kSel>(LO, N, E));   // (mantissa, exp_lo) = ~(P ^ (e1, e1))
+  const uint32_t B = bop3<kXnorAnd>(E, N, LO);      // (exp_hi, sign) = ~(E ^ (e1, 0))
   nib2 r;
-  r.even = (A & 0x33333333u) | ((B << 2) & 0xCCCCCCCCu);
-  r.odd = ((A >> 2) & 0x33333333u) | (B & 0xCCCCCCCCu);
+  r.even = bop3<kSel>(M33, A, B << 2);
+  r.odd = bop3<kSel>(M33, A >> 2, B);
   return r;
 }
 

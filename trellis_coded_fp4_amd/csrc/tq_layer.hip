@@ -528,13 +528,43 @@ __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *sro
   }
 }
 
+// The first kPre pieces of a trellis window decoded ahead of the matrix-core
+// loop: a down-projection item decodes them while it waits for its h, so
+// only the rest of the decode is left once h arrives.
+constexpr int kPre = 6;
+struct PreDec {
+  uint4 s[kPre][2];   // A operands of steps 2q and 2q+1
+};
+
+__device__ __forceinline__ void predecode(PreDec &d, const Tile &t, int np, uint32_t &carry, int lane) {
+  const int g = lane >> 4;
+  const int src = ((lane - 16) & 63) << 2;
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) {
+    if (q < np) {
+      const uint4 a = t.a[q];
+      const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
+      const uint32_t hist = g == 0 ? carry : rot;
+      carry = rot;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
+        const nib2 d0 = decode_word(w0, hw);
+        const nib2 d1 = decode_word(w1, w0);
+        d.s[q][hh] = make_uint4(d0.even, d0.odd, d1.even, d1.odd);
+      }
+    }
+  }
+}
+
 // Decode window pieces [0, np) (global piece p0 + q) and accumulate them
 // against NT N-tiles of the window's LDS columns. Lane
 // (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
 // (zeros when !on[n]).
 template <typename F, int NT>
-__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool tile_ok, int wpr, const uint8_t *as_w,
-                                         int astride, int a_p0, int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
+__device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int npre, int p0, int np, bool tile_ok,
+                                         int wpr, const uint8_t *as_w, int astride, int a_p0, int nb,
+                                         const uint8_t *lq, const uint8_t *ls, int psteps,
                                          const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
                                          uint32_t &carry, int lane) {
   const int g = lane >> 4, i16 = lane & 15;
@@ -573,10 +603,15 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool til
       // Words past the row end (clamped loads) decode to finite E2M1 values
       // that meet the zero codes of the activations' K padding, and rows past
       // the matrix give outputs that are never stored: no masking needed.
+      // pieces [0, npre) were decoded ahead (predecode); the rest decode here
+      const bool pre = q < kPre && q < npre;
       const uint4 a = t.a[q];
-      const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
-      const uint32_t hist = g == 0 ? carry : rot;
-      carry = rot;
+      uint32_t hist = 0u;
+      if (!pre) {
+        const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
+        hist = g == 0 ? carry : rot;
+        carry = rot;
+      }
       const int sb_a = 8 * j + 2 * g;
       const uint32_t sa =
           tile_ok && sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * (a_p0 + q) + 2 * g) : 0x7F7Fu;
@@ -596,10 +631,16 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool til
           B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
           sb[n] = ls[((size_t)c * psteps + step) * 4 + g];
         }
-        const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
-        const nib2 d0 = decode_word(w0, hw);
-        const nib2 d1 = decode_word(w1, w0);
-        const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        v8i A;
+        if (q < kPre && pre) {
+          const uint4 x = pd.s[q < kPre ? q : 0][hh];
+          A = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        } else {
+          const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
+          const nib2 d0 = decode_word(w0, hw);
+          const nib2 d1 = decode_word(w1, w0);
+          A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           if (hh == 0)
@@ -684,11 +725,12 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
 // loads are issued; stage(c0, ncol, p0, np) then fills the LDS;
 // epilogue(c0, ncol, acc) runs per slot group with the LDS free. With one
 // window the weight tile stays in registers across slot groups.
-// shared_cols: every slot reads LDS columns 0 (hi) and 1 (lo).
+// shared_cols: every slot reads LDS columns 0 (hi) and 1 (lo). predec:
+// decode the first pieces before stage runs (stage may wait).
 template <typename F, int NT, bool ALIGNED, typename Ahead, typename Stage, typename Epi>
 __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
-                                          int fast, int e, int r0, int ne, bool shared_cols, Ahead fetch_ahead,
-                                          Stage stage, Epi epilogue) {
+                                          int fast, int e, int r0, int ne, bool shared_cols, bool predec,
+                                          Ahead fetch_ahead, Stage stage, Epi epilogue) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const bool tile_ok = r0 < rows;
@@ -719,6 +761,10 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
     fetch_ahead(0, ne, 0, J);
     load_tile<ALIGNED>(tl, rowp, wpr, 0, J, g);
     TQ_MARK(S, 3);
+    PreDec pd;
+    // (not with 3-4 N-tiles: their accumulators leave no registers for it)
+    const int npre = predec && F::kSteps == 2 && NT <= 2 ? min(J, kPre) : 0;
+    if (npre) predecode(pd, tl, npre, carry, lane);
     stage(0, ne, 0, J);
     TQ_MARK(S, 4);
     if (fast) {
@@ -731,8 +777,8 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
     TQ_MARK(S, 5);
     __syncthreads();
     TQ_MARK(S, 6);
-    mma_tile<F, NT>(tl, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on, acc, carry,
-                    lane);
+    mma_tile<F, NT>(tl, pd, npre, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on, acc,
+                    carry, lane);
     TQ_MARK(S, 7);
     __syncthreads();
     epilogue(0, ne, acc);
@@ -766,8 +812,9 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
         ascale_generic<F>(as_w, srow, nb, p0, np, tile_ok);
       }
       __syncthreads();
-      mma_tile<F, NT>(tl, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np, col,
-                      on, acc, carry, lane);
+      PreDec pd;
+      mma_tile<F, NT>(tl, pd, 0, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np,
+                      col, on, acc, carry, lane);
       __syncthreads();   // everyone is done with the window's columns
     }
     epilogue(c0, ncol, acc);
@@ -878,7 +925,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       else a.y[(size_t)slot * a.rows1 + r0 + rr] = v;
     });
   };
-  gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, ahead, stage, epilogue);
+  gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, !s1, ahead, stage, epilogue);
   if (obsp_old >= 0 && obsp_old == min(a.grid, S.n_active * a.n_rg1) - 1) {
     // every workgroup that reads the split has fetched it: clear for the next call
     st_ctr(a.cntp, 0);
