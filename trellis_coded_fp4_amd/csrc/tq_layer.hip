@@ -1,1232 +1,7 @@
-// tq_layer.hip -- fused trellis-decode mixture-of-experts GEMV / small-batch GEMM on gfx950.
-//
-// HEPH abstract (ICLR 2027 submission page): in "fused" serving the
-// compressed streams stay resident and every weight is decoded inside the
-// grouped-MoE kernel on each forward pass. Here the decoded E2M1 nibbles go
-// straight into the FP4 x FP8 block-scaled matrix cores, with the weights'
-// UE8M0 exponents as the A scales, at every batch size: the vector ALUs do
-// the decode, the matrix cores the multiply-accumulate.
-//
-// One persistent launch per call; its workgroups take work items
-// round-robin. An item is one active expert x 64 output rows (a 16-row tile
-// per wave) of a grouped GEMM whose columns are the routing slots sent to
-// that expert:
-//   stage-1 items  the first (or only) matrix; the activations are split on
-//                  the spot into two FP8 E4M3 terms (hi + lo, UE8M0 scale per
-//                  32) in matrix-core B layout in LDS. Epilogue: per-slot
-//                  output; or per-slot partial output + combine (below); or,
-//                  in a layer, SwiGLU over 32 gate rows and the matching 32
-//                  up rows, writing h (bf16) and its FP8 hi/lo split, which
-//                  is exactly one K-block of the down projection.
-//   stage-2 items  a layer's down projection; its columns are the h splits
-//                  of the expert's slots, copied into LDS once every
-//                  stage-1 item of that expert has finished.
-// Combine: per-slot partial outputs go to the workspace; the item that
-// arrives last at a 64-row output tile (a counter per tile) sums them with
-// the gate weights, in slot order, into y. No atomics touch outputs and the
-// summation order is fixed, so results are deterministic.
-//
-// Synchronisation costs no grid-wide barrier: counters live one per
-// 128-byte line (device-scope atomics on one address serialise), each is
-// cleared by the last work item that reads it, so a workspace returns to
-// zero at the end of every call. Cross-workgroup data (h splits, partial
-// outputs) moves through device-coherent stores and loads; a producer waits
-// for its stores to complete before it counts. The grid never exceeds the
-// co-resident workgroup count and items run in index order, so every wait
-// is for running work; waits are bounded and set an error word on timeout.
-//
-// Weight streaming: a wave owns one 16-row tile. Lane (row i, lane-group g)
-// loads "piece" j = 16 bytes = blocks 8j+2g, 8j+2g+1 of its row and feeds
-// them to matrix-core steps 2j and 2j+1 as K-block g (the activations are
-// laid out to match). A wave instruction reads 16 rows x 64 contiguous bytes;
-// up to 16 pieces (K <= 4096) are in flight at once. The tile's UE8M0 bytes
-// are one contiguous run (rows are contiguous): they are fetched with a few
-// 16-byte loads into the wave's LDS slot instead of one 2-byte load per
-// piece. Activation loads are issued before the weight loads, because loads
-// complete in issue order. The decoder history of a block is the word before
-// it: from the neighbouring lane-group's piece via ds_bpermute, or the
-// previous piece.
-#include <hip/hip_runtime.h>
-
-#include <algorithm>
-#include <cstring>
-
-#include "tq_common.h"
-
-namespace tq {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxT = 32;
-constexpr int kMaxK = 32;
-constexpr int kMaxSlots = 1024;
-constexpr int kMaxExperts = 1024;
-constexpr int kPieceMax = 16;               // pieces per register window: 16 x 256 weights
-constexpr unsigned kSpinLimit = 1u << 20;   // polls (device-coherent load + sleep)
-constexpr int kBBytes = 32 * 1024;          // LDS for one pass of activation columns (codes)
-constexpr int kBScaleBytes = 1024;          // and their UE8M0 scales
-constexpr int kAScaleBytes = 2048;          // per wave: its tile's UE8M0 bytes (16 rows x <= 128)
-constexpr int kXPre = 16;                   // activation values per lane fetched ahead of the weights
-constexpr int kLineInts = 32;               // one counter per 128-byte line
-
-enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
-
-// Weight formats. A "piece" is what a lane loads with one 16-byte load from
-// its row: for trellis-coded weights 8 blocks of 32 (256 two-bit symbols)
-// feeding two matrix-core steps; for expanded MXFP4 weights one step's 4
-// blocks (128 E2M1 nibbles, natural order). Each format has its own
-// activation layout: block b of a column goes to byte offset(b, pos) of the
-// step-chunk layout, its UE8M0 byte to scale_index(b).
-struct FmtTrellis {
-  static constexpr int kSteps = 2;    // matrix-core steps per piece
-  static constexpr int kBlocks = 8;   // 32-weight blocks per piece
-  static constexpr int kWords = 2;    // 32-bit words per block
-  __device__ __host__ static int offset(int b, int pos) { return act_offset(b, pos); }
-  __device__ __host__ static int scale_index(int b) { return act_scale_index(b); }
-  // block of step st (within a pass) whose data is K-block beta of the step
-  __device__ __host__ static int block_of(int st, int beta) { return 8 * (st >> 1) + 2 * beta + (st & 1); }
-};
-struct FmtMx {
-  static constexpr int kSteps = 1;
-  static constexpr int kBlocks = 4;
-  static constexpr int kWords = 4;
-  __device__ __host__ static int offset(int b, int pos) { return (b >> 2) * 128 + bchunk_offset(32 * (b & 3) + pos); }
-  __device__ __host__ static int scale_index(int b) { return b; }
-  __device__ __host__ static int block_of(int st, int beta) { return 4 * st + beta; }
-};
-template <typename F>
-__host__ __device__ inline int fmt_steps(int nb) { return F::kSteps * ((nb + F::kBlocks - 1) / F::kBlocks); }
-
-// int words at the start of the workspace (public)
-enum { ST_SKIPPED = 0, ST_ERROR = 1 };
-
-// Every device lambda is inlined: a real call would force the argument
-// block and the live registers through scratch memory.
-#define TQ_INLINE __attribute__((always_inline))
-
-// Timeline instrumentation, compiled in only with -DTQ_TRACE: per workgroup
-// 64 u64 slots of s_memrealtime stamps (entry, routing done, then ten per
-// item: id, start, marks 2..8, end).
-#ifdef TQ_TRACE
-#define TQ_MARK(S, k) do { if (threadIdx.x == 0 && (S).trp) (S).trp[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
-static void *g_trace = nullptr;
-#else
-#define TQ_MARK(S, k) do { } while (0)
-#endif
-
-struct Layout {
-  size_t status, cntp, cnt1, obs1, cnt2, yslot, hq, hs, xq, xs, total;
-};
-
-static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-// n_act: first-stage completion counters (layer only); n_rt: 64-row output
-// tiles that combine partial outputs; n_slots x y_rows partial outputs;
-// h_cols: width of the h splits (layer only); x_cols: width of one token's
-// split (the resident-token case).
-template <typename F>
-static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int x_cols) {
-  Layout L;
-  size_t o = 0;
-  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
-  L.status = take(256);
-  L.cntp = take(2 * kLineInts * 4);   // resident-token split: done count, readers count
-  L.cnt1 = take((size_t)n_act * kLineInts * 4);
-  L.obs1 = take((size_t)n_act * kLineInts * 4);
-  L.cnt2 = take((size_t)n_rt * kLineInts * 4);
-  L.yslot = take((size_t)n_slots * y_rows * 4);
-  const size_t hs = h_cols ? (size_t)fmt_steps<F>(h_cols / 32) : 0;
-  L.hq = take((size_t)n_slots * 2 * hs * 128);
-  L.hs = take((size_t)n_slots * 2 * hs * 4);
-  const size_t xs = (size_t)fmt_steps<F>(x_cols / 32);
-  L.xq = take(2 * xs * 128);
-  L.xs = take(2 * xs * 4);
-  L.total = o;
-  return L;
-}
-
-struct LayerArgs {
-  int mode;
-  const uint32_t *w1; const uint8_t *s1; int rows1, cols1, fast1;   // stage-1 matrices
-  const uint32_t *w2; const uint8_t *s2; int rows2, cols2, fast2;   // stage-2 matrices (layer)
-  int E, T, k;
-  const int32_t *ids;
-  const float *gate_w;          // may be null (all ones)
-  const void *x; int x_bf16; int x_per_slot;
-  int inter;                    // layer: intermediate width
-  uint16_t *h;                  // layer: [T][k][inter]
-  int h_steps; uint8_t *hq; uint8_t *hs;
-  float *yslot;                 // partial outputs [T*k][y_rows]
-  float *y;                     // SLOTS: [T][k][rows1]; COMBINE / layer: [T][y_rows]
-  int y_rows;
-  int *status, *cnt1, *obs1, *cnt2;
-  int n_rg1, n_s1;              // stage-1 row groups per expert, items
-  int n_rt2, n_s2;              // stage-2 row tiles per expert, items
-  int x_resident;               // one token, K <= 4096: split once per call, copied into each workgroup
-  int n_xprep;                  // workgroups that split it (at most; one 32-value block per half-wave)
-  uint8_t *xq; uint8_t *xs;     // the split token: columns 0 (hi), 1 (lo), step-chunk layout
-  int *cntp;                    // [0] split blocks done (x 1 per workgroup), [kLineInts] readers
-  int grid;
-#ifdef TQ_TRACE
-  unsigned long long *trace;
-#endif
-};
-
-struct Shared {
-  int16_t ids[kMaxSlots];       // expert per slot: -1 empty, >= E skipped (clamped)
-  int16_t slots[kMaxSlots];     // slots of the current expert, in slot order
-  int16_t active[kMaxExperts];  // active experts in id order
-  float gw[kMaxSlots];
-  unsigned mask[kMaxExperts / 32];
-  int wpre[kMaxExperts / 32 + 1];
-  int wcnt[kWaves];
-  int n_active;
-  int last;
-  int x_done;                   // the resident token's columns are in place
-#ifdef TQ_TRACE
-  unsigned long long *trp;
-#endif
-  // One pass of activation columns (step-chunk layout: 128 code bytes and 4
-  // scale bytes per column and step); after the matrix-core loop its upper
-  // half is reused for the per-wave accumulator dumps (a resident single
-  // token's columns, in the lower half, stay).
-  uint8_t bq[kBBytes] __attribute__((aligned(16)));
-  uint8_t bs[kBScaleBytes] __attribute__((aligned(16)));
-  uint8_t as[kWaves][kAScaleBytes] __attribute__((aligned(16)));
-};
-static_assert(kWaves * 4 * 256 * sizeof(float) <= kBBytes / 2, "accumulator dump must fit the column area");
-
-// ---------------------------------------------------------------- helpers
-
-__device__ __forceinline__ float load_x(const void *x, int bf16, size_t i) {
-  return bf16 ? bf16_to_f32(((const uint16_t *)x)[i]) : ((const float *)x)[i];
-}
-
-// Device-coherent accesses for data handed between workgroups.
-__device__ __forceinline__ void st_dc8(uint8_t *p, uint32_t v) {
-  __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dcf(float *p, float v) {
-  __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_dc64(const uint8_t *p) {
-  return __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dc32(const void *p) {
-  return __hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_ctr(const int *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_ctr(int *p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Every thread's device-coherent stores have completed (the workgroup's
-// results are visible device-wide); then one thread may count.
-__device__ __forceinline__ void stores_done() {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-}
-
-// Thread 0 waits until the counter reaches `target`; bounded: on timeout
-// the error word is set. The caller synchronises the workgroup after.
-__device__ __forceinline__ void spin_until(const int *ctr, int target, int *status) {
-  unsigned spins = 0;
-  while (ld_ctr(ctr) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_fetch_or(&status[ST_ERROR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-  }
-}
-
-// Maximum of a non-negative float over the 32 lanes of a half-wave. On
-// non-negative IEEE floats the bit patterns order like the values, so this
-// is an integer max: four DPP steps (quad xor 1, quad xor 2, half-row
-// mirror, row mirror) give the maximum over each 16-lane row, a swizzle
-// (xor 16) combines the two rows.
-__device__ __forceinline__ float halfwave_max(float v) {
-  int m = __float_as_int(v);
-  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));
-  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));
-  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x141, 0xF, 0xF, false));
-  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x140, 0xF, 0xF, false));
-  m = max(m, __builtin_amdgcn_ds_swizzle(m, 0x401F));
-  return __int_as_float(m);
-}
-
-// Two-term FP8 split of one 32-value block held by the 32 lanes of a
-// half-wave (lane = position in the block).
-struct Split {
-  uint32_t hi, lo;
-  int E, El;
-};
-__device__ __forceinline__ Split split_block(float v) {
-  Split s;
-  s.E = block_exponent(halfwave_max(fabsf(v)));
-  s.hi = f32_to_e4m3(ldexpf(v, -s.E));
-  const float r = v - ldexpf(e4m3_to_f32(s.hi), s.E);
-  s.El = block_exponent(halfwave_max(fabsf(r)));
-  s.lo = f32_to_e4m3(ldexpf(r, -s.El));
-  return s;
-}
-
-// Slot list of expert e into S.slots (slot order); returns the count.
-__device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int total = 0;
-  for (int base = 0; base < n; base += kThreads) {
-    const int i = base + threadIdx.x;
-    const bool p = i < n && S.ids[i] == e;
-    const unsigned long long bal = __ballot(p);
-    if (lane == 0) S.wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = total;
-    for (int w = 0; w < wave; ++w) off += S.wcnt[w];
-    if (p) S.slots[off + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)i;
-    for (int w = 0; w < kWaves; ++w) total += S.wcnt[w];
-    __syncthreads();
-  }
-  return total;
-}
-
-// ---------------------------------------------------------------- activation columns in LDS
-//
-// A pass covers pieces [kp, kp + np) of K: column c holds 2*np step chunks
-// (128 code bytes each, then 4 scale bytes per step in the scale area).
-// Column 2c / 2c+1 is the hi / lo term of column pair c.
-
-// Activation values of the pass, one unit = (column pair, block) per
-// half-wave; the first kXPre units of every half-wave can be fetched ahead.
-typedef uint32_t u32xp __attribute__((ext_vector_type(kXPre)));
-struct XPre {
-  u32xp v;                  // raw 32-bit words holding the values (a vector: stays in registers)
-};
-
-// Register hygiene for the loads below: a load's destination is never
-// written before the load (no "zero, then load if in range"), because that
-// makes the compiler wait for every load in flight. Out-of-range lanes load
-// from a clamped, valid address and the value is discarded at its use.
-
-// Element index of activation unit u (column pair, block) of the pass for
-// this lane's position; ok false past the pass or the row.
-template <typename F, typename RowMap>
-__device__ __forceinline__ size_t x_elem(const LayerArgs &a, int K, int nb, int kp, int np, int npairs, int u,
-                                         RowMap row_of, bool &ok) {
-  const int nbp = F::kBlocks * np, c = u / nbp, blk = F::kBlocks * kp + u - c * nbp;
-  ok = u < npairs * nbp && blk < nb;
-  return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (threadIdx.x & 31) : 0;
-}
-
-// One dword load per value for either dtype: the aligned word holding it
-// (a bf16 row has an even length, so the word stays inside the buffer).
-__device__ __forceinline__ uint32_t x_word(const LayerArgs &a, size_t elem) {
-  const size_t byte = elem << (a.x_bf16 ? 1 : 2);
-  return *(const uint32_t *)((const uint8_t *)a.x + (byte & ~(size_t)3));
-}
-
-__device__ __forceinline__ float x_value(const LayerArgs &a, size_t elem, uint32_t word) {
-  if (!a.x_bf16) return __uint_as_float(word);
-  return __uint_as_float((elem & 1 ? word >> 16 : word & 0xFFFFu) << 16);
-}
-
-// Raw words of units first, first + 8, ... (kXPre of them) of the pass.
-template <typename F, typename RowMap>
-__device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int nb, int kp, int np,
-                                       int npairs, int first, RowMap row_of) {
-  constexpr int kStride = kThreads / 32;
-  const int nbp = F::kBlocks * np, total = npairs * nbp;
-  int c = first / nbp, b = first - c * nbp;   // unit (c, b); nbp >= 4, so b wraps at most twice a step
-  size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
-#pragma unroll
-  for (int m = 0; m < kXPre; ++m) {
-    const int u = first + m * kStride, blk = F::kBlocks * kp + b;
-    const bool ok = u < total && blk < nb;
-    v[m] = x_word(a, ok ? rbase + (size_t)blk * 32 : 0);
-    b += kStride;
-    if (b >= nbp) {
-      b -= nbp;
-      ++c;
-      if (b >= nbp) {
-        b -= nbp;
-        ++c;
-      }
-      rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
-    }
-  }
-}
-
-template <typename F, typename RowMap>
-__device__ __forceinline__ void x_prefetch(XPre &xp, const LayerArgs &a, int K, int nb, int kp, int np, int npairs,
-                                           RowMap row_of) {
-  x_load<F>(xp.v, a, K, nb, kp, np, npairs, threadIdx.x >> 5, row_of);
-}
-
-template <typename F>
-__device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v, bool store) {
-  const int nbp = F::kBlocks * np, psteps = F::kSteps * np;
-  const int c = u / nbp, b = u % nbp, pos = threadIdx.x & 31;
-  const Split s = split_block(v);
-  if (!store) return;
-  const int off = F::offset(b, pos);
-  lq[(size_t)(2 * c) * psteps * 128 + off] = (uint8_t)s.hi;
-  lq[(size_t)(2 * c + 1) * psteps * 128 + off] = (uint8_t)s.lo;
-  if (pos == 0) {
-    ls[(size_t)(2 * c) * psteps * 4 + F::scale_index(b)] = (uint8_t)(s.E + 127);
-    ls[(size_t)(2 * c + 1) * psteps * 4 + F::scale_index(b)] = (uint8_t)(s.El + 127);
-  }
-}
-
-// Split the prefetched units, then load and split the rest of the pass.
-template <typename F, typename RowMap>
-__device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *ls, const LayerArgs &a, int K, int nb,
-                                         int kp, int np, int npairs, RowMap row_of) {
-  const int hw = threadIdx.x >> 5, total = npairs * F::kBlocks * np;
-  constexpr int kStride = kThreads / 32;
-  // Every half-wave splits all its prefetched units without branches (the
-  // cross-lane steps need the whole half-wave) and stores the real ones.
-#pragma unroll
-  for (int m = 0; m < kXPre; ++m) {
-    const int u = hw + m * kStride;
-    bool ok;
-    const size_t el = x_elem<F>(a, K, nb, kp, np, npairs, u, row_of, ok);
-    x_store_unit<F>(lq, ls, np, u, ok ? x_value(a, el, xp.v[m]) : 0.0f, u < total);
-  }
-  for (int base = hw + kXPre * kStride; base < total; base += kXPre * kStride) {
-    u32xp v;
-    x_load<F>(v, a, K, nb, kp, np, npairs, base, row_of);
-#pragma unroll
-    for (int m = 0; m < kXPre; ++m) {
-      const int u = base + m * kStride;
-      bool ok;
-      const size_t el = x_elem<F>(a, K, nb, kp, np, npairs, u, row_of, ok);
-      x_store_unit<F>(lq, ls, np, u, ok ? x_value(a, el, v[m]) : 0.0f, u < total);
-    }
-  }
-}
-
-// Block (0-based in the pass) held at byte `o` of pass step `st`'s chunk:
-// the chunk's 16-byte halves belong to K-blocks 0, 2, 0, 2, 1, 3, 1, 3.
-template <typename F>
-__device__ __forceinline__ int chunk_block(int st, int o) {
-  return F::block_of(st, 2 * ((o >> 4) & 1) + (o >> 6));
-}
-
-// Copy the pass's slice of stored activation columns (global step-chunk
-// layout, gsteps steps per column; LDS column c <- global column src_col(c))
-// with device-coherent loads, issued 8 per thread before any LDS write.
-// Blocks >= nb (the K padding, never written in global memory) become zero
-// codes with scale 127.
-template <typename F, typename ColMap>
-__device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
-                                          int gsteps, int kp, int np, int nb, int ncols, ColMap src_col) {
-  constexpr int kBatch = 8;
-  const int psteps = F::kSteps * np, per_col = psteps * 16;   // 8-byte pieces per column
-  const int total = ncols * per_col;
-  for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
-    uint64_t v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = min(base + u * kThreads, total - 1);
-      const int c = idx / per_col, p = idx - c * per_col;
-      v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + F::kSteps * kp + (p >> 4)) * 128 + (p & 15) * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = base + u * kThreads;
-      if (idx < total) {
-        const int p = idx % per_col;
-        const bool pad = F::kBlocks * kp + chunk_block<F>(p >> 4, (p & 15) * 8) >= nb;   // never written: zero it
-        *(uint64_t *)(lq + (size_t)idx * 8) = pad ? 0ull : v[u];
-      }
-    }
-  }
-  const int stotal = ncols * psteps;
-  for (int idx = threadIdx.x; idx < stotal; idx += kThreads) {
-    const int c = idx / psteps, st = idx - c * psteps;
-    uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + F::kSteps * kp + st) * 4);
-#pragma unroll
-    for (int beta = 0; beta < 4; ++beta)
-      if (F::kBlocks * kp + F::block_of(st, beta) >= nb) w = (w & ~(0xFFu << (8 * beta))) | (127u << (8 * beta));
-    *(uint32_t *)(ls + (size_t)idx * 4) = w;
-  }
-}
-
-// ---------------------------------------------------------------- weight tiles
-
-struct Tile {
-  uint4 a[kPieceMax];       // piece q: words 16(p0+q)+4g .. +3 of this lane's row
-};
-
-// Issue the loads of pieces [p0, p0 + np) of one row (`row` is always a
-// valid row; the caller masks tiles past the matrix). Lanes past the row end
-// load a clamped address; mma_tile zeroes those words. ALIGNED: words per
-// row % 4 == 0, so a piece is one 16-byte load.
-template <bool ALIGNED>
-__device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, int wpr, int p0, int np, int g) {
-  // Every piece but the last lies inside the row: one base address plus
-  // immediate offsets. Only the last piece's address is clamped.
-  const uint32_t *base = row + 16 * p0 + 4 * g;
-  const int wl = 16 * (p0 + np - 1) + 4 * g;   // the last piece's first word
-#pragma unroll
-  for (int q = 0; q < kPieceMax; ++q) {
-    if (q < np - 1) {   // uniform
-      if (ALIGNED) {
-        t.a[q] = *(const uint4 *)(base + 16 * q);
-      } else {
-        const uint2 lo = *(const uint2 *)(base + 16 * q);
-        const uint2 hi = *(const uint2 *)(base + 16 * q + 2);
-        t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    } else if (q == np - 1) {
-      if (ALIGNED) {
-        t.a[q] = *(const uint4 *)(row + min(wl, wpr - 4));
-      } else {
-        const uint2 lo = *(const uint2 *)(row + min(wl, wpr - 2));
-        const uint2 hi = *(const uint2 *)(row + min(wl + 2, wpr - 2));
-        t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
-  }
-}
-
-// The tile's UE8M0 bytes in the wave's LDS slot, row i at i * stride:
-//  fast   (16-byte aligned base, whole row in one window): the tile's 16 x nb
-//         bytes are contiguous; two 16-byte loads per lane, stride nb.
-//  generic: per window, each lane fetches its two bytes per piece, stride 128.
-struct AScalePre {
-  uint4 v0, v1;
-};
-
-__device__ __forceinline__ void ascale_prefetch(AScalePre &sp, const uint8_t *sblk, int nb) {
-  const int lane = threadIdx.x & 63;
-  sp.v0 = ((const uint4 *)sblk)[min(lane, nb - 1)];
-  sp.v1 = ((const uint4 *)sblk)[min(lane + 64, nb - 1)];
-}
-
-__device__ __forceinline__ void ascale_store(uint8_t *as_w, const AScalePre &sp, int nb) {
-  const int lane = threadIdx.x & 63;
-  if (lane < nb) ((uint4 *)as_w)[lane] = sp.v0;
-  if (lane + 64 < nb) ((uint4 *)as_w)[lane + 64] = sp.v1;
-}
-
-// (A lane's blocks of piece j: trellis 8j+2g and 8j+2g+1, MXFP4 4j+g.)
-template <typename F>
-__device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *srow, int nb, int p0, int np, bool ok) {
-  const int lane = threadIdx.x & 63, i16 = lane & 15, g = lane >> 4;
-  constexpr int kPer = F::kBlocks / 4;   // blocks per lane and piece
-#pragma unroll
-  for (int q = 0; q < kPieceMax; ++q) {
-    if (q < np) {
-      const int b = F::kBlocks * (p0 + q) + kPer * g;
-#pragma unroll
-      for (int h = 0; h < kPer; ++h)
-        as_w[i16 * 128 + F::kBlocks * q + kPer * g + h] = ok && b + h < nb ? srow[b + h] : (uint8_t)127;
-    }
-  }
-}
-
-// The first kPre pieces of a trellis window decoded ahead of the matrix-core
-// loop: a down-projection item decodes them while it waits for its h, so
-// only the rest of the decode is left once h arrives.
-constexpr int kPre = 6;
-struct PreDec {
-  uint4 s[kPre][2];   // A operands of steps 2q and 2q+1
-};
-
-__device__ __forceinline__ void predecode(PreDec &d, const Tile &t, int np, uint32_t &carry, int lane) {
-  const int g = lane >> 4;
-  const int src = ((lane - 16) & 63) << 2;
-#pragma unroll
-  for (int q = 0; q < kPre; ++q) {
-    if (q < np) {
-      const uint4 a = t.a[q];
-      const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
-      const uint32_t hist = g == 0 ? carry : rot;
-      carry = rot;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
-        const nib2 d0 = decode_word(w0, hw);
-        const nib2 d1 = decode_word(w1, w0);
-        d.s[q][hh] = make_uint4(d0.even, d0.odd, d1.even, d1.odd);
-      }
-    }
-  }
-}
-
-// Decode window pieces [0, np) (global piece p0 + q) and accumulate them
-// against NT N-tiles of the window's LDS columns. Lane
-// (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
-// (zeros when !on[n]).
-template <typename F, int NT>
-__device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int npre, int p0, int np, bool tile_ok,
-                                         int wpr, const uint8_t *as_w, int astride, int a_p0, int nb,
-                                         const uint8_t *lq, const uint8_t *ls, int psteps,
-                                         const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
-                                         uint32_t &carry, int lane) {
-  const int g = lane >> 4, i16 = lane & 15;
-  const int src = ((lane - 16) & 63) << 2;   // lane-group g-1 (mod 4), same row
-  if (F::kSteps == 1) {
-    // Expanded MXFP4: a piece is one step's A operand as stored, scaled by
-    // the UE8M0 byte of block 4j + g.
-#pragma unroll
-    for (int q = 0; q < kPieceMax; ++q) {
-      if (q < np) {
-        const int j = p0 + q;
-        const uint4 a = t.a[q];
-        const uint32_t sa = tile_ok && 4 * j + g < nb ? (uint32_t)as_w[i16 * astride + 4 * (a_p0 + q) + g] : 0x7Fu;
-        v8i B[NT];
-        uint32_t sb[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int c = on[n] ? col[n] : (col[n] & 1);
-          const uint4 *p = (const uint4 *)(lq + ((size_t)c * psteps + q) * 128 + g * 32);
-          const uint4 u0 = p[0], u1 = p[1];
-          B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-          sb[n] = ls[((size_t)c * psteps + q) * 4 + g];
-        }
-        const v8i A = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-          acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)sa, 0, (int)sb[n]);
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int q = 0; q < kPieceMax; ++q) {
-    if (q < np) {
-      const int j = p0 + q;
-      // Words past the row end (clamped loads) decode to finite E2M1 values
-      // that meet the zero codes of the activations' K padding, and rows past
-      // the matrix give outputs that are never stored: no masking needed.
-      // pieces [0, npre) were decoded ahead (predecode); the rest decode here
-      const bool pre = q < kPre && q < npre;
-      const uint4 a = t.a[q];
-      uint32_t hist = 0u;
-      if (!pre) {
-        const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
-        hist = g == 0 ? carry : rot;
-        carry = rot;
-      }
-      const int sb_a = 8 * j + 2 * g;
-      const uint32_t sa =
-          tile_ok && sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * (a_p0 + q) + 2 * g) : 0x7F7Fu;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int step = 2 * q + hh;
-        v8i B[NT];
-        uint32_t sb[NT];
-        // Output column c of D depends only on B column c, and the columns
-        // of unused N-tile lanes are never read: those lanes load column 0
-        // or 1 instead of zeros, so the loads need no lane masking.
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int c = on[n] ? col[n] : (col[n] & 1);
-          const uint4 *p = (const uint4 *)(lq + ((size_t)c * psteps + step) * 128 + g * 32);
-          const uint4 u0 = p[0], u1 = p[1];
-          B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-          sb[n] = ls[((size_t)c * psteps + step) * 4 + g];
-        }
-        v8i A;
-        if (q < kPre && pre) {
-          const uint4 x = pd.s[q < kPre ? q : 0][hh];
-          A = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-          const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
-          const nib2 d0 = decode_word(w0, hw);
-          const nib2 d1 = decode_word(w1, w0);
-          A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (hh == 0)
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)sa, 0,
-                                                                     (int)sb[n]);
-          else
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 1, (int)sa, 0,
-                                                                     (int)sb[n]);
-        }
-      }
-    }
-  }
-}
-
-template <int NT>
-__device__ __forceinline__ int d_index(int wave, int nt, int row, int col) {
-  const int lane = (row >> 2) * 16 + col;
-  return ((wave * NT + nt) * 64 + lane) * 4 + (row & 3);
-}
-
-// Dump the wave accumulators into the (now free) column area; the caller
-// synchronises before and after.
-template <int NT>
-__device__ __forceinline__ void dump_acc(Shared &S, const v4f (&acc)[NT], int wave, int lane) {
-  float *red = (float *)(S.bq + kBBytes / 2);
-#pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[((wave * NT + n) * 64 + lane) * 4 + r] = acc[n][r];
-}
-
-// hi + lo of column pair (n*8 + i16/2), row 4g + r, summed in the even lane.
-template <int NT, typename Out>
-__device__ __forceinline__ void per_slot_out(const v4f (&acc)[NT], int ncol, int lane, Out out) {
-  const int i16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = acc[n][r] + __shfl_xor(acc[n][r], 1);
-      const int c = n * 8 + (i16 >> 1);
-      if ((i16 & 1) == 0 && c < ncol) out(c, 4 * g + r, v);
-    }
-}
-
-// Sum the partial outputs of rows [rt*64, rt*64 + 64) over each token's live
-// slots, in slot order, weighted by the gate weights.
-__device__ __forceinline__ void combine_rows(const LayerArgs &a, const Shared &S, int rt) {
-  for (int idx = threadIdx.x; idx < a.T * 64; idx += kThreads) {
-    const int t = idx >> 6, r = rt * 64 + (idx & 63);
-    if (r >= a.y_rows) continue;
-    float v = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-      const int s = t * a.k + j, e = S.ids[s];
-      if (e >= 0 && e < a.E) v += S.gw[s] * __uint_as_float(ld_dc32(a.yslot + (size_t)s * a.y_rows + r));
-    }
-    a.y[(size_t)t * a.y_rows + r] = v;
-  }
-}
-
-// The item's partial outputs are stored; count it at its output tile and,
-// if it is the last of the n_active experts there, combine the tile.
-__device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S, int rt) {
-  stores_done();
-  if (threadIdx.x == 0) {
-    int *ctr = a.cnt2 + (size_t)rt * kLineInts;
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    S.last = old == S.n_active - 1;
-    if (S.last) st_ctr(ctr, 0);   // every arrival is in: clear for the next call
-  }
-  __syncthreads();
-  if (S.last) combine_rows(a, S, rt);
-}
-
-// ---------------------------------------------------------------- work items
-
-// The grouped GEMM of one item: expert e, 16 rows per wave starting at r0
-// (past the matrix: zeros, no output), columns = the expert's ne slots. K
-// is covered in register windows of up to 16 pieces; the LDS holds one
-// window of activation columns for a group of slots (as many as fit, at
-// most 8*NT). fetch_ahead(c0, ncol, p0, np) runs before the window's weight
-// loads are issued; stage(c0, ncol, p0, np) then fills the LDS;
-// epilogue(c0, ncol, acc) runs per slot group with the LDS free. With one
-// window the weight tile stays in registers across slot groups.
-// shared_cols: every slot reads LDS columns 0 (hi) and 1 (lo). predec:
-// decode the first pieces before stage runs (stage may wait).
-template <typename F, int NT, bool ALIGNED, typename Ahead, typename Stage, typename Epi>
-__device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
-                                          int fast, int e, int r0, int ne, bool shared_cols, bool predec,
-                                          Ahead fetch_ahead, Stage stage, Epi epilogue) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, g = lane >> 4;
-  const bool tile_ok = r0 < rows;
-  const int wpr = K / 32 * F::kWords, nb = K / 32, J = (nb + F::kBlocks - 1) / F::kBlocks;
-  const size_t row0 = (size_t)e * rows + (tile_ok ? r0 : 0);
-  const uint32_t *rowp = w + (row0 + i16) * wpr;
-  const uint8_t *srow = sc + (row0 + i16) * nb;
-  uint8_t *as_w = S.as[wave];
-  const int astride = fast ? nb : 128;
-  const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * F::kSteps * 256));
-  Tile tl;
-  if (J <= kPieceMax && ne <= gsz) {
-    // The common case, one window and one slot group, as straight-line code.
-    // Load order: activations, the tile's pieces, whatever the stage loads,
-    // then the tile's scales (loads complete in issue order; the scales are
-    // needed only once the pieces are, and issuing them late keeps them from
-    // occupying registers across the stage).
-    int col[NT];
-    bool on[NT];
-    v4f acc[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      col[n] = shared_cols ? (i16 & 1) : n * 16 + i16;
-      on[n] = n * 8 + (i16 >> 1) < ne;
-      acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-    uint32_t carry = 0u;
-    fetch_ahead(0, ne, 0, J);
-    load_tile<ALIGNED>(tl, rowp, wpr, 0, J, g);
-    TQ_MARK(S, 3);
-    PreDec pd;
-    // (not with 3-4 N-tiles: their accumulators leave no registers for it)
-    const int npre = predec && F::kSteps == 2 && NT <= 2 ? min(J, kPre) : 0;
-    if (npre) predecode(pd, tl, npre, carry, lane);
-    stage(0, ne, 0, J);
-    TQ_MARK(S, 4);
-    if (fast) {
-      AScalePre sp;
-      ascale_prefetch(sp, sc + row0 * nb, nb);
-      ascale_store(as_w, sp, nb);
-    } else {
-      ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
-    }
-    TQ_MARK(S, 5);
-    __syncthreads();
-    TQ_MARK(S, 6);
-    mma_tile<F, NT>(tl, pd, npre, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on, acc,
-                    carry, lane);
-    TQ_MARK(S, 7);
-    __syncthreads();
-    epilogue(0, ne, acc);
-    TQ_MARK(S, 8);
-    return;
-  }
-  for (int c0 = 0; c0 < ne; c0 += gsz) {
-    const int ncol = min(ne - c0, gsz);
-    int col[NT];
-    bool on[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      col[n] = shared_cols ? (i16 & 1) : n * 16 + i16;
-      on[n] = n * 8 + (i16 >> 1) < ncol;
-    }
-    v4f acc[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-    uint32_t carry = 0u;
-    for (int p0 = 0; p0 < J; p0 += kPieceMax) {
-      const int np = min(J - p0, kPieceMax);
-      const bool reload = c0 == 0 || J > kPieceMax;
-      fetch_ahead(c0, ncol, p0, np);
-      if (reload) load_tile<ALIGNED>(tl, rowp, wpr, p0, np, g);
-      stage(c0, ncol, p0, np);
-      if (reload && fast) {
-        AScalePre sp;
-        ascale_prefetch(sp, sc + row0 * nb, nb);
-        ascale_store(as_w, sp, nb);
-      } else if (reload) {
-        ascale_generic<F>(as_w, srow, nb, p0, np, tile_ok);
-      }
-      __syncthreads();
-      PreDec pd;
-      mma_tile<F, NT>(tl, pd, 0, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np,
-                      col, on, acc, carry, lane);
-      __syncthreads();   // everyone is done with the window's columns
-    }
-    epilogue(c0, ncol, acc);
-  }
-}
-
-// One work item. Stage-1 items (item < n_s1): expert active[item / n_rg1],
-// row group item % n_rg1 of the first matrix; columns from the activations.
-// Stage-2 items: expert active[i / n_rt2], row tile i % n_rt2 of the down
-// projection (i = item - n_s1); columns from the h splits. A single call
-// site of the grouped GEMM serves every kind, so the kernel holds one copy
-// of the matrix-core loop.
-template <typename F, int NT, bool ALIGNED>
-__device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool s1 = item < a.n_s1;
-  const int i2 = item - a.n_s1;
-  const int ai = s1 ? item / a.n_rg1 : i2 / a.n_rt2;
-  const int tile = s1 ? item % a.n_rg1 : i2 % a.n_rt2;   // row group (stage 1) / row tile (stage 2)
-  if (ai >= S.n_active) return;   // no such active expert: nothing to do
-  const int e = S.active[ai];
-  const bool ffn = a.mode == MODE_FFN;
-  const int r0 = s1 && ffn ? (wave < 2 ? 0 : a.inter) + tile * 32 + 16 * (wave & 1) : tile * 64 + 16 * wave;
-  const uint32_t *w = s1 ? a.w1 : a.w2;
-  const uint8_t *sc = s1 ? a.s1 : a.s2;
-  const int rows = s1 ? a.rows1 : a.rows2, K = s1 ? a.cols1 : a.cols2, fast = s1 ? a.fast1 : a.fast2;
-  const int nb = K / 32;
-  const int ne = gather_slots(S, e, a.T * a.k);
-  TQ_MARK(S, 2);
-  auto row_of = [&](int c) TQ_INLINE {
-    const int slot = S.slots[c];
-    return a.x_per_slot ? slot : slot / a.k;
-  };
-  XPre xp;
-  const bool resident = s1 && a.x_resident;
-  int obs_old = 0, obsp_old = -1;
-  bool waited = false;
-  auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
-    if (s1 && !resident) x_prefetch<F>(xp, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
-  };
-  auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
-    if (resident) {
-      if (!S.x_done) {   // this workgroup's first stage-1 item: fetch the token's split
-        if (threadIdx.x == 0) {
-          spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
-          obsp_old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        copy_pass<F>(S.bq, S.bs, a.xq, a.xs, F::kSteps * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
-        S.x_done = 1;    // read after the caller's barrier
-      }
-      return;
-    }
-    if (s1) {
-      x_finish<F>(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
-      return;
-    }
-    if (!waited) {
-      // the expert's h is complete once all its stage-1 items have counted;
-      // the first window's weight loads are already in flight
-      if (threadIdx.x == 0) {
-        spin_until(a.cnt1 + (size_t)ai * kLineInts, a.n_rg1, a.status);
-        obs_old = __hip_atomic_fetch_add(a.obs1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      waited = true;
-    }
-    copy_pass<F>(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
-      return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
-    });
-  };
-  auto epilogue = [&](int c0, int ncol, const v4f (&acc)[NT]) TQ_INLINE {
-    if (s1 && ffn) {
-      // SwiGLU: gate rows in waves 0, 1, the matching up rows in waves 2, 3
-      dump_acc<NT>(S, acc, wave, lane);
-      __syncthreads();
-      const float *red = (const float *)(S.bq + kBBytes / 2);
-      for (int base = 0; base < ncol; base += kThreads / 32) {
-        const int c = base + (threadIdx.x >> 5), i = threadIdx.x & 31;
-        if (c < ncol) {   // uniform over the half-wave
-          const int n = c >> 3, cj = 2 * (c & 7), wv = i >> 4, ri = i & 15;
-          const float gate = red[d_index<NT>(wv, n, ri, cj)] + red[d_index<NT>(wv, n, ri, cj + 1)];
-          const float up = red[d_index<NT>(wv + 2, n, ri, cj)] + red[d_index<NT>(wv + 2, n, ri, cj + 1)];
-          const float silu = gate / (1.0f + expf(-gate));
-          const uint16_t hb = f32_to_bf16_rne(silu * up);
-          const int slot = S.slots[c0 + c];
-          a.h[(size_t)slot * a.inter + tile * 32 + i] = hb;
-          const Split s = split_block(bf16_to_f32(hb));
-          uint8_t *q_hi = a.hq + (size_t)(slot * 2) * a.h_steps * 128;
-          uint8_t *q_lo = a.hq + (size_t)(slot * 2 + 1) * a.h_steps * 128;
-          st_dc8(q_hi + F::offset(tile, i), s.hi);
-          st_dc8(q_lo + F::offset(tile, i), s.lo);
-          if (i == 0) {
-            st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + F::scale_index(tile), (uint32_t)(s.E + 127));
-            st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + F::scale_index(tile), (uint32_t)(s.El + 127));
-          }
-        }
-      }
-      __syncthreads();
-      return;
-    }
-    if (r0 >= rows) return;
-    const bool partial = !s1 || a.mode == MODE_COMBINE;
-    per_slot_out<NT>(acc, ncol, lane, [&](int c, int rr, float v) TQ_INLINE {
-      const int slot = S.slots[c0 + c];
-      if (partial) st_dcf(a.yslot + (size_t)slot * a.y_rows + r0 + rr, v);
-      else a.y[(size_t)slot * a.rows1 + r0 + rr] = v;
-    });
-  };
-  gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, !s1, ahead, stage, epilogue);
-  if (obsp_old >= 0 && obsp_old == min(a.grid, S.n_active * a.n_rg1) - 1) {
-    // every workgroup that reads the split has fetched it: clear for the next call
-    st_ctr(a.cntp, 0);
-    st_ctr(a.cntp + kLineInts, 0);
-  }
-  if (s1 && ffn) {
-    stores_done();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(a.cnt1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  if (!s1 && threadIdx.x == 0 && obs_old == a.n_rt2 - 1) {
-    // the last of the expert's row tiles to see its h clears the expert's counters
-    st_ctr(a.cnt1 + (size_t)ai * kLineInts, 0);
-    st_ctr(a.obs1 + (size_t)ai * kLineInts, 0);
-  }
-  if (!s1 || a.mode == MODE_COMBINE) arrive_and_combine(a, S, tile);
-}
-
-// Work done once per call by workgroup 0: status words and the outputs of
-// dead (empty / out-of-range) slots.
-__device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
-  const int tid = threadIdx.x, n = a.T * a.k;
-  if (tid == 0) {
-    int skipped = 0;
-    for (int s = 0; s < n; ++s) skipped += S.ids[s] >= a.E;
-    st_ctr(&a.status[ST_SKIPPED], skipped);
-    st_ctr(&a.status[ST_ERROR], 0);
-  }
-  for (int s = 0; s < n; ++s) {
-    const int e = S.ids[s];
-    if (e >= 0 && e < a.E) continue;
-    if (a.mode == MODE_SLOTS)
-      for (int r = tid; r < a.rows1; r += kThreads) a.y[(size_t)s * a.rows1 + r] = 0.0f;
-    if (a.mode == MODE_FFN)
-      for (int c = tid; c < a.inter; c += kThreads) a.h[(size_t)s * a.inter + c] = 0;
-  }
-  if (S.n_active == 0 && a.mode != MODE_SLOTS)
-    for (int i = tid; i < a.T * a.y_rows; i += kThreads) a.y[i] = 0.0f;
-}
-
-template <typename F, int NT, bool ALIGNED>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_layer(LayerArgs a) {
-  __shared__ Shared S;
-  const int tid = threadIdx.x;
-#ifdef TQ_TRACE
-  unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 64 : nullptr;
-  if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
-  if (tid == 0) S.trp = nullptr;
-#endif
-  // A single token's activations are split once per call, one 32-value
-  // block per half-wave of the first n_xprep workgroups, into the
-  // workspace; every workgroup copies the split into LDS once.
-  const int n_prep = min(a.n_xprep, a.grid);
-  if (a.x_resident && (int)blockIdx.x < n_prep) {
-    const int nb1 = a.cols1 / 32, steps = fmt_steps<F>(nb1), pos = tid & 31;
-    for (int base = blockIdx.x * (kThreads / 32); base < 4 * steps; base += n_prep * (kThreads / 32)) {
-      const int blk = base + (tid >> 5);   // uniform per half-wave
-      const size_t el = blk < nb1 ? (size_t)blk * 32 + pos : 0;
-      const uint32_t word = x_word(a, el);
-      const Split sp = split_block(blk < nb1 ? x_value(a, el, word) : 0.0f);
-      if (blk < 4 * steps) {
-        st_dc8(a.xq + F::offset(blk, pos), sp.hi);
-        st_dc8(a.xq + (size_t)steps * 128 + F::offset(blk, pos), sp.lo);
-        if (pos == 0) {
-          st_dc8(a.xs + F::scale_index(blk), (uint32_t)(sp.E + 127));
-          st_dc8(a.xs + (size_t)steps * 4 + F::scale_index(blk), (uint32_t)(sp.El + 127));
-        }
-      }
-    }
-    stores_done();
-    if (tid == 0) __hip_atomic_fetch_add(a.cntp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (tid == 0) S.x_done = 0;
-  // routing, redundantly in every workgroup: active experts in id order
-  const int n = a.T * a.k;
-  const int nw = (a.E + 31) >> 5;
-  for (int i = tid; i < n; i += kThreads) {
-    const int e = a.ids[i];
-    S.ids[i] = (int16_t)(e < 0 ? -1 : (e >= a.E ? kMaxExperts : e));
-    S.gw[i] = a.gate_w ? a.gate_w[i] : 1.0f;
-  }
-  for (int w = tid; w < nw; w += kThreads) S.mask[w] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += kThreads) {
-    const int e = S.ids[i];
-    if (e >= 0 && e < a.E) atomicOr(&S.mask[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int w = 0; w < nw; ++w) { S.wpre[w] = acc; acc += __popc(S.mask[w]); }
-    S.n_active = acc;
-  }
-  __syncthreads();
-  for (int w = tid; w < nw; w += kThreads) {
-    unsigned m = S.mask[w];
-    int o = S.wpre[w];
-    while (m) {
-      const int b = __ffs(m) - 1;
-      S.active[o++] = (int16_t)(w * 32 + b);
-      m &= m - 1u;
-    }
-  }
-  __syncthreads();
-  if (blockIdx.x == 0) bookkeeping(a, S);
-
-#ifdef TQ_TRACE
-  if (TR && tid == 0) TR[1] = __builtin_amdgcn_s_memrealtime();
-  int it_no = 0;
-#endif
-  const int n_items = a.n_s1 + a.n_s2;
-  for (int item = blockIdx.x; item < n_items; item += a.grid) {
-#ifdef TQ_TRACE
-    if (tid == 0) {
-      S.trp = (TR && it_no < 6) ? TR + 2 + 10 * it_no : nullptr;
-      if (S.trp) S.trp[0] = (unsigned long long)item;
-    }
-    __syncthreads();
-    TQ_MARK(S, 1);
-    ++it_no;
-#endif
-    run_item<F, NT, ALIGNED>(a, S, item);
-    __syncthreads();
-    TQ_MARK(S, 9);
-  }
-}
-
-// ---------------------------------------------------------------- host side
-
-static int device_check(int *cus) {
-  static int cached[64];
-  static int ncu[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return TRELLIS_EHIP;
-  if (cached[dev] == 0) {
-    hipDeviceProp_t p;
-    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return TRELLIS_EHIP;
-    cached[dev] = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
-    ncu[dev] = p.multiProcessorCount;
-  }
-  *cus = ncu[dev];
-  return cached[dev] > 0 ? TRELLIS_OK : TRELLIS_EDEVICE;
-}
-
-template <typename F, int NT, bool ALIGNED>
-static int resident_blocks() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-  if (cached[dev] == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_layer<F, NT, ALIGNED>, kThreads, 0) != hipSuccess ||
-        nb < 1)
-      nb = 1;
-    cached[dev] = nb;
-  }
-  return cached[dev];
-}
-
-// A stack of n_mat matrices of either format: base pointers as given.
-struct Mats {
-  const void *w;
-  const uint8_t *scales;
-  int n_mat, rows, cols;
-};
-
-static int check_mats(const Mats &m) {
-  if (!m.w || !m.scales) return TRELLIS_ENULL;
-  if (m.n_mat < 1 || m.rows < 1 || m.cols < 32 || m.cols % 32) return TRELLIS_EINVAL;
-  if (m.rows % 16 || m.n_mat > kMaxExperts) return TRELLIS_EINVAL;
-  return TRELLIS_OK;
-}
-
-static int check_routing(int T, int k) {
-  if (T < 1 || T > kMaxT || k < 1 || k > kMaxK || T * k > kMaxSlots) return TRELLIS_EINVAL;
-  return TRELLIS_OK;
-}
-
-template <typename F, int NT, bool ALIGNED>
-static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
-  const int n_items = a.n_s1 + a.n_s2;
-  a.grid = std::max(1, std::min(n_items, cus * resident_blocks<F, NT, ALIGNED>()));
-  hipLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
-}
-
-template <typename F, bool ALIGNED>
-static int launch_al(LayerArgs &a, int cus, hipStream_t s) {
-  switch ((a.T + 7) / 8) {
-    case 1: return launch_nt<F, 1, ALIGNED>(a, cus, s);
-    case 2: return launch_nt<F, 2, ALIGNED>(a, cus, s);
-    case 3: return launch_nt<F, 3, ALIGNED>(a, cus, s);
-    default: return launch_nt<F, 4, ALIGNED>(a, cus, s);
-  }
-}
-
-// The aligned instances need every streamed matrix to have whole 16-byte
-// pieces per row (words per row % 4 == 0) and a 16-byte aligned base. The
-// fast scale path needs a 16-byte aligned scale base and cols <= 4096.
-template <typename F>
-static int launch(LayerArgs &a, int cus, hipStream_t s) {
-  const bool aligned = (a.cols1 / 32 * F::kWords) % 4 == 0 && (a.cols2 / 32 * F::kWords) % 4 == 0 &&
-                       ((uintptr_t)a.w1 & 15) == 0 && ((uintptr_t)a.w2 & 15) == 0;
-  a.fast1 = aligned && ((uintptr_t)a.s1 & 15) == 0 && a.cols1 / 32 <= kAScaleBytes / 16;
-  a.fast2 = aligned && ((uintptr_t)a.s2 & 15) == 0 && a.cols2 / 32 <= kAScaleBytes / 16;
-  return aligned ? launch_al<F, true>(a, cus, s) : launch_al<F, false>(a, cus, s);
-}
-
-template <typename F>
-static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x_dtype, int32_t x_per_slot,
-                     const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k, float *y,
-                     void *workspace, size_t workspace_bytes) {
-  int rc = check_mats(w);
-  if (rc) return rc;
-  if (!x || !topk_ids || !y || !workspace) return TRELLIS_ENULL;
-  if ((x_dtype != TRELLIS_F32 && x_dtype != TRELLIS_BF16) || (x_per_slot != 0 && x_per_slot != 1))
-    return TRELLIS_EINVAL;
-  if ((rc = check_routing(T, k))) return rc;
-  const bool combine = topk_w != nullptr;
-  const int n_rt = (w.rows + 63) / 64;
-  const Layout L = make_layout<F>(0, n_rt, T * k, w.rows, 0, w.cols);
-  if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
-  int cus = 0;
-  if ((rc = device_check(&cus))) return rc;
-  char *ws = (char *)workspace;
-  LayerArgs a{};
-  a.mode = combine ? MODE_COMBINE : MODE_SLOTS;
-  a.w1 = (const uint32_t *)w.w; a.s1 = w.scales; a.rows1 = w.rows; a.cols1 = w.cols;
-  a.w2 = (const uint32_t *)w.w; a.s2 = w.scales; a.rows2 = w.rows; a.cols2 = w.cols;
-  a.E = w.n_mat; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
-  a.x = x; a.x_bf16 = x_dtype == TRELLIS_BF16; a.x_per_slot = x_per_slot;
-  a.y = y; a.y_rows = w.rows;
-  a.status = (int *)(ws + L.status);
-  a.cnt2 = (int *)(ws + L.cnt2);
-  a.yslot = (float *)(ws + L.yslot);
-  a.n_rg1 = n_rt;
-  a.n_s1 = std::min(w.n_mat, T * k) * a.n_rg1;
-  a.n_rt2 = 1; a.n_s2 = 0;
-  const int J = (w.cols / 32 + F::kBlocks - 1) / F::kBlocks;
-  a.x_resident = T == 1 && !x_per_slot && J <= kPieceMax;
-  a.n_xprep = (4 * fmt_steps<F>(w.cols / 32) + kThreads / 32 - 1) / (kThreads / 32);
-  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
-  return launch<F>(a, cus, stream);
-}
-
-template <typename F>
-static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const void *x, int32_t x_dtype,
-                    const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k, uint16_t *h, float *y,
-                    void *workspace, size_t workspace_bytes, hipEvent_t *events) {
-  int rc;
-  if ((rc = check_mats(gu)) || (rc = check_mats(dn))) return rc;
-  if (!x || !topk_ids || !h || !y || !workspace) return TRELLIS_ENULL;
-  if (x_dtype != TRELLIS_F32 && x_dtype != TRELLIS_BF16) return TRELLIS_EINVAL;
-  if ((rc = check_routing(T, k))) return rc;
-  const int E = gu.n_mat, hidden = gu.cols, inter = gu.rows / 2;
-  if (gu.rows % 64 || dn.n_mat != E || dn.rows != hidden || dn.cols != inter) return TRELLIS_EINVAL;
-  const int max_act = std::min(E, T * k);
-  const Layout L = make_layout<F>(max_act, (hidden + 63) / 64, T * k, hidden, inter, hidden);
-  if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
-  int cus = 0;
-  if ((rc = device_check(&cus))) return rc;
-  char *ws = (char *)workspace;
-  LayerArgs a{};
-  a.mode = MODE_FFN;
-  a.w1 = (const uint32_t *)gu.w; a.s1 = gu.scales; a.rows1 = gu.rows; a.cols1 = hidden;
-  a.w2 = (const uint32_t *)dn.w; a.s2 = dn.scales; a.rows2 = hidden; a.cols2 = inter;
-  a.E = E; a.T = T; a.k = k; a.ids = topk_ids; a.gate_w = topk_w;
-  a.x = x; a.x_bf16 = x_dtype == TRELLIS_BF16; a.x_per_slot = 0;
-  a.inter = inter; a.h = h;
-  a.h_steps = fmt_steps<F>(inter / 32);
-  a.hq = (uint8_t *)(ws + L.hq); a.hs = (uint8_t *)(ws + L.hs);
-  a.yslot = (float *)(ws + L.yslot);
-  a.y = y; a.y_rows = hidden;
-  a.status = (int *)(ws + L.status);
-  a.cnt1 = (int *)(ws + L.cnt1); a.obs1 = (int *)(ws + L.obs1); a.cnt2 = (int *)(ws + L.cnt2);
-#ifdef TQ_TRACE
-  a.trace = (unsigned long long *)g_trace;
-#endif
-  a.n_rg1 = inter / 32;
-  a.n_s1 = max_act * a.n_rg1;
-  a.n_rt2 = (hidden + 63) / 64;
-  a.n_s2 = max_act * a.n_rt2;
-  const int J = (hidden / 32 + F::kBlocks - 1) / F::kBlocks;
-  a.x_resident = T == 1 && J <= kPieceMax;
-  a.n_xprep = (4 * fmt_steps<F>(hidden / 32) + kThreads / 32 - 1) / (kThreads / 32);
-  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
-  if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
-  rc = launch<F>(a, cus, stream);
-  if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
-  return rc;
-}
-
-static Mats trellis_mats(const trellis_mat_t *w) {
-  return w ? Mats{w->syms, w->scales, w->n_mat, w->rows, w->cols} : Mats{nullptr, nullptr, 0, 0, 0};
-}
-static Mats mx_mats(const trellis_mx_t *w) {
-  return w ? Mats{w->codes, w->scales, w->n_mat, w->rows, w->cols} : Mats{nullptr, nullptr, 0, 0, 0};
-}
-
-}  // namespace tq
+// tq_layer.hip -- C ABI of the fused trellis-decode MoE GEMV and layer
+// (the kernels and their host launch code are in tq_layer.h; this unit
+// instantiates them for trellis-coded weights).
+#include "tq_layer.h"
 
 using namespace tq;
 
@@ -1266,34 +41,6 @@ extern "C" int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_u
                                size_t workspace_bytes) {
   return trellis_moe_ffn_timed(stream, w_gate_up, w_down, x, x_dtype, topk_ids, topk_w, T, k, h, y, workspace,
                                workspace_bytes, nullptr);
-}
-
-// Expanded MXFP4 weights: the same kernels with the weights' nibbles fed to
-// the matrix cores as stored. MXFP4 steps never outnumber trellis steps for
-// a width, so the trellis workspace sizes cover both.
-static int check_mx_align(const trellis_mx_t *w) {
-  if (!w) return TRELLIS_ENULL;
-  if (((uintptr_t)w->codes & 15) || ((uintptr_t)w->scales & 15)) return TRELLIS_EINVAL;
-  return TRELLIS_OK;
-}
-
-extern "C" int trellis_mxfp4_moe_gemv(hipStream_t stream, const trellis_mx_t *w, const void *x, int32_t x_dtype,
-                                      int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w,
-                                      int32_t T, int32_t k, float *y, void *workspace, size_t workspace_bytes) {
-  int rc = check_mx_align(w);
-  if (rc) return rc;
-  return gemv_impl<FmtMx>(stream, mx_mats(w), x, x_dtype, x_per_slot, topk_ids, topk_w, T, k, y, workspace,
-                          workspace_bytes);
-}
-
-extern "C" int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, const trellis_mx_t *w_down,
-                                     const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,
-                                     int32_t T, int32_t k, uint16_t *h, float *y, void *workspace,
-                                     size_t workspace_bytes) {
-  int rc;
-  if ((rc = check_mx_align(w_gate_up)) || (rc = check_mx_align(w_down))) return rc;
-  return ffn_impl<FmtMx>(stream, mx_mats(w_gate_up), mx_mats(w_down), x, x_dtype, topk_ids, topk_w, T, k, h, y,
-                         workspace, workspace_bytes, nullptr);
 }
 
 #ifdef TQ_TRACE
