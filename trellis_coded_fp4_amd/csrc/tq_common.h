@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/trellis.h"
+#include "trellis.h"   // include/ is on the include path (build.py)
 #include "tq_decode.h"
 
 namespace tq {
