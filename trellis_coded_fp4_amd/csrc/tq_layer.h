@@ -230,6 +230,48 @@ __device__ __forceinline__ void stores_done() {
   __syncthreads();
 }
 
+// LDS direct loads (global_load_lds): lane l of a wave moves its 16 (or 4)
+// bytes to lds + 16 l (4 l), the LDS base being wave-uniform; no registers
+// are involved. sc1 makes them the same device-coherent reads as ld_dc64
+// (the sources are written by other workgroups). Such a load counts in
+// vmcnt like any other: before the data is read, the issuing wave waits
+// with vm_wait and the workgroup synchronises.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kCpolSc1 = 16;
+
+// Copy `bytes` (a multiple of 16, both addresses 16-byte aligned) into LDS;
+// the waves take 1 KB chunks in turn.
+__device__ __forceinline__ void lds_copy16(uint8_t *lds, const uint8_t *g, int bytes) {
+  const int lane = threadIdx.x & 63;
+  for (int c = (int)(threadIdx.x >> 6) * 1024; c < bytes; c += kWaves * 1024)
+    if (c + lane * 16 < bytes)
+      __builtin_amdgcn_global_load_lds(g + c + lane * 16, (lds_void *)(lds + c), 16, 0, kCpolSc1);
+}
+// The same with 4-byte lanes (256-byte chunks; 4-byte alignment).
+__device__ __forceinline__ void lds_copy4(uint8_t *lds, const uint8_t *g, int bytes) {
+  const int lane = threadIdx.x & 63;
+  for (int c = (int)(threadIdx.x >> 6) * 256; c < bytes; c += kWaves * 256)
+    if (c + lane * 4 < bytes)
+      __builtin_amdgcn_global_load_lds(g + c + lane * 4, (lds_void *)(lds + c), 4, 0, kCpolSc1);
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS writes are
+// complete (its LDS direct loads must have been waited for with vm_wait),
+// then s_barrier. Unlike __syncthreads it does not wait for this wave's
+// outstanding global loads, so weight loads stay in flight across it. The
+// memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Thread 0 waits until the counter reaches `target`; bounded: on timeout
 // the error word is set. The caller synchronises the workgroup after.
 __device__ __forceinline__ void spin_until(const int *ctr, int target, int *status) {
@@ -493,6 +535,37 @@ __device__ __forceinline__ void load_tile(Tile &t, const uint32_t *row, int wpr,
   }
 }
 
+// load_tile for the single-window case with a fixed instruction count:
+// exactly NLOAD loads (2 NLOAD unaligned), pieces past np re-reading the
+// last one. With a count that does not depend on np, the compiler's
+// wait before piece q's first use lets the later pieces stay in flight, so
+// the decode of the first pieces overlaps the arrival of the rest.
+template <bool ALIGNED, int NLOAD>
+__device__ __forceinline__ void load_tile_full(Tile &t, const uint32_t *row, int wpr, int np, int g) {
+  const uint32_t *base = row + 4 * g;
+  const int wl = 16 * (np - 1) + 4 * g;
+#pragma unroll
+  for (int q = 0; q < NLOAD; ++q) {
+    if (q < np - 1) {   // uniform; one load (pair) on either side
+      if (ALIGNED) {
+        t.a[q] = *(const uint4 *)(base + 16 * q);
+      } else {
+        const uint2 lo = *(const uint2 *)(base + 16 * q);
+        const uint2 hi = *(const uint2 *)(base + 16 * q + 2);
+        t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    } else {
+      if (ALIGNED) {
+        t.a[q] = *(const uint4 *)(row + min(wl, wpr - 4));
+      } else {
+        const uint2 lo = *(const uint2 *)(row + min(wl, wpr - 2));
+        const uint2 hi = *(const uint2 *)(row + min(wl + 2, wpr - 2));
+        t.a[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+  }
+}
+
 // The tile's UE8M0 bytes in the wave's LDS slot, row i at i * stride:
 //  fast   (16-byte aligned base, whole row in one window): the tile's 16 x nb
 //         bytes are contiguous; two 16-byte loads per lane, stride nb.
@@ -531,7 +604,8 @@ __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *sro
 
 // The first kPre pieces of a trellis window decoded ahead of the matrix-core
 // loop: a down-projection item decodes them while it waits for its h, so
-// only the rest of the decode is left once h arrives.
+// only the rest of the decode is left once h arrives. (More of them would
+// not fit the register file next to the tile.)
 constexpr int kPre = 6;
 struct PreDec {
   uint4 s[kPre][2];   // A operands of steps 2q and 2q+1
@@ -562,7 +636,7 @@ __device__ __forceinline__ void predecode(PreDec &d, const Tile &t, int np, uint
 // against NT N-tiles of the window's LDS columns. Lane
 // (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
 // (zeros when !on[n]).
-template <typename F, int NT>
+template <typename F, int NT, bool PRE>
 __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int npre, int p0, int np, bool tile_ok,
                                          int wpr, const uint8_t *as_w, int astride, int a_p0, int nb,
                                          const uint8_t *lq, const uint8_t *ls, int psteps,
@@ -604,8 +678,8 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
       // Words past the row end (clamped loads) decode to finite E2M1 values
       // that meet the zero codes of the activations' K padding, and rows past
       // the matrix give outputs that are never stored: no masking needed.
-      // pieces [0, npre) were decoded ahead (predecode); the rest decode here
-      const bool pre = q < kPre && q < npre;
+      // PRE: pieces [0, npre) were decoded ahead (npre <= kPre)
+      const bool pre = PRE && q < kPre && q < npre;
       const uint4 a = t.a[q];
       uint32_t hist = 0u;
       if (!pre) {
@@ -633,7 +707,7 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
           sb[n] = ls[((size_t)c * psteps + step) * 4 + g];
         }
         v8i A;
-        if (q < kPre && pre) {
+        if (pre) {
           const uint4 x = pd.s[q < kPre ? q : 0][hh];
           A = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
         } else {
@@ -759,15 +833,30 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
     }
     uint32_t carry = 0u;
+    // Loads go out in the order they are needed, and they complete in that
+    // order: the token's split (first stage-1 item of a workgroup), the
+    // tile's scales, then the pieces, a fixed number of them. Each piece is
+    // waited for only where its decode starts. The scales ride in the two
+    // last piece registers when the tile leaves them free; otherwise they
+    // are loaded after the pieces.
     fetch_ahead(0, ne, 0, J);
-    load_tile<ALIGNED>(tl, rowp, wpr, 0, J, g);
-    // The tile's scales ride in the two last piece registers when the tile
-    // leaves them free: their loads go out right behind the pieces.
     const bool sp_in_tile = fast && J <= kPieceMax - 2;
+    __builtin_amdgcn_sched_barrier(0);
     if (sp_in_tile) {
-      const int lane_ = threadIdx.x & 63;
-      tl.a[kPieceMax - 2] = ((const uint4 *)(sc + row0 * nb))[min(lane_, nb - 1)];
-      tl.a[kPieceMax - 1] = ((const uint4 *)(sc + row0 * nb))[min(lane_ + 64, nb - 1)];
+      const uint4 *sblk = (const uint4 *)(sc + row0 * nb);
+      tl.a[kPieceMax - 2] = sblk[min(lane, nb - 1)];
+      tl.a[kPieceMax - 1] = sblk[min(lane + 64, nb - 1)];
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile_full<ALIGNED, kPieceMax - 2>(tl, rowp, wpr, J, g);
+    } else {
+      load_tile_full<ALIGNED, kPieceMax>(tl, rowp, wpr, J, g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (sp_in_tile) {
+      AScalePre sp;
+      sp.v0 = tl.a[kPieceMax - 2];
+      sp.v1 = tl.a[kPieceMax - 1];
+      ascale_store(as_w, sp, nb);
     }
     TQ_MARK(S, 3);
     PreDec pd;
@@ -776,23 +865,27 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
     if (npre) predecode(pd, tl, npre, carry, lane);
     stage(0, ne, 0, J);
     TQ_MARK(S, 4);
-    if (sp_in_tile) {
-      AScalePre sp;
-      sp.v0 = tl.a[kPieceMax - 2];
-      sp.v1 = tl.a[kPieceMax - 1];
-      ascale_store(as_w, sp, nb);
-    } else if (fast) {
+    if (!sp_in_tile && fast) {
       AScalePre sp;
       ascale_prefetch(sp, sc + row0 * nb, nb);
       ascale_store(as_w, sp, nb);
-    } else {
+    } else if (!fast) {
       ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
     }
+    if (!sp_in_tile) vm_wait<0>();   // (done already; tells the compiler)
     TQ_MARK(S, 5);
-    __syncthreads();
+    lds_barrier();
     TQ_MARK(S, 6);
-    mma_tile<F, NT>(tl, pd, npre, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on, acc,
-                    carry, lane);
+    // Two copies of the matrix-core loop: with pre-decoded pieces (a
+    // down-projection item, whose loads have all completed by now), and
+    // without, whose simpler control flow lets the compiler wait for each
+    // piece only where its decode starts.
+    if (npre)
+      mma_tile<F, NT, true>(tl, pd, npre, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col,
+                            on, acc, carry, lane);
+    else
+      mma_tile<F, NT, false>(tl, pd, 0, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on,
+                             acc, carry, lane);
     TQ_MARK(S, 7);
     __syncthreads();
     epilogue(0, ne, acc);
@@ -825,9 +918,10 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       } else if (reload) {
         ascale_generic<F>(as_w, srow, nb, p0, np, tile_ok);
       }
+      vm_wait<0>();   // LDS copies of the stage
       __syncthreads();
       PreDec pd;
-      mma_tile<F, NT>(tl, pd, 0, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np,
+      mma_tile<F, NT, false>(tl, pd, 0, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np,
                       col, on, acc, carry, lane);
       __syncthreads();   // everyone is done with the window's columns
     }
@@ -862,28 +956,39 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     const int slot = S.slots[c];
     return a.x_per_slot ? slot : slot / a.k;
   };
-  XPre xp;
   const bool resident = s1 && a.x_resident;
   int obs_old = 0, obsp_old = -1;
   bool waited = false;
   auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
-    if (s1 && !resident) x_prefetch<F>(xp, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
+    if (resident && !S.x_done) {
+      // this workgroup's first stage-1 item: once the token's split is
+      // complete, copy it into LDS (columns 0, 1: contiguous in the
+      // workspace and in LDS) before any weight load is issued. The copy is
+      // waited for right here: with LDS direct loads still in flight the
+      // compiler could no longer count which weight loads are done.
+      if (threadIdx.x == 0) {
+        spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
+        obsp_old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      const int psteps = F::kSteps * np;
+      lds_copy16(S.bq, a.xq, 2 * psteps * 128);
+      lds_copy4(S.bs, a.xs, 2 * psteps * 4);
+      vm_wait<0>();
+      S.x_done = 1;    // read after the caller's barrier
+    }
   };
   auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
-    if (resident) {
-      if (!S.x_done) {   // this workgroup's first stage-1 item: fetch the token's split
-        if (threadIdx.x == 0) {
-          spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
-          obsp_old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        copy_pass<F>(S.bq, S.bs, a.xq, a.xs, F::kSteps * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
-        S.x_done = 1;    // read after the caller's barrier
-      }
-      return;
-    }
+    if (resident) return;
     if (s1) {
+      // Several tokens: split their activations here. All of this
+      // branch's loads are consumed within it, so none stays pending where
+      // the item kinds' paths meet (the compiler's waits are not
+      // path-sensitive).
+      XPre xp;
+      x_prefetch<F>(xp, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
       x_finish<F>(xp, S.bq, S.bs, a, K, nb, kp, np, ncol, [&](int c) TQ_INLINE { return row_of(c0 + c); });
+      vm_wait<0>();
       return;
     }
     if (!waited) {
@@ -897,9 +1002,23 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       __syncthreads();
       waited = true;
     }
+    if (kp == 0 && F::kSteps * np == a.h_steps) {
+      // the whole of K in one window: each slot's hi and lo columns are one
+      // contiguous run in the workspace and in LDS (the K padding was
+      // written by the expert's last stage-1 row group)
+      const int psteps = a.h_steps;
+      for (int c = 0; c < ncol; ++c) {
+        const int slot = S.slots[c0 + c];
+        lds_copy16(S.bq + (size_t)2 * c * psteps * 128, a.hq + (size_t)slot * 2 * psteps * 128, 2 * psteps * 128);
+        lds_copy4(S.bs + (size_t)2 * c * psteps * 4, a.hs + (size_t)slot * 2 * psteps * 4, 2 * psteps * 4);
+      }
+      vm_wait<0>();
+      return;
+    }
     copy_pass<F>(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
       return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
     });
+    vm_wait<0>();   // (loads whose store a lane skipped count as pending for the compiler)
   };
   auto epilogue = [&](int c0, int ncol, const v4f (&acc)[NT]) TQ_INLINE {
     if (s1 && ffn) {
@@ -925,6 +1044,21 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
           if (i == 0) {
             st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + F::scale_index(tile), (uint32_t)(s.E + 127));
             st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + F::scale_index(tile), (uint32_t)(s.El + 127));
+          }
+        }
+      }
+      if (tile == a.n_rg1 - 1) {
+        // the last row group also writes the K padding of its slots' h
+        // splits (zero codes, scale 2^0), which the down projection copies
+        const int npad = F::kBlocks * (a.h_steps / F::kSteps) - a.n_rg1;
+        for (int idx = threadIdx.x; idx < ncol * npad * 32; idx += kThreads) {
+          const int c = idx / (npad * 32), r = idx - c * npad * 32, b = a.n_rg1 + (r >> 5), pos = r & 31;
+          const int slot = S.slots[c0 + c];
+          st_dc8(a.hq + (size_t)(slot * 2) * a.h_steps * 128 + F::offset(b, pos), 0u);
+          st_dc8(a.hq + (size_t)(slot * 2 + 1) * a.h_steps * 128 + F::offset(b, pos), 0u);
+          if (pos == 0) {
+            st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + F::scale_index(b), 127u);
+            st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + F::scale_index(b), 127u);
           }
         }
       }
@@ -1063,6 +1197,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     ++it_no;
 #endif
     run_item<F, NT, ALIGNED>(a, S, item);
+    // nothing of this item stays in flight into the next one (the
+    // compiler's waits in the next item then count only its own loads)
+    vm_wait<0>();
     __syncthreads();
     TQ_MARK(S, 9);
   }
