@@ -221,3 +221,39 @@ def test_ffn_128_experts_sweep_sampled(trellis_lib, orc, T):
     n_gu = 48 if T <= 8 else 16
     _check_layer(trellis_lib, orc, layer, rows_gu=np.sort(rs.choice(1536, n_gu, replace=False)),
                  rows_dn=np.sort(rs.choice(4096, 64, replace=False)))
+
+
+def test_single_token_calls_share_a_workspace(trellis_lib, orc):
+    """One token (the split-once path): calls on one workspace, with a call
+    whose slots are all empty in between, each see their own activations."""
+    announce("single-token calls on one workspace, with an all-empty call between")
+    import torch
+    E, rows, cols, k = 4, 64, 2880, 4
+    g = workloads.rng(604, 0)
+    syms, sc = workloads.symbols(g, E, rows, cols), workloads.scales(g, E, rows, cols)
+    ws = trellis_lib.gemv_workspace(E, rows, cols, 1, k)
+    empty = -np.ones((1, k), np.int32)
+    for i in range(3):
+        x = workloads.activations(g, 1, cols, True)
+        ids, gw = workloads.routing_topk(g, 1, E, k)
+        y = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(ids), dev(gw), workspace=ws)
+        y_ref, bound, _ = orc.moe_gemv(syms, sc, x, ids, gate_w=gw)
+        check_tol(y.cpu().numpy(), y_ref, bound, f"gemv call {i}")
+        y0 = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(empty), dev(gw), workspace=ws)
+        assert (y0.cpu().numpy() == 0).all()
+    torch.cuda.synchronize()
+    assert int(ws[:8].view(torch.int32)[1]) == 0   # no wait timed out
+
+    cfg = workloads.MoEConfig(91, "small-1", 4, 256, 96, 3, 1, True)
+    wsf = trellis_lib.ffn_workspace(cfg.n_exp, cfg.hidden, cfg.inter, 1, cfg.k)
+    for i in range(3):
+        layer = workloads.moe_layer(cfg, layer_id=i)
+        run = lambda L: trellis_lib.moe_ffn(dev(L.gu_syms), dev(L.gu_scales), dev(L.dn_syms), dev(L.dn_scales),
+                                            x_dev(L.x, True), dev(L.ids), dev(L.gate_w), workspace=wsf)
+        _check_layer(trellis_lib, orc, layer, run=run)
+        ye, he = trellis_lib.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms),
+                                     dev(layer.dn_scales), x_dev(layer.x, True), dev(-np.ones((1, 3), np.int32)),
+                                     dev(layer.gate_w), workspace=wsf)
+        assert (ye.cpu().numpy() == 0).all() and (he.float().cpu().numpy() == 0).all()
+    torch.cuda.synchronize()
+    assert int(wsf[:8].view(torch.int32)[1]) == 0

@@ -230,31 +230,6 @@ __device__ __forceinline__ void stores_done() {
   __syncthreads();
 }
 
-// LDS direct loads (global_load_lds): lane l of a wave moves its 16 (or 4)
-// bytes to lds + 16 l (4 l), the LDS base being wave-uniform; no registers
-// are involved. sc1 makes them the same device-coherent reads as ld_dc64
-// (the sources are written by other workgroups). Such a load counts in
-// vmcnt like any other: before the data is read, the issuing wave waits
-// with vm_wait and the workgroup synchronises.
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kCpolSc1 = 16;
-
-// Copy `bytes` (a multiple of 16, both addresses 16-byte aligned) into LDS;
-// the waves take 1 KB chunks in turn.
-__device__ __forceinline__ void lds_copy16(uint8_t *lds, const uint8_t *g, int bytes) {
-  const int lane = threadIdx.x & 63;
-  for (int c = (int)(threadIdx.x >> 6) * 1024; c < bytes; c += kWaves * 1024)
-    if (c + lane * 16 < bytes)
-      __builtin_amdgcn_global_load_lds(g + c + lane * 16, (lds_void *)(lds + c), 16, 0, kCpolSc1);
-}
-// The same with 4-byte lanes (256-byte chunks; 4-byte alignment).
-__device__ __forceinline__ void lds_copy4(uint8_t *lds, const uint8_t *g, int bytes) {
-  const int lane = threadIdx.x & 63;
-  for (int c = (int)(threadIdx.x >> 6) * 256; c < bytes; c += kWaves * 256)
-    if (c + lane * 4 < bytes)
-      __builtin_amdgcn_global_load_lds(g + c + lane * 4, (lds_void *)(lds + c), 4, 0, kCpolSc1);
-}
-
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order).
 template <int N>
@@ -730,6 +705,150 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
   }
 }
 
+// ---------------------------------------------------------------- streamed window
+//
+// The single-window case without pre-decoding streams its pieces through a
+// ring of kRing registers with kAhead loads in flight per wave: piece q is
+// decoded and multiplied while pieces q+1 .. q+kAhead are on their way, and
+// each step issues the load of piece q+kAhead. Issuing a whole tile up front
+// instead would stall the wave at the issue (the memory pipeline accepts a
+// limited number of requests per compute unit) until most of the tile had
+// arrived, and the decode would start only then. Every step issues exactly
+// one load (past the window's end, a re-read of its last piece), so the
+// compiler's wait before piece q always leaves the kAhead younger loads in
+// flight.
+constexpr int kRing = 8;
+constexpr int kAhead = 6;   // < kRing; ring slots kAhead.. carry the tile's scales at first
+struct Ring {
+  uint4 r[kRing];
+};
+
+// Piece p of a window of np pieces; p >= np - 1 reads the (clamped) last one.
+template <bool ALIGNED>
+__device__ __forceinline__ uint4 load_piece(const uint32_t *row, int wpr, int p, int np, int g) {
+  if (p < np - 1) {   // uniform; one load (pair) on either side
+    if (ALIGNED) return *(const uint4 *)(row + 16 * p + 4 * g);
+    const uint2 lo = *(const uint2 *)(row + 16 * p + 4 * g);
+    const uint2 hi = *(const uint2 *)(row + 16 * p + 4 * g + 2);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  const int wl = 16 * (np - 1) + 4 * g;
+  if (ALIGNED) return *(const uint4 *)(row + min(wl, wpr - 4));
+  const uint2 lo = *(const uint2 *)(row + min(wl, wpr - 2));
+  const uint2 hi = *(const uint2 *)(row + min(wl + 2, wpr - 2));
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+template <int NT>
+struct StreamCtx {
+  const uint32_t *row;
+  int wpr, np, nb, astride, psteps, lane, g, i16, src;
+  bool tile_ok;
+  const uint8_t *as_w, *lq, *ls;
+  int col[NT];
+  bool on[NT];
+  uint32_t carry;
+  uint32_t rot;   // the current piece's last word from lane-group g-1 (fetched a piece ahead)
+};
+
+// One piece of the stream; the pieces are chained by template recursion so
+// that a window that ends early leaves straight away (no join after each
+// piece, which would make the compiler's count of loads in flight drop by
+// one per piece).
+template <typename F, int NT, bool ALIGNED, int Q>
+__device__ __forceinline__ void stream_piece(StreamCtx<NT> &c, Ring &R, v4f (&acc)[NT]) {
+  if constexpr (Q < kPieceMax) {
+    if (Q >= c.np) return;
+    R.r[(Q + kAhead) % kRing] = load_piece<ALIGNED>(c.row, c.wpr, Q + kAhead, c.np, c.g);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 a = R.r[Q % kRing];
+    if constexpr (F::kSteps == 1) {
+      const uint32_t sa =
+          c.tile_ok && 4 * Q + c.g < c.nb ? (uint32_t)c.as_w[c.i16 * c.astride + 4 * Q + c.g] : 0x7Fu;
+      v8i B[NT];
+      uint32_t sb[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int cc = c.on[n] ? c.col[n] : (c.col[n] & 1);
+        const uint4 *p = (const uint4 *)(c.lq + ((size_t)cc * c.psteps + Q) * 128 + c.g * 32);
+        const uint4 u0 = p[0], u1 = p[1];
+        B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        sb[n] = c.ls[((size_t)cc * c.psteps + Q) * 4 + c.g];
+      }
+      const v8i A = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)sa, 0, (int)sb[n]);
+    } else {
+      // All of the piece's LDS reads go out before its decode, so that
+      // their latency hides behind it; the next piece's history word is
+      // fetched here too (its slot always holds a loaded piece).
+      const uint32_t rot = c.rot;
+      const uint32_t sa = c.tile_ok && 8 * Q + 2 * c.g < c.nb
+                              ? (uint32_t)*(const uint16_t *)(c.as_w + c.i16 * c.astride + 8 * Q + 2 * c.g)
+                              : 0x7F7Fu;
+      v8i B[2][NT];
+      uint32_t sb[2][NT];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const int cc = c.on[n] ? c.col[n] : (c.col[n] & 1);
+          const uint4 *p = (const uint4 *)(c.lq + ((size_t)cc * c.psteps + 2 * Q + hh) * 128 + c.g * 32);
+          const uint4 u0 = p[0], u1 = p[1];
+          B[hh][n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+          sb[hh][n] = c.ls[((size_t)cc * c.psteps + 2 * Q + hh) * 4 + c.g];
+        }
+      }
+      c.rot = (uint32_t)__builtin_amdgcn_ds_bpermute(c.src, (int)R.r[(Q + 1) % kRing].w);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t hist = c.g == 0 ? c.carry : rot;
+      c.carry = rot;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
+        const nib2 d0 = decode_word(w0, hw);
+        const nib2 d1 = decode_word(w1, w0);
+        const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          if (hh == 0)
+            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[0][n], acc[n], 4, 0, 0, (int)sa, 0,
+                                                                     (int)sb[0][n]);
+          else
+            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[1][n], acc[n], 4, 0, 1, (int)sa, 0,
+                                                                     (int)sb[1][n]);
+        }
+      }
+    }
+    stream_piece<F, NT, ALIGNED, Q + 1>(c, R, acc);
+  }
+}
+
+// Decode and multiply the window's np pieces, the first kAhead of which
+// the caller has issued into the ring (later ones are issued here).
+template <typename F, int NT, bool ALIGNED>
+__device__ __forceinline__ void mma_stream(Ring &R, const uint32_t *row, int wpr, int np, bool tile_ok,
+                                           const uint8_t *as_w, int astride, int nb, const uint8_t *lq,
+                                           const uint8_t *ls, int psteps, const int (&col)[NT],
+                                           const bool (&on)[NT], v4f (&acc)[NT], int lane) {
+  StreamCtx<NT> c;
+  c.row = row; c.wpr = wpr; c.np = np; c.nb = nb; c.astride = astride; c.psteps = psteps;
+  c.lane = lane; c.g = lane >> 4; c.i16 = lane & 15; c.src = ((lane - 16) & 63) << 2;
+  c.tile_ok = tile_ok; c.as_w = as_w; c.lq = lq; c.ls = ls; c.carry = 0u;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) { c.col[n] = col[n]; c.on[n] = on[n]; }
+  if (F::kSteps == 2) c.rot = (uint32_t)__builtin_amdgcn_ds_bpermute(c.src, (int)R.r[0].w);
+  stream_piece<F, NT, ALIGNED, 0>(c, R, acc);
+  // Every ring slot is read once more here (never-true store): without a
+  // use on the early-exit paths the compiler would sink each load down to
+  // its piece, and nothing would be in flight ahead of the decode.
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) keep ^= R.r[i].x;
+  if (np < 0 && keep == 0x9E3779B9u) *(volatile uint32_t *)as_w = keep;
+}
+
 template <int NT>
 __device__ __forceinline__ int d_index(int wave, int nt, int row, int col) {
   const int lane = (row >> 2) * 16 + col;
@@ -785,6 +904,9 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
     const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.last = old == S.n_active - 1;
     if (S.last) st_ctr(ctr, 0);   // every arrival is in: clear for the next call
+    // a layer's final combines follow every stage-1 item, so every reader
+    // of the resident split is done with its counter
+    if (S.last && a.mode == MODE_FFN && a.x_resident) st_ctr(a.cntp, 0);
   }
   __syncthreads();
   if (S.last) combine_rows(a, S, rt);
@@ -832,60 +954,91 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       on[n] = n * 8 + (i16 >> 1) < ne;
       acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    uint32_t carry = 0u;
-    // Loads go out in the order they are needed, and they complete in that
-    // order: the token's split (first stage-1 item of a workgroup), the
-    // tile's scales, then the pieces, a fixed number of them. Each piece is
-    // waited for only where its decode starts. The scales ride in the two
-    // last piece registers when the tile leaves them free; otherwise they
-    // are loaded after the pieces.
-    fetch_ahead(0, ne, 0, J);
-    const bool sp_in_tile = fast && J <= kPieceMax - 2;
-    __builtin_amdgcn_sched_barrier(0);
-    if (sp_in_tile) {
-      const uint4 *sblk = (const uint4 *)(sc + row0 * nb);
-      tl.a[kPieceMax - 2] = sblk[min(lane, nb - 1)];
-      tl.a[kPieceMax - 1] = sblk[min(lane + 64, nb - 1)];
-      __builtin_amdgcn_sched_barrier(0);
-      load_tile_full<ALIGNED, kPieceMax - 2>(tl, rowp, wpr, J, g);
-    } else {
-      load_tile_full<ALIGNED, kPieceMax>(tl, rowp, wpr, J, g);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (sp_in_tile) {
-      AScalePre sp;
-      sp.v0 = tl.a[kPieceMax - 2];
-      sp.v1 = tl.a[kPieceMax - 1];
-      ascale_store(as_w, sp, nb);
-    }
-    TQ_MARK(S, 3);
-    PreDec pd;
     // (not with 3-4 N-tiles: their accumulators leave no registers for it)
     const int npre = predec && F::kSteps == 2 && NT <= 2 ? min(J, kPre) : 0;
-    if (npre) predecode(pd, tl, npre, carry, lane);
-    stage(0, ne, 0, J);
-    TQ_MARK(S, 4);
-    if (!sp_in_tile && fast) {
-      AScalePre sp;
-      ascale_prefetch(sp, sc + row0 * nb, nb);
-      ascale_store(as_w, sp, nb);
-    } else if (!fast) {
-      ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
-    }
-    if (!sp_in_tile) vm_wait<0>();   // (done already; tells the compiler)
-    TQ_MARK(S, 5);
-    lds_barrier();
-    TQ_MARK(S, 6);
-    // Two copies of the matrix-core loop: with pre-decoded pieces (a
-    // down-projection item, whose loads have all completed by now), and
-    // without, whose simpler control flow lets the compiler wait for each
-    // piece only where its decode starts.
-    if (npre)
+    if (npre) {
+      // A down-projection item: the whole tile is loaded (it has time until
+      // its h is complete) and its first pieces decoded while it waits.
+      // Loads go out in the order they are needed, and they complete in
+      // that order: the tile's scales, then a fixed number of pieces. The
+      // scales ride in the two last piece registers when the tile leaves
+      // them free; otherwise they are loaded after the pieces.
+      uint32_t carry = 0u;
+      fetch_ahead(0, ne, 0, J);
+      const bool sp_in_tile = fast && J <= kPieceMax - 2;
+      __builtin_amdgcn_sched_barrier(0);
+      if (sp_in_tile) {
+        const uint4 *sblk = (const uint4 *)(sc + row0 * nb);
+        tl.a[kPieceMax - 2] = sblk[min(lane, nb - 1)];
+        tl.a[kPieceMax - 1] = sblk[min(lane + 64, nb - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile_full<ALIGNED, kPieceMax - 2>(tl, rowp, wpr, J, g);
+      } else {
+        load_tile_full<ALIGNED, kPieceMax>(tl, rowp, wpr, J, g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (sp_in_tile) {
+        AScalePre sp;
+        sp.v0 = tl.a[kPieceMax - 2];
+        sp.v1 = tl.a[kPieceMax - 1];
+        ascale_store(as_w, sp, nb);
+      }
+      TQ_MARK(S, 3);
+      PreDec pd;
+      predecode(pd, tl, npre, carry, lane);
+      stage(0, ne, 0, J);
+      TQ_MARK(S, 4);
+      if (!sp_in_tile && fast) {
+        AScalePre sp;
+        ascale_prefetch(sp, sc + row0 * nb, nb);
+        ascale_store(as_w, sp, nb);
+      } else if (!fast) {
+        ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
+      }
+      vm_wait<0>();
+      TQ_MARK(S, 5);
+      lds_barrier();
+      TQ_MARK(S, 6);
       mma_tile<F, NT, true>(tl, pd, npre, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col,
                             on, acc, carry, lane);
-    else
-      mma_tile<F, NT, false>(tl, pd, 0, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col, on,
-                             acc, carry, lane);
+    } else {
+      // Streamed (see mma_stream). fetch_ahead first (a resident token's
+      // split, on a workgroup's first stage-1 item: it waits for the split
+      // to be complete and copies it; loads complete in issue order, so
+      // behind weight loads it would wait for them too), then the tile's
+      // scales (in the ring slots the first kAhead pieces leave free) and
+      // the first kAhead pieces.
+      Ring R;
+      fetch_ahead(0, ne, 0, J);
+      __builtin_amdgcn_sched_barrier(0);
+      if (fast) {
+        const uint4 *sblk = (const uint4 *)(sc + row0 * nb);
+        R.r[kAhead] = sblk[min(lane, nb - 1)];
+        R.r[kAhead + 1] = sblk[min(lane + 64, nb - 1)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 0; p < kAhead; ++p) R.r[p] = load_piece<ALIGNED>(rowp, wpr, p, J, g);
+      __builtin_amdgcn_sched_barrier(0);
+      TQ_MARK(S, 3);
+      TQ_MARK(S, 4);
+      if (fast) {
+        AScalePre sp;
+        sp.v0 = R.r[kAhead];
+        sp.v1 = R.r[kAhead + 1];
+        ascale_store(as_w, sp, nb);
+      }
+      stage(0, ne, 0, J);
+      if (!fast) {
+        ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
+        vm_wait<kAhead * (ALIGNED ? 1 : 2)>();
+      }
+      TQ_MARK(S, 5);
+      lds_barrier();
+      TQ_MARK(S, 6);
+      mma_stream<F, NT, ALIGNED>(R, rowp, wpr, J, tile_ok, as_w, astride, nb, S.bq, S.bs, F::kSteps * J, col, on,
+                                 acc, lane);
+    }
     TQ_MARK(S, 7);
     __syncthreads();
     epilogue(0, ne, acc);
@@ -957,24 +1110,17 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     return a.x_per_slot ? slot : slot / a.k;
   };
   const bool resident = s1 && a.x_resident;
-  int obs_old = 0, obsp_old = -1;
-  bool waited = false;
+  int obs_old = 0;
+  bool waited = false, fetched = false;
   auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
     if (resident && !S.x_done) {
       // this workgroup's first stage-1 item: once the token's split is
-      // complete, copy it into LDS (columns 0, 1: contiguous in the
-      // workspace and in LDS) before any weight load is issued. The copy is
-      // waited for right here: with LDS direct loads still in flight the
-      // compiler could no longer count which weight loads are done.
-      if (threadIdx.x == 0) {
-        spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
-        obsp_old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      // complete, copy it into LDS
+      if (threadIdx.x == 0) spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
       __syncthreads();
-      const int psteps = F::kSteps * np;
-      lds_copy16(S.bq, a.xq, 2 * psteps * 128);
-      lds_copy4(S.bs, a.xs, 2 * psteps * 4);
-      vm_wait<0>();
+      fetched = true;
+      copy_pass<F>(S.bq, S.bs, a.xq, a.xs, F::kSteps * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
+      vm_wait<0>();   // (loads whose store a lane skipped count as pending for the compiler)
       S.x_done = 1;    // read after the caller's barrier
     }
   };
@@ -1001,19 +1147,6 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       }
       __syncthreads();
       waited = true;
-    }
-    if (kp == 0 && F::kSteps * np == a.h_steps) {
-      // the whole of K in one window: each slot's hi and lo columns are one
-      // contiguous run in the workspace and in LDS (the K padding was
-      // written by the expert's last stage-1 row group)
-      const int psteps = a.h_steps;
-      for (int c = 0; c < ncol; ++c) {
-        const int slot = S.slots[c0 + c];
-        lds_copy16(S.bq + (size_t)2 * c * psteps * 128, a.hq + (size_t)slot * 2 * psteps * 128, 2 * psteps * 128);
-        lds_copy4(S.bs + (size_t)2 * c * psteps * 4, a.hs + (size_t)slot * 2 * psteps * 4, 2 * psteps * 4);
-      }
-      vm_wait<0>();
-      return;
     }
     copy_pass<F>(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
       return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
@@ -1047,21 +1180,6 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
           }
         }
       }
-      if (tile == a.n_rg1 - 1) {
-        // the last row group also writes the K padding of its slots' h
-        // splits (zero codes, scale 2^0), which the down projection copies
-        const int npad = F::kBlocks * (a.h_steps / F::kSteps) - a.n_rg1;
-        for (int idx = threadIdx.x; idx < ncol * npad * 32; idx += kThreads) {
-          const int c = idx / (npad * 32), r = idx - c * npad * 32, b = a.n_rg1 + (r >> 5), pos = r & 31;
-          const int slot = S.slots[c0 + c];
-          st_dc8(a.hq + (size_t)(slot * 2) * a.h_steps * 128 + F::offset(b, pos), 0u);
-          st_dc8(a.hq + (size_t)(slot * 2 + 1) * a.h_steps * 128 + F::offset(b, pos), 0u);
-          if (pos == 0) {
-            st_dc8(a.hs + (size_t)(slot * 2) * a.h_steps * 4 + F::scale_index(b), 127u);
-            st_dc8(a.hs + (size_t)(slot * 2 + 1) * a.h_steps * 4 + F::scale_index(b), 127u);
-          }
-        }
-      }
       __syncthreads();
       return;
     }
@@ -1074,10 +1192,18 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     });
   };
   gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, !s1, ahead, stage, epilogue);
-  if (obsp_old >= 0 && obsp_old == min(a.grid, S.n_active * a.n_rg1) - 1) {
-    // every workgroup that reads the split has fetched it: clear for the next call
-    st_ctr(a.cntp, 0);
-    st_ctr(a.cntp + kLineInts, 0);
+  if (fetched && ffn) {
+    // (a layer clears the split's counter in its final combine, which
+    // follows every stage-1 item)
+  } else if (fetched && threadIdx.x == 0) {
+    // counted only now, off the path to the first matrix-core step: the
+    // workgroups arrive here spread out in time, not all at once
+    const int old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == min(a.grid, S.n_active * a.n_rg1) - 1) {
+      // every workgroup that reads the split has fetched it: clear for the next call
+      st_ctr(a.cntp, 0);
+      st_ctr(a.cntp + kLineInts, 0);
+    }
   }
   if (s1 && ffn) {
     stores_done();
@@ -1113,6 +1239,12 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
   }
   if (S.n_active == 0 && a.mode != MODE_SLOTS)
     for (int i = tid; i < a.T * a.y_rows; i += kThreads) a.y[i] = 0.0f;
+  if (S.n_active == 0 && a.x_resident && tid == 0) {
+    // no work item reads the resident split: clear its counter once the
+    // workgroups that write it are done
+    spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
+    st_ctr(a.cntp, 0);
+  }
 }
 
 template <typename F, int NT, bool ALIGNED>
@@ -1146,6 +1278,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
     stores_done();
     if (tid == 0) __hip_atomic_fetch_add(a.cntp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#ifdef TQ_TRACE
+    if (TR && tid == 0) TR[63] = __builtin_amdgcn_s_memrealtime();
+#endif
   }
   if (tid == 0) S.x_done = 0;
   // routing, redundantly in every workgroup: active experts in id order
