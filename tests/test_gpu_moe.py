@@ -239,10 +239,12 @@ def test_single_token_calls_share_a_workspace(trellis_lib, orc):
         y = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(ids), dev(gw), workspace=ws)
         y_ref, bound, _ = orc.moe_gemv(syms, sc, x, ids, gate_w=gw)
         check_tol(y.cpu().numpy(), y_ref, bound, f"gemv call {i}")
+        torch.cuda.synchronize()
+        assert int(ws[:8].view(torch.int32)[1]) == 0   # no wait timed out
         y0 = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(empty), dev(gw), workspace=ws)
         assert (y0.cpu().numpy() == 0).all()
-    torch.cuda.synchronize()
-    assert int(ws[:8].view(torch.int32)[1]) == 0   # no wait timed out
+        torch.cuda.synchronize()
+        assert int(ws[:8].view(torch.int32)[1]) == 0
 
     cfg = workloads.MoEConfig(91, "small-1", 4, 256, 96, 3, 1, True)
     wsf = trellis_lib.ffn_workspace(cfg.n_exp, cfg.hidden, cfg.inter, 1, cfg.k)
@@ -251,9 +253,10 @@ def test_single_token_calls_share_a_workspace(trellis_lib, orc):
         run = lambda L: trellis_lib.moe_ffn(dev(L.gu_syms), dev(L.gu_scales), dev(L.dn_syms), dev(L.dn_scales),
                                             x_dev(L.x, True), dev(L.ids), dev(L.gate_w), workspace=wsf)
         _check_layer(trellis_lib, orc, layer, run=run)
+        assert int(wsf[:8].view(torch.int32)[1]) == 0   # no wait timed out
         ye, he = trellis_lib.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms),
                                      dev(layer.dn_scales), x_dev(layer.x, True), dev(-np.ones((1, 3), np.int32)),
                                      dev(layer.gate_w), workspace=wsf)
         assert (ye.cpu().numpy() == 0).all() and (he.float().cpu().numpy() == 0).all()
-    torch.cuda.synchronize()
-    assert int(wsf[:8].view(torch.int32)[1]) == 0
+        torch.cuda.synchronize()
+        assert int(wsf[:8].view(torch.int32)[1]) == 0

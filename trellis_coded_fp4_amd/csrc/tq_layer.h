@@ -69,6 +69,7 @@ constexpr int kBScaleBytes = 1024;          // and their UE8M0 scales
 constexpr int kAScaleBytes = 2048;          // per wave: its tile's UE8M0 bytes (16 rows x <= 128)
 constexpr int kXPre = 16;                   // activation values per lane fetched ahead of the weights
 constexpr int kLineInts = 32;               // one counter per 128-byte line
+constexpr int kSplitCopies = 8;             // lines holding the single-token split's done count
 
 enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 
@@ -131,7 +132,7 @@ static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_co
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.status = take(256);
-  L.cntp = take(2 * kLineInts * 4);   // resident-token split: done count, readers count
+  L.cntp = take((kSplitCopies + 1) * kLineInts * 4);   // resident-token split: done counts, readers count
   L.cnt1 = take((size_t)n_act * kLineInts * 4);
   L.obs1 = take((size_t)n_act * kLineInts * 4);
   L.cnt2 = take((size_t)n_rt * kLineInts * 4);
@@ -166,7 +167,7 @@ struct LayerArgs {
   int x_resident;               // one token, K <= 4096: split once per call, copied into each workgroup
   int n_xprep;                  // workgroups that split it (at most; one 32-value block per half-wave)
   uint8_t *xq; uint8_t *xs;     // the split token: columns 0 (hi), 1 (lo), step-chunk layout
-  int *cntp;                    // [0] split blocks done (x 1 per workgroup), [kLineInts] readers
+  int *cntp;                    // kSplitCopies lines: split done (+1 per workgroup that writes it); then readers
   int grid;
 #ifdef TQ_TRACE
   unsigned long long *trace;
@@ -257,6 +258,16 @@ __device__ __forceinline__ void spin_until(const int *ctr, int target, int *stat
       __hip_atomic_fetch_or(&status[ST_ERROR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
+  }
+}
+
+// Reset the single-token split's done counts for the next call (thread 0,
+// once no reader will poll them again): each copy is cleared only after
+// every writer's increment of it has landed.
+__device__ __forceinline__ void clear_split_counts(int *cntp, int writers, int *status) {
+  for (int r = 0; r < kSplitCopies; ++r) {
+    spin_until(cntp + r * kLineInts, writers, status);
+    st_ctr(cntp + r * kLineInts, 0);
   }
 }
 
@@ -577,11 +588,12 @@ __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *sro
   }
 }
 
-// The first kPre pieces of a trellis window decoded ahead of the matrix-core
-// loop: a down-projection item decodes them while it waits for its h, so
-// only the rest of the decode is left once h arrives. (More of them would
-// not fit the register file next to the tile.)
-constexpr int kPre = 6;
+// A whole trellis window (K <= 3072) decoded ahead of the matrix-core loop:
+// a down-projection item decodes it while it waits for its h, so only the
+// matrix-core steps are left once h arrives; the tile's registers are free
+// again once it is decoded. (Longer windows are not pre-decoded: their
+// decoded pieces would not fit the register file.)
+constexpr int kPre = 12;
 struct PreDec {
   uint4 s[kPre][2];   // A operands of steps 2q and 2q+1
 };
@@ -654,8 +666,9 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
       // that meet the zero codes of the activations' K padding, and rows past
       // the matrix give outputs that are never stored: no masking needed.
       // PRE: pieces [0, npre) were decoded ahead (npre <= kPre)
-      const bool pre = PRE && q < kPre && q < npre;
-      const uint4 a = t.a[q];
+      if (PRE && q >= kPre) break;
+      const bool pre = PRE;
+      const uint4 a = PRE ? make_uint4(0u, 0u, 0u, 0u) : t.a[q];
       uint32_t hist = 0u;
       if (!pre) {
         const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
@@ -905,8 +918,9 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
     S.last = old == S.n_active - 1;
     if (S.last) st_ctr(ctr, 0);   // every arrival is in: clear for the next call
     // a layer's final combines follow every stage-1 item, so every reader
-    // of the resident split is done with its counter
-    if (S.last && a.mode == MODE_FFN && a.x_resident) st_ctr(a.cntp, 0);
+    // of the resident split is done with its counter (one of them clears it)
+    if (S.last && rt == 0 && a.mode == MODE_FFN && a.x_resident)
+      clear_split_counts(a.cntp, min(a.n_xprep, a.grid), a.status);
   }
   __syncthreads();
   if (S.last) combine_rows(a, S, rt);
@@ -955,7 +969,7 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
     }
     // (not with 3-4 N-tiles: their accumulators leave no registers for it)
-    const int npre = predec && F::kSteps == 2 && NT <= 2 ? min(J, kPre) : 0;
+    const int npre = predec && F::kSteps == 2 && NT <= 2 && J <= kPre ? J : 0;
     if (npre) {
       // A down-projection item: the whole tile is loaded (it has time until
       // its h is complete) and its first pieces decoded while it waits.
@@ -1116,7 +1130,8 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     if (resident && !S.x_done) {
       // this workgroup's first stage-1 item: once the token's split is
       // complete, copy it into LDS
-      if (threadIdx.x == 0) spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
+      if (threadIdx.x == 0)
+        spin_until(a.cntp + (blockIdx.x % kSplitCopies) * kLineInts, min(a.n_xprep, a.grid), a.status);
       __syncthreads();
       fetched = true;
       copy_pass<F>(S.bq, S.bs, a.xq, a.xs, F::kSteps * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
@@ -1198,11 +1213,12 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   } else if (fetched && threadIdx.x == 0) {
     // counted only now, off the path to the first matrix-core step: the
     // workgroups arrive here spread out in time, not all at once
-    const int old = __hip_atomic_fetch_add(a.cntp + kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int *readers = a.cntp + kSplitCopies * kLineInts;
+    const int old = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == min(a.grid, S.n_active * a.n_rg1) - 1) {
       // every workgroup that reads the split has fetched it: clear for the next call
-      st_ctr(a.cntp, 0);
-      st_ctr(a.cntp + kLineInts, 0);
+      clear_split_counts(a.cntp, min(a.n_xprep, a.grid), a.status);
+      st_ctr(readers, 0);
     }
   }
   if (s1 && ffn) {
@@ -1242,8 +1258,7 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
   if (S.n_active == 0 && a.x_resident && tid == 0) {
     // no work item reads the resident split: clear its counter once the
     // workgroups that write it are done
-    spin_until(a.cntp, min(a.n_xprep, a.grid), a.status);
-    st_ctr(a.cntp, 0);
+    clear_split_counts(a.cntp, min(a.n_xprep, a.grid), a.status);
   }
 }
 
@@ -1277,7 +1292,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       }
     }
     stores_done();
-    if (tid == 0) __hip_atomic_fetch_add(a.cntp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // one copy of the count per kSplitCopies: the readers poll different lines
+    if (tid < kSplitCopies)
+      __hip_atomic_fetch_add(a.cntp + tid * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #ifdef TQ_TRACE
     if (TR && tid == 0) TR[63] = __builtin_amdgcn_s_memrealtime();
 #endif
