@@ -28,25 +28,18 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, v8i b, v4f c, int sa, int sb)
 
 // ---------------------------------------------------------------- FP8 E4M3
 
-// Round a float (|v| < 448) to OCP E4M3, ties to even.
+// Round a float (|v| <= 448) to OCP E4M3, ties to even, subnormals kept:
+// gfx950's v_cvt_pk_fp8_f32, which converts to the OCP formats on this chip.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  // |v| >= 2^-6: normal E4M3, keep 3 mantissa bits (round half to even),
-  // saturate at 448. Below: subnormals, multiples of 2^-9 (0..8; 8 is the
-  // smallest normal). Both are computed and selected, without branches.
-  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-  const uint32_t normal = min(r - ((127u - 7u) << 3), 0x7Eu);
-  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  return sign | (a >= 0x3C800000u ? normal : sub);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFu;
+}
+// Two at once: a in byte 0, b in byte 1.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
-  return (c & 0x80u) ? -mag : mag;
-}
+// The value of E4M3 code c (its low byte; exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // UE8M0 exponent E such that amax / 2^E lies in [128, 256); 2^E is exact.
 __device__ __forceinline__ int block_exponent(float amax) {

@@ -69,7 +69,6 @@ constexpr int kBScaleBytes = 1024;          // and their UE8M0 scales
 constexpr int kAScaleBytes = 2048;          // per wave: its tile's UE8M0 bytes (16 rows x <= 128)
 constexpr int kXPre = 16;                   // activation values per lane fetched ahead of the weights
 constexpr int kLineInts = 32;               // one counter per 128-byte line
-constexpr int kSplitCopies = 8;             // lines holding the single-token split's done count
 
 enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 
@@ -117,7 +116,7 @@ static void *g_trace = nullptr;
 #endif
 
 struct Layout {
-  size_t status, cntp, cnt1, obs1, cnt2, yslot, hq, hs, xq, xs, total;
+  size_t status, cnt1, obs1, cnt2, yslot, hq, hs, total;
 };
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -132,7 +131,6 @@ static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_co
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.status = take(256);
-  L.cntp = take((kSplitCopies + 1) * kLineInts * 4);   // resident-token split: done counts, readers count
   L.cnt1 = take((size_t)n_act * kLineInts * 4);
   L.obs1 = take((size_t)n_act * kLineInts * 4);
   L.cnt2 = take((size_t)n_rt * kLineInts * 4);
@@ -140,9 +138,6 @@ static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_co
   const size_t hs = h_cols ? (size_t)fmt_steps<F>(h_cols / 32) : 0;
   L.hq = take((size_t)n_slots * 2 * hs * 128);
   L.hs = take((size_t)n_slots * 2 * hs * 4);
-  const size_t xs = (size_t)fmt_steps<F>(x_cols / 32);
-  L.xq = take(2 * xs * 128);
-  L.xs = take(2 * xs * 4);
   L.total = o;
   return L;
 }
@@ -164,10 +159,7 @@ struct LayerArgs {
   int *status, *cnt1, *obs1, *cnt2;
   int n_rg1, n_s1;              // stage-1 row groups per expert, items
   int n_rt2, n_s2;              // stage-2 row tiles per expert, items
-  int x_resident;               // one token, K <= 4096: split once per call, copied into each workgroup
-  int n_xprep;                  // workgroups that split it (at most; one 32-value block per half-wave)
-  uint8_t *xq; uint8_t *xs;     // the split token: columns 0 (hi), 1 (lo), step-chunk layout
-  int *cntp;                    // kSplitCopies lines: split done (+1 per workgroup that writes it); then readers
+  int x_resident;               // one token, K <= 4096, 16-byte aligned: split by each workgroup once, kept in LDS
   int grid;
 #ifdef TQ_TRACE
   unsigned long long *trace;
@@ -258,16 +250,6 @@ __device__ __forceinline__ void spin_until(const int *ctr, int target, int *stat
       __hip_atomic_fetch_or(&status[ST_ERROR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
-  }
-}
-
-// Reset the single-token split's done counts for the next call (thread 0,
-// once no reader will poll them again): each copy is cleared only after
-// every writer's increment of it has landed.
-__device__ __forceinline__ void clear_split_counts(int *cntp, int writers, int *status) {
-  for (int r = 0; r < kSplitCopies; ++r) {
-    spin_until(cntp + r * kLineInts, writers, status);
-    st_ctr(cntp + r * kLineInts, 0);
   }
 }
 
@@ -432,6 +414,88 @@ __device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *l
       bool ok;
       const size_t el = x_elem<F>(a, K, nb, kp, np, npairs, u, row_of, ok);
       x_store_unit<F>(lq, ls, np, u, ok ? x_value(a, el, v[m]) : 0.0f, u < total);
+    }
+  }
+}
+
+// A single token's activations, split by each workgroup that needs them
+// (once, on its first stage-1 item) into LDS columns 0 (hi) and 1 (lo): four
+// lanes per 32-value block, eight values per lane, the block's maxima over
+// the four lanes of a quad. Blocks past K (up to the window's end) get zero
+// codes. 64 blocks per round, two rounds: K <= 4096. The raw values are
+// loaded first (tok_load), ahead of the weight loads, so that only they
+// are waited for when the split runs (tok_split).
+constexpr int kTokRounds = 2;
+struct TokRaw {
+  uint4 v[kTokRounds][2];   // bf16: v[r][0]; fp32: v[r][0..1]
+};
+
+template <typename F>
+__device__ __forceinline__ void tok_load(TokRaw &t, const LayerArgs &a, int nb, int np) {
+  const int j = threadIdx.x & 3;
+#pragma unroll
+  for (int r = 0; r < kTokRounds; ++r) {
+    const int b = 64 * r + (threadIdx.x >> 2);
+    const size_t el = b < nb ? (size_t)b * 32 + 8 * j : 0;   // (past K: a valid address, value unused)
+    if (a.x_bf16) {
+      t.v[r][0] = *(const uint4 *)((const uint16_t *)a.x + el);
+      t.v[r][1] = t.v[r][0];
+    } else {
+      t.v[r][0] = *(const uint4 *)((const float *)a.x + el);
+      t.v[r][1] = *(const uint4 *)((const float *)a.x + el + 4);
+    }
+  }
+}
+
+__device__ __forceinline__ float quad_max(float v) {
+  int m = __float_as_int(v);   // non-negative: integer order is float order
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));
+  return __int_as_float(m);
+}
+
+template <typename F>
+__device__ __forceinline__ void tok_split(const TokRaw &t, uint8_t *lq, uint8_t *ls, int psteps, int nb,
+                                          bool bf16) {
+  const int j = threadIdx.x & 3, nblk = F::kBlocks * (psteps / F::kSteps);
+#pragma unroll
+  for (int r = 0; r < kTokRounds; ++r) {
+    const int b = 64 * r + (threadIdx.x >> 2);
+    float f[8];
+    const uint32_t w[8] = {t.v[r][0].x, t.v[r][0].y, t.v[r][0].z, t.v[r][0].w,
+                           t.v[r][1].x, t.v[r][1].y, t.v[r][1].z, t.v[r][1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = bf16 ? (w[i >> 1] >> (16 * (i & 1))) << 16 : w[i];
+      f[i] = b < nb ? __uint_as_float(bits) : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    const int E = block_exponent(quad_max(m));
+    uint32_t hi[4], lo[4];
+    float res[8], m2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      hi[i / 2] = f32x2_to_e4m3(ldexpf(f[i], -E), ldexpf(f[i + 1], -E));
+      res[i] = f[i] - ldexpf(e4m3_to_f32(hi[i / 2]), E);
+      res[i + 1] = f[i + 1] - ldexpf(e4m3_to_f32(hi[i / 2] >> 8), E);
+      m2 = fmaxf(m2, fmaxf(fabsf(res[i]), fabsf(res[i + 1])));
+    }
+    const int El = block_exponent(quad_max(m2));
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) lo[i / 2] = f32x2_to_e4m3(ldexpf(res[i], -El), ldexpf(res[i + 1], -El));
+    if (b < nblk) {   // uniform over the quad
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int off = F::offset(b, 8 * j + i);
+        lq[off] = (uint8_t)(hi[i / 2] >> (8 * (i & 1)));
+        lq[(size_t)psteps * 128 + off] = (uint8_t)(lo[i / 2] >> (8 * (i & 1)));
+      }
+      if (j == 0) {
+        ls[F::scale_index(b)] = (uint8_t)(E + 127);
+        ls[(size_t)psteps * 4 + F::scale_index(b)] = (uint8_t)(El + 127);
+      }
     }
   }
 }
@@ -917,10 +981,6 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
     const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.last = old == S.n_active - 1;
     if (S.last) st_ctr(ctr, 0);   // every arrival is in: clear for the next call
-    // a layer's final combines follow every stage-1 item, so every reader
-    // of the resident split is done with its counter (one of them clears it)
-    if (S.last && rt == 0 && a.mode == MODE_FFN && a.x_resident)
-      clear_split_counts(a.cntp, min(a.n_xprep, a.grid), a.status);
   }
   __syncthreads();
   if (S.last) combine_rows(a, S, rt);
@@ -1117,29 +1177,29 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   const uint8_t *sc = s1 ? a.s1 : a.s2;
   const int rows = s1 ? a.rows1 : a.rows2, K = s1 ? a.cols1 : a.cols2, fast = s1 ? a.fast1 : a.fast2;
   const int nb = K / 32;
+  // (read before gather_slots' barriers: a thread may set it in this item)
+  // (one token means one N-tile: compiled for NT == 1 only)
+  const bool tok_first = NT == 1 && s1 && a.x_resident && !S.x_done;
   const int ne = gather_slots(S, e, a.T * a.k);
   TQ_MARK(S, 2);
   auto row_of = [&](int c) TQ_INLINE {
     const int slot = S.slots[c];
     return a.x_per_slot ? slot : slot / a.k;
   };
-  const bool resident = s1 && a.x_resident;
+  const bool resident = NT == 1 && s1 && a.x_resident;
   int obs_old = 0;
-  bool waited = false, fetched = false;
+  bool waited = false;
+  TokRaw tok;
   auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
-    if (resident && !S.x_done) {
-      // this workgroup's first stage-1 item: once the token's split is
-      // complete, copy it into LDS
-      if (threadIdx.x == 0)
-        spin_until(a.cntp + (blockIdx.x % kSplitCopies) * kLineInts, min(a.n_xprep, a.grid), a.status);
-      __syncthreads();
-      fetched = true;
-      copy_pass<F>(S.bq, S.bs, a.xq, a.xs, F::kSteps * np, 0, np, nb, 2, [&](int c) TQ_INLINE { return c; });
-      vm_wait<0>();   // (loads whose store a lane skipped count as pending for the compiler)
-      S.x_done = 1;    // read after the caller's barrier
-    }
+    // this workgroup's first stage-1 item: the token's raw values, ahead of
+    // the weight loads (split once those are out)
+    if (tok_first) tok_load<F>(tok, a, nb, np);
   };
   auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
+    if (tok_first) {
+      tok_split<F>(tok, S.bq, S.bs, F::kSteps * np, nb, a.x_bf16);
+      if (threadIdx.x == 0) S.x_done = 1;
+    }
     if (resident) return;
     if (s1) {
       // Several tokens: split their activations here. All of this
@@ -1207,20 +1267,6 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     });
   };
   gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, !s1, ahead, stage, epilogue);
-  if (fetched && ffn) {
-    // (a layer clears the split's counter in its final combine, which
-    // follows every stage-1 item)
-  } else if (fetched && threadIdx.x == 0) {
-    // counted only now, off the path to the first matrix-core step: the
-    // workgroups arrive here spread out in time, not all at once
-    int *readers = a.cntp + kSplitCopies * kLineInts;
-    const int old = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == min(a.grid, S.n_active * a.n_rg1) - 1) {
-      // every workgroup that reads the split has fetched it: clear for the next call
-      clear_split_counts(a.cntp, min(a.n_xprep, a.grid), a.status);
-      st_ctr(readers, 0);
-    }
-  }
   if (s1 && ffn) {
     stores_done();
     if (threadIdx.x == 0)
@@ -1255,11 +1301,6 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
   }
   if (S.n_active == 0 && a.mode != MODE_SLOTS)
     for (int i = tid; i < a.T * a.y_rows; i += kThreads) a.y[i] = 0.0f;
-  if (S.n_active == 0 && a.x_resident && tid == 0) {
-    // no work item reads the resident split: clear its counter once the
-    // workgroups that write it are done
-    clear_split_counts(a.cntp, min(a.n_xprep, a.grid), a.status);
-  }
 }
 
 template <typename F, int NT, bool ALIGNED>
@@ -1271,34 +1312,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) S.trp = nullptr;
 #endif
-  // A single token's activations are split once per call, one 32-value
-  // block per half-wave of the first n_xprep workgroups, into the
-  // workspace; every workgroup copies the split into LDS once.
-  const int n_prep = min(a.n_xprep, a.grid);
-  if (a.x_resident && (int)blockIdx.x < n_prep) {
-    const int nb1 = a.cols1 / 32, steps = fmt_steps<F>(nb1), pos = tid & 31;
-    for (int base = blockIdx.x * (kThreads / 32); base < 4 * steps; base += n_prep * (kThreads / 32)) {
-      const int blk = base + (tid >> 5);   // uniform per half-wave
-      const size_t el = blk < nb1 ? (size_t)blk * 32 + pos : 0;
-      const uint32_t word = x_word(a, el);
-      const Split sp = split_block(blk < nb1 ? x_value(a, el, word) : 0.0f);
-      if (blk < 4 * steps) {
-        st_dc8(a.xq + F::offset(blk, pos), sp.hi);
-        st_dc8(a.xq + (size_t)steps * 128 + F::offset(blk, pos), sp.lo);
-        if (pos == 0) {
-          st_dc8(a.xs + F::scale_index(blk), (uint32_t)(sp.E + 127));
-          st_dc8(a.xs + (size_t)steps * 4 + F::scale_index(blk), (uint32_t)(sp.El + 127));
-        }
-      }
-    }
-    stores_done();
-    // one copy of the count per kSplitCopies: the readers poll different lines
-    if (tid < kSplitCopies)
-      __hip_atomic_fetch_add(a.cntp + tid * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#ifdef TQ_TRACE
-    if (TR && tid == 0) TR[63] = __builtin_amdgcn_s_memrealtime();
-#endif
-  }
   if (tid == 0) S.x_done = 0;
   // routing, redundantly in every workgroup: active experts in id order
   const int n = a.T * a.k;
@@ -1469,9 +1482,7 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   a.n_s1 = std::min(w.n_mat, T * k) * a.n_rg1;
   a.n_rt2 = 1; a.n_s2 = 0;
   const int J = (w.cols / 32 + F::kBlocks - 1) / F::kBlocks;
-  a.x_resident = T == 1 && !x_per_slot && J <= kPieceMax;
-  a.n_xprep = (4 * fmt_steps<F>(w.cols / 32) + kThreads / 32 - 1) / (kThreads / 32);
-  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
+  a.x_resident = T == 1 && !x_per_slot && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
   return launch<F>(a, cus, stream);
 }
 
@@ -1513,9 +1524,7 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   a.n_rt2 = (hidden + 63) / 64;
   a.n_s2 = max_act * a.n_rt2;
   const int J = (hidden / 32 + F::kBlocks - 1) / F::kBlocks;
-  a.x_resident = T == 1 && J <= kPieceMax;
-  a.n_xprep = (4 * fmt_steps<F>(hidden / 32) + kThreads / 32 - 1) / (kThreads / 32);
-  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs); a.cntp = (int *)(ws + L.cntp);
+  a.x_resident = T == 1 && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
   if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
   rc = launch<F>(a, cus, stream);
   if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
