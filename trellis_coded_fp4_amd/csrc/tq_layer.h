@@ -820,10 +820,11 @@ template <int NT>
 struct StreamCtx {
   const uint32_t *row;
   int wpr, np, nb, astride, psteps, lane, g, i16, src;
-  bool tile_ok;
-  const uint8_t *as_w, *lq, *ls;
-  int col[NT];
-  bool on[NT];
+  const uint32_t *rowg;   // this lane's first word of piece 0 (row + 4g)
+  int lastw;              // piece p starts at rowg + min(16p, lastw) (aligned rows)
+  const uint8_t *sa;      // this lane's A scales of piece 0 in the wave's LDS slot
+  const uint8_t *bq[NT];  // N-tile n's B bytes of step 0 for this lane
+  const uint8_t *bs[NT];  // and its B scale
   uint32_t carry;
   uint32_t rot;   // the current piece's last word from lane-group g-1 (fetched a piece ahead)
 };
@@ -836,21 +837,23 @@ template <typename F, int NT, bool ALIGNED, int Q>
 __device__ __forceinline__ void stream_piece(StreamCtx<NT> &c, Ring &R, v4f (&acc)[NT]) {
   if constexpr (Q < kPieceMax) {
     if (Q >= c.np) return;
-    R.r[(Q + kAhead) % kRing] = load_piece<ALIGNED>(c.row, c.wpr, Q + kAhead, c.np, c.g);
+    if (ALIGNED)
+      R.r[(Q + kAhead) % kRing] = *(const uint4 *)(c.rowg + min(16 * (Q + kAhead), c.lastw));
+    else
+      R.r[(Q + kAhead) % kRing] = load_piece<ALIGNED>(c.row, c.wpr, Q + kAhead, c.np, c.g);
     __builtin_amdgcn_sched_barrier(0);
     const uint4 a = R.r[Q % kRing];
     if constexpr (F::kSteps == 1) {
-      const uint32_t sa =
-          c.tile_ok && 4 * Q + c.g < c.nb ? (uint32_t)c.as_w[c.i16 * c.astride + 4 * Q + c.g] : 0x7Fu;
+      // (A scales past the row's blocks: finite bytes that meet zero codes)
+      const uint32_t sa = c.sa[4 * Q];
       v8i B[NT];
       uint32_t sb[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const int cc = c.on[n] ? c.col[n] : (c.col[n] & 1);
-        const uint4 *p = (const uint4 *)(c.lq + ((size_t)cc * c.psteps + Q) * 128 + c.g * 32);
+        const uint4 *p = (const uint4 *)(c.bq[n] + Q * 128);
         const uint4 u0 = p[0], u1 = p[1];
         B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-        sb[n] = c.ls[((size_t)cc * c.psteps + Q) * 4 + c.g];
+        sb[n] = c.bs[n][Q * 4];
       }
       const v8i A = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
 #pragma unroll
@@ -861,20 +864,18 @@ __device__ __forceinline__ void stream_piece(StreamCtx<NT> &c, Ring &R, v4f (&ac
       // their latency hides behind it; the next piece's history word is
       // fetched here too (its slot always holds a loaded piece).
       const uint32_t rot = c.rot;
-      const uint32_t sa = c.tile_ok && 8 * Q + 2 * c.g < c.nb
-                              ? (uint32_t)*(const uint16_t *)(c.as_w + c.i16 * c.astride + 8 * Q + 2 * c.g)
-                              : 0x7F7Fu;
+      // (A scales past the row's blocks: finite bytes that meet zero codes)
+      const uint32_t sa = *(const uint16_t *)(c.sa + 8 * Q);
       v8i B[2][NT];
       uint32_t sb[2][NT];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const int cc = c.on[n] ? c.col[n] : (c.col[n] & 1);
-          const uint4 *p = (const uint4 *)(c.lq + ((size_t)cc * c.psteps + 2 * Q + hh) * 128 + c.g * 32);
+          const uint4 *p = (const uint4 *)(c.bq[n] + (2 * Q + hh) * 128);
           const uint4 u0 = p[0], u1 = p[1];
           B[hh][n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-          sb[hh][n] = c.ls[((size_t)cc * c.psteps + 2 * Q + hh) * 4 + c.g];
+          sb[hh][n] = c.bs[n][(2 * Q + hh) * 4];
         }
       }
       c.rot = (uint32_t)__builtin_amdgcn_ds_bpermute(c.src, (int)R.r[(Q + 1) % kRing].w);
@@ -912,9 +913,16 @@ __device__ __forceinline__ void mma_stream(Ring &R, const uint32_t *row, int wpr
   StreamCtx<NT> c;
   c.row = row; c.wpr = wpr; c.np = np; c.nb = nb; c.astride = astride; c.psteps = psteps;
   c.lane = lane; c.g = lane >> 4; c.i16 = lane & 15; c.src = ((lane - 16) & 63) << 2;
-  c.tile_ok = tile_ok; c.as_w = as_w; c.lq = lq; c.ls = ls; c.carry = 0u;
+  c.rowg = row + 4 * c.g;
+  c.lastw = min(16 * (np - 1), wpr - 4 - 4 * c.g);
+  c.sa = as_w + c.i16 * astride + (F::kSteps == 2 ? 2 : 1) * c.g;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) { c.col[n] = col[n]; c.on[n] = on[n]; }
+  for (int n = 0; n < NT; ++n) {
+    const int cc = on[n] ? col[n] : (col[n] & 1);
+    c.bq[n] = lq + (size_t)cc * psteps * 128 + c.g * 32;
+    c.bs[n] = ls + (size_t)cc * psteps * 4 + c.g;
+  }
+  c.carry = 0u;
   if (F::kSteps == 2) c.rot = (uint32_t)__builtin_amdgcn_ds_bpermute(c.src, (int)R.r[0].w);
   stream_piece<F, NT, ALIGNED, 0>(c, R, acc);
   // Every ring slot is read once more here (never-true store): without a
@@ -1101,6 +1109,9 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
         sp.v0 = R.r[kAhead];
         sp.v1 = R.r[kAhead + 1];
         ascale_store(as_w, sp, nb);
+        // the last row's last piece may read up to 7 bytes past the tile's
+        // scales: finite ones (2^0)
+        if (lane == 0 && 16 * nb + 8 <= kAScaleBytes) *(uint64_t *)(as_w + 16 * nb) = 0x7F7F7F7F7F7F7F7Full;
       }
       stage(0, ne, 0, J);
       if (!fast) {
