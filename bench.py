@@ -64,6 +64,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-stage-events", action="store_true",
                    help="no events around each launch (time only the whole timed region)")
+    p.add_argument("--event-every", type=int, default=8, metavar="N",
+                   help="bracket every N-th launch of the timed region with a pair of events (each pair costs "
+                        "the stream a few microseconds, so bracketing every launch slows the loop it measures)")
+    p.add_argument("--event-release", choices=("device", "none", "system"), default="none",
+                   help="memory release of the per-launch events: device scope (default), no system fence, "
+                        "or HIP's default system scope, which writes back and invalidates the caches each record")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB ten times (reference for the HBM "
                         "byte counters of a profiler) and exit")
@@ -90,20 +96,37 @@ class Hip:
     def __init__(self):
         L = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
         L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.L = L
 
-    def event(self):
+    # hipEventDisableSystemFence, hipEventReleaseToDevice (hip_runtime_api.h)
+    FLAGS = {"system": 0, "none": 0x20000000, "device": 0x40000000}
+
+    def event(self, release="system"):
         e = ctypes.c_void_p()
-        rc = self.L.hipEventCreate(ctypes.byref(e))
+        rc = self.L.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS[release])
         assert rc == 0, rc
         return e.value
 
     def record(self, ev, stream):
         rc = self.L.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
         assert rc == 0, rc
+
+    def bracket(self, call, events, stream):
+        """call, or a callable that records events[0] / events[1] on stream around it."""
+        if not events:
+            return call
+        rec, e0, e1, st = self.L.hipEventRecord, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]), \
+            ctypes.c_void_p(stream)
+
+        def run():
+            rec(e0, st)
+            call()
+            rec(e1, st)
+        return run
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -126,8 +149,9 @@ def ring_copies(tensors, bytes_per_copy, ring_gb):
 
 # ---------------------------------------------------------------- workloads
 #
-# Each returns a dict: name/config, step(s, events) that enqueues one step
-# (recording events[0] / events[1] around the launch when given), per-step
+# Each returns a dict: name/config, make(s, events) that returns a callable
+# enqueueing step s (recording events[0] / events[1] around the launch when
+# given) with its arguments already checked and marshalled, per-step
 # algorithmic bytes, and optionally flops and a CPU-oracle sample.
 
 def layer_workload(args, cfg, mx=False):
@@ -159,18 +183,14 @@ def layer_workload(args, cfg, mx=False):
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def step(s, events=None):
+    def make(s, events=None):
         a, b, c, d = ring[s % len(ring)]
         xs, ids, gw = routes[s]
         if mx:
-            if events:
-                hip.record(events[0], stream)
-            tq.mxfp4_moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws)
-            if events:
-                hip.record(events[1], stream)
-        else:
-            tq.moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws,
-                       events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
+            return hip.bracket(tq.mxfp4_moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True),
+                               events, stream)
+        return tq.moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True,
+                          events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
 
     def cpu_sample(seconds):
         import oracle
@@ -188,7 +208,7 @@ def layer_workload(args, cfg, mx=False):
               "k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 matrix-core "
               "gate_up + SwiGLU, down + combine)")
     return dict(
-        name=cfg.name + (" [expanded MXFP4]" if mx else ""), step=step, hip=hip, stream=stream,
+        name=cfg.name + (" [expanded MXFP4]" if mx else ""), make=make, hip=hip, stream=stream,
         bytes=lambda s: uniq[s] * expert_weights * bpw,
         flops=lambda s: 2.0 * slots[s] * expert_weights,
         tokens=T, kernel=kernel, cpu=cpu_sample,
@@ -213,13 +233,9 @@ def gemv_workload(args):
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def step(s, events=None):
+    def make(s, events=None):
         a, b = ring[s % len(ring)]
-        if events:
-            hip.record(events[0], stream)
-        tq.moe_gemv(a, b, xs, ids, y=y, workspace=ws)
-        if events:
-            hip.record(events[1], stream)
+        return hip.bracket(tq.moe_gemv(a, b, xs, ids, y=y, workspace=ws, prepare=True), events, stream)
 
     def cpu_sample(seconds):
         import oracle
@@ -232,7 +248,7 @@ def gemv_workload(args):
         dt = time.perf_counter() - t0
         return done * rows * cols * TRELLIS_BPW / dt / 1e9, f"{done} GEMV(s), single-threaded C oracle, {dt:.1f} s"
 
-    return dict(name=c["name"], step=step, hip=hip, stream=stream, bytes=lambda s: rows * cols * TRELLIS_BPW,
+    return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: rows * cols * TRELLIS_BPW,
                 flops=lambda s: 2.0 * rows * cols, tokens=1, cpu=cpu_sample,
                 kernel="k_layer<FmtTrellis> (routed GEMV, one slot)",
                 config={"rows": rows, "cols": cols, "tokens": 1, "x": "fp32", "ring_copies": len(ring)})
@@ -255,12 +271,9 @@ def expand_workload(args):
     stream = torch.cuda.current_stream().cuda_stream
     weights = n * rows * cols
 
-    def step(s, events=None):
-        if events:
-            hip.record(events[0], stream)
-        tq.decode_expand(syms, sc, codes_out=codes, scales_out=scales_out)
-        if events:
-            hip.record(events[1], stream)
+    def make(s, events=None):
+        return hip.bracket(tq.decode_expand(syms, sc, codes_out=codes, scales_out=scales_out, prepare=True),
+                           events, stream)
 
     g = workloads.rng(c["config_id"], 0)
     small = (workloads.symbols(g, 1, 64, cols), workloads.scales(g, 1, 64, cols))
@@ -277,7 +290,7 @@ def expand_workload(args):
         return done * 64 * cols * TRELLIS_BPW / dt / 1e9, \
             f"{done} expand(s) of a 64x{cols} matrix, single-threaded C oracle, {dt:.1f} s"
 
-    return dict(name=c["name"], step=step, hip=hip, stream=stream, bytes=lambda s: weights * TRELLIS_BPW,
+    return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: weights * TRELLIS_BPW,
                 flops=None, tokens=None, cpu=cpu_sample, traffic_bytes=weights * (TRELLIS_BPW + MX_BPW),
                 kernel="k_expand_quads (decode to packed E2M1 + scale copy)",
                 config={"matrices": n, "rows": rows, "cols": cols, "read_bytes": weights * TRELLIS_BPW,
@@ -327,16 +340,22 @@ def main():
     torch.cuda.set_device(0)
     W = pick(args)
     hip, stream = W["hip"], W["stream"]
-    evs = [(hip.event(), hip.event()) for _ in range(args.steps)] if not args.no_stage_events else None
+    every = max(1, args.event_every)
+    evs = [(hip.event(args.event_release), hip.event(args.event_release)) if s % every == 0 else None
+           for s in range(args.steps)] if not args.no_stage_events else None
     t0e, t1e = hip.event(), hip.event()
 
-    for s in range(args.warmup):
-        W["step"](s)
+    # Every step's call is checked and marshalled here, before the timed region:
+    # inside it each step is one entry into the C library.
+    warm = [W["make"](s) for s in range(args.warmup)]
+    calls = [W["make"](args.warmup + s, evs[s] if evs else None) for s in range(args.steps)]
+    for c in warm:
+        c()
     torch.cuda.synchronize()
     hip.record(t0e, stream)
     w0 = time.perf_counter()
-    for s in range(args.steps):
-        W["step"](args.warmup + s, evs[s] if evs else None)
+    for c in calls:
+        c()
     hip.record(t1e, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -348,10 +367,11 @@ def main():
 
     roofline, launch = None, None
     if evs:
-        d = np.array([hip.elapsed_ms(a, b) for a, b in evs])
+        d = np.array([hip.elapsed_ms(*e) for e in evs if e])
         launch = {"kernel_us_mean": float(d.mean() * 1e3), "kernel_us_min": float(d.min() * 1e3),
-                  "step_us": float(ms_per_step * 1e3)}
-        per_launch = float(np.mean([W["bytes"](s) for s in timed]))
+                  "step_us": float(ms_per_step * 1e3), "launches_bracketed": len(d), "every": every,
+                  "event_release": args.event_release}
+        per_launch = float(np.mean([W["bytes"](s) for s, e in zip(timed, evs) if e]))
         achieved = per_launch / (d.mean() * 1e-3) / 1e9
         traffic = None
         if os.path.exists(PROFILE_TRAFFIC):
@@ -367,7 +387,7 @@ def main():
         if W.get("traffic_bytes"):
             roofline["read_plus_write_GBs"] = round(W["traffic_bytes"] / (d.mean() * 1e-3) / 1e9, 1)
         if W.get("flops"):
-            fl = float(np.mean([W["flops"](s) for s in timed]))
+            fl = float(np.mean([W["flops"](s) for s, e in zip(timed, evs) if e]))
             tf = fl / (d.mean() * 1e-3) / 1e12
             roofline["matrix_core"] = {"useful_tflops": round(tf, 3), "fp4_dense_peak_tflops": FP4_PEAK_TFLOPS,
                                        "frac": round(tf / FP4_PEAK_TFLOPS, 6), "flops_per_launch": fl}
@@ -399,7 +419,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(W["tokens"] / (ms_per_step * 1e-3), 1) if W.get("tokens") else None,
         "config": dict({"workload": W["name"]}, **W["config"],
-                       **{"stage_events": bool(evs), "wall_s": round(wall, 4)}),
+                       **{"wall_s": round(wall, 4)}),
         "launch": launch,
         "roofline": roofline,
         "cpu_baseline": cpu,

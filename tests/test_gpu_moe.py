@@ -260,3 +260,32 @@ def test_single_token_calls_share_a_workspace(trellis_lib, orc):
         assert (ye.cpu().numpy() == 0).all() and (he.float().cpu().numpy() == 0).all()
         torch.cuda.synchronize()
         assert int(wsf[:8].view(torch.int32)[1]) == 0
+
+
+def test_prepared_calls(trellis_lib, orc):
+    """Calls checked and marshalled once (prepare=True) and entered many times
+    give the eager results: a layer on two weight copies, alternated."""
+    announce("prepared moe_ffn / moe_gemv calls, replayed")
+    import torch
+    cfg = workloads.MoEConfig(92, "small-prep", 4, 256, 96, 2, 1, True)
+    layer = workloads.moe_layer(cfg, layer_id=0)
+    w = [(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales)) for _ in range(2)]
+    x, ids, gw = x_dev(layer.x, True), dev(layer.ids), dev(layer.gate_w)
+    ws = trellis_lib.ffn_workspace(cfg.n_exp, cfg.hidden, cfg.inter, 1, cfg.k)
+    calls = [trellis_lib.moe_ffn(*w[i], x, ids, gw, workspace=ws, prepare=True) for i in range(2)]
+    assert isinstance(calls[0], trellis_lib.Call)
+    for r in range(4):
+        y, h = calls[r % 2]()
+        torch.cuda.synchronize()
+        _check_layer(trellis_lib, orc, layer, run=lambda L, y=y, h=h: (y, h))
+        assert int(ws[:8].view(torch.int32)[1]) == 0
+
+    E, rows, cols, k = 4, 64, 512, 2
+    g = workloads.rng(605, 0)
+    syms, sc = workloads.symbols(g, E, rows, cols), workloads.scales(g, E, rows, cols)
+    xg = workloads.activations(g, 1, cols, True)
+    idg, gwg = workloads.routing_topk(g, 1, E, k)
+    call = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(xg, True), dev(idg), dev(gwg), prepare=True)
+    y_ref, bound, _ = orc.moe_gemv(syms, sc, xg, idg, gate_w=gwg)
+    for r in range(3):
+        check_tol(call().cpu().numpy(), y_ref, bound, f"prepared gemv replay {r}")

@@ -126,6 +126,31 @@ def _check(t, dtype, name, shape=None):
     return t
 
 
+class Call:
+    """One library call with its arguments marshalled ahead of time.
+
+    ``fn(..., prepare=True)`` runs every check and builds the ctypes arguments
+    once and returns a Call instead of launching; ``call()`` then only enters
+    the C function (for loops that launch the same shapes many times).
+    ``result`` is what the eager function returns (the output tensors)."""
+
+    __slots__ = ("fn", "args", "name", "result", "keep")
+
+    def __init__(self, fn, args, name, result, keep):
+        self.fn, self.args, self.name, self.result, self.keep = fn, args, name, result, keep
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc:
+            raise TrellisError(rc, self.name)
+        return self.result
+
+
+def _run(prepare, fn, args, name, result, keep=()):
+    c = Call(fn, args, name, result, keep)
+    return c if prepare else c()
+
+
 def mat(syms, scales) -> Mat:
     """trellis_mat_t for syms [n_mat, rows, cols/16] int32/uint32 and scales [n_mat, rows, cols/32] uint8."""
     torch = _torch()
@@ -141,7 +166,7 @@ def mat(syms, scales) -> Mat:
     return Mat(syms.data_ptr(), scales.data_ptr(), n_mat, rows, wpr * 16)
 
 
-def decode_expand(syms, scales, codes_out=None, scales_out=None, stream=None):
+def decode_expand(syms, scales, codes_out=None, scales_out=None, stream=None, prepare=False):
     """Expand to resident MXFP4: returns (codes [n_mat, rows, cols/2] uint8, scales copy)."""
     torch = _torch()
     m = mat(syms, scales)
@@ -151,11 +176,9 @@ def decode_expand(syms, scales, codes_out=None, scales_out=None, stream=None):
         scales_out = torch.empty((m.n_mat, m.rows, m.cols // 32), dtype=torch.uint8, device=syms.device)
     _check(codes_out, torch.uint8, "codes_out", (m.n_mat, m.rows, m.cols // 2))
     _check(scales_out, torch.uint8, "scales_out", (m.n_mat, m.rows, m.cols // 32))
-    rc = lib().trellis_decode_expand(_stream(stream), ctypes.byref(m), codes_out.data_ptr(),
-                                     scales_out.data_ptr())
-    if rc:
-        raise TrellisError(rc, "trellis_decode_expand")
-    return codes_out, scales_out
+    return _run(prepare, lib().trellis_decode_expand,
+                (_stream(stream), ctypes.byref(m), codes_out.data_ptr(), scales_out.data_ptr()),
+                "trellis_decode_expand", (codes_out, scales_out), (m,))
 
 
 def _x_dtype(x):
@@ -184,7 +207,7 @@ def ffn_workspace(n_exp, hidden, inter, T, k, device="cuda"):
 
 
 def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
-             stream=None):
+             stream=None, prepare=False):
     """Routed fused-decode GEMV. y is [T, k, rows] without topk_w, [T, rows] with it."""
     torch = _torch()
     m = mat(syms, scales)
@@ -199,16 +222,14 @@ def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, w
     _check(y, torch.float32, "y", shape)
     if workspace is None:
         workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
-    rc = lib().trellis_moe_gemv(_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x),
-                                int(bool(x_per_slot)), topk_ids.data_ptr(), _ptr(topk_w), T, k,
-                                y.data_ptr(), workspace.data_ptr(), workspace.numel())
-    if rc:
-        raise TrellisError(rc, "trellis_moe_gemv")
-    return y
+    return _run(prepare, lib().trellis_moe_gemv,
+                (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
+                 topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
+                "trellis_moe_gemv", y, (m,))
 
 
 def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
-            workspace=None, stream=None, events=None):
+            workspace=None, stream=None, events=None, prepare=False):
     """Whole fused MoE layer; returns (y [T, hidden] fp32, h [T, k, inter] bf16).
 
     ``events``: optional ctypes array of 4 hipEvent_t recorded at the stage
@@ -230,12 +251,11 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
     _check(y, torch.float32, "y", (T, hidden))
     if workspace is None:
         workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
-    rc = lib().trellis_moe_ffn_timed(_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(),
-                                     _x_dtype(x), topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(),
-                                     y.data_ptr(), workspace.data_ptr(), workspace.numel(), events)
-    if rc:
-        raise TrellisError(rc, "trellis_moe_ffn")
-    return y, h
+    return _run(prepare, lib().trellis_moe_ffn_timed,
+                (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
+                 topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+                 workspace.numel(), events),
+                "trellis_moe_ffn", (y, h), (mg, md, events))
 
 
 # ---------------------------------------------------------------- expanded (MXFP4) weights
@@ -255,7 +275,7 @@ def mx_mat(codes, scales) -> MxMat:
 
 
 def mxfp4_moe_gemv(codes, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
-                   stream=None):
+                   stream=None, prepare=False):
     """moe_gemv on expanded MXFP4 weights (trellis_mxfp4_moe_gemv)."""
     torch = _torch()
     m = mx_mat(codes, scales)
@@ -270,16 +290,14 @@ def mxfp4_moe_gemv(codes, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=
     _check(y, torch.float32, "y", shape)
     if workspace is None:
         workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
-    rc = lib().trellis_mxfp4_moe_gemv(_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x),
-                                      int(bool(x_per_slot)), topk_ids.data_ptr(), _ptr(topk_w), T, k,
-                                      y.data_ptr(), workspace.data_ptr(), workspace.numel())
-    if rc:
-        raise TrellisError(rc, "trellis_mxfp4_moe_gemv")
-    return y
+    return _run(prepare, lib().trellis_mxfp4_moe_gemv,
+                (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
+                 topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
+                "trellis_mxfp4_moe_gemv", y, (m,))
 
 
 def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, prepare=False):
     """moe_ffn on expanded MXFP4 weights (trellis_mxfp4_moe_ffn); returns (y, h)."""
     torch = _torch()
     mg = mx_mat(gu_codes, gu_scales)
@@ -298,9 +316,8 @@ def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=
     _check(y, torch.float32, "y", (T, hidden))
     if workspace is None:
         workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
-    rc = lib().trellis_mxfp4_moe_ffn(_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(),
-                                     _x_dtype(x), topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(),
-                                     y.data_ptr(), workspace.data_ptr(), workspace.numel())
-    if rc:
-        raise TrellisError(rc, "trellis_mxfp4_moe_ffn")
-    return y, h
+    return _run(prepare, lib().trellis_mxfp4_moe_ffn,
+                (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
+                 topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+                 workspace.numel()),
+                "trellis_mxfp4_moe_ffn", (y, h), (mg, md))
