@@ -687,8 +687,8 @@ __device__ __forceinline__ void predecode(PreDec &d, const Tile &t, int np, uint
 // against NT N-tiles of the window's LDS columns. Lane
 // (column jc = lane & 15, lane-group g): N-tile n reads LDS column col[n]
 // (zeros when !on[n]).
-template <typename F, int NT, bool PRE>
-__device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int npre, int p0, int np, bool tile_ok,
+template <typename F, int NT>
+__device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool tile_ok,
                                          int wpr, const uint8_t *as_w, int astride, int a_p0, int nb,
                                          const uint8_t *lq, const uint8_t *ls, int psteps,
                                          const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT],
@@ -729,16 +729,10 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
       // Words past the row end (clamped loads) decode to finite E2M1 values
       // that meet the zero codes of the activations' K padding, and rows past
       // the matrix give outputs that are never stored: no masking needed.
-      // PRE: pieces [0, npre) were decoded ahead (npre <= kPre)
-      if (PRE && q >= kPre) break;
-      const bool pre = PRE;
-      const uint4 a = PRE ? make_uint4(0u, 0u, 0u, 0u) : t.a[q];
-      uint32_t hist = 0u;
-      if (!pre) {
-        const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
-        hist = g == 0 ? carry : rot;
-        carry = rot;
-      }
+      const uint4 a = t.a[q];
+      const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.w);
+      const uint32_t hist = g == 0 ? carry : rot;
+      carry = rot;
       const int sb_a = 8 * j + 2 * g;
       const uint32_t sa =
           tile_ok && sb_a < nb ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 8 * (a_p0 + q) + 2 * g) : 0x7F7Fu;
@@ -758,16 +752,10 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
           B[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
           sb[n] = ls[((size_t)c * psteps + step) * 4 + g];
         }
-        v8i A;
-        if (pre) {
-          const uint4 x = pd.s[q < kPre ? q : 0][hh];
-          A = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-          const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
-          const nib2 d0 = decode_word(w0, hw);
-          const nib2 d1 = decode_word(w1, w0);
-          A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
-        }
+        const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
+        const nib2 d0 = decode_word(w0, hw);
+        const nib2 d1 = decode_word(w1, w0);
+        const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           if (hh == 0)
@@ -780,6 +768,104 @@ __device__ __forceinline__ void mma_tile(const Tile &t, const PreDec &pd, int np
       }
     }
   }
+}
+
+// One matrix-core step's B operands (LDS) for the NT N-tiles.
+template <int NT>
+struct BStep {
+  v8i b[NT];
+  uint32_t s[NT];
+};
+
+template <int NT>
+__device__ __forceinline__ void read_bstep(BStep<NT> &o, const uint8_t *lq, const uint8_t *ls, int psteps, int step,
+                                           const int (&c)[NT], int g) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const uint4 *p = (const uint4 *)(lq + ((size_t)c[n] * psteps + step) * 128 + g * 32);
+    const uint4 u0 = p[0], u1 = p[1];
+    o.b[n] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+    o.s[n] = ls[((size_t)c[n] * psteps + step) * 4 + g];
+  }
+}
+
+// Matrix-core pass over a window whose np (<= kPre) pieces were all decoded
+// ahead. Nothing waits for memory here, so the pass is latency-bound unless
+// it is pipelined: each step's LDS operands are read kD steps ahead, and the
+// even and odd steps of a piece accumulate in separate registers (summed at
+// the end), so consecutive matrix-core ops do not depend on each other. The
+// steps are a compile-time recursion that returns past the last one: a loop
+// of guarded steps would rejoin after each, and at every join the compiler
+// waits for all outstanding LDS reads, which undoes the reading ahead.
+template <int NT>
+struct PreCtx {
+  const uint8_t *as_row;   // this lane's A-scale bytes of piece 0 (LDS)
+  const uint8_t *lq, *ls;
+  int c[NT];
+  int psteps, ns, nb, g;
+  bool tile_ok;
+};
+
+template <int NT>
+__device__ __forceinline__ uint32_t pre_sa(const PreCtx<NT> &x, int q) {
+  return x.tile_ok && 8 * q + 2 * x.g < x.nb ? (uint32_t)*(const uint16_t *)(x.as_row + 8 * q) : 0x7F7Fu;
+}
+
+template <int NT, int S>
+__device__ __forceinline__ void pre_step(const PreCtx<NT> &x, const PreDec &pd, BStep<NT> (&ring)[NT == 1 ? 3 : 1],
+                                         uint32_t (&sa)[2], v4f (&acc)[NT], v4f (&acc2)[NT]) {
+  constexpr int kD = NT == 1 ? 2 : 0;
+  if constexpr (S < 2 * kPre) {
+    if (S >= x.ns) return;
+    constexpr int q = S >> 1, hh = S & 1;
+    if (S + kD < x.ns) read_bstep<NT>(ring[(S + kD) % (kD + 1)], x.lq, x.ls, x.psteps, S + kD, x.c, x.g);
+    if (hh == 0 && S + 2 < x.ns) sa[(q + 1) & 1] = pre_sa(x, q + 1);
+    const uint4 w = pd.s[q][hh];
+    const v8i A = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    const BStep<NT> &cur = ring[S % (kD + 1)];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (hh == 0)
+        acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, cur.b[n], acc[n], 4, 0, 0, (int)sa[q & 1], 0,
+                                                                 (int)cur.s[n]);
+      else
+        acc2[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, cur.b[n], acc2[n], 4, 0, 1, (int)sa[q & 1], 0,
+                                                                  (int)cur.s[n]);
+    }
+    pre_step<NT, S + 1>(x, pd, ring, sa, acc, acc2);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void mma_pre(const PreDec &pd, int np, bool tile_ok, const uint8_t *as_w, int astride,
+                                        int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
+                                        const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT], int lane) {
+  constexpr int kD = NT == 1 ? 2 : 0;   // steps read ahead (registers: only with one N-tile)
+  PreCtx<NT> x;
+  x.g = lane >> 4;
+  x.as_row = as_w + (lane & 15) * astride + 2 * x.g;
+  x.lq = lq;
+  x.ls = ls;
+  x.psteps = psteps;
+  x.ns = 2 * np;
+  x.nb = nb;
+  x.tile_ok = tile_ok;
+  v4f acc2[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    // unused N-tile lanes read column 0 or 1 (see mma_tile)
+    x.c[n] = on[n] ? col[n] : (col[n] & 1);
+    acc2[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  BStep<NT> ring[kD + 1];
+  uint32_t sa[2];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) read_bstep<NT>(ring[d], lq, ls, psteps, d < x.ns ? d : 0, x.c, x.g);
+  sa[0] = pre_sa(x, 0);
+  sa[1] = 0x7F7Fu;
+  pre_step<NT, 0>(x, pd, ring, sa, acc, acc2);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] += acc2[n];
 }
 
 // ---------------------------------------------------------------- streamed window
@@ -1081,8 +1167,7 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       TQ_MARK(S, 5);
       lds_barrier();
       TQ_MARK(S, 6);
-      mma_tile<F, NT, true>(tl, pd, npre, 0, J, tile_ok, wpr, as_w, astride, 0, nb, S.bq, S.bs, F::kSteps * J, col,
-                            on, acc, carry, lane);
+      mma_pre<NT>(pd, J, tile_ok, as_w, astride, nb, S.bq, S.bs, F::kSteps * J, col, on, acc, lane);
     } else {
       // Streamed (see mma_stream). fetch_ahead first (a resident token's
       // split, on a workgroup's first stage-1 item: it waits for the split
@@ -1158,9 +1243,8 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       }
       vm_wait<0>();   // LDS copies of the stage
       __syncthreads();
-      PreDec pd;
-      mma_tile<F, NT, false>(tl, pd, 0, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np,
-                      col, on, acc, carry, lane);
+      mma_tile<F, NT>(tl, p0, np, tile_ok, wpr, as_w, astride, fast ? p0 : 0, nb, S.bq, S.bs, F::kSteps * np, col, on,
+                      acc, carry, lane);
       __syncthreads();   // everyone is done with the window's columns
     }
     epilogue(c0, ncol, acc);
