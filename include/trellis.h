@@ -143,7 +143,12 @@ size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t int
  *               live slot, bf16(silu(gate) * up) with silu(z) = z / (1 + e^-z),
  *               rounded to nearest even; zero for empty/skipped slots.
  *   y:          device float [T][hidden], sum over slots of topk_w * W_down h.
+ *               The slots' contributions are added into y with device-scope
+ *               float atomics, so their order (and the last bits of y) can
+ *               differ from call to call; the accuracy bound below holds for
+ *               every order.
  * hidden and inter: multiples of 32; T, k limits as for trellis_moe_gemv.
+ * Accuracy: as for trellis_moe_gemv, per GEMV; h is rounded to bf16 first.
  */
 int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_up, const trellis_mat_t *w_down,
                     const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,

@@ -215,6 +215,10 @@ __device__ __forceinline__ int ld_ctr(const int *p) {
 __device__ __forceinline__ void st_ctr(int *p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// y += v at the device's coherence point (no value returned).
+__device__ __forceinline__ void add_dcf(float *p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Every thread's device-coherent stores have completed (the workgroup's
 // results are visible device-wide); then one thread may count.
@@ -1282,7 +1286,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     return a.x_per_slot ? slot : slot / a.k;
   };
   const bool resident = NT == 1 && s1 && a.x_resident;
-  int obs_old = 0;
+  int obs_old = 0, obs0_old = 0;
   bool waited = false;
   TokRaw tok;
   auto ahead = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
@@ -1314,6 +1318,12 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
         spin_until(a.cnt1 + (size_t)ai * kLineInts, a.n_rg1, a.status);
         obs_old = __hip_atomic_fetch_add(a.obs1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
+        if (ai != 0) {
+          // y is cleared by the first active expert's stage-1 items: their
+          // count must be complete before this item adds into y
+          spin_until(a.cnt1, a.n_rg1, a.status);
+          obs0_old = __hip_atomic_fetch_add(a.obs1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
       __syncthreads();
       waited = true;
@@ -1354,7 +1364,15 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       return;
     }
     if (r0 >= rows) return;
-    const bool partial = !s1 || a.mode == MODE_COMBINE;
+    if (!s1) {
+      // down projection: the gate-weighted rows go straight into y
+      per_slot_out<NT>(acc, ncol, lane, [&](int c, int rr, float v) TQ_INLINE {
+        const int slot = S.slots[c0 + c];
+        add_dcf(a.y + (size_t)(slot / a.k) * a.y_rows + r0 + rr, S.gw[slot] * v);
+      });
+      return;
+    }
+    const bool partial = a.mode == MODE_COMBINE;
     per_slot_out<NT>(acc, ncol, lane, [&](int c, int rr, float v) TQ_INLINE {
       const int slot = S.slots[c0 + c];
       if (partial) st_dcf(a.yslot + (size_t)slot * a.y_rows + r0 + rr, v);
@@ -1363,17 +1381,37 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   };
   gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, !s1, ahead, stage, epilogue);
   if (s1 && ffn) {
+    if (ai == 0) {
+      // y starts at zero: the first active expert's stage-1 items clear it,
+      // a slice of rows each, before they count (every down-projection item
+      // waits for that count before adding into y)
+      const int z = (a.y_rows + a.n_rg1 - 1) / a.n_rg1, lo = tile * z, nz = min(a.y_rows - lo, z);
+      for (int i = threadIdx.x; i < a.T * z; i += kThreads)
+        if (i % z < nz) st_dcf(a.y + (size_t)(i / z) * a.y_rows + lo + i % z, 0.0f);
+    }
     stores_done();
     if (threadIdx.x == 0)
       __hip_atomic_fetch_add(a.cnt1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (!s1 && threadIdx.x == 0 && obs_old == a.n_rt2 - 1) {
-    // the last of the expert's row tiles to see its h clears the expert's counters
-    st_ctr(a.cnt1 + (size_t)ai * kLineInts, 0);
-    st_ctr(a.obs1 + (size_t)ai * kLineInts, 0);
+  if (!s1) {
+    // The last reader of a stage-1 count clears it (and its readers' count)
+    // for the next call. Expert 0's count is read by every down-projection
+    // item (see stage), the others' by their own expert's items.
+    if (threadIdx.x == 0) {
+      const int n0 = S.n_active * a.n_rt2;
+      if (obs_old == (ai == 0 ? n0 : a.n_rt2) - 1) {
+        st_ctr(a.cnt1 + (size_t)ai * kLineInts, 0);
+        st_ctr(a.obs1 + (size_t)ai * kLineInts, 0);
+      }
+      if (ai != 0 && obs0_old == n0 - 1) {
+        st_ctr(a.cnt1, 0);
+        st_ctr(a.obs1, 0);
+      }
+    }
+    return;
   }
-  if (!s1 || a.mode == MODE_COMBINE) arrive_and_combine(a, S, tile);
+  if (a.mode == MODE_COMBINE) arrive_and_combine(a, S, tile);
 }
 
 // Work done once per call by workgroup 0: status words and the outputs of
