@@ -56,6 +56,17 @@
 
 namespace tq {
 
+// threadIdx.x behind an empty asm: the compiler cannot see that it is the
+// same value on every read, so it recomputes the lane-derived indexes where
+// they are used instead of hoisting them out of the item loop. Hoisted, they
+// outlive everything else in the kernel and are spilled to scratch (several
+// MB of HBM writes per launch, written back at the kernel's end).
+__device__ __forceinline__ int tix() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxT = 32;
@@ -109,7 +120,7 @@ enum { ST_SKIPPED = 0, ST_ERROR = 1 };
 // 64 u64 slots of s_memrealtime stamps (entry, routing done, then ten per
 // item: id, start, marks 2..8, end).
 #ifdef TQ_TRACE
-#define TQ_MARK(S, k) do { if (threadIdx.x == 0 && (S).trp) (S).trp[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define TQ_MARK(S, k) do { if (tix() == 0 && (S).trp) (S).trp[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
 static void *g_trace = nullptr;
 #else
 #define TQ_MARK(S, k) do { } while (0)
@@ -290,10 +301,10 @@ __device__ __forceinline__ Split split_block(float v) {
 
 // Slot list of expert e into S.slots (slot order); returns the count.
 __device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tix() & 63, wave = tix() >> 6;
   int total = 0;
   for (int base = 0; base < n; base += kThreads) {
-    const int i = base + threadIdx.x;
+    const int i = base + tix();
     const bool p = i < n && S.ids[i] == e;
     const unsigned long long bal = __ballot(p);
     if (lane == 0) S.wcnt[wave] = __popcll(bal);
@@ -332,7 +343,7 @@ __device__ __forceinline__ size_t x_elem(const LayerArgs &a, int K, int nb, int 
                                          RowMap row_of, bool &ok) {
   const int nbp = F::kBlocks * np, c = u / nbp, blk = F::kBlocks * kp + u - c * nbp;
   ok = u < npairs * nbp && blk < nb;
-  return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (threadIdx.x & 31) : 0;
+  return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (tix() & 31) : 0;
 }
 
 // One dword load per value for either dtype: the aligned word holding it
@@ -354,7 +365,7 @@ __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int 
   constexpr int kStride = kThreads / 32;
   const int nbp = F::kBlocks * np, total = npairs * nbp;
   int c = first / nbp, b = first - c * nbp;   // unit (c, b); nbp >= 4, so b wraps at most twice a step
-  size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
+  size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (tix() & 31);
 #pragma unroll
   for (int m = 0; m < kXPre; ++m) {
     const int u = first + m * kStride, blk = F::kBlocks * kp + b;
@@ -368,7 +379,7 @@ __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int 
         b -= nbp;
         ++c;
       }
-      rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
+      rbase = (size_t)row_of(min(c, npairs - 1)) * K + (tix() & 31);
     }
   }
 }
@@ -376,13 +387,13 @@ __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int 
 template <typename F, typename RowMap>
 __device__ __forceinline__ void x_prefetch(XPre &xp, const LayerArgs &a, int K, int nb, int kp, int np, int npairs,
                                            RowMap row_of) {
-  x_load<F>(xp.v, a, K, nb, kp, np, npairs, threadIdx.x >> 5, row_of);
+  x_load<F>(xp.v, a, K, nb, kp, np, npairs, tix() >> 5, row_of);
 }
 
 template <typename F>
 __device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v, bool store) {
   const int nbp = F::kBlocks * np, psteps = F::kSteps * np;
-  const int c = u / nbp, b = u % nbp, pos = threadIdx.x & 31;
+  const int c = u / nbp, b = u % nbp, pos = tix() & 31;
   const Split s = split_block(v);
   if (!store) return;
   const int off = F::offset(b, pos);
@@ -398,7 +409,7 @@ __device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, i
 template <typename F, typename RowMap>
 __device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *ls, const LayerArgs &a, int K, int nb,
                                          int kp, int np, int npairs, RowMap row_of) {
-  const int hw = threadIdx.x >> 5, total = npairs * F::kBlocks * np;
+  const int hw = tix() >> 5, total = npairs * F::kBlocks * np;
   constexpr int kStride = kThreads / 32;
   // Every half-wave splits all its prefetched units without branches (the
   // cross-lane steps need the whole half-wave) and stores the real ones.
@@ -436,10 +447,10 @@ struct TokRaw {
 
 template <typename F>
 __device__ __forceinline__ void tok_load(TokRaw &t, const LayerArgs &a, int nb, int np) {
-  const int j = threadIdx.x & 3;
+  const int j = tix() & 3;
 #pragma unroll
   for (int r = 0; r < kTokRounds; ++r) {
-    const int b = 64 * r + (threadIdx.x >> 2);
+    const int b = 64 * r + (tix() >> 2);
     const size_t el = b < nb ? (size_t)b * 32 + 8 * j : 0;   // (past K: a valid address, value unused)
     if (a.x_bf16) {
       t.v[r][0] = *(const uint4 *)((const uint16_t *)a.x + el);
@@ -461,10 +472,10 @@ __device__ __forceinline__ float quad_max(float v) {
 template <typename F>
 __device__ __forceinline__ void tok_split(const TokRaw &t, uint8_t *lq, uint8_t *ls, int psteps, int nb,
                                           bool bf16) {
-  const int j = threadIdx.x & 3, nblk = F::kBlocks * (psteps / F::kSteps);
+  const int j = tix() & 3, nblk = F::kBlocks * (psteps / F::kSteps);
 #pragma unroll
   for (int r = 0; r < kTokRounds; ++r) {
-    const int b = 64 * r + (threadIdx.x >> 2);
+    const int b = 64 * r + (tix() >> 2);
     float f[8];
     const uint32_t w[8] = {t.v[r][0].x, t.v[r][0].y, t.v[r][0].z, t.v[r][0].w,
                            t.v[r][1].x, t.v[r][1].y, t.v[r][1].z, t.v[r][1].w};
@@ -522,7 +533,7 @@ __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_
   constexpr int kBatch = 8;
   const int psteps = F::kSteps * np, per_col = psteps * 16;   // 8-byte pieces per column
   const int total = ncols * per_col;
-  for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
+  for (int base = tix(); base < total; base += kBatch * kThreads) {
     uint64_t v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -541,7 +552,7 @@ __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_
     }
   }
   const int stotal = ncols * psteps;
-  for (int idx = threadIdx.x; idx < stotal; idx += kThreads) {
+  for (int idx = tix(); idx < stotal; idx += kThreads) {
     const int c = idx / psteps, st = idx - c * psteps;
     uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + F::kSteps * kp + st) * 4);
 #pragma unroll
@@ -629,13 +640,13 @@ struct AScalePre {
 };
 
 __device__ __forceinline__ void ascale_prefetch(AScalePre &sp, const uint8_t *sblk, int nb) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tix() & 63;
   sp.v0 = ((const uint4 *)sblk)[min(lane, nb - 1)];
   sp.v1 = ((const uint4 *)sblk)[min(lane + 64, nb - 1)];
 }
 
 __device__ __forceinline__ void ascale_store(uint8_t *as_w, const AScalePre &sp, int nb) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tix() & 63;
   if (lane < nb) ((uint4 *)as_w)[lane] = sp.v0;
   if (lane + 64 < nb) ((uint4 *)as_w)[lane + 64] = sp.v1;
 }
@@ -643,7 +654,7 @@ __device__ __forceinline__ void ascale_store(uint8_t *as_w, const AScalePre &sp,
 // (A lane's blocks of piece j: trellis 8j+2g and 8j+2g+1, MXFP4 4j+g.)
 template <typename F>
 __device__ __forceinline__ void ascale_generic(uint8_t *as_w, const uint8_t *srow, int nb, int p0, int np, bool ok) {
-  const int lane = threadIdx.x & 63, i16 = lane & 15, g = lane >> 4;
+  const int lane = tix() & 63, i16 = lane & 15, g = lane >> 4;
   constexpr int kPer = F::kBlocks / 4;   // blocks per lane and piece
 #pragma unroll
   for (int q = 0; q < kPieceMax; ++q) {
@@ -1058,7 +1069,7 @@ __device__ __forceinline__ void per_slot_out(const v4f (&acc)[NT], int ncol, int
 // Sum the partial outputs of rows [rt*64, rt*64 + 64) over each token's live
 // slots, in slot order, weighted by the gate weights.
 __device__ __forceinline__ void combine_rows(const LayerArgs &a, const Shared &S, int rt) {
-  for (int idx = threadIdx.x; idx < a.T * 64; idx += kThreads) {
+  for (int idx = tix(); idx < a.T * 64; idx += kThreads) {
     const int t = idx >> 6, r = rt * 64 + (idx & 63);
     if (r >= a.y_rows) continue;
     float v = 0.0f;
@@ -1074,7 +1085,7 @@ __device__ __forceinline__ void combine_rows(const LayerArgs &a, const Shared &S
 // if it is the last of the n_active experts there, combine the tile.
 __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S, int rt) {
   stores_done();
-  if (threadIdx.x == 0) {
+  if (tix() == 0) {
     int *ctr = a.cnt2 + (size_t)rt * kLineInts;
     const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.last = old == S.n_active - 1;
@@ -1100,7 +1111,7 @@ template <typename F, int NT, bool ALIGNED, typename Ahead, typename Stage, type
 __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
                                           int fast, int e, int r0, int ne, bool shared_cols, bool predec,
                                           Ahead fetch_ahead, Stage stage, Epi epilogue) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tix() & 63, wave = tix() >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const bool tile_ok = r0 < rows;
   const int wpr = K / 32 * F::kWords, nb = K / 32, J = (nb + F::kBlocks - 1) / F::kBlocks;
@@ -1239,9 +1250,11 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       if (reload) load_tile<ALIGNED>(tl, rowp, wpr, p0, np, g);
       stage(c0, ncol, p0, np);
       if (reload && fast) {
-        AScalePre sp;
-        ascale_prefetch(sp, sc + row0 * nb, nb);
-        ascale_store(as_w, sp, nb);
+        // (straight copy: through an AScalePre here the pair lands in scratch)
+        const uint4 *sblk = (const uint4 *)(sc + row0 * nb);
+        const uint4 v0 = sblk[min(lane, nb - 1)], v1 = sblk[min(lane + 64, nb - 1)];
+        if (lane < nb) ((uint4 *)as_w)[lane] = v0;
+        if (lane + 64 < nb) ((uint4 *)as_w)[lane + 64] = v1;
       } else if (reload) {
         ascale_generic<F>(as_w, srow, nb, p0, np, tile_ok);
       }
@@ -1263,7 +1276,7 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
 // of the matrix-core loop.
 template <typename F, int NT, bool ALIGNED>
 __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tix() & 63, wave = tix() >> 6;
   const bool s1 = item < a.n_s1;
   const int i2 = item - a.n_s1;
   const int ai = s1 ? item / a.n_rg1 : i2 / a.n_rt2;
@@ -1297,7 +1310,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
     if (tok_first) {
       tok_split<F>(tok, S.bq, S.bs, F::kSteps * np, nb, a.x_bf16);
-      if (threadIdx.x == 0) S.x_done = 1;
+      if (tix() == 0) S.x_done = 1;
     }
     if (resident) return;
     if (s1) {
@@ -1314,7 +1327,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     if (!waited) {
       // the expert's h is complete once all its stage-1 items have counted;
       // the first window's weight loads are already in flight
-      if (threadIdx.x == 0) {
+      if (tix() == 0) {
         spin_until(a.cnt1 + (size_t)ai * kLineInts, a.n_rg1, a.status);
         obs_old = __hip_atomic_fetch_add(a.obs1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
@@ -1340,7 +1353,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       __syncthreads();
       const float *red = (const float *)(S.bq + kBBytes / 2);
       for (int base = 0; base < ncol; base += kThreads / 32) {
-        const int c = base + (threadIdx.x >> 5), i = threadIdx.x & 31;
+        const int c = base + (tix() >> 5), i = tix() & 31;
         if (c < ncol) {   // uniform over the half-wave
           const int n = c >> 3, cj = 2 * (c & 7), wv = i >> 4, ri = i & 15;
           const float gate = red[d_index<NT>(wv, n, ri, cj)] + red[d_index<NT>(wv, n, ri, cj + 1)];
@@ -1386,11 +1399,11 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       // a slice of rows each, before they count (every down-projection item
       // waits for that count before adding into y)
       const int z = (a.y_rows + a.n_rg1 - 1) / a.n_rg1, lo = tile * z, nz = min(a.y_rows - lo, z);
-      for (int i = threadIdx.x; i < a.T * z; i += kThreads)
+      for (int i = tix(); i < a.T * z; i += kThreads)
         if (i % z < nz) st_dcf(a.y + (size_t)(i / z) * a.y_rows + lo + i % z, 0.0f);
     }
     stores_done();
-    if (threadIdx.x == 0)
+    if (tix() == 0)
       __hip_atomic_fetch_add(a.cnt1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
@@ -1398,7 +1411,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     // The last reader of a stage-1 count clears it (and its readers' count)
     // for the next call. Expert 0's count is read by every down-projection
     // item (see stage), the others' by their own expert's items.
-    if (threadIdx.x == 0) {
+    if (tix() == 0) {
       const int n0 = S.n_active * a.n_rt2;
       if (obs_old == (ai == 0 ? n0 : a.n_rt2) - 1) {
         st_ctr(a.cnt1 + (size_t)ai * kLineInts, 0);
@@ -1417,7 +1430,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
 // Work done once per call by workgroup 0: status words and the outputs of
 // dead (empty / out-of-range) slots.
 __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
-  const int tid = threadIdx.x, n = a.T * a.k;
+  const int tid = tix(), n = a.T * a.k;
   if (tid == 0) {
     int skipped = 0;
     for (int s = 0; s < n; ++s) skipped += S.ids[s] >= a.E;
@@ -1439,7 +1452,7 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
 template <typename F, int NT, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_layer(LayerArgs a) {
   __shared__ Shared S;
-  const int tid = threadIdx.x;
+  const int tid = tix();
 #ifdef TQ_TRACE
   unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 64 : nullptr;
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
