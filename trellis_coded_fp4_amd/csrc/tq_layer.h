@@ -66,6 +66,13 @@ __device__ __forceinline__ int tix() {
   asm volatile("" : "+v"(t));
   return t;
 }
+// Only the one-N-tile kernel spills without it; the others run faster with
+// the plain index (so do the several-token activation split's loops).
+template <int NT>
+__device__ __forceinline__ int tidx() {
+  if constexpr (NT == 1) return tix();
+  else return threadIdx.x;
+}
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -300,11 +307,12 @@ __device__ __forceinline__ Split split_block(float v) {
 }
 
 // Slot list of expert e into S.slots (slot order); returns the count.
+template <int NT>
 __device__ __forceinline__ int gather_slots(Shared &S, int e, int n) {
-  const int lane = tix() & 63, wave = tix() >> 6;
+  const int lane = tidx<NT>() & 63, wave = tidx<NT>() >> 6;
   int total = 0;
   for (int base = 0; base < n; base += kThreads) {
-    const int i = base + tix();
+    const int i = base + tidx<NT>();
     const bool p = i < n && S.ids[i] == e;
     const unsigned long long bal = __ballot(p);
     if (lane == 0) S.wcnt[wave] = __popcll(bal);
@@ -343,7 +351,7 @@ __device__ __forceinline__ size_t x_elem(const LayerArgs &a, int K, int nb, int 
                                          RowMap row_of, bool &ok) {
   const int nbp = F::kBlocks * np, c = u / nbp, blk = F::kBlocks * kp + u - c * nbp;
   ok = u < npairs * nbp && blk < nb;
-  return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (tix() & 31) : 0;
+  return ok ? (size_t)row_of(c) * K + (size_t)blk * 32 + (threadIdx.x & 31) : 0;
 }
 
 // One dword load per value for either dtype: the aligned word holding it
@@ -365,7 +373,7 @@ __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int 
   constexpr int kStride = kThreads / 32;
   const int nbp = F::kBlocks * np, total = npairs * nbp;
   int c = first / nbp, b = first - c * nbp;   // unit (c, b); nbp >= 4, so b wraps at most twice a step
-  size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (tix() & 31);
+  size_t rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
 #pragma unroll
   for (int m = 0; m < kXPre; ++m) {
     const int u = first + m * kStride, blk = F::kBlocks * kp + b;
@@ -379,7 +387,7 @@ __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int 
         b -= nbp;
         ++c;
       }
-      rbase = (size_t)row_of(min(c, npairs - 1)) * K + (tix() & 31);
+      rbase = (size_t)row_of(min(c, npairs - 1)) * K + (threadIdx.x & 31);
     }
   }
 }
@@ -387,13 +395,13 @@ __device__ __forceinline__ void x_load(u32xp &v, const LayerArgs &a, int K, int 
 template <typename F, typename RowMap>
 __device__ __forceinline__ void x_prefetch(XPre &xp, const LayerArgs &a, int K, int nb, int kp, int np, int npairs,
                                            RowMap row_of) {
-  x_load<F>(xp.v, a, K, nb, kp, np, npairs, tix() >> 5, row_of);
+  x_load<F>(xp.v, a, K, nb, kp, np, npairs, threadIdx.x >> 5, row_of);
 }
 
 template <typename F>
 __device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, int u, float v, bool store) {
   const int nbp = F::kBlocks * np, psteps = F::kSteps * np;
-  const int c = u / nbp, b = u % nbp, pos = tix() & 31;
+  const int c = u / nbp, b = u % nbp, pos = threadIdx.x & 31;
   const Split s = split_block(v);
   if (!store) return;
   const int off = F::offset(b, pos);
@@ -409,7 +417,7 @@ __device__ __forceinline__ void x_store_unit(uint8_t *lq, uint8_t *ls, int np, i
 template <typename F, typename RowMap>
 __device__ __forceinline__ void x_finish(const XPre &xp, uint8_t *lq, uint8_t *ls, const LayerArgs &a, int K, int nb,
                                          int kp, int np, int npairs, RowMap row_of) {
-  const int hw = tix() >> 5, total = npairs * F::kBlocks * np;
+  const int hw = threadIdx.x >> 5, total = npairs * F::kBlocks * np;
   constexpr int kStride = kThreads / 32;
   // Every half-wave splits all its prefetched units without branches (the
   // cross-lane steps need the whole half-wave) and stores the real ones.
@@ -527,13 +535,13 @@ __device__ __forceinline__ int chunk_block(int st, int o) {
 // with device-coherent loads, issued 8 per thread before any LDS write.
 // Blocks >= nb (the K padding, never written in global memory) become zero
 // codes with scale 127.
-template <typename F, typename ColMap>
+template <typename F, int NT, typename ColMap>
 __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
                                           int gsteps, int kp, int np, int nb, int ncols, ColMap src_col) {
   constexpr int kBatch = 8;
   const int psteps = F::kSteps * np, per_col = psteps * 16;   // 8-byte pieces per column
   const int total = ncols * per_col;
-  for (int base = tix(); base < total; base += kBatch * kThreads) {
+  for (int base = tidx<NT>(); base < total; base += kBatch * kThreads) {
     uint64_t v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -552,7 +560,7 @@ __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_
     }
   }
   const int stotal = ncols * psteps;
-  for (int idx = tix(); idx < stotal; idx += kThreads) {
+  for (int idx = tidx<NT>(); idx < stotal; idx += kThreads) {
     const int c = idx / psteps, st = idx - c * psteps;
     uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + F::kSteps * kp + st) * 4);
 #pragma unroll
@@ -1111,7 +1119,7 @@ template <typename F, int NT, bool ALIGNED, typename Ahead, typename Stage, type
 __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const uint8_t *sc, int rows, int K,
                                           int fast, int e, int r0, int ne, bool shared_cols, bool predec,
                                           Ahead fetch_ahead, Stage stage, Epi epilogue) {
-  const int lane = tix() & 63, wave = tix() >> 6;
+  const int lane = tidx<NT>() & 63, wave = tidx<NT>() >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const bool tile_ok = r0 < rows;
   const int wpr = K / 32 * F::kWords, nb = K / 32, J = (nb + F::kBlocks - 1) / F::kBlocks;
@@ -1276,7 +1284,7 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
 // of the matrix-core loop.
 template <typename F, int NT, bool ALIGNED>
 __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item) {
-  const int lane = tix() & 63, wave = tix() >> 6;
+  const int lane = tidx<NT>() & 63, wave = tidx<NT>() >> 6;
   const bool s1 = item < a.n_s1;
   const int i2 = item - a.n_s1;
   const int ai = s1 ? item / a.n_rg1 : i2 / a.n_rt2;
@@ -1292,7 +1300,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   // (read before gather_slots' barriers: a thread may set it in this item)
   // (one token means one N-tile: compiled for NT == 1 only)
   const bool tok_first = NT == 1 && s1 && a.x_resident && !S.x_done;
-  const int ne = gather_slots(S, e, a.T * a.k);
+  const int ne = gather_slots<NT>(S, e, a.T * a.k);
   TQ_MARK(S, 2);
   auto row_of = [&](int c) TQ_INLINE {
     const int slot = S.slots[c];
@@ -1310,7 +1318,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   auto stage = [&](int c0, int ncol, int kp, int np) TQ_INLINE {
     if (tok_first) {
       tok_split<F>(tok, S.bq, S.bs, F::kSteps * np, nb, a.x_bf16);
-      if (tix() == 0) S.x_done = 1;
+      if (tidx<NT>() == 0) S.x_done = 1;
     }
     if (resident) return;
     if (s1) {
@@ -1327,7 +1335,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     if (!waited) {
       // the expert's h is complete once all its stage-1 items have counted;
       // the first window's weight loads are already in flight
-      if (tix() == 0) {
+      if (tidx<NT>() == 0) {
         spin_until(a.cnt1 + (size_t)ai * kLineInts, a.n_rg1, a.status);
         obs_old = __hip_atomic_fetch_add(a.obs1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
@@ -1341,7 +1349,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       __syncthreads();
       waited = true;
     }
-    copy_pass<F>(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
+    copy_pass<F, NT>(S.bq, S.bs, a.hq, a.hs, a.h_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
       return S.slots[c0 + (c >> 1)] * 2 + (c & 1);
     });
     vm_wait<0>();   // (loads whose store a lane skipped count as pending for the compiler)
@@ -1353,7 +1361,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       __syncthreads();
       const float *red = (const float *)(S.bq + kBBytes / 2);
       for (int base = 0; base < ncol; base += kThreads / 32) {
-        const int c = base + (tix() >> 5), i = tix() & 31;
+        const int c = base + (tidx<NT>() >> 5), i = tidx<NT>() & 31;
         if (c < ncol) {   // uniform over the half-wave
           const int n = c >> 3, cj = 2 * (c & 7), wv = i >> 4, ri = i & 15;
           const float gate = red[d_index<NT>(wv, n, ri, cj)] + red[d_index<NT>(wv, n, ri, cj + 1)];
@@ -1399,11 +1407,11 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       // a slice of rows each, before they count (every down-projection item
       // waits for that count before adding into y)
       const int z = (a.y_rows + a.n_rg1 - 1) / a.n_rg1, lo = tile * z, nz = min(a.y_rows - lo, z);
-      for (int i = tix(); i < a.T * z; i += kThreads)
+      for (int i = tidx<NT>(); i < a.T * z; i += kThreads)
         if (i % z < nz) st_dcf(a.y + (size_t)(i / z) * a.y_rows + lo + i % z, 0.0f);
     }
     stores_done();
-    if (tix() == 0)
+    if (tidx<NT>() == 0)
       __hip_atomic_fetch_add(a.cnt1 + (size_t)ai * kLineInts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
@@ -1411,7 +1419,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     // The last reader of a stage-1 count clears it (and its readers' count)
     // for the next call. Expert 0's count is read by every down-projection
     // item (see stage), the others' by their own expert's items.
-    if (tix() == 0) {
+    if (tidx<NT>() == 0) {
       const int n0 = S.n_active * a.n_rt2;
       if (obs_old == (ai == 0 ? n0 : a.n_rt2) - 1) {
         st_ctr(a.cnt1 + (size_t)ai * kLineInts, 0);
@@ -1452,7 +1460,7 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
 template <typename F, int NT, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_layer(LayerArgs a) {
   __shared__ Shared S;
-  const int tid = tix();
+  const int tid = tidx<NT>();
 #ifdef TQ_TRACE
   unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 64 : nullptr;
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
