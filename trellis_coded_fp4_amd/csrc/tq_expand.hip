@@ -5,8 +5,9 @@
 //
 // Bandwidth-bound: 0.28125 B/weight read, 0.53125 B/weight written. Each
 // thread streams 4 consecutive symbol words (64 weights) of one row: one
-// 16-byte load, the preceding word for history (0 at a row start), 32 bytes
-// of codes stored as two 16-byte stores. A wave covers 1 KiB of symbols.
+// 16-byte load, the preceding word for history (0 at a row start; from the
+// neighbouring lane), 32 bytes of codes stored as two 16-byte non-temporal
+// stores. A wave covers 1 KiB of symbols.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -16,6 +17,7 @@
 namespace tq {
 
 constexpr int kExpandThreads = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct ExpandArgs {
   const uint32_t *syms;
@@ -35,15 +37,20 @@ __global__ void __launch_bounds__(kExpandThreads) k_expand_quads(ExpandArgs a) {
   if (q < a.n_quads) {
     const int64_t w0 = 4 * q;
     const uint4 g = *(const uint4 *)(a.syms + w0);
-    const uint32_t prev = (w0 % a.wpr) ? a.syms[w0 - 1] : 0u;
+    // The preceding word is the last one of the lane below (DPP wave shift
+    // right by one); lane 0 of a wave loads it.
+    uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g.w, 0x138, 0xF, 0xF, false);
+    if ((threadIdx.x & 63) == 0) prev = w0 ? a.syms[w0 - 1] : 0u;
+    if (w0 % a.wpr == 0) prev = 0u;
     uint32_t o[8];
     natural_order(decode_word(g.x, prev), &o[0], &o[1]);
     natural_order(decode_word(g.y, g.x), &o[2], &o[3]);
     natural_order(decode_word(g.z, g.y), &o[4], &o[5]);
     natural_order(decode_word(g.w, g.z), &o[6], &o[7]);
-    uint4 *dst = (uint4 *)(a.codes + 8 * w0);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    // written once and not read back here: non-temporal stores
+    u32x4 *dst = (u32x4 *)(a.codes + 8 * w0);
+    __builtin_nontemporal_store((u32x4){o[0], o[1], o[2], o[3]}, dst);
+    __builtin_nontemporal_store((u32x4){o[4], o[5], o[6], o[7]}, dst + 1);
   }
   // scale copy: 16 bytes per thread over the same grid
   if (q < a.n_scale_u4) ((uint4 *)a.scales_out)[q] = ((const uint4 *)a.scales)[q];
