@@ -140,11 +140,11 @@ struct Layout {
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // n_act: first-stage completion counters (layer only); n_rt: 64-row output
-// tiles that combine partial outputs; n_slots x y_rows partial outputs;
-// h_cols: width of the h splits (layer only); x_cols: width of one token's
-// split (the resident-token case).
+// tiles that combine partial outputs and n_slots x y_rows partial outputs
+// (the routed GEMV's combine; zero for the layer, which adds into y);
+// h_cols: width of the h splits (layer only).
 template <typename F>
-static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int x_cols) {
+static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
@@ -1617,7 +1617,7 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   if ((rc = check_routing(T, k))) return rc;
   const bool combine = topk_w != nullptr;
   const int n_rt = (w.rows + 63) / 64;
-  const Layout L = make_layout<F>(0, n_rt, T * k, w.rows, 0, w.cols);
+  const Layout L = make_layout<F>(0, n_rt, T * k, w.rows, 0);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -1652,7 +1652,8 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   const int E = gu.n_mat, hidden = gu.cols, inter = gu.rows / 2;
   if (gu.rows % 64 || dn.n_mat != E || dn.rows != hidden || dn.cols != inter) return TRELLIS_EINVAL;
   const int max_act = std::min(E, T * k);
-  const Layout L = make_layout<F>(max_act, (hidden + 63) / 64, T * k, hidden, inter, hidden);
+  // (no partial outputs or combine counters: the down projection adds into y)
+  const Layout L = make_layout<F>(max_act, 0, T * k, 0, inter);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -1666,10 +1667,9 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   a.inter = inter; a.h = h;
   a.h_steps = fmt_steps<F>(inter / 32);
   a.hq = (uint8_t *)(ws + L.hq); a.hs = (uint8_t *)(ws + L.hs);
-  a.yslot = (float *)(ws + L.yslot);
   a.y = y; a.y_rows = hidden;
   a.status = (int *)(ws + L.status);
-  a.cnt1 = (int *)(ws + L.cnt1); a.obs1 = (int *)(ws + L.obs1); a.cnt2 = (int *)(ws + L.cnt2);
+  a.cnt1 = (int *)(ws + L.cnt1); a.obs1 = (int *)(ws + L.obs1);
 #ifdef TQ_TRACE
   a.trace = (unsigned long long *)g_trace;
 #endif
