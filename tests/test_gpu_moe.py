@@ -289,3 +289,42 @@ def test_prepared_calls(trellis_lib, orc):
     y_ref, bound, _ = orc.moe_gemv(syms, sc, xg, idg, gate_w=gwg)
     for r in range(3):
         check_tol(call().cpu().numpy(), y_ref, bound, f"prepared gemv replay {r}")
+
+
+def test_ffn_calls_share_a_workspace_varying_experts(trellis_lib, orc):
+    """Layer calls on one workspace whose active-expert count changes (6, 1,
+    2) and that leave tokens with no live slot: y starts from garbage each
+    time, so every row must be written (the empty tokens' rows exactly 0),
+    and no wait may time out (the stage-1 counts are cleared by their last
+    readers, expert 0's by every down-projection item)."""
+    announce("ffn calls on one workspace, varying active experts and empty tokens")
+    import torch
+    cfg = workloads.MoEConfig(93, "small-ws", 6, 128, 64, 2, 3, True)
+    ws = trellis_lib.ffn_workspace(cfg.n_exp, cfg.hidden, cfg.inter, cfg.T, cfg.k)
+    routings = [np.array([[0, 1], [2, 3], [4, 5]], np.int32),
+                np.array([[-1, -1], [1, 1], [-1, -1]], np.int32),
+                np.array([[5, -1], [9, 2], [-1, -1]], np.int32)]
+    for i, ids in enumerate(routings):
+        layer = workloads.moe_layer(cfg, layer_id=10 + i)
+        layer.ids[:] = ids
+        y = torch.full((cfg.T, cfg.hidden), 1e30, dtype=torch.float32, device="cuda")
+        y, h = trellis_lib.moe_ffn(dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms),
+                                   dev(layer.dn_scales), x_dev(layer.x, True), dev(layer.ids), dev(layer.gate_w),
+                                   y=y, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:8].view(torch.int32)[1]) == 0, f"call {i}: a wait timed out"
+        y, h = y.cpu().numpy(), h.float().cpu().numpy()
+        yg, bg = np.zeros_like(y, dtype=np.float64), np.zeros_like(y, dtype=np.float64)
+        for t in range(cfg.T):
+            for j in range(cfg.k):
+                e = int(ids[t, j])
+                if e < 0 or e >= cfg.n_exp:
+                    assert (h[t, j] == 0).all()
+                    continue
+                yd, bd = orc.gemv(layer.dn_syms[e], layer.dn_scales[e], h[t, j].astype(np.float64))
+                yg[t] += layer.gate_w[t, j] * yd[0]
+                bg[t] += abs(layer.gate_w[t, j]) * bd[0]
+        for t in range(cfg.T):
+            if all(int(e) < 0 or int(e) >= cfg.n_exp for e in ids[t]):
+                assert (y[t] == 0).all(), f"call {i}: empty token {t} not zero"
+        check_tol(y, yg, bg, f"shared workspace call {i}")
