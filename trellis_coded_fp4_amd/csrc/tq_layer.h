@@ -134,7 +134,7 @@ static void *g_trace = nullptr;
 #endif
 
 struct Layout {
-  size_t status, cnt1, obs1, cnt2, yslot, hq, hs, total;
+  size_t status, cnt1, obs1, cnt2, cntp, obsp, yslot, hq, hs, xq, xs, total;
 };
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -142,9 +142,10 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // n_act: first-stage completion counters (layer only); n_rt: 64-row output
 // tiles that combine partial outputs and n_slots x y_rows partial outputs
 // (the routed GEMV's combine; zero for the layer, which adds into y);
-// h_cols: width of the h splits (layer only).
+// h_cols: width of the h splits (layer only); n_tok x x_cols: the tokens'
+// activations, split once per call for every stage-1 item.
 template <typename F>
-static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols) {
+static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int n_tok, int x_cols) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
@@ -156,6 +157,11 @@ static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_co
   const size_t hs = h_cols ? (size_t)fmt_steps<F>(h_cols / 32) : 0;
   L.hq = take((size_t)n_slots * 2 * hs * 128);
   L.hs = take((size_t)n_slots * 2 * hs * 4);
+  L.cntp = take(kLineInts * 4);
+  L.obsp = take(kLineInts * 4);
+  const size_t xs = (size_t)fmt_steps<F>(x_cols / 32);
+  L.xq = take((size_t)n_tok * 2 * xs * 128);
+  L.xs = take((size_t)n_tok * 2 * xs * 4);
   L.total = o;
   return L;
 }
@@ -178,6 +184,9 @@ struct LayerArgs {
   int n_rg1, n_s1;              // stage-1 row groups per expert, items
   int n_rt2, n_s2;              // stage-2 row tiles per expert, items
   int x_resident;               // one token, K <= 4096, 16-byte aligned: split by each workgroup once, kept in LDS
+  int n_prep;                   // otherwise (x shared by a token's slots): tokens split once per call, by the first items
+  int x_steps; uint8_t *xq; uint8_t *xs;   // ... into these columns (hi, lo per token)
+  int *cntp, *obsp;             // split tokens; stage-1 items that have seen them all
   int grid;
 #ifdef TQ_TRACE
   unsigned long long *trace;
@@ -453,21 +462,26 @@ struct TokRaw {
   uint4 v[kTokRounds][2];   // bf16: v[r][0]; fp32: v[r][0..1]
 };
 
-template <typename F>
-__device__ __forceinline__ void tok_load(TokRaw &t, const LayerArgs &a, int nb, int np) {
+// One token's raw values (x: its first element, 16-byte aligned).
+__device__ __forceinline__ void tok_load_at(TokRaw &t, const void *x, bool bf16, int nb) {
   const int j = tix() & 3;
 #pragma unroll
   for (int r = 0; r < kTokRounds; ++r) {
     const int b = 64 * r + (tix() >> 2);
     const size_t el = b < nb ? (size_t)b * 32 + 8 * j : 0;   // (past K: a valid address, value unused)
-    if (a.x_bf16) {
-      t.v[r][0] = *(const uint4 *)((const uint16_t *)a.x + el);
+    if (bf16) {
+      t.v[r][0] = *(const uint4 *)((const uint16_t *)x + el);
       t.v[r][1] = t.v[r][0];
     } else {
-      t.v[r][0] = *(const uint4 *)((const float *)a.x + el);
-      t.v[r][1] = *(const uint4 *)((const float *)a.x + el + 4);
+      t.v[r][0] = *(const uint4 *)((const float *)x + el);
+      t.v[r][1] = *(const uint4 *)((const float *)x + el + 4);
     }
   }
+}
+
+template <typename F>
+__device__ __forceinline__ void tok_load(TokRaw &t, const LayerArgs &a, int nb, int np) {
+  tok_load_at(t, a.x, a.x_bf16, nb);
 }
 
 __device__ __forceinline__ float quad_max(float v) {
@@ -1321,8 +1335,25 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
       if (tidx<NT>() == 0) S.x_done = 1;
     }
     if (resident) return;
+    if (s1 && a.n_prep) {
+      // The tokens were split once for the call (run_prep): wait until all
+      // of them are, then copy this group's columns.
+      if (!waited) {
+        if (tidx<NT>() == 0) {
+          spin_until(a.cntp, a.n_prep, a.status);
+          obs_old = __hip_atomic_fetch_add(a.obsp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        waited = true;
+      }
+      copy_pass<F, NT>(S.bq, S.bs, a.xq, a.xs, a.x_steps, kp, np, nb, 2 * ncol, [&](int c) TQ_INLINE {
+        return row_of(c0 + (c >> 1)) * 2 + (c & 1);
+      });
+      vm_wait<0>();
+      return;
+    }
     if (s1) {
-      // Several tokens: split their activations here. All of this
+      // Each slot its own activations: split them here. All of this
       // branch's loads are consumed within it, so none stays pending where
       // the item kinds' paths meet (the compiler's waits are not
       // path-sensitive).
@@ -1401,6 +1432,11 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
     });
   };
   gemm_item<F, NT, ALIGNED>(S, w, sc, rows, K, fast, e, r0, ne, resident, !s1, ahead, stage, epilogue);
+  if (s1 && a.n_prep && tidx<NT>() == 0 && obs_old == S.n_active * a.n_rg1 - 1) {
+    // the last stage-1 item to see the split tokens clears their counts
+    st_ctr(a.cntp, 0);
+    st_ctr(a.obsp, 0);
+  }
   if (s1 && ffn) {
     if (ai == 0) {
       // y starts at zero: the first active expert's stage-1 items clear it,
@@ -1457,6 +1493,25 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
     for (int i = tid; i < a.T * a.y_rows; i += kThreads) a.y[i] = 0.0f;
 }
 
+// Split token t's activations (the stage-1 input width) once for the whole
+// call: hi and lo E4M3 columns with their UE8M0 scales, in the step-chunk
+// layout the stage-1 items copy into LDS. Splitting per item instead redid
+// the same work for every item of every expert the token is routed to.
+template <typename F, int NT>
+__device__ __forceinline__ void run_prep(const LayerArgs &a, int t) {
+  const int K = a.cols1, nb = K / 32;
+  const size_t el = (size_t)t * K;
+  const void *xt = a.x_bf16 ? (const void *)((const uint16_t *)a.x + el) : (const void *)((const float *)a.x + el);
+  TokRaw tok;
+  tok_load_at(tok, xt, a.x_bf16, nb);
+  tok_split<F>(tok, a.xq + (size_t)t * 2 * a.x_steps * 128, a.xs + (size_t)t * 2 * a.x_steps * 4, a.x_steps, nb,
+               a.x_bf16);
+  // visible device-wide before it is counted
+  __threadfence();
+  __syncthreads();
+  if (tidx<NT>() == 0) __hip_atomic_fetch_add(a.cntp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename F, int NT, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_layer(LayerArgs a) {
   __shared__ Shared S;
@@ -1504,7 +1559,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if (TR && tid == 0) TR[1] = __builtin_amdgcn_s_memrealtime();
   int it_no = 0;
 #endif
-  const int n_items = a.n_s1 + a.n_s2;
+  const int n_items = a.n_prep + a.n_s1 + a.n_s2;
   for (int item = blockIdx.x; item < n_items; item += a.grid) {
 #ifdef TQ_TRACE
     if (tid == 0) {
@@ -1515,7 +1570,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     TQ_MARK(S, 1);
     ++it_no;
 #endif
-    run_item<F, NT, ALIGNED>(a, S, item);
+    if (item < a.n_prep) run_prep<F, NT>(a, item);
+    else run_item<F, NT, ALIGNED>(a, S, item - a.n_prep);
     // nothing of this item stays in flight into the next one (the
     // compiler's waits in the next item then count only its own loads)
     vm_wait<0>();
@@ -1577,7 +1633,7 @@ static int check_routing(int T, int k) {
 
 template <typename F, int NT, bool ALIGNED>
 static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
-  const int n_items = a.n_s1 + a.n_s2;
+  const int n_items = a.n_prep + a.n_s1 + a.n_s2;
   a.grid = std::max(1, std::min(n_items, cus * resident_blocks<F, NT, ALIGNED>()));
   hipLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
@@ -1605,6 +1661,17 @@ static int launch(LayerArgs &a, int cus, hipStream_t s) {
   return aligned ? launch_al<F, true>(a, cus, s) : launch_al<F, false>(a, cus, s);
 }
 
+// Tokens split once per call (see run_prep) when the token is not resident,
+// the slots share their token's activations, K <= 4096 and x is 16-byte
+// aligned (the single-token split's loads); otherwise each item splits them.
+template <typename F>
+static void set_prep(LayerArgs &a, const Layout &L, char *ws, bool on) {
+  a.n_prep = on ? a.T : 0;
+  a.x_steps = fmt_steps<F>(a.cols1 / 32);
+  a.xq = (uint8_t *)(ws + L.xq); a.xs = (uint8_t *)(ws + L.xs);
+  a.cntp = (int *)(ws + L.cntp); a.obsp = (int *)(ws + L.obsp);
+}
+
 template <typename F>
 static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x_dtype, int32_t x_per_slot,
                      const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k, float *y,
@@ -1617,7 +1684,7 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   if ((rc = check_routing(T, k))) return rc;
   const bool combine = topk_w != nullptr;
   const int n_rt = (w.rows + 63) / 64;
-  const Layout L = make_layout<F>(0, n_rt, T * k, w.rows, 0);
+  const Layout L = make_layout<F>(0, n_rt, T * k, w.rows, 0, T, w.cols);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -1637,6 +1704,7 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   a.n_rt2 = 1; a.n_s2 = 0;
   const int J = (w.cols / 32 + F::kBlocks - 1) / F::kBlocks;
   a.x_resident = T == 1 && !x_per_slot && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
+  set_prep<F>(a, L, ws, !a.x_resident && !x_per_slot && J <= kPieceMax && ((uintptr_t)x & 15) == 0);
   return launch<F>(a, cus, stream);
 }
 
@@ -1653,7 +1721,7 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   if (gu.rows % 64 || dn.n_mat != E || dn.rows != hidden || dn.cols != inter) return TRELLIS_EINVAL;
   const int max_act = std::min(E, T * k);
   // (no partial outputs or combine counters: the down projection adds into y)
-  const Layout L = make_layout<F>(max_act, 0, T * k, 0, inter);
+  const Layout L = make_layout<F>(max_act, 0, T * k, 0, inter, T, hidden);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
@@ -1679,6 +1747,7 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   a.n_s2 = max_act * a.n_rt2;
   const int J = (hidden / 32 + F::kBlocks - 1) / F::kBlocks;
   a.x_resident = T == 1 && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
+  set_prep<F>(a, L, ws, !a.x_resident && J <= kPieceMax && ((uintptr_t)x & 15) == 0);
   if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
   rc = launch<F>(a, cus, stream);
   if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;

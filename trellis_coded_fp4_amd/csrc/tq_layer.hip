@@ -8,7 +8,7 @@ using namespace tq;
 extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
                                                   int32_t k) {
   if (n_mat < 1 || cols < 32 || cols % 32 || rows < 1 || check_routing(T, k)) return 0;
-  return make_layout<FmtTrellis>(0, (rows + 63) / 64, T * k, rows, 0).total;
+  return make_layout<FmtTrellis>(0, (rows + 63) / 64, T * k, rows, 0, T, cols).total;
 }
 
 extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
@@ -22,7 +22,7 @@ extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, cons
 extern "C" size_t trellis_moe_ffn_workspace_size(int32_t n_exp, int32_t hidden, int32_t inter, int32_t T,
                                                  int32_t k) {
   if (n_exp < 1 || hidden < 32 || hidden % 32 || inter < 32 || inter % 32 || check_routing(T, k)) return 0;
-  return make_layout<FmtTrellis>(std::min(n_exp, T * k), 0, T * k, 0, inter).total;
+  return make_layout<FmtTrellis>(std::min(n_exp, T * k), 0, T * k, 0, inter, T, hidden).total;
 }
 
 extern "C" int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
