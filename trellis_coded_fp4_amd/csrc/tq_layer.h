@@ -1704,7 +1704,7 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   a.n_rt2 = 1; a.n_s2 = 0;
   const int J = (w.cols / 32 + F::kBlocks - 1) / F::kBlocks;
   a.x_resident = T == 1 && !x_per_slot && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
-  set_prep<F>(a, L, ws, !a.x_resident && !x_per_slot && J <= kPieceMax && ((uintptr_t)x & 15) == 0);
+  set_prep<F>(a, L, ws, !a.x_resident && !x_per_slot && w.cols / 32 <= 64 * kTokRounds && ((uintptr_t)x & 15) == 0);
   return launch<F>(a, cus, stream);
 }
 
@@ -1747,7 +1747,7 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   a.n_s2 = max_act * a.n_rt2;
   const int J = (hidden / 32 + F::kBlocks - 1) / F::kBlocks;
   a.x_resident = T == 1 && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
-  set_prep<F>(a, L, ws, !a.x_resident && J <= kPieceMax && ((uintptr_t)x & 15) == 0);
+  set_prep<F>(a, L, ws, !a.x_resident && hidden / 32 <= 64 * kTokRounds && ((uintptr_t)x & 15) == 0);
   if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
   rc = launch<F>(a, cus, stream);
   if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
