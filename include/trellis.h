@@ -209,6 +209,41 @@ int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, con
                           int32_t T, int32_t k, uint16_t *h, float *y, void *workspace,
                           size_t workspace_bytes);
 
+/*
+ * Workspace bytes needed by trellis_viterbi_encode for `rows` rows of n
+ * positions on the current device: 1 KB per position for each row searched
+ * at once (at most 2 per compute unit). 0 for rows < 1 or n < 1, or when
+ * the device cannot be queried. The workspace needs no clearing.
+ */
+size_t trellis_viterbi_workspace_size(int32_t rows, int32_t n);
+
+/*
+ * trellis_viterbi_encode -- the encoder's symbol search (XOR-Trellis news
+ * article, aimodeling.com, bullet "Curvature-aware Viterbi objective"): for
+ * each row, the branch-symbol sequence that starts from state 0 and
+ * minimises sum_k d[k] * (target[k] - value_k)^2, where value_k is the
+ * palette value the decoder above gives position k (at scale 1, no block
+ * scale).
+ *   target:   device, [rows][n] float64, finite.
+ *   d:        device, [rows][n] float64 per-position weights (the diagonal
+ *             curvature factor), or NULL for all ones.
+ *   syms_out: device, [rows][n] bytes, one symbol (0..3) per position.
+ *   cost_out: device, [rows] float64, the minimum of the objective.
+ * Arithmetic is float64 with every operation rounded (no fused multiply-add):
+ * each step adds (d * err) * err, err = target - value, to the path cost, in
+ * position order. Where several paths tie, the one kept at each position is
+ * the one through the smaller predecessor, and the path ends in the smallest
+ * final state. One workgroup searches one row over the 4096 histories of six
+ * symbols (the value depends on the current symbol and the six before it).
+ * Errors: ENULL for a NULL target, syms_out, cost_out or workspace; EINVAL for
+ * rows or n < 1 or float64 arrays not 8-byte aligned; EWORKSPACE for a
+ * workspace that is not 256-byte aligned or smaller than
+ * trellis_viterbi_workspace_size(rows, n).
+ */
+int trellis_viterbi_encode(hipStream_t stream, const double *target, const double *d, int32_t rows,
+                           int32_t n, uint8_t *syms_out, double *cost_out, void *workspace,
+                           size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

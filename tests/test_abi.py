@@ -132,3 +132,21 @@ def test_mxfp4_argument_checks():
                                                        None, 1, 1, h, FAKE, 0x10000, 1 << 30)
     assert f(gu, dn, h=None) == -2
     assert f(gu, tq.MxMat(0x10000, 0x20000, 2, 64, 32)) == -1    # down cols != inter
+
+
+def test_viterbi_argument_checks():
+    lib = tq.lib()
+    call = lambda t=FAKE, d=None, rows=4, n=16, s=FAKE, c=0x30000, ws=0x10000: lib.trellis_viterbi_encode(
+        None, t, d, rows, n, s, c, ws, 1 << 30)
+    assert call(t=None) == -2
+    assert call(s=None) == -2
+    assert call(c=None) == -2
+    assert call(ws=None) == -2
+    assert call(rows=0) == -1
+    assert call(n=0) == -1
+    assert call(t=FAKE + 4) == -1          # float64 target not 8-byte aligned
+    assert call(d=FAKE + 4) == -1
+    assert call(c=0x30004) == -1
+    assert call(ws=0x10040) == -3          # workspace not 256-byte aligned
+    assert lib.trellis_viterbi_workspace_size(0, 16) == 0
+    assert lib.trellis_viterbi_workspace_size(4, 0) == 0

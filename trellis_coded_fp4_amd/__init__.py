@@ -27,7 +27,8 @@ ERRORS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_ENULL", -3: "TRELL
 EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_gemv_workspace_size", "trellis_moe_gemv",
            "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
-           "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn"]
+           "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn",
+           "trellis_viterbi_workspace_size", "trellis_viterbi_encode"]
 
 
 class TrellisError(RuntimeError):
@@ -82,6 +83,10 @@ def lib():
         L.trellis_mxfp4_moe_gemv.restype = ctypes.c_int
         L.trellis_mxfp4_moe_ffn.argtypes = [P, XP, XP, P, I32, P, P, I32, I32, P, P, P, SZ]
         L.trellis_mxfp4_moe_ffn.restype = ctypes.c_int
+        L.trellis_viterbi_workspace_size.argtypes = [I32, I32]
+        L.trellis_viterbi_workspace_size.restype = SZ
+        L.trellis_viterbi_encode.argtypes = [P, P, P, I32, I32, P, P, P, SZ]
+        L.trellis_viterbi_encode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -321,3 +326,35 @@ def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
                  workspace.numel()),
                 "trellis_mxfp4_moe_ffn", (y, h), (mg, md))
+
+
+def viterbi_workspace(rows, n, device="cuda"):
+    torch = _torch()
+    nb = lib().trellis_viterbi_workspace_size(rows, n)
+    if nb == 0:
+        raise TrellisError(-1, "trellis_viterbi_workspace_size")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def viterbi_encode(target, d=None, syms_out=None, cost_out=None, workspace=None, stream=None, prepare=False):
+    """Curvature-aware Viterbi symbol search per row: target [rows, n] float64,
+    d [rows, n] float64 or None (ones). Returns (symbols [rows, n] uint8, cost [rows] float64)."""
+    torch = _torch()
+    if target.dim() == 1:
+        target = target.unsqueeze(0)
+    _check(target, torch.float64, "target")
+    rows, n = target.shape
+    if d is not None:
+        _check(d, torch.float64, "d", (rows, n))
+    if syms_out is None:
+        syms_out = torch.empty((rows, n), dtype=torch.uint8, device=target.device)
+    if cost_out is None:
+        cost_out = torch.empty((rows,), dtype=torch.float64, device=target.device)
+    _check(syms_out, torch.uint8, "syms_out", (rows, n))
+    _check(cost_out, torch.float64, "cost_out", (rows,))
+    if workspace is None:
+        workspace = viterbi_workspace(rows, n, device=target.device)
+    return _run(prepare, lib().trellis_viterbi_encode,
+                (_stream(stream), target.data_ptr(), _ptr(d), rows, n, syms_out.data_ptr(), cost_out.data_ptr(),
+                 workspace.data_ptr(), workspace.numel() * workspace.element_size()),
+                "trellis_viterbi_encode", (syms_out, cost_out), (workspace,))

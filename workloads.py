@@ -186,3 +186,20 @@ def moe_layer(cfg: MoEConfig, layer_id: int = 0, rep: int = 0,
     x, ids, w = moe_batch(cfg, layer_id, rr, n_exp=E)
     return MoELayer(cfg, gu_s, gu_e, dn_s, dn_e, x, ids, w)
 
+
+
+# ---------------------------------------------------------------- encoder search
+#
+# Rows to encode: targets are weights already divided by their block scale,
+# N(0, 2^2), so that they span the palettes' range [-6, 6]; the per-position
+# weights d (the curvature diagonal) are positive, lognormal(0, 0.5).
+T_TARGET = 9
+T_CURV = 10
+VITERBI = dict(config_id=6, name="Viterbi encode 512 rows x 2880 positions", rows=512, n=2880)
+
+
+def encode_rows(config_id: int, rows: int, n: int, rep: int = 0):
+    """(target [rows, n] float64, d [rows, n] float64) for the encoder search."""
+    target = rng(config_id, T_TARGET, 0, rep).standard_normal((rows, n)) * 2.0
+    d = rng(config_id, T_CURV, 0, rep).lognormal(0.0, 0.5, (rows, n))
+    return target, d
