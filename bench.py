@@ -17,6 +17,9 @@ Other workloads (--workload):
   mx128:T   expand mode, second half: the 128-expert layer on the expanded
             MXFP4 weights (trellis_mxfp4_moe_ffn)
   mx32      the default layer shape on expanded MXFP4 weights
+  viterbi   the encoder's curvature-aware Viterbi search: 512 rows x 2880
+            positions per call (trellis_viterbi_encode), float64; reported
+            in encoded weights/s against the fp64 vector ALU roofline
 
 All data is synthetic (workloads.py) and resident in HBM before timing. To
 keep the 256 MB Infinity Cache from serving repeated weights, steps walk a
@@ -48,6 +51,9 @@ TRELLIS_BPW = 0.25 + 1.0 / 32.0           # 2-bit symbol + one UE8M0 byte per 32
 MX_BPW = 0.5 + 1.0 / 32.0                 # E2M1 nibble + UE8M0 byte per 32 weights
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
 FP4_PEAK_TFLOPS = 10100.0                 # MI355X dense FP4 matrix cores, published
+FP64_PEAK_TFLOPS = 78.6                   # MI355X fp64 vector, published
+VIT_FLOPS_PER_EDGE = 4                    # err = t - v, (d * err) * err, cost + that
+VIT_EDGES_PER_POSITION = 4096 * 4         # histories x branches
 METRIC = "compressed-weight GB/s of fused trellis-decode MoE GEMV (batch 1) + % HBM peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -58,7 +64,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="moe32",
-                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32")
+                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | viterbi")
     p.add_argument("--ring-gb", type=float, default=1.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -297,6 +303,44 @@ def expand_workload(args):
                         "write_bytes": weights * MX_BPW})
 
 
+def viterbi_workload(args):
+    import torch
+    import trellis_coded_fp4_amd as tq
+    c = workloads.VITERBI
+    rows, n = c["rows"], c["n"]
+    target_h, d_h = workloads.encode_rows(c["config_id"], rows, n)
+    target, d = dev(target_h), dev(d_h)
+    syms = torch.empty((rows, n), dtype=torch.uint8, device="cuda")
+    cost = torch.empty((rows,), dtype=torch.float64, device="cuda")
+    ws = tq.viterbi_workspace(rows, n)
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def make(s, events=None):
+        return hip.bracket(tq.viterbi_encode(target, d, syms_out=syms, cost_out=cost, workspace=ws, prepare=True),
+                           events, stream)
+
+    def cpu_sample(seconds):
+        import oracle
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.viterbi(target_h[done % rows], d_h[done % rows])
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return done * n / dt, f"{done} row(s) of {n} positions of the same workload, single-threaded C oracle " \
+                              f"(65536 states x 4 branches per position), {dt:.1f} s"
+
+    return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: rows * n,
+                units="weights/s", scale=1.0,
+                metric="Viterbi-encoded weights/s (curvature-aware search, 4096 histories x 4 branches, fp64)",
+                alu_flops=rows * n * VIT_EDGES_PER_POSITION * VIT_FLOPS_PER_EDGE,
+                flops=None, tokens=None, cpu=cpu_sample,
+                kernel="k_viterbi (one workgroup per row, fp64 add-compare-select in LDS)",
+                config={"rows": rows, "positions": n, "histories": 4096, "branches": 4})
+
+
 def pick(args):
     w = args.workload
     if w == "moe32":
@@ -309,6 +353,8 @@ def pick(args):
         return gemv_workload(args)
     if w == "expand":
         return expand_workload(args)
+    if w == "viterbi":
+        return viterbi_workload(args)
     if w.startswith("moe128:"):
         return layer_workload(args, workloads.moe_128e(int(w.split(":")[1])))
     if w.startswith("mx128:"):
@@ -363,7 +409,8 @@ def main():
     ms_per_step = total_ms / args.steps
     timed = range(args.warmup, args.warmup + args.steps)
     total_bytes = sum(W["bytes"](s) for s in timed)
-    value = total_bytes / (total_ms * 1e-3) / 1e9
+    scale = W.get("scale", 1e-9)   # bytes -> GB by default
+    value = total_bytes / (total_ms * 1e-3) * scale
 
     roofline, launch = None, None
     if evs:
@@ -386,6 +433,11 @@ def main():
                     "bytes_per_launch": per_launch}
         if W.get("traffic_bytes"):
             roofline["read_plus_write_GBs"] = round(W["traffic_bytes"] / (d.mean() * 1e-3) / 1e9, 1)
+        if W.get("alu_flops"):
+            tf = W["alu_flops"] / (d.mean() * 1e-3) / 1e12
+            roofline = {"bound": "alu", "achieved": round(tf, 3), "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / FP64_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": W["kernel"],
+                        "flops_per_launch": W["alu_flops"]}
         if W.get("flops"):
             fl = float(np.mean([W["flops"](s) for s, e in zip(timed, evs) if e]))
             tf = fl / (d.mean() * 1e-3) / 1e12
@@ -395,9 +447,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         v, sample = W["cpu"](args.cpu_seconds)
-        cpu = {"value": round(v, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
+        cpu = {"value": round(v, 6), "unit": W.get("units", "GB/s"), "cores": 1, "kind": "oracle",
+               "sample": sample}
 
-    if args.workload == "moe32":
+    if W.get("metric"):
+        metric = W["metric"]
+    elif args.workload == "moe32":
         metric = METRIC
     elif args.workload == "expand":
         metric = "decode GB/s (compressed bytes read) of expand to MXFP4"
@@ -406,7 +461,7 @@ def main():
     out = {
         "metric": metric,
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": W.get("units", "GB/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -414,9 +469,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32 decode, e2m1 x e4m3(hi+lo) -> f32" if args.workload != "expand" else "u32 -> u8",
+        "dtype": {"expand": "u32 -> u8", "viterbi": "f64"}.get(args.workload, "u32 decode, e2m1 x e4m3(hi+lo) -> f32"),
         "data": "synthetic",
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2) if "units" not in W else None,
         "tokens_per_s": round(W["tokens"] / (ms_per_step * 1e-3), 1) if W.get("tokens") else None,
         "config": dict({"workload": W["name"]}, **W["config"],
                        **{"wall_s": round(wall, 4)}),
