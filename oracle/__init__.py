@@ -228,3 +228,29 @@ def viterbi(target: np.ndarray, d: Optional[np.ndarray] = None):
     out = np.empty(n, dtype=np.uint8)
     cost = lib().oracle_viterbi(_p(t), _p(dv), n, _p(out))
     return out, float(cost)
+
+
+def router_topk(x: np.ndarray, w_router: np.ndarray, k: int):
+    """Router in front of the layer: logits, top-k, gate weights.
+
+    The pages leave routing unspecified; the reading taken is the usual
+    mixture-of-experts router: logits[t, e] = sum_h x[t, h] * W_r[e, h] in
+    float64 (a matmul of the exact float64 images of the inputs), the k
+    largest logits of each token in descending order with ties going to the
+    lower expert id, and gate weights = softmax over those k logits
+    (float64: exp(l - l_max) / sum). Returns (ids int32 [T, k], gate weights
+    float64 [T, k], logits float64 [T, E]).
+    """
+    xv = _f64(np.atleast_2d(x))
+    wv = _f64(w_router)
+    logits = xv @ wv.T
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    gw = np.empty((T, k))
+    for t in range(T):
+        picked = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        ids[t] = picked
+        sel = logits[t, picked]
+        ex = np.exp(sel - sel[0])
+        gw[t] = ex / ex.sum()
+    return ids, gw, logits

@@ -381,3 +381,60 @@ def test_viterbi_reproduces_an_encodable_target(orc):
     target = np.array([orc.e2m1_value(c) for c in codes])
     syms, cost = orc.viterbi(target)
     assert cost == 0.0
+
+
+# ---------------------------------------------------------------- router (top-k, softmax)
+
+@pytest.mark.parametrize("E,k,seed", [(6, 2, 0), (7, 3, 1), (8, 8, 2), (5, 1, 3)])
+def test_router_topk_brute_force(orc, E, k, seed):
+    """The picked experts are the k-subset with the largest logit sum (brute
+    force over all subsets; logits distinct), listed in descending logit order."""
+    import itertools
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((3, 16))
+    w = g.standard_normal((E, 16))
+    ids, gw, logits = orc.router_topk(x, w, k)
+    for t in range(3):
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(Fraction(logits[t, e]) for e in c))
+        assert sorted(ids[t].tolist()) == sorted(best)
+        assert all(logits[t, ids[t, j]] > logits[t, ids[t, j + 1]] for j in range(k - 1))
+
+
+def test_router_one_hot_rows(orc):
+    """Router rows that are unit vectors: logit e is exactly x[perm[e]], so
+    the picks are the largest entries of x (a library sort)."""
+    g = np.random.default_rng(5)
+    H, E, k = 32, 12, 4
+    perm = g.permutation(H)[:E]
+    w = np.zeros((E, H))
+    w[np.arange(E), perm] = 1.0
+    x = g.standard_normal((2, H))
+    ids, gw, logits = orc.router_topk(x, w, k)
+    for t in range(2):
+        assert np.array_equal(logits[t], x[t, perm])
+        assert ids[t].tolist() == list(np.argsort(-x[t, perm], kind="stable")[:k])
+
+
+def test_router_ties_go_to_the_lower_id(orc):
+    g = np.random.default_rng(6)
+    row = g.standard_normal(8)
+    w = np.stack([row * 0.5, row, row * 0.5, row, -row])   # experts 1 and 3 tie, then 0 and 2
+    x = row[None, :]
+    ids, gw, _ = orc.router_topk(x, w, 4)
+    assert ids[0].tolist() == [1, 3, 0, 2]
+    assert gw[0, 0] == gw[0, 1] and gw[0, 2] == gw[0, 3]
+
+
+def test_router_gate_weights_closed_form(orc):
+    """Softmax over the picked logits: weights sum to 1, and
+    w_i / w_j = exp(l_i - l_j)."""
+    g = np.random.default_rng(7)
+    x = g.standard_normal((4, 24))
+    w = g.standard_normal((10, 24)) * 0.3
+    ids, gw, logits = orc.router_topk(x, w, 3)
+    for t in range(4):
+        assert abs(gw[t].sum() - 1.0) < 1e-15
+        l = logits[t, ids[t]]
+        for i in range(3):
+            for j in range(3):
+                assert math.isclose(gw[t, i] / gw[t, j], math.exp(l[i] - l[j]), rel_tol=1e-13)
