@@ -210,6 +210,26 @@ int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, con
                           size_t workspace_bytes);
 
 /*
+ * trellis_router_topk -- the router in front of the layer, so that
+ * trellis_moe_ffn can follow it on the same stream with no host round trip.
+ * The pages leave routing unspecified; this is the usual mixture-of-experts
+ * router: logits[t][e] = sum_h x[t][h] * w_router[e][h]; topk_ids[t] = the k
+ * experts with the largest logits, in descending order, the lower id first
+ * on equal logits; topk_w[t] = softmax over those k logits.
+ *   x:        device, [T][H], fp32 or bf16 (x_dtype), 4- / 2-byte aligned.
+ *   w_router: device, [E][H] bf16, 16-byte aligned.
+ *   topk_ids: device, [T][k] int32 (written); topk_w: device, [T][k] fp32.
+ * Products are exact and sums are float64, so a logit is within a few float64
+ * roundings of the exact sum; the softmax is float64, rounded to fp32. One
+ * workgroup per token. Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64),
+ * 8 <= H <= 8192 with H % 8 == 0, T >= 1.
+ * Errors: ENULL for a NULL pointer; EINVAL for a shape outside the limits, a
+ * bad x_dtype or misaligned pointers.
+ */
+int trellis_router_topk(hipStream_t stream, const void *x, int32_t x_dtype, const uint16_t *w_router,
+                        int32_t E, int32_t H, int32_t T, int32_t k, int32_t *topk_ids, float *topk_w);
+
+/*
  * Workspace bytes needed by trellis_viterbi_encode for `rows` rows of n
  * positions on the current device: 1 KB per position for each row searched
  * at once (at most 2 per compute unit). 0 for rows < 1 or n < 1, or when

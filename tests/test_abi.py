@@ -150,3 +150,22 @@ def test_viterbi_argument_checks():
     assert call(ws=0x10040) == -3          # workspace not 256-byte aligned
     assert lib.trellis_viterbi_workspace_size(0, 16) == 0
     assert lib.trellis_viterbi_workspace_size(4, 0) == 0
+
+
+def test_router_argument_checks():
+    lib = tq.lib()
+    call = lambda x=FAKE, dt=1, w=0x20000, E=32, H=2880, T=1, k=4, i=0x30000, g=0x40000: lib.trellis_router_topk(
+        None, x, dt, w, E, H, T, k, i, g)
+    assert call(x=None) == -2
+    assert call(w=None) == -2
+    assert call(i=None) == -2
+    assert call(g=None) == -2
+    assert call(dt=7) == -1
+    assert call(E=0) == -1
+    assert call(E=1025) == -1
+    assert call(k=0) == -1
+    assert call(k=33, E=32) == -1          # k > E
+    assert call(H=2884) == -1              # H % 8
+    assert call(H=8200) == -1              # H > 8192
+    assert call(T=0) == -1
+    assert call(w=0x20008) == -1           # router rows not 16-byte aligned
