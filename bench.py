@@ -17,6 +17,9 @@ Other workloads (--workload):
   mx128:T   expand mode, second half: the 128-expert layer on the expanded
             MXFP4 weights (trellis_mxfp4_moe_ffn)
   mx32      the default layer shape on expanded MXFP4 weights
+  moe32r    the default layer with the device-side router in front of it
+            (trellis_router_topk then trellis_moe_ffn, one stream): the
+            per-layer latency from activations to output
   viterbi   the encoder's curvature-aware Viterbi search: 512 rows x 2880
             positions per call (trellis_viterbi_encode), float64; reported
             in encoded weights/s against the fp64 vector ALU roofline
@@ -64,7 +67,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="moe32",
-                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | viterbi")
+                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | moe32r | viterbi")
     p.add_argument("--ring-gb", type=float, default=1.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -160,7 +163,7 @@ def ring_copies(tensors, bytes_per_copy, ring_gb):
 # given) with its arguments already checked and marshalled, per-step
 # algorithmic bytes, and optionally flops and a CPU-oracle sample.
 
-def layer_workload(args, cfg, mx=False):
+def layer_workload(args, cfg, mx=False, router=False):
     import torch
     import trellis_coded_fp4_amd as tq
     E, H, I = cfg.n_exp, cfg.hidden, cfg.inter
@@ -188,10 +191,33 @@ def layer_workload(args, cfg, mx=False):
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
+    if router:
+        # the router (bf16 [E][H], N(0, 1/H)) picks each step's experts on the
+        # device; the experts a step touches are read back once, before timing
+        wr = workloads.bf16_bits_to_f32(workloads.to_bf16_bits(
+            workloads.rng(cfg.config_id, workloads.T_ROUTER).standard_normal((E, H)).astype(np.float32)
+            / np.sqrt(H)))
+        wr = dev(workloads.to_bf16_bits(wr).view(np.int16)).view(torch.bfloat16)
+        r_ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        r_gw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        r_ws = tq.router_workspace(E, T)
+        for s in range(len(routes)):
+            ids_s, _ = tq.router_topk(routes[s][0], wr, k, workspace=r_ws)
+            live = ids_s.cpu().numpy()
+            uniq[s], slots[s] = len(np.unique(live)), live.size
 
     def make(s, events=None):
         a, b, c, d = ring[s % len(ring)]
         xs, ids, gw = routes[s]
+        if router:
+            rcall = tq.router_topk(xs, wr, k, topk_ids=r_ids, topk_w=r_gw, workspace=r_ws, prepare=True)
+            lcall = tq.moe_ffn(a, b, c, d, xs, r_ids, r_gw, h=h, y=y, workspace=ws, prepare=True,
+                               events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
+
+            def step():
+                rcall()
+                lcall()
+            return step
         if mx:
             return hip.bracket(tq.mxfp4_moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True),
                                events, stream)
@@ -213,8 +239,11 @@ def layer_workload(args, cfg, mx=False):
     kernel = ("k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)" if mx else
               "k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 matrix-core "
               "gate_up + SwiGLU, down + combine)")
+    if router:
+        kernel += "; each step is k_router then k_layer, the events bracket k_layer"
     return dict(
-        name=cfg.name + (" [expanded MXFP4]" if mx else ""), make=make, hip=hip, stream=stream,
+        name=("router + " if router else "") + cfg.name + (" [expanded MXFP4]" if mx else ""), make=make, hip=hip,
+        stream=stream,
         bytes=lambda s: uniq[s] * expert_weights * bpw,
         flops=lambda s: 2.0 * slots[s] * expert_weights,
         tokens=T, kernel=kernel, cpu=cpu_sample,
@@ -347,6 +376,8 @@ def pick(args):
         return layer_workload(args, workloads.MOE_32E)
     if w == "mx32":
         return layer_workload(args, workloads.MOE_32E, mx=True)
+    if w == "moe32r":
+        return layer_workload(args, workloads.MOE_32E, router=True)
     if w == "ffn1":
         return layer_workload(args, workloads.EXPERT_FFN)
     if w == "gemv1":

@@ -210,24 +210,36 @@ int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, con
                           size_t workspace_bytes);
 
 /*
+ * Workspace bytes needed by trellis_router_topk: T counters and T * E
+ * float64 logits. 0 for E outside 1..1024 or T < 1. Like the layer's
+ * workspaces it is zero-filled once before first use; every call leaves
+ * the counters zero again.
+ */
+size_t trellis_router_workspace_size(int32_t E, int32_t T);
+
+/*
  * trellis_router_topk -- the router in front of the layer, so that
  * trellis_moe_ffn can follow it on the same stream with no host round trip.
  * The pages leave routing unspecified; this is the usual mixture-of-experts
  * router: logits[t][e] = sum_h x[t][h] * w_router[e][h]; topk_ids[t] = the k
  * experts with the largest logits, in descending order, the lower id first
  * on equal logits; topk_w[t] = softmax over those k logits.
- *   x:        device, [T][H], fp32 or bf16 (x_dtype), 4- / 2-byte aligned.
+ *   x:        device, [T][H], fp32 or bf16 (x_dtype), 16-byte aligned.
  *   w_router: device, [E][H] bf16, 16-byte aligned.
  *   topk_ids: device, [T][k] int32 (written); topk_w: device, [T][k] fp32.
+ *   workspace: device, 256-byte aligned, trellis_router_workspace_size bytes.
  * Products are exact and sums are float64, so a logit is within a few float64
- * roundings of the exact sum; the softmax is float64, rounded to fp32. One
- * workgroup per token. Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64),
- * 8 <= H <= 8192 with H % 8 == 0, T >= 1.
+ * roundings of the exact sum; the softmax is float64, rounded to fp32. Each
+ * workgroup computes four experts' logits of one token; the last one of a
+ * token to finish picks the top k. Limits: 1 <= E <= 1024,
+ * 1 <= k <= min(E, 64), 8 <= H <= 8192 with H % 8 == 0, 1 <= T <= 65535.
  * Errors: ENULL for a NULL pointer; EINVAL for a shape outside the limits, a
- * bad x_dtype or misaligned pointers.
+ * bad x_dtype or misaligned pointers; EWORKSPACE for a small or misaligned
+ * workspace.
  */
 int trellis_router_topk(hipStream_t stream, const void *x, int32_t x_dtype, const uint16_t *w_router,
-                        int32_t E, int32_t H, int32_t T, int32_t k, int32_t *topk_ids, float *topk_w);
+                        int32_t E, int32_t H, int32_t T, int32_t k, int32_t *topk_ids, float *topk_w,
+                        void *workspace, size_t workspace_bytes);
 
 /*
  * Workspace bytes needed by trellis_viterbi_encode for `rows` rows of n

@@ -154,8 +154,8 @@ def test_viterbi_argument_checks():
 
 def test_router_argument_checks():
     lib = tq.lib()
-    call = lambda x=FAKE, dt=1, w=0x20000, E=32, H=2880, T=1, k=4, i=0x30000, g=0x40000: lib.trellis_router_topk(
-        None, x, dt, w, E, H, T, k, i, g)
+    call = lambda x=FAKE, dt=1, w=0x20000, E=32, H=2880, T=1, k=4, i=0x30000, g=0x40000, ws=0x50000, wsb=1 << 20: \
+        lib.trellis_router_topk(None, x, dt, w, E, H, T, k, i, g, ws, wsb)
     assert call(x=None) == -2
     assert call(w=None) == -2
     assert call(i=None) == -2
@@ -169,3 +169,9 @@ def test_router_argument_checks():
     assert call(H=8200) == -1              # H > 8192
     assert call(T=0) == -1
     assert call(w=0x20008) == -1           # router rows not 16-byte aligned
+    assert call(x=FAKE + 8) == -1          # x not 16-byte aligned
+    assert call(ws=None) == -2
+    assert call(ws=0x50040) == -3          # workspace not 256-byte aligned
+    assert call(wsb=16) == -3              # workspace too small
+    assert lib.trellis_router_workspace_size(32, 1) == 256 + 32 * 8
+    assert lib.trellis_router_workspace_size(0, 1) == 0

@@ -86,3 +86,13 @@ def test_router_chained_into_the_layer(trellis_lib, orc):
     _check(orc, layer.x, w, cfg.k, ids_h, gw_h)
     chained = dataclasses.replace(layer, ids=ids_h, gate_w=gw_h)
     _check_layer(trellis_lib, orc, chained, run=lambda L: (y, h))
+
+
+def test_router_calls_share_a_workspace(trellis_lib, orc):
+    """The per-token counters return to zero: one workspace serves calls of
+    different shapes back to back."""
+    ws = trellis_lib.router_workspace(128, 32)
+    for i, (T, E, H, k) in enumerate([(32, 128, 4096, 8), (1, 32, 2880, 4), (5, 100, 256, 7), (32, 128, 4096, 8)]):
+        x, w = _router_inputs(20 + i, T, E, H, False)
+        ids, gw = trellis_lib.router_topk(_x_dev(x, False), _w_dev(w), k, workspace=ws)
+        _check(orc, x, w, k, ids.cpu().numpy(), gw.cpu().numpy())

@@ -28,7 +28,8 @@ EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_gemv_workspace_size", "trellis_moe_gemv",
            "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
            "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn",
-           "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_topk"]
+           "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_workspace_size",
+           "trellis_router_topk"]
 
 
 class TrellisError(RuntimeError):
@@ -87,7 +88,9 @@ def lib():
         L.trellis_viterbi_workspace_size.restype = SZ
         L.trellis_viterbi_encode.argtypes = [P, P, P, I32, I32, P, P, P, SZ]
         L.trellis_viterbi_encode.restype = ctypes.c_int
-        L.trellis_router_topk.argtypes = [P, P, I32, P, I32, I32, I32, I32, P, P]
+        L.trellis_router_workspace_size.argtypes = [I32, I32]
+        L.trellis_router_workspace_size.restype = SZ
+        L.trellis_router_topk.argtypes = [P, P, I32, P, I32, I32, I32, I32, P, P, P, SZ]
         L.trellis_router_topk.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -362,7 +365,15 @@ def viterbi_encode(target, d=None, syms_out=None, cost_out=None, workspace=None,
                 "trellis_viterbi_encode", (syms_out, cost_out), (workspace,))
 
 
-def router_topk(x, w_router, k, topk_ids=None, topk_w=None, stream=None, prepare=False):
+def router_workspace(E, T, device="cuda"):
+    torch = _torch()
+    n = lib().trellis_router_workspace_size(E, T)
+    if n == 0:
+        raise TrellisError(-1, "trellis_router_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)   # zero-filled before first use
+
+
+def router_topk(x, w_router, k, topk_ids=None, topk_w=None, workspace=None, stream=None, prepare=False):
     """Router: x [T, H] fp32/bf16, w_router [E, H] bf16 -> (topk_ids [T, k] int32, topk_w [T, k] fp32)."""
     torch = _torch()
     if x.dim() == 1:
@@ -379,7 +390,10 @@ def router_topk(x, w_router, k, topk_ids=None, topk_w=None, stream=None, prepare
         topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     _check(topk_ids, torch.int32, "topk_ids", (T, k))
     _check(topk_w, torch.float32, "topk_w", (T, k))
+    if workspace is None:
+        workspace = router_workspace(E, T, device=x.device)
     return _run(prepare, lib().trellis_router_topk,
                 (_stream(stream), x.data_ptr(), _x_dtype(x), w_router.data_ptr(), E, H, T, k,
-                 topk_ids.data_ptr(), topk_w.data_ptr()),
-                "trellis_router_topk", (topk_ids, topk_w))
+                 topk_ids.data_ptr(), topk_w.data_ptr(), workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size()),
+                "trellis_router_topk", (topk_ids, topk_w), (workspace,))

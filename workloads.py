@@ -38,6 +38,7 @@ T_ROUTE = 5
 T_ROUTE_W = 6
 T_SYMS_UP = 7          # third matrix of the expand workload
 T_SCALES_UP = 8
+T_ROUTER = 11          # router weights of the router-in-front workload
 
 SCALE_LO = 124
 SCALE_HI = 130
