@@ -117,7 +117,7 @@ size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols
  *   y:          device float. With topk_w == NULL: y[T][k][rows],
  *               y[t][j] = W_e x_(t or t,j) (zero for empty/skipped slots).
  *               With topk_w: y[T][rows] = sum_j topk_w[t][j] * W_e x.
- * T in 1..32, k in 1..32, T*k <= 1024; rows % 16 == 0.
+ * T in 1..128, k in 1..32, T*k <= 1024; rows % 16 == 0.
  * Accuracy: activations enter the block-scaled FP4 x FP8 matrix cores as a
  * two-term FP8 (E4M3) split with UE8M0 scales per 32; sums are fp32; each
  * output satisfies |y - y_exact| <= 2e-3 * sum |w| |x| (|topk_w| included).

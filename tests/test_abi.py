@@ -78,7 +78,7 @@ def test_gemv_argument_checks():
     assert _gemv(lib, dtype=7) == -1
     assert _gemv(lib, per_slot=2) == -1
     assert _gemv(lib, T=0) == -1
-    assert _gemv(lib, T=33) == -1
+    assert _gemv(lib, T=129) == -1                # T > 128
     assert _gemv(lib, k=0) == -1
     assert _gemv(lib, k=33) == -1
     assert _gemv(lib, m=_mat(rows=24)) == -1          # rows % 16

@@ -212,7 +212,7 @@ def test_ffn_32_experts_sampled(trellis_lib, orc):
                  rows_dn=np.sort(rs.choice(2880, 160, replace=False)))
 
 
-@pytest.mark.parametrize("T", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("T", [1, 4, 8, 16, 32, 64, 128])
 def test_ffn_128_experts_sweep_sampled(trellis_lib, orc, T):
     """128 experts, hidden 4096, intermediate 1536, top-8, Zipf(1.1) routing."""
     announce(f"ffn 128 experts top-8 T={T}")

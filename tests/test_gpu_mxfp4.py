@@ -128,7 +128,7 @@ def test_mxfp4_ffn_32_experts_sampled(trellis_lib, orc):
                  rows_dn=np.sort(rs.choice(2880, 96, replace=False)), run=_mx_run(trellis_lib, orc))
 
 
-@pytest.mark.parametrize("T", [1, 8, 32])
+@pytest.mark.parametrize("T", [1, 8, 32, 128])
 def test_mxfp4_ffn_128_experts_sampled(trellis_lib, orc, T):
     """128 experts, hidden 4096, intermediate 1536, top-8 on expanded weights."""
     announce(f"mxfp4 ffn 128 experts top-8 T={T}")

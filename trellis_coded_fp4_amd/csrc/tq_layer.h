@@ -76,7 +76,7 @@ __device__ __forceinline__ int tidx() {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxT = 32;
+constexpr int kMaxT = 128;
 constexpr int kMaxK = 32;
 constexpr int kMaxSlots = 1024;
 constexpr int kMaxExperts = 1024;
