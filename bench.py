@@ -393,12 +393,21 @@ def pick(args):
     raise SystemExit(f"unknown workload {w}")
 
 
-def kernel_sha():
+# The device sources each workload's kernel is compiled from: a recorded
+# traffic figure stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer.h", "tq_common.h", "tq_decode.h"],
+    "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
+    "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],
+}
+
+
+def kernel_sha(workload="moe32"):
+    kind = workload if workload in KERNEL_SOURCES else "layer"
     h = hashlib.sha256()
     d = os.path.join(ROOT, "trellis_coded_fp4_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in sorted(KERNEL_SOURCES[kind]):
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -455,7 +464,7 @@ def main():
         if os.path.exists(PROFILE_TRAFFIC):
             try:
                 tr = json.load(open(PROFILE_TRAFFIC)).get(args.workload, {})
-                if tr.get("kernel_source_sha") == kernel_sha():
+                if tr.get("kernel_source_sha") == kernel_sha(args.workload):
                     traffic = tr.get("bytes_per_launch")
             except (OSError, ValueError):
                 traffic = None
