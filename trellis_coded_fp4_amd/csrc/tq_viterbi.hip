@@ -15,15 +15,27 @@
 //
 // Arithmetic: fp64, each candidate cost formed as cost + (d * err) * err with
 // err = target - value, rounded at every operation (no contraction), in
-// position order. Ties keep the smaller predecessor (smaller t), and the
-// final history with the smallest cost (smaller index on ties) ends the path.
+// position order. Costs are never NaN, so the minimum of the four is exact;
+// ties keep the smaller predecessor (the smallest t whose cost equals the
+// minimum), and the final history with the smallest cost (smaller index on
+// ties) ends the path.
 //
-// Layout: one workgroup per row (rows beyond the grid loop), 256 threads;
-// thread i owns m = i + 256 j (j = 0..3), i.e. histories 4m .. 4m + 3. The
-// costs of one position live in LDS (two 32 KB buffers). Each position's
-// choices (2 bits per history) are one 32-bit word per thread, written to
-// the workspace, 1 KB per position; the traceback stages them back through
-// LDS 64 positions at a time.
+// Work split: the palette and entry of the state (t << 12) | (m << 2) | b
+// depend on m only through four parities of its bits (m1^m5, m2^m6,
+// m0^m3^m7^m9, m4^m8: the m-part of the decoder's masks), the "class" of m.
+// Each of the 16 classes holds 64 values of m. Wave w, slot j (j = 0..3)
+// takes the 64 m of class 4w + j, one per lane, so in every candidate the
+// palette entry is known when the code is compiled (one copy of the step per
+// wave index). Per position a thread forms the 16 distortion terms
+// (d * err) * err once, one per palette entry, and each candidate is then a
+// single add to the predecessor's cost: the same operations and roundings as
+// forming err per candidate.
+//
+// Layout: one workgroup per row (rows beyond the grid loop), 256 threads,
+// 16 histories 4m .. 4m + 3 per thread. The costs of one position live in
+// LDS (two 32 KB buffers). Each position's choices (2 bits per history) are
+// one 32-bit word per thread, written to the workspace, 1 KB per position;
+// the traceback stages them back through LDS 64 positions at a time.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -49,17 +61,72 @@ struct VitArgs {
   int rows, n;
 };
 
-// The palette value of a 14-bit state (current symbol in bits 0..1), times 2
-// so that it is an integer.
-__device__ __forceinline__ int vit_value2(uint32_t s) {
-  const int p0 = __popc(s & 0x1089u) & 1, p1 = __popc(s & 0x2112u) & 1;
-  const int q0 = __popc(s & 0x0A24u) & 1, q1 = __popc(s & 0x2441u) & 1;
-  const int palette = p0 | (p1 << 1);
-  const int entry = (int)(s & 3u) ^ (q0 | (q1 << 1));
-  // P0..P3 times 2; P3's -0 becomes 0 (the sign of a zero value does not
-  // change (target - value)^2)
-  const int pal2[16] = {-12, -3, 0, 4, -8, -2, 1, 6, -6, -1, 2, 8, -4, 0, 3, 12};
-  return pal2[palette * 4 + entry];
+// Palette values times 2 (integers), indexed palette * 4 + entry; P3's -0
+// becomes 0 (the sign of a zero value does not change (target - value)^2).
+__constant__ int kVPal2[16] = {-12, -3, 0, 4, -8, -2, 1, 6, -6, -1, 2, 8, -4, 0, 3, 12};
+
+// Palette * 4 + entry of the state (t << 12) | (m << 2) | b for m of class c
+// (bit 0: m1^m5, bit 1: m2^m6, bit 2: m0^m3^m7^m9, bit 3: m4^m8).
+constexpr int vit_index(int c, int t, int b) {
+  const int b0 = b & 1, b1 = b >> 1, t0 = t & 1, t1 = t >> 1;
+  const int p0 = b0 ^ (c & 1) ^ t0, p1 = b1 ^ ((c >> 1) & 1) ^ t1;
+  const int q0 = (c >> 2) & 1, q1 = b0 ^ ((c >> 3) & 1) ^ t1;
+  return (p0 | (p1 << 1)) * 4 + (b ^ (q0 | (q1 << 1)));
+}
+
+// The m of class c at lane f: f's bits are m3, m5, m6, m7, m8, m9, and the
+// class fixes m1, m2, m4 and m0.
+__device__ __forceinline__ int vit_m(int c, int f) {
+  const int m3 = f & 1, m5 = (f >> 1) & 1, m6 = (f >> 2) & 1, m7 = (f >> 3) & 1, m8 = (f >> 4) & 1,
+            m9 = (f >> 5) & 1;
+  const int m1 = (c & 1) ^ m5, m2 = ((c >> 1) & 1) ^ m6, m0 = ((c >> 2) & 1) ^ m3 ^ m7 ^ m9,
+            m4 = ((c >> 3) & 1) ^ m8;
+  return m0 | (m1 << 1) | (m2 << 2) | (m3 << 3) | (m4 << 4) | (m5 << 5) | (m6 << 6) | (m7 << 7) | (m8 << 8) |
+         (m9 << 9);
+}
+
+// Thread and bit of history h's choice in a position's 256 words.
+__device__ __forceinline__ void vit_owner(int h, int *thread, int *shift) {
+  const int m = h >> 2, b = h & 3;
+  const int c = (((m >> 1) ^ (m >> 5)) & 1) | ((((m >> 2) ^ (m >> 6)) & 1) << 1) |
+                ((((m >> 0) ^ (m >> 3) ^ (m >> 7) ^ (m >> 9)) & 1) << 2) | ((((m >> 4) ^ (m >> 8)) & 1) << 3);
+  const int f = ((m >> 3) & 1) | (((m >> 5) & 1) << 1) | (((m >> 6) & 1) << 2) | (((m >> 7) & 1) << 3) |
+                (((m >> 8) & 1) << 4) | (((m >> 9) & 1) << 5);
+  *thread = (c >> 2) * 64 + f;
+  *shift = 2 * (4 * (c & 3) + b);
+}
+
+// One position for a thread of wave W: candidates from the costs ci, the
+// cheapest of each history's four into co, the choices returned as a word.
+template <int W>
+__device__ __forceinline__ uint32_t vit_step(const double *ci, double *co, const int (&m)[4], const double (&D)[16]) {
+  uint32_t word = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    constexpr int kC0 = 4 * W;
+    double c[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c[t] = ci[m[j] | (t << 10)];
+    double o[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      double q[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) q[t] = c[t] + D[vit_index(kC0 + j, t, b)];
+      // the cheapest of the four, and the smallest t that reaches it
+      const double best = fmin(fmin(q[0], q[1]), fmin(q[2], q[3]));
+      const int sh = 2 * (4 * j + b);
+      uint32_t bits = q[2] == best ? 2u << sh : 3u << sh;
+      bits = q[1] == best ? 1u << sh : bits;
+      bits = q[0] == best ? 0u : bits;
+      o[b] = best;
+      word |= bits;
+    }
+    double2 *dst = (double2 *)(co + 4 * m[j]);
+    dst[0] = make_double2(o[0], o[1]);
+    dst[1] = make_double2(o[2], o[3]);
+  }
+  return word;
 }
 
 __global__ void __launch_bounds__(kVThreads) k_viterbi(VitArgs a) {
@@ -71,15 +138,15 @@ __global__ void __launch_bounds__(kVThreads) k_viterbi(VitArgs a) {
   const int tid = threadIdx.x;
   uint32_t *bpw = a.bp + (size_t)blockIdx.x * a.n * kVThreads;
 
-  // the values this thread meets, fixed for the whole search
-  double v[4][4][4];   // [j][t][b]
+  // this thread's four m (class 4 * wave + j, lane = free bits) and the
+  // palette values, times 2
+  const int wave = tid >> 6, lane = tid & 63;
+  int m[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 4; ++j) m[j] = vit_m(4 * wave + j, lane);
+  double pv[16];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        v[j][t][b] = 0.5 * (double)vit_value2(((uint32_t)t << 12) | ((uint32_t)(tid + 256 * j) << 2) | (uint32_t)b);
+  for (int e = 0; e < 16; ++e) pv[e] = 0.5 * (double)kVPal2[e];
 
   for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const double *tr = a.target + (size_t)row * a.n;
@@ -98,33 +165,19 @@ __global__ void __launch_bounds__(kVThreads) k_viterbi(VitArgs a) {
         const double tk = tt[kk], dk = dd[kk];
         const double *ci = cst[cur];
         double *co = cst[cur ^ 1];
-        uint32_t word = 0u;
+        // the distortion of each palette entry at this position
+        double D[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = tid + 256 * j;
-          double c[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) c[t] = ci[m | (t << 10)];
-          double o[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            double best = 0.0;
-            uint32_t bt = 0u;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const double e = tk - v[j][t][b];
-              const double q = c[t] + (dk * e) * e;
-              if (t == 0 || q < best) {
-                best = q;
-                bt = (uint32_t)t;
-              }
-            }
-            o[b] = best;
-            word |= bt << (2 * (4 * j + b));
-          }
-          double2 *dst = (double2 *)(co + 4 * m);
-          dst[0] = make_double2(o[0], o[1]);
-          dst[1] = make_double2(o[2], o[3]);
+        for (int e = 0; e < 16; ++e) {
+          const double er = tk - pv[e];
+          D[e] = (dk * er) * er;
+        }
+        uint32_t word;
+        switch (wave) {   // uniform over the wave
+          case 0: word = vit_step<0>(ci, co, m, D); break;
+          case 1: word = vit_step<1>(ci, co, m, D); break;
+          case 2: word = vit_step<2>(ci, co, m, D); break;
+          default: word = vit_step<3>(ci, co, m, D); break;
         }
         bpw[(size_t)(k0 + kk) * kVThreads + tid] = word;
         cur ^= 1;
@@ -140,9 +193,9 @@ __global__ void __launch_bounds__(kVThreads) k_viterbi(VitArgs a) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int h = 4 * (tid + 256 * j) + b;
+          const int h = 4 * m[j] + b;
           const double c = cst[cur][h];
-          if (bh < 0 || c < bc) { bc = c; bh = h; }
+          if (bh < 0 || c < bc || (c == bc && h < bh)) { bc = c; bh = h; }
         }
       best_c[tid] = bc;
       best_h[tid] = bh;
@@ -181,11 +234,12 @@ __global__ void __launch_bounds__(kVThreads) k_viterbi(VitArgs a) {
       __syncthreads();
       if (tid == 0) {
         for (int k = k1 - 1; k >= k0; --k) {
-          const int m = h >> 2, b = h & 3;
-          so[k] = (uint8_t)b;
-          const uint32_t w = stage[(k - k0) * kVThreads + (m & 255)];
-          const int t = (int)(w >> (2 * (4 * (m >> 8) + b))) & 3;
-          h = m | (t << 10);
+          int owner, shift;
+          vit_owner(h, &owner, &shift);
+          so[k] = (uint8_t)(h & 3);
+          const uint32_t w = stage[(k - k0) * kVThreads + owner];
+          const int t = (int)(w >> shift) & 3;
+          h = (h >> 2) | (t << 10);
         }
       }
     }
