@@ -234,7 +234,9 @@ def layer_workload(args, cfg, mx=False, router=False):
                 break
         dt = time.perf_counter() - t0
         return done * uniq[0] * expert_weights * TRELLIS_BPW / dt / 1e9, \
-            f"{done} full layer step(s) of the same workload (routing of step 0), single-threaded C oracle, {dt:.1f} s"
+            f"{done} full layer step(s) of the same workload (routing of step 0" + \
+            ("; the router itself is not part of the sample" if router else "") + \
+            f"), single-threaded C oracle, {dt:.1f} s"
 
     kernel = ("k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)" if mx else
               "k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 matrix-core "

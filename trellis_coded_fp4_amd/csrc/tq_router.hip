@@ -16,7 +16,8 @@
 // go to the workspace with device-coherent stores; the last workgroup of a
 // token to count (a per-token counter it clears again) reads them back and
 // picks the top k in wave 0: k rounds of a wave-wide argmax (largest value,
-// lower id on ties). Softmax in fp64, rounded to fp32.
+// lower id on ties). Softmax in fp64 (one exp per lane, the sum a wave
+// butterfly), rounded to fp32.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -47,8 +48,6 @@ struct RouterArgs {
 
 __global__ void __launch_bounds__(kRThreads) k_router(RouterArgs a) {
   __shared__ float xs[kRMaxH];
-  __shared__ int pick[kRMaxK];
-  __shared__ double pval[kRMaxK];
   __shared__ int last;
   const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = blockIdx.x * kRExpertsPerBlock + wave;
@@ -125,6 +124,8 @@ __global__ void __launch_bounds__(kRThreads) k_router(RouterArgs a) {
     lv[i] = __longlong_as_double((long long)__hip_atomic_load(
         (const uint64_t *)(lt + min(lane + 64 * i, a.E - 1)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   uint32_t mine = 0u;
+  int my_pick = 0;
+  double my_val = 0.0, top = 0.0;
   for (int j = 0; j < a.k; ++j) {
     double bv = -INFINITY;
     int be = -1;
@@ -141,22 +142,25 @@ __global__ void __launch_bounds__(kRThreads) k_router(RouterArgs a) {
       if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
     }
     if ((be & 63) == lane) mine |= 1u << (be >> 6);
-    if (lane == 0) {
-      pick[j] = be;
-      pval[j] = bv;
+    // every lane holds the round's pick: lane j keeps pick j, all keep the first
+    if (lane == j) {
+      my_pick = be;
+      my_val = bv;
     }
+    if (j == 0) top = bv;
   }
-  if (lane == 0) {
-    const double m = pval[0];
-    double sum = 0.0;
-    for (int j = 0; j < a.k; ++j) sum += exp(pval[j] - m);
-    for (int j = 0; j < a.k; ++j) {
-      a.ids[(size_t)t * a.k + j] = pick[j];
-      a.gw[(size_t)t * a.k + j] = (float)(exp(pval[j] - m) / sum);
-    }
-    // every workgroup of this token has counted: clear for the next call
-    __hip_atomic_store(a.cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // softmax: lane j < k takes pick j (one exp each), the sum is a wave
+  // butterfly (k <= 64)
+  const double ex = lane < a.k ? exp(my_val - top) : 0.0;
+  double sum = ex;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < a.k) {
+    a.ids[(size_t)t * a.k + lane] = my_pick;
+    a.gw[(size_t)t * a.k + lane] = (float)(ex / sum);
   }
+  // every workgroup of this token has counted: clear for the next call
+  if (lane == 0) __hip_atomic_store(a.cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static size_t router_cnt_bytes(int T) { return ((size_t)T * sizeof(int) + 255) & ~(size_t)255; }
