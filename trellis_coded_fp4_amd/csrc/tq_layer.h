@@ -188,6 +188,7 @@ struct LayerArgs {
   int x_steps; uint8_t *xq; uint8_t *xs;   // ... into these columns (hi, lo per token)
   int *cntp, *obsp;             // split tokens; stage-1 items that have seen them all
   int grid;
+  int s1_ilv;                   // stage-1 items take the active experts in turn (see launch_nt)
 #ifdef TQ_TRACE
   unsigned long long *trace;
 #endif
@@ -1301,8 +1302,11 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, Shared &S, int item
   const int lane = tidx<NT>() & 63, wave = tidx<NT>() >> 6;
   const bool s1 = item < a.n_s1;
   const int i2 = item - a.n_s1;
-  const int ai = s1 ? item / a.n_rg1 : i2 / a.n_rt2;
-  const int tile = s1 ? item % a.n_rg1 : i2 % a.n_rt2;   // row group (stage 1) / row tile (stage 2)
+  // Stage-1 items in expert order, or (s1_ilv) the experts in turn: item i
+  // is row group i / n_active of expert i % n_active.
+  if (s1 && a.s1_ilv && item >= S.n_active * a.n_rg1) return;   // no such item: nothing to do
+  const int ai = s1 ? (a.s1_ilv ? item % S.n_active : item / a.n_rg1) : i2 / a.n_rt2;
+  const int tile = s1 ? (a.s1_ilv ? item / S.n_active : item % a.n_rg1) : i2 % a.n_rt2;   // row group / row tile
   if (ai >= S.n_active) return;   // no such active expert: nothing to do
   const int e = S.active[ai];
   const bool ffn = a.mode == MODE_FFN;
@@ -1635,6 +1639,13 @@ template <typename F, int NT, bool ALIGNED>
 static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
   const int n_items = a.n_prep + a.n_s1 + a.n_s2;
   a.grid = std::max(1, std::min(n_items, cus * resident_blocks<F, NT, ALIGNED>()));
+  // A single resident token whose items about fit one round of workgroups:
+  // the stage-1 items take the experts in turn, so that every expert's h is
+  // complete at about the same time instead of the last expert's well after
+  // the first's (items dispatched later are served later by the memory
+  // system). With many rounds of items (several tokens, or many experts'
+  // down projections) expert order is faster.
+  a.s1_ilv = a.mode == MODE_FFN && a.x_resident && 4 * n_items <= 5 * a.grid;
   hipLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
 }
