@@ -91,15 +91,19 @@ int trellis_decode_expand(hipStream_t stream, const trellis_mat_t *w, uint8_t *c
  *
  * Workspaces (for trellis_moe_gemv and trellis_moe_ffn) are device scratch
  * owned by the caller, 256-byte aligned, and must be ZERO-FILLED once before
- * their first use; every call leaves the synchronisation words zero again,
- * so a workspace can be reused by later calls (of any shape that fits)
- * without clearing. Each call runs as one persistent kernel whose work items
- * wait on counters in the workspace; the waits are bounded. After a call
- * completes:
+ * their first use; afterwards the calls keep their own bookkeeping in it (the
+ * synchronisation counters return to zero, a call counter advances), so a
+ * workspace can be reused by later calls (of any shape that fits) without
+ * clearing. Each call runs as one persistent kernel whose work items wait on
+ * counters or tagged data in the workspace; the waits are bounded. After a
+ * call completes:
  *   int32 at byte 0: routing slots skipped because their expert id >= n_mat;
- *   int32 at byte 4: nonzero if a wait timed out (results are then invalid;
- *                    this happens only if other work keeps the kernel's
- *                    workgroups from being resident at the same time).
+ *   int32 at byte 4: nonzero once a wait has timed out (this happens only if
+ *                    other work keeps the kernel's workgroups from being
+ *                    resident at the same time). The word is sticky: the call
+ *                    that timed out and every later call on the workspace
+ *                    write NaN to y and compute nothing else, until the
+ *                    workspace is zero-filled again.
  */
 size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
                                        int32_t k);

@@ -53,6 +53,7 @@
 #include <cstring>
 
 #include "tq_common.h"
+#include "tq_tok.h"
 
 namespace tq {
 
@@ -134,7 +135,7 @@ static void *g_trace = nullptr;
 #endif
 
 struct Layout {
-  size_t status, cnt1, obs1, cnt2, cntp, obsp, yslot, hq, hs, xq, xs, total;
+  size_t status, reserve, cnt1, obs1, cnt2, cntp, obsp, yslot, hq, hs, xq, xs, total;
 };
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -144,12 +145,16 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // (the routed GEMV's combine; zero for the layer, which adds into y);
 // h_cols: width of the h splits (layer only); n_tok x x_cols: the tokens'
 // activations, split once per call for every stage-1 item.
+// reserve: bytes kept right after the status words (the single-token layer
+// kernel's region; zero for the routed GEMV).
 template <typename F>
-static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int n_tok, int x_cols) {
+static Layout make_layout(int n_act, int n_rt, int n_slots, int y_rows, int h_cols, int n_tok, int x_cols,
+                          size_t reserve = 0) {
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.status = take(256);
+  L.reserve = take(reserve);
   L.cnt1 = take((size_t)n_act * kLineInts * 4);
   L.obs1 = take((size_t)n_act * kLineInts * 4);
   L.cnt2 = take((size_t)n_rt * kLineInts * 4);
@@ -1483,7 +1488,6 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
     int skipped = 0;
     for (int s = 0; s < n; ++s) skipped += S.ids[s] >= a.E;
     st_ctr(&a.status[ST_SKIPPED], skipped);
-    st_ctr(&a.status[ST_ERROR], 0);
   }
   for (int s = 0; s < n; ++s) {
     const int e = S.ids[s];
@@ -1525,7 +1529,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) S.trp = nullptr;
 #endif
-  if (tid == 0) S.x_done = 0;
+  if (tid == 0) {
+    S.x_done = 0;
+    // a wait of an earlier call on this workspace timed out: its counters
+    // may be off, so the call only marks its output invalid
+    S.last = __hip_atomic_load(&a.status[ST_ERROR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (S.last) {
+    if (blockIdx.x == 0) {
+      const size_t ny = a.mode == MODE_SLOTS ? (size_t)a.T * a.k * a.rows1 : (size_t)a.T * a.y_rows;
+      for (size_t i = tid; i < ny; i += kThreads) a.y[i] = __builtin_nanf("");
+    }
+    return;
+  }
   // routing, redundantly in every workgroup: active experts in id order
   const int n = a.T * a.k;
   const int nw = (a.E + 31) >> 5;
@@ -1732,11 +1749,23 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   if (gu.rows % 64 || dn.n_mat != E || dn.rows != hidden || dn.cols != inter) return TRELLIS_EINVAL;
   const int max_act = std::min(E, T * k);
   // (no partial outputs or combine counters: the down projection adds into y)
-  const Layout L = make_layout<F>(max_act, 0, T * k, 0, inter, T, hidden);
+  const Layout L = make_layout<F>(max_act, 0, T * k, 0, inter, T, hidden, tok_region(E, hidden, inter).total);
   if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
   char *ws = (char *)workspace;
+  if constexpr (F::kSteps == 2) {
+    // one token of trellis-coded weights: the single-token layer kernel
+    TokCall c{(const uint32_t *)gu.w, gu.scales, (const uint32_t *)dn.w, dn.scales, E, hidden, inter, k,
+              topk_ids, topk_w, x, x_dtype == TRELLIS_BF16, h, y, ws, L.reserve};
+    if (T == 1 && tok_supported(c, cus)) {
+      if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
+      rc = tok_launch(c, cus, stream);
+      if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess)
+        rc = TRELLIS_EHIP;
+      return rc;
+    }
+  }
   LayerArgs a{};
   a.mode = MODE_FFN;
   a.w1 = (const uint32_t *)gu.w; a.s1 = gu.scales; a.rows1 = gu.rows; a.cols1 = hidden;

@@ -1,0 +1,39 @@
+// tq_tok.h -- host interface of the single-token mixture-of-experts layer
+// kernel (tq_tok.hip), which trellis_moe_ffn uses for one token.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq {
+
+// Workspace region of the single-token kernel (inside the layer workspace,
+// right after the status words): per-workspace call counter and arrival
+// count, h of each active expert as tagged words, and one tag per 16-row
+// tile of y recording that the tile was cleared in this call.
+struct TokRegion {
+  size_t sync, hx, yz, total;
+};
+TokRegion tok_region(int n_exp, int hidden, int inter);
+
+struct TokCall {
+  const uint32_t *w1; const uint8_t *s1;   // gate_up [E][2I][H]
+  const uint32_t *w2; const uint8_t *s2;   // down    [E][H][I]
+  int E, H, I, k;
+  const int32_t *ids; const float *gate_w;
+  const void *x; int x_bf16;
+  uint16_t *h; float *y;
+  char *ws;                                // layer workspace (status words at 0)
+  size_t region_off;                       // offset of the TokRegion
+};
+
+// True when the kernel takes this shape (otherwise the general layer kernel
+// runs): one token, k <= 32, hidden and inter multiples of 64 and at most
+// 4096, 16-byte aligned streams and activations, and per-workgroup work
+// that fits the kernel's register arrays on this device.
+bool tok_supported(const TokCall &c, int cus);
+
+// Enqueue the kernel on `s` (argument checks already done by the caller).
+int tok_launch(const TokCall &c, int cus, hipStream_t s);
+
+}  // namespace tq

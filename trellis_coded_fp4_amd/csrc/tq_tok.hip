@@ -1,0 +1,738 @@
+// tq_tok.hip -- one mixture-of-experts layer for a single token, weights
+// decoded inside the kernel, on gfx950.
+//
+// HEPH abstract (ICLR 2027 submission page), fused serving mode: the trellis
+// streams stay resident and are decoded in the grouped-MoE kernel on every
+// forward pass. The decoder is the XOR-Trellis one (news article, bullet
+// "XOR-Trellis FP4 decoder"), bit-sliced in tq_decode.h; the decoded E2M1
+// nibbles and the weights' UE8M0 bytes feed the block-scaled FP4 x FP8
+// matrix cores, the token's activations entering as a two-term FP8 split.
+//
+// Why a kernel of its own for one token: the layer moves ~28 MB at the
+// 32-expert shape and every weight costs ~1.5 VALU operations to decode, so
+// the decode work alone keeps all 1024 SIMDs busy for about as long as HBM
+// needs to deliver the bytes. Both must overlap on every compute unit, and
+// every compute unit must carry the same share. So:
+//  - one workgroup per compute unit (the grid is the compute-unit count; a
+//    large dynamic LDS request keeps a second one off each unit);
+//  - work comes in units of equal decode cost: a "pair" (16 gate rows and
+//    the 16 matching up rows of one active expert, giving 16 values of h)
+//    and a "down tile" (16 rows of one active expert's down projection).
+//    Workgroup w takes pairs [w NP / G, (w+1) NP / G) and down tiles
+//    [w' ND / G, (w'+1) ND / G) with w' = G-1-w, so no unit carries more
+//    than one pair or one down tile above the average;
+//  - inside a workgroup the waves split every tile along K: wave v owns
+//    piece v (16 rows x 64 bytes, 256 weights per row) of each of the
+//    workgroup's tiles, so the four SIMDs share the decode evenly and a
+//    wave's activation operand (its piece of x) is read from LDS once and
+//    used for all its tiles. Partial sums meet in LDS and are added in
+//    piece order (h is deterministic);
+//  - every weight load of a wave is issued at the start, in the order it is
+//    consumed (loads complete in issue order): pairs first, then the down
+//    tiles, which are decoded ahead while the workgroup waits for h;
+//  - h crosses workgroups as tagged 64-bit words (call tag in the high
+//    half, two bf16 values in the low half) stored device-coherently: a
+//    consumer polls the words themselves, so no counter round trip and no
+//    fence lies between the last pair and the down projection;
+//  - y is cleared tile by tile (each 16-row tile by one workgroup, which
+//    then tags it) and the down tiles add their gate-weighted rows into it
+//    with device-scope float atomics.
+// The call tag comes from a counter in the workspace: every workgroup reads
+// it at entry and then counts itself in; the last to count advances it.
+// Every wait is bounded; a timeout sets a sticky error word, and a call
+// that finds it set writes NaN to y and does nothing else.
+#include "tq_tok.h"
+
+#include <algorithm>
+
+#include "tq_common.h"
+
+namespace tq {
+namespace {
+
+constexpr int kMaxJ = 16;            // 256-weight pieces per row: K <= 4096
+constexpr int kMaxSlots = 32;        // k
+constexpr int kMaxEx = 2;            // experts spanned by one workgroup's down tiles
+constexpr int kMaxPairs = 3;         // pairs per workgroup
+constexpr int kMaxDown = 8;          // down tiles per workgroup
+constexpr size_t kCuLds = 160 * 1024;   // LDS of a compute unit
+constexpr unsigned kPolls = 1u << 20;
+
+struct Args {
+  const uint32_t *w1; const uint8_t *s1;
+  const uint32_t *w2; const uint8_t *s2;
+  int E, H, I, k;
+  const int32_t *ids; const float *gate_w;
+  const void *x; int x_bf16;
+  uint16_t *h; float *y;
+  int *status;          // [0] skipped slots, [1] sticky error
+  uint32_t *sync;       // [0] call counter, [32] arrivals (own 128-byte line)
+  uint64_t *hx;         // [n_exp <= 32][I / 2]: tag << 32 | bf16 pair
+  uint32_t *yz;         // [H / 16]: tag of the call that cleared the tile
+  int G;
+#ifdef TQ_TRACE
+  unsigned long long *trace;   // [G][16] s_memrealtime stamps
+#endif
+};
+
+// Timeline instrumentation, compiled in only with -DTQ_TRACE: thread 0 of
+// each workgroup stamps s_memrealtime at the phase boundaries.
+#ifdef TQ_TRACE
+#define TOK_MARK_T(k, t) do { if (threadIdx.x == (t) && a.trace) a.trace[blockIdx.x * 16 + (k)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define TOK_MARK(k) TOK_MARK_T(k, 0)
+static unsigned long long *g_tok_trace = nullptr;
+#else
+#define TOK_MARK(k) do { } while (0)
+#define TOK_MARK_T(k, t) do { } while (0)
+#endif
+
+struct Smem {
+  // activation splits in the matrix-core step-chunk layout: column c holds
+  // 2J steps of 128 code bytes, its scales 2J x 4 bytes
+  uint8_t xq[2 * 2 * kMaxJ * 128];                 // x: hi, lo
+  uint8_t xs[2 * 2 * kMaxJ * 4];
+  uint8_t hq[2 * kMaxEx * 2 * kMaxJ * 128];        // h of up to two experts: hi, lo each
+  uint8_t hs[2 * kMaxEx * 2 * kMaxJ * 4];
+  float red1[2 * kMaxPairs][4][16];                // [tile][wave][row] partial sums
+  float red2[kMaxDown][4][16];
+  uint32_t tag;
+  int poisoned;
+  int x_ready;      // the call tag is in LDS
+  int up_issued;    // gate/up waves that have issued all their loads
+  int up_done;      // gate/up waves that have stored their partial sums
+};
+
+__device__ __forceinline__ uint64_t ld_dc64(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dc32(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dc64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dc32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void set_error(int *status) {
+  __hip_atomic_fetch_or(&status[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Maximum of non-negative floats over the four lanes of a quad (integer
+// order equals float order for them).
+__device__ __forceinline__ float quad_max4(float v) {
+  int m = __float_as_int(v);
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));
+  return __int_as_float(m);
+}
+
+// Two-term FP8 split of one 32-value block held by a quad (lane j of the
+// quad: values 8j .. 8j+7): hi = E4M3(v / 2^E), lo = E4M3((v - hi 2^E) / 2^El),
+// each with its UE8M0 exponent, written into column pair (lq, lq + psteps*128)
+// at block b's place in the step-chunk layout. `store` is uniform per quad.
+__device__ __forceinline__ void split_block8(const float (&f)[8], int b, int j, uint8_t *lq, uint8_t *ls,
+                                             int psteps, bool store) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  const int E = block_exponent(quad_max4(m));
+  uint32_t hi[4], lo[4];
+  float res[8], m2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    hi[i / 2] = f32x2_to_e4m3(ldexpf(f[i], -E), ldexpf(f[i + 1], -E));
+    res[i] = f[i] - ldexpf(e4m3_to_f32(hi[i / 2]), E);
+    res[i + 1] = f[i + 1] - ldexpf(e4m3_to_f32(hi[i / 2] >> 8), E);
+    m2 = fmaxf(m2, fmaxf(fabsf(res[i]), fabsf(res[i + 1])));
+  }
+  const int El = block_exponent(quad_max4(m2));
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) lo[i / 2] = f32x2_to_e4m3(ldexpf(res[i], -El), ldexpf(res[i + 1], -El));
+  if (!store) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int off = act_offset(b, 8 * j + i);
+    lq[off] = (uint8_t)(hi[i / 2] >> (8 * (i & 1)));
+    lq[(size_t)psteps * 128 + off] = (uint8_t)(lo[i / 2] >> (8 * (i & 1)));
+  }
+  if (j == 0) {
+    ls[act_scale_index(b)] = (uint8_t)(E + 127);
+    ls[(size_t)psteps * 4 + act_scale_index(b)] = (uint8_t)(El + 127);
+  }
+}
+
+// The 32 bytes of B operand (column c, step st) for this lane's K-block g,
+// and the column's UE8M0 byte of that block.
+struct BOp {
+  v8i b;
+  uint32_t s;
+};
+__device__ __forceinline__ BOp read_b(const uint8_t *lq, const uint8_t *ls, int psteps, int c, int st, int g) {
+  const uint4 *p = (const uint4 *)(lq + ((size_t)c * psteps + st) * 128 + g * 32);
+  const uint4 u0 = p[0], u1 = p[1];
+  BOp o;
+  o.b = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+  o.s = ls[((size_t)c * psteps + st) * 4 + g];
+  return o;
+}
+
+// Matrix-core steps 2p and 2p+1 of a decoded piece (A), x or h operands (B).
+struct DecA {
+  uint4 s0, s1;
+};
+__device__ __forceinline__ v4f mma2(const DecA &d, const BOp &b0, const BOp &b1, uint32_t sa, v4f acc) {
+  const v8i A0 = v8i{(int)d.s0.x, (int)d.s0.y, (int)d.s0.z, (int)d.s0.w, 0, 0, 0, 0};
+  const v8i A1 = v8i{(int)d.s1.x, (int)d.s1.y, (int)d.s1.z, (int)d.s1.w, 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, b0.b, acc, 4, 0, 0, (int)sa, 0, (int)b0.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, b1.b, acc, 4, 0, 1, (int)sa, 0, (int)b1.s);
+  return acc;
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for LDS hand-offs: this wave's LDS accesses are done,
+// then s_barrier. Unlike __syncthreads it does not wait for the wave's
+// outstanding global loads, so weight loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Row i of the 16-row tile as fp32: D column 0 (hi term) + column 1 (lo
+// term). Lane (i16 = 0, g) returns rows 4g .. 4g+3.
+__device__ __forceinline__ float pair_sum(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Keep a decoded operand in registers here: the compiler would otherwise
+// sink the decode of the down pieces to their use, after the wait for h.
+__device__ __forceinline__ void pin(DecA &d) {
+  asm volatile("" : "+v"(d.s0.x), "+v"(d.s0.y), "+v"(d.s0.z), "+v"(d.s0.w), "+v"(d.s1.x), "+v"(d.s1.y),
+               "+v"(d.s1.z), "+v"(d.s1.w));
+}
+
+// One wave's loads of one tile: its PPW pieces (16 bytes per lane each) and
+// the word before its first piece (decoder history of lane-group 0).
+template <int PPW>
+struct TileLd {
+  uint4 w[PPW];
+  uint32_t hist;
+  uint32_t sc[PPW];   // UE8M0 bytes of blocks 8p+2g, 8p+2g+1 of each piece p
+};
+
+// Decode piece words `a` whose history is `hist` (lane-group 0: the word
+// before the piece; others: the neighbour's last word).
+__device__ __forceinline__ DecA decode_words(const uint4 &a, uint32_t hist) {
+  const nib2 d0 = decode_word(a.x, hist), d1 = decode_word(a.y, a.x);
+  const nib2 d2 = decode_word(a.z, a.y), d3 = decode_word(a.w, a.z);
+  DecA d;
+  d.s0 = make_uint4(d0.even, d0.odd, d1.even, d1.odd);
+  d.s1 = make_uint4(d2.even, d2.odd, d3.even, d3.odd);
+  return d;
+}
+
+// Eight waves, two per SIMD, in two roles. Waves 0-3 ("gate/up waves")
+// each own PPW consecutive pieces of every gate/up tile of the workgroup
+// (T1 tiles at most), streamed through a register ring AT tiles deep (a
+// wave that issued all its loads at once would sit at the issue, which
+// stalls until the memory pipeline has room, instead of decoding what has
+// arrived); they run at raised priority. Waves 4-7 ("down waves") split x
+// and clear the workgroup's tiles of y, then, once every gate/up load of
+// the workgroup is issued, load PPW pieces of each down tile (T2 at most)
+// and decode them while the gate/up waves work and h is on its way; after
+// h arrives they run the down projection's matrix-core steps. The roles
+// meet through LDS flags until the gate/up work is done, so neither waits
+// at a barrier for the other's loads.
+template <int PPW, int T1, int T2, int AT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k_tok(Args a) {
+  constexpr int NW = 8, NR = 4;   // waves, waves per role
+  __shared__ Smem S;
+#ifdef TQ_TRACE
+  const unsigned long long t_entry = __builtin_amdgcn_s_memrealtime();
+#endif
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool up_role = wave < NR;           // gate/up wave
+  const int rw = wave & (NR - 1);           // index within the role
+  const int i16 = lane & 15, g = lane >> 4;
+  const int w = blockIdx.x, G = a.G;
+  const int H = a.H, I = a.I;
+  const int nb1 = H >> 5, J1 = (nb1 + 7) >> 3, wpr1 = H >> 4, ps1 = 2 * J1;
+  const int nb2 = I >> 5, J2 = (nb2 + 7) >> 3, wpr2 = I >> 4, ps2 = 2 * J2;
+  const int rt_per = H >> 4, pr_per = I >> 4;   // down tiles / pairs per expert
+  const int src = ((lane - 16) & 63) << 2;       // lane-group g-1, same row (ds_bpermute address)
+  const int rtid = tid & (64 * NR - 1);          // thread index within the role
+  if (tid == 0) {
+    S.x_ready = 0;
+    S.up_issued = 0;
+    S.up_done = 0;
+  }
+  __syncthreads();   // (nothing is in flight yet)
+#ifdef TQ_TRACE
+  if (tid == 0 && a.trace) a.trace[blockIdx.x * 16] = t_entry;
+#endif
+
+  // ---- routing inputs (every wave), x and the call counter (down waves).
+  // Every global load up to the wait for h is unconditional within its
+  // role (clamped addresses), so the compiler's waits count exactly the
+  // loads issued after each one.
+  const int sl = lane & 31, slc = sl < a.k ? sl : 0;
+  const int idv = a.ids[slc];
+  const float gwr = *(a.gate_w ? a.gate_w + slc : (const float *)(a.ids + slc));
+  // x: a gate/up wave splits the 32-value blocks of its own pieces
+  // (8 PPW of them, four lanes each, 16 per pass), loaded ahead of its tiles
+  constexpr int kXPass = (8 * PPW + 15) / 16;
+  uint4 xr[kXPass][2];
+  uint32_t epoch = 0;
+  int err0 = 0;
+  if (up_role) {
+    const int pa1 = min(rw * PPW, J1);
+#pragma unroll
+    for (int ps = 0; ps < kXPass; ++ps) {
+      const int xb = 8 * pa1 + 16 * ps + (lane >> 2), xj = lane & 3;
+      const int xbc = xb < nb1 ? xb : 0;
+      const char *xp = (const char *)a.x + (size_t)(32 * xbc + 8 * xj) * (a.x_bf16 ? 2 : 4);
+      xr[ps][0] = *(const uint4 *)xp;
+      xr[ps][1] = *(const uint4 *)(a.x_bf16 ? xp : xp + 16);
+    }
+  } else {
+    epoch = ld_dc32(a.sync);
+    err0 = __hip_atomic_load(&a.status[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- routing, in every wave's registers: lane s (< k) is slot s. Active
+  // experts in order of first occurrence; a duplicate slot shares its
+  // expert's units and adds its gate weight to it.
+  const bool valid = sl < a.k && idv >= 0 && idv < a.E;
+  const int e_me = valid ? idv : -1;
+  const float gw_me = a.gate_w ? gwr : 1.0f;
+  bool first = valid;
+  int dup_of = sl;
+  float gsum = 0.0f;
+  for (int s2 = 0; s2 < a.k; ++s2) {
+    const int e2 = __builtin_amdgcn_readlane(e_me, s2);
+    const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gw_me), s2));
+    if (valid && e2 == e_me) {
+      gsum += w2;
+      if (s2 < sl && first) {
+        first = false;
+        dup_of = s2;
+      }
+    }
+  }
+  const uint64_t fm = __ballot(first) & 0xFFFFFFFFull;
+  const int n_skipped = __popcll(__ballot(sl < a.k && idv >= a.E) & 0xFFFFFFFFull);
+  const int n_act = __popcll(fm);
+  const int rank = __popcll(fm & ((1ull << dup_of) - 1ull));   // active index of this slot's expert
+  auto act_lane = [&](int r) {   // lane holding active expert r
+    uint64_t m = fm;
+    for (int i = 0; i < r; ++i) m &= m - 1ull;
+    return (int)__builtin_ctzll(m | (1ull << 63));
+  };
+  auto act_expert = [&](int r) { return __builtin_amdgcn_readlane(e_me, act_lane(r)); };
+  TOK_MARK(1);
+
+  // ---- this workgroup's units: pairs [p0, p0 + np), down tiles [d0, d0 + nd)
+  const int NP = n_act * pr_per, ND = n_act * rt_per;
+  const int p0 = (int)((long long)w * NP / G), np = (int)((long long)(w + 1) * NP / G) - p0;
+  const int wd = G - 1 - w;
+  const int d0 = (int)((long long)wd * ND / G), nd = (int)((long long)(wd + 1) * ND / G) - d0;
+  const int n1 = 2 * np;
+  // first matrix row of every tile (gate/up tiles: gate even, up odd; then
+  // down tiles); positions past the workgroup's tiles repeat a valid tile
+  size_t row[T1 + T2];
+#pragma unroll
+  for (int t = 0; t < T1; ++t) {
+    const int tc = n1 > 0 ? min(t, n1 - 1) : 0;
+    const int u = p0 + (tc >> 1), ai = u / pr_per, j = u - ai * pr_per;
+    row[t] = n1 > 0 ? (size_t)act_expert(ai) * 2 * I + (tc & 1 ? I : 0) + 16 * j : 0;
+  }
+#pragma unroll
+  for (int t = 0; t < T2; ++t) {
+    const int tc = nd > 0 ? min(t, nd - 1) : 0;
+    const int d = d0 + tc, ai = d / rt_per, rt = d - ai * rt_per;
+    row[T1 + t] = nd > 0 ? (size_t)act_expert(ai) * H + 16 * rt : 0;
+  }
+  // this wave's pieces [pa, pa + c) of each of its role's tiles
+  const int J = up_role ? J1 : J2;
+  const int pa = min(rw * PPW, J), c = min(J - pa, PPW);
+  auto load_tile = [&](int t) -> TileLd<PPW> {   // tile position t (0 .. T1 + T2 - 1)
+    TileLd<PPW> L;
+    const bool s1 = t < T1;
+    const size_t r = row[t] + i16;
+    const uint32_t *rp = s1 ? a.w1 + r * wpr1 : a.w2 + r * wpr2;
+    const uint8_t *sp = s1 ? a.s1 + r * nb1 : a.s2 + r * nb2;
+    const int wpr = s1 ? wpr1 : wpr2, nb = s1 ? nb1 : nb2;
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) L.sc[q] = *(const uint16_t *)(sp + min(8 * (pa + q) + 2 * g, nb - 2));
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) L.w[q] = *(const uint4 *)(rp + min(16 * (pa + q) + 4 * g, wpr - 4));
+    L.hist = rp[min(max(16 * pa - 1, 0), wpr - 1)];
+    return L;
+  };
+  // A-scale pair of piece p (blocks past the row: 2^0, meeting zero codes)
+  auto a_scale = [&](uint32_t sc, int nb, int p) -> uint32_t { return 8 * p + 2 * g < nb ? sc : 0x7F7Fu; };
+
+  DecA D2[T2][PPW];
+  uint32_t sc2[T2][PPW];
+  uint32_t tag;
+  bool poisoned;
+  if (up_role) {
+    // ---- gate/up tiles, AT loads ahead
+    __builtin_amdgcn_s_setprio(2);
+    TileLd<PPW> R[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t) R[t] = load_tile(t);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (AT >= T1 && lane == 0) __hip_atomic_fetch_add(&S.up_issued, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // split this wave's blocks of x into LDS (blocks past K, up to the last
+    // piece, get zero codes); the wave reads them back itself
+#pragma unroll
+    for (int ps = 0; ps < kXPass; ++ps) {
+      const int xb = 8 * pa + 16 * ps + (lane >> 2), xj = lane & 3;
+      float f[8];
+      const uint32_t wv[8] = {xr[ps][0].x, xr[ps][0].y, xr[ps][0].z, xr[ps][0].w,
+                              xr[ps][1].x, xr[ps][1].y, xr[ps][1].z, xr[ps][1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t bits = a.x_bf16 ? (wv[i >> 1] >> (16 * (i & 1))) << 16 : wv[i];
+        f[i] = xb < nb1 ? __uint_as_float(bits) : 0.0f;
+      }
+      split_block8(f, xb, xj, S.xq, S.xs, ps1, xb < 8 * (pa + c));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    TOK_MARK(2);
+    // this wave's x operands (B), read once
+    BOp bx[PPW][2];
+#pragma unroll
+    for (int q = 0; q < PPW; ++q)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        bx[q][hh] = read_b(S.xq, S.xs, ps1, i16 & 1, min(2 * (pa + q) + hh, ps1 - 1), g);
+#pragma unroll
+    for (int t = 0; t < T1; ++t) {
+      const TileLd<PPW> cur = R[t % AT];
+      if (t + AT < T1) {
+        R[t % AT] = load_tile(t + AT);
+        if (t + AT == T1 - 1 && lane == 0)
+          __hip_atomic_fetch_add(&S.up_issued, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (t < n1 && c > 0) {
+        uint32_t carry = pa == 0 ? 0u : cur.hist;
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < PPW; ++q) {
+          if (q < c) {
+            const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
+            const DecA d = decode_words(cur.w[q], g == 0 ? carry : rot);
+            carry = rot;
+            acc = mma2(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], nb1, pa + q), acc);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = pair_sum(acc[r]);
+          if (i16 == 0) S.red1[t][rw][4 * g + r] = v;
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    TOK_MARK(4);
+    // the call tag (set by the down waves at entry)
+    while (__hip_atomic_load(&S.x_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 1)
+      __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+    tag = S.tag;
+    poisoned = S.poisoned != 0;
+    // the last gate/up wave to finish computes SwiGLU for the workgroup:
+    // thread q < 16 np, row q % 16 of pair q / 16 (its partial sums are
+    // stored before it counts: LDS accesses of a wave complete in order)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    int arrived = 0;
+    if (lane == 0) arrived = __hip_atomic_fetch_add(&S.up_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    arrived = __builtin_amdgcn_readfirstlane(arrived);
+    if (arrived == NR - 1 && !poisoned) {
+      asm volatile("" ::: "memory");
+      for (int qq = lane; qq < 16 * np; qq += 64) {
+        const int uo = qq >> 4, r = qq & 15;
+        float gs = 0.0f, us = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NR; ++v) {
+          gs += S.red1[2 * uo][v][r];
+          us += S.red1[2 * uo + 1][v][r];
+        }
+        const float silu = gs / (1.0f + expf(-gs));
+        const uint32_t hb = f32_to_bf16_rne(silu * us);
+        const int u = p0 + uo, ai = u / pr_per, j = u - ai * pr_per;
+        const int col = 16 * j + r;
+        // two values per tagged word: the even row's lane stores
+        const uint32_t hb_next = __shfl_down(hb, 1, 64);
+        if ((r & 1) == 0)
+          st_dc64(a.hx + ((size_t)ai * I + col) / 2, ((uint64_t)tag << 32) | (hb | (hb_next << 16)));
+        for (int s = 0; s < a.k; ++s)
+          if (__builtin_amdgcn_readlane((int)valid, s) && __builtin_amdgcn_readlane(rank, s) == ai)
+            a.h[(size_t)s * I + col] = (uint16_t)hb;
+      }
+    }
+    TOK_MARK(5);
+  } else {
+    // clear this workgroup's tiles of y (tagged once the zeros are at the
+    // coherence point, after the down tiles are decoded)
+    if (rw == 0)
+      for (int rt = w; rt < rt_per; rt += G)
+        if (lane < 16) __hip_atomic_store(&a.y[16 * rt + lane], err0 ? __builtin_nanf("") : 0.0f,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tag = epoch + 1u;   // 1 .. 2^32 - 1 (the counter skips 2^32 - 1)
+    poisoned = err0 != 0;
+    if (rtid == 0) {
+      S.tag = tag;
+      S.poisoned = err0;
+    }
+    // the tag is in LDS before the flag goes up
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (rtid == 0) __hip_atomic_store(&S.x_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // ---- down tiles: loads once every gate/up load is issued, then the decode
+    while (__hip_atomic_load(&S.up_issued, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NR)
+      __builtin_amdgcn_s_sleep(2);
+    asm volatile("" ::: "memory");
+    TileLd<PPW> L2[T2];
+#pragma unroll
+    for (int t = 0; t < T2; ++t) L2[t] = load_tile(T1 + t);
+#pragma unroll
+    for (int t = 0; t < T2; ++t) {
+      if (!poisoned && t < nd && c > 0) {
+        uint32_t carry = pa == 0 ? 0u : L2[t].hist;
+#pragma unroll
+        for (int q = 0; q < PPW; ++q) {
+          if (q < c) {
+            const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)L2[t].w[q].w);
+            D2[t][q] = decode_words(L2[t].w[q], g == 0 ? carry : rot);
+            carry = rot;
+            sc2[t][q] = a_scale(L2[t].sc[q], nb2, pa + q);
+            pin(D2[t][q]);
+          }
+        }
+      }
+    }
+    TOK_MARK_T(6, 256);
+    // count the workgroup in and tag its tiles of y (the zeros were stored
+    // at entry; this wait also covers them)
+    if (rw == 0) {
+      uint32_t seen_old = 0;
+      if (lane == 0) seen_old = __hip_atomic_fetch_add(&a.sync[32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      for (int rt = w; rt < rt_per; rt += G)
+        if (lane == 0) st_dc32(a.yz + rt, tag);
+      // the last workgroup to count in advances the call counter (every
+      // workgroup read it before counting in)
+      if (lane == 0 && seen_old == (uint32_t)(G - 1)) {
+        st_dc32(&a.sync[32], 0u);
+        st_dc32(&a.sync[0], epoch + 1u == 0xFFFFFFFFu ? 0u : epoch + 1u);
+      }
+    }
+    TOK_MARK_T(7, 256);
+  }
+
+  // ---- h of the experts of this workgroup's down tiles, polled as tagged
+  // words (all waves) and split into LDS columns (2 ex, 2 ex + 1) for expert a_lo + ex
+  const int a_lo = nd > 0 ? d0 / rt_per : 0;
+  const int n_ex = nd > 0 ? (d0 + nd - 1) / rt_per - a_lo + 1 : 0;
+  constexpr int kHPass = (8 * kMaxJ + 16 * NW - 1) / (16 * NW);
+  for (int ex = 0; ex < n_ex && !poisoned; ++ex) {
+    const int ai = a_lo + ex;
+    uint64_t v[kHPass][4];
+    for (unsigned it = 0;; ++it) {
+      bool ok = true;
+#pragma unroll
+      for (int ps = 0; ps < kHPass; ++ps) {
+        const int hb = ps * 16 * NW + (tid >> 2), hj = tid & 3;
+        const uint64_t *hsrc = a.hx + ((size_t)ai * I + 32 * (hb < nb2 ? hb : 0) + 8 * hj) / 2;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[ps][q] = ld_dc64(hsrc + q);
+          ok = ok && (hb >= nb2 || (uint32_t)(v[ps][q] >> 32) == tag);
+        }
+      }
+      if (__syncthreads_and(ok)) break;
+      if (it >= kPolls) {
+        if (tid == 0) set_error(a.status);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int ps = 0; ps < kHPass; ++ps) {
+      const int hb = ps * 16 * NW + (tid >> 2), hj = tid & 3;
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        f[i] = hb < nb2 ? __uint_as_float(((uint32_t)(v[ps][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16) : 0.0f;
+      split_block8(f, hb, hj, S.hq + (size_t)(2 * ex) * ps2 * 128, S.hs + (size_t)(2 * ex) * ps2 * 4, ps2,
+                   hb < 8 * J2);
+    }
+  }
+  __syncthreads();
+  TOK_MARK(8);
+
+  // ---- down projection (down waves): matrix-core steps on the pre-decoded pieces
+  if (!up_role) {
+#pragma unroll
+    for (int t = 0; t < T2; ++t) {
+      if (!poisoned && t < nd && c > 0) {
+        const int ex = (d0 + t) / rt_per - a_lo;
+        const int col = 2 * ex + (i16 & 1);
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < PPW; ++q) {
+          if (q < c) {
+            const BOp b0 = read_b(S.hq, S.hs, ps2, col, 2 * (pa + q), g);
+            const BOp b1 = read_b(S.hq, S.hs, ps2, col, 2 * (pa + q) + 1, g);
+            acc = mma2(D2[t][q], b0, b1, sc2[t][q], acc);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = pair_sum(acc[r]);
+          if (i16 == 0) S.red2[t][rw][4 * g + r] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  TOK_MARK(9);
+
+  // ---- y += gate weight x row, once the tile is cleared in this call
+  for (int q = tid; q < 16 * nd && !poisoned; q += 64 * NW) {
+    const int t = q >> 4, r = q & 15;
+    float v = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < NR; ++wv) v += S.red2[t][wv][r];
+    const int d = d0 + t, ai = d / rt_per, rt = d - ai * rt_per;
+    const float gw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum), act_lane(ai)));
+    for (unsigned it = 0; ld_dc32(a.yz + rt) != tag; ++it) {
+      if (it >= kPolls) {
+        set_error(a.status);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __hip_atomic_fetch_add(a.y + 16 * rt + r, gw * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  TOK_MARK(10);
+
+  // ---- once per call: skipped-slot count, h rows of dead slots
+  if (w == 0) {
+    if (tid == 0) __hip_atomic_store(&a.status[0], n_skipped, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int s = 0; s < a.k; ++s)
+      if (!__builtin_amdgcn_readlane((int)valid, s))
+        for (int cc = tid; cc < I; cc += 64 * NW) a.h[(size_t)s * I + cc] = 0;
+  }
+  TOK_MARK(11);
+}
+
+// Kernel instances: (pieces per wave, gate/up tiles, down tiles).
+struct Inst {
+  int ppw, t1, t2;
+  const void *fn;
+};
+#ifndef TQ_TOK_AT
+#define TQ_TOK_AT 2
+#endif
+#define TQ_TOK_INST(PPW, T1, T2) {PPW, T1, T2, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT>}
+const Inst kInsts[] = {
+    TQ_TOK_INST(3, 6, 3), TQ_TOK_INST(4, 6, 3), TQ_TOK_INST(3, 6, 4), TQ_TOK_INST(4, 6, 4),
+};
+
+// Worst-case work of a workgroup (every slot a distinct expert).
+struct Plan {
+  int nw, ppw, t1, t2;
+  bool ok;
+};
+Plan plan(const TokCall &c, int cus) {
+  Plan p{4, 0, 0, 0, false};   // four waves per role
+  const int J1 = (c.H / 32 + 7) / 8, J2 = (c.I / 32 + 7) / 8;
+  if (J1 > kMaxJ || J2 > kMaxJ) return p;
+  p.ppw = std::max((J1 + p.nw - 1) / p.nw, (J2 + p.nw - 1) / p.nw);
+  const int n_act = std::min(c.E, c.k);
+  const int NP = n_act * (c.I / 16), ND = n_act * (c.H / 16);
+  p.t1 = 2 * ((NP + cus - 1) / cus);
+  p.t2 = (ND + cus - 1) / cus;
+  // a workgroup's down tiles span at most two experts
+  const bool span_ok = p.t2 <= c.H / 16 + 1;
+  p.ok = p.t1 <= 2 * kMaxPairs && p.t2 <= kMaxDown && span_ok;
+  return p;
+}
+
+const Inst *pick(const Plan &p) {
+  const Inst *best = nullptr;
+  for (const Inst &i : kInsts)
+    if (i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
+        (!best || i.ppw * (i.t1 + i.t2) < best->ppw * (best->t1 + best->t2)))
+      best = &i;
+  return best;
+}
+
+}  // namespace
+
+TokRegion tok_region(int n_exp, int hidden, int inter) {
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  TokRegion r;
+  r.sync = 0;
+  r.hx = 256;
+  r.yz = al(r.hx + (size_t)std::min(n_exp, kMaxSlots) * inter * 4);
+  r.total = al(r.yz + (size_t)(hidden / 16) * 4);
+  return r;
+}
+
+bool tok_supported(const TokCall &c, int cus) {
+  if (c.k < 1 || c.k > kMaxSlots || c.H % 64 || c.I % 64 || c.H < 64 || c.I < 64) return false;
+  if (((uintptr_t)c.w1 & 15) || ((uintptr_t)c.w2 & 15) || ((uintptr_t)c.x & 15)) return false;
+  if (((uintptr_t)c.s1 & 15) || ((uintptr_t)c.s2 & 15)) return false;
+  const Plan p = plan(c, cus);
+  return p.ok && pick(p) != nullptr;
+}
+
+int tok_launch(const TokCall &c, int cus, hipStream_t s) {
+  const Plan p = plan(c, cus);
+  const Inst *inst = p.ok ? pick(p) : nullptr;
+  if (!inst) return TRELLIS_EINVAL;
+  const TokRegion R = tok_region(c.E, c.H, c.I);
+  char *base = c.ws + c.region_off;
+  Args a;
+  a.w1 = c.w1; a.s1 = c.s1; a.w2 = c.w2; a.s2 = c.s2;
+  a.E = c.E; a.H = c.H; a.I = c.I; a.k = c.k;
+  a.ids = c.ids; a.gate_w = c.gate_w;
+  a.x = c.x; a.x_bf16 = c.x_bf16;
+  a.h = c.h; a.y = c.y;
+  a.status = (int *)c.ws;
+  a.sync = (uint32_t *)(base + R.sync);
+  a.hx = (uint64_t *)(base + R.hx);
+  a.yz = (uint32_t *)(base + R.yz);
+  a.G = cus;
+#ifdef TQ_TRACE
+  a.trace = g_tok_trace;
+#endif
+  // dynamic LDS (unused) bringing the workgroup above half a compute
+  // unit's LDS, so that no unit holds two of them
+  static size_t pad[sizeof(kInsts) / sizeof(kInsts[0])];
+  const size_t ii = (size_t)(inst - kInsts);
+  if (!pad[ii]) {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, inst->fn) != hipSuccess) return TRELLIS_EHIP;
+    pad[ii] = std::max<size_t>(kCuLds / 2 + 1024 - std::min<size_t>(fa.sharedSizeBytes, kCuLds / 2), 1);
+  }
+  void *args[] = {&a};
+  if (hipLaunchKernel(inst->fn, dim3(cus), dim3(512), args, pad[ii], s) != hipSuccess)
+    return TRELLIS_EHIP;
+  return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
+}
+
+}  // namespace tq
+
+#ifdef TQ_TRACE
+extern "C" void tq_tok_set_trace(void *p) { tq::g_tok_trace = (unsigned long long *)p; }
+#endif
