@@ -68,17 +68,26 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="moe32",
                    help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | moe32r | viterbi")
-    p.add_argument("--ring-gb", type=float, default=1.0)
+    p.add_argument("--ring-gb", type=float, default=1.0,
+                   help="minimum total size of the ring of weight copies (GiB)")
+    p.add_argument("--reuse-mb", type=float, default=512.0,
+                   help="minimum MiB of other weight traffic between two reads of the same copy's bytes "
+                        "(the Infinity Cache holds 256 MB): the ring gets enough copies for it")
+    p.add_argument("--rounds", type=int, default=4,
+                   help="after the timed region: this many interleaved rounds, cold ring / warm (one copy "
+                        "repeated) / warm / cold ..., 50 steps each, reported as a spread check")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="seconds of oracle work for each CPU-baseline leg (one thread, then all cores)")
     p.add_argument("--no-stage-events", action="store_true",
                    help="no events around each launch (time only the whole timed region)")
     p.add_argument("--event-every", type=int, default=8, metavar="N",
                    help="bracket every N-th launch of the timed region with a pair of events (each pair costs "
                         "the stream a few microseconds, so bracketing every launch slows the loop it measures)")
     p.add_argument("--event-release", choices=("device", "none", "system"), default="none",
-                   help="memory release of the per-launch events: device scope (default), no system fence, "
-                        "or HIP's default system scope, which writes back and invalidates the caches each record")
+                   help="memory release of the per-launch events: none (default: no system fence), device "
+                        "scope, or HIP's default system scope, which writes back and invalidates the caches "
+                        "each record")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB ten times (reference for the HBM "
                         "byte counters of a profiler) and exit")
@@ -150,10 +159,77 @@ def dev(a):
     return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).cuda()
 
 
-def ring_copies(tensors, bytes_per_copy, ring_gb):
-    """Distinct device copies of `tensors`, enough to total >= ring_gb GiB."""
+def ring_copies(tensors, bytes_per_copy, ring_gb, step_bytes=None, reuse_mb=0.0):
+    """Distinct device copies of `tensors`: enough to total >= ring_gb GiB and,
+    when the bytes a step reads are given (the least of any step), enough
+    that steps walking the copies in turn read >= reuse_mb MiB of other
+    weights between two reads of the same copy. Returns (copies, reuse
+    distance in bytes: (copies - 1) x the least bytes of a step)."""
     n = max(1, int(np.ceil(ring_gb * (1 << 30) / bytes_per_copy)))
-    return [tensors] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
+    if step_bytes:
+        n = max(n, int(np.ceil(reuse_mb * (1 << 20) / step_bytes)) + 1)
+    ring = [tensors] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
+    return ring, ((n - 1) * step_bytes if step_bytes else None)
+
+
+def cpu_run(fn, seconds, threads):
+    """Call fn repeatedly on `threads` threads (the oracle's C calls release
+    the GIL) for about `seconds`; returns (calls completed, elapsed s)."""
+    import threading
+    t0 = time.perf_counter()
+    counts = [0] * threads
+
+    def worker(i):
+        while True:
+            fn()
+            counts[i] += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return sum(counts), time.perf_counter() - t0
+
+
+def host_cpu():
+    """(usable hardware threads, CPU model) of this host."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def stream_read_peak(nbytes, reuse_mb, steps=100):
+    """GB/s of a plain device reduction (torch.sum) over nbytes per step,
+    walking a ring of copies as the layer steps do: the practical read rate
+    at this size, launch gaps included, for comparison with the kernel."""
+    import torch
+    n = max(2, int(np.ceil(reuse_mb * (1 << 20) / nbytes)) + 1)
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(n)]
+    for i in range(10):
+        bufs[i % n].sum()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        bufs[i % n].sum()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    del bufs
+    return round(nbytes / (us * 1e-6) / 1e9, 1), round(us, 2)
 
 
 # ---------------------------------------------------------------- workloads
@@ -176,15 +252,17 @@ def layer_workload(args, cfg, mx=False, router=False):
         torch.cuda.synchronize()
         w0 = (gc, gs, dc, ds)
     expert_weights = 3 * H * I
-    ring = ring_copies(w0, E * expert_weights * bpw, args.ring_gb)
     routes, uniq, slots = [], [], []
-    for s in range(args.warmup + args.steps):
+    n_steps = args.warmup + args.steps + 50 * max(args.rounds, 0)
+    for s in range(n_steps):
         x, ids, gw = (L0.x, L0.ids, L0.gate_w) if s == 0 else workloads.moe_batch(cfg, 0, 1000 + s)
         xs = dev(x).to(torch.bfloat16) if cfg.x_bf16 else dev(x)
         routes.append((xs, dev(ids), dev(gw)))
         live = ids[(ids >= 0) & (ids < E)]
         uniq.append(len(np.unique(live)))
         slots.append(len(live))
+    ring, reuse = ring_copies(w0, E * expert_weights * bpw, args.ring_gb,
+                              step_bytes=min(uniq) * expert_weights * bpw, reuse_mb=args.reuse_mb)
     T, k = cfg.T, cfg.k
     ws = tq.ffn_workspace(E, H, I, T, k)
     h = torch.empty((T, k, I), dtype=torch.bfloat16, device="cuda")
@@ -206,8 +284,8 @@ def layer_workload(args, cfg, mx=False, router=False):
             live = ids_s.cpu().numpy()
             uniq[s], slots[s] = len(np.unique(live)), live.size
 
-    def make(s, events=None):
-        a, b, c, d = ring[s % len(ring)]
+    def make(s, events=None, copy=None):
+        a, b, c, d = ring[s % len(ring) if copy is None else copy]
         xs, ids, gw = routes[s]
         if router:
             rcall = tq.router_topk(xs, wr, k, topk_ids=r_ids, topk_w=r_gw, workspace=r_ws, prepare=True)
@@ -224,23 +302,23 @@ def layer_workload(args, cfg, mx=False, router=False):
         return tq.moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True,
                           events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
 
-    def cpu_sample(seconds):
+    def cpu_sample(seconds, threads=1):
         import oracle
-        done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.moe_ffn(L0.gu_syms, L0.gu_scales, L0.dn_syms, L0.dn_scales, L0.x, L0.ids, L0.gate_w)
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
+        done, dt = cpu_run(lambda: oracle.moe_ffn(L0.gu_syms, L0.gu_scales, L0.dn_syms, L0.dn_scales, L0.x,
+                                                  L0.ids, L0.gate_w), seconds, threads)
         return done * uniq[0] * expert_weights * TRELLIS_BPW / dt / 1e9, \
             f"{done} full layer step(s) of the same workload (routing of step 0" + \
             ("; the router itself is not part of the sample" if router else "") + \
-            f"), single-threaded C oracle, {dt:.1f} s"
+            f"), C oracle on {threads} thread(s), {dt:.1f} s"
 
-    kernel = ("k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)" if mx else
-              "k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 matrix-core "
-              "gate_up + SwiGLU, down + combine)")
+    if mx:
+        kernel = "k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)"
+    elif T == 1:
+        kernel = ("k_tok (single-token MoE layer: routing, fused decode + FP4 matrix-core gate_up + SwiGLU, "
+                  "tagged h hand-off, down + gate-weighted atomic combine)")
+    else:
+        kernel = ("k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 "
+                  "matrix-core gate_up + SwiGLU, down + combine)")
     if router:
         kernel += "; each step is k_router then k_layer, the events bracket k_layer"
     return dict(
@@ -248,10 +326,10 @@ def layer_workload(args, cfg, mx=False, router=False):
         stream=stream,
         bytes=lambda s: uniq[s] * expert_weights * bpw,
         flops=lambda s: 2.0 * slots[s] * expert_weights,
-        tokens=T, kernel=kernel, cpu=cpu_sample,
+        tokens=T, kernel=kernel, cpu=cpu_sample, workspace=ws, ring=len(ring),
         config={"n_experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
                 "bytes_per_weight": bpw, "weights": "expanded MXFP4" if mx else "trellis-coded",
-                "ring_copies": len(ring)})
+                "ring_copies": len(ring), "reuse_distance_mb": round(reuse / (1 << 20), 1)})
 
 
 def gemv_workload(args):
@@ -263,32 +341,28 @@ def gemv_workload(args):
     sc = workloads.scales(workloads.rng(c["config_id"], 1), 1, rows, cols)
     x = workloads.activations(workloads.rng(c["config_id"], workloads.T_X), 1, cols, bf16=False)
     w0 = (dev(syms), dev(sc))
-    ring = ring_copies(w0, rows * cols * TRELLIS_BPW, args.ring_gb)
+    ring, reuse = ring_copies(w0, rows * cols * TRELLIS_BPW, args.ring_gb, step_bytes=rows * cols * TRELLIS_BPW,
+                              reuse_mb=args.reuse_mb)
     xs, ids = dev(x), dev(np.zeros((1, 1), np.int32))
     ws = tq.gemv_workspace(1, rows, cols, 1, 1)
     y = torch.empty((1, 1, rows), dtype=torch.float32, device="cuda")
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def make(s, events=None):
-        a, b = ring[s % len(ring)]
+    def make(s, events=None, copy=None):
+        a, b = ring[s % len(ring) if copy is None else copy]
         return hip.bracket(tq.moe_gemv(a, b, xs, ids, y=y, workspace=ws, prepare=True), events, stream)
 
-    def cpu_sample(seconds):
+    def cpu_sample(seconds, threads=1):
         import oracle
-        done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.moe_gemv(syms, sc, x, np.zeros((1, 1), np.int32))
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
-        return done * rows * cols * TRELLIS_BPW / dt / 1e9, f"{done} GEMV(s), single-threaded C oracle, {dt:.1f} s"
+        done, dt = cpu_run(lambda: oracle.moe_gemv(syms, sc, x, np.zeros((1, 1), np.int32)), seconds, threads)
+        return done * rows * cols * TRELLIS_BPW / dt / 1e9, f"{done} GEMV(s), C oracle on {threads} thread(s), {dt:.1f} s"
 
     return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: rows * cols * TRELLIS_BPW,
-                flops=lambda s: 2.0 * rows * cols, tokens=1, cpu=cpu_sample,
+                flops=lambda s: 2.0 * rows * cols, tokens=1, cpu=cpu_sample, workspace=ws, ring=len(ring),
                 kernel="k_layer<FmtTrellis> (routed GEMV, one slot)",
-                config={"rows": rows, "cols": cols, "tokens": 1, "x": "fp32", "ring_copies": len(ring)})
+                config={"rows": rows, "cols": cols, "tokens": 1, "x": "fp32", "ring_copies": len(ring),
+                        "reuse_distance_mb": round(reuse / (1 << 20), 3)})
 
 
 def expand_workload(args):
@@ -308,24 +382,18 @@ def expand_workload(args):
     stream = torch.cuda.current_stream().cuda_stream
     weights = n * rows * cols
 
-    def make(s, events=None):
+    def make(s, events=None, copy=None):
         return hip.bracket(tq.decode_expand(syms, sc, codes_out=codes, scales_out=scales_out, prepare=True),
                            events, stream)
 
     g = workloads.rng(c["config_id"], 0)
     small = (workloads.symbols(g, 1, 64, cols), workloads.scales(g, 1, 64, cols))
 
-    def cpu_sample(seconds):
+    def cpu_sample(seconds, threads=1):
         import oracle
-        done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.expand(*small)
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
+        done, dt = cpu_run(lambda: oracle.expand(*small), seconds, threads)
         return done * 64 * cols * TRELLIS_BPW / dt / 1e9, \
-            f"{done} expand(s) of a 64x{cols} matrix, single-threaded C oracle, {dt:.1f} s"
+            f"{done} expand(s) of a 64x{cols} matrix, C oracle on {threads} thread(s), {dt:.1f} s"
 
     return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: weights * TRELLIS_BPW,
                 flops=None, tokens=None, cpu=cpu_sample, traffic_bytes=weights * (TRELLIS_BPW + MX_BPW),
@@ -347,21 +415,17 @@ def viterbi_workload(args):
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def make(s, events=None):
+    def make(s, events=None, copy=None):
         return hip.bracket(tq.viterbi_encode(target, d, syms_out=syms, cost_out=cost, workspace=ws, prepare=True),
                            events, stream)
 
-    def cpu_sample(seconds):
+    def cpu_sample(seconds, threads=1):
         import oracle
-        done, t0 = 0, time.perf_counter()
-        while True:
-            oracle.viterbi(target_h[done % rows], d_h[done % rows])
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
-        return done * n / dt, f"{done} row(s) of {n} positions of the same workload, single-threaded C oracle " \
-                              f"(65536 states x 4 branches per position), {dt:.1f} s"
+        counter = iter(range(1 << 30))
+        done, dt = cpu_run(lambda: (lambda i: oracle.viterbi(target_h[i % rows], d_h[i % rows]))(next(counter)),
+                           seconds, threads)
+        return done * n / dt, f"{done} row(s) of {n} positions of the same workload, C oracle on {threads} " \
+                              f"thread(s) (65536 states x 4 branches per position), {dt:.1f} s"
 
     return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: rows * n,
                 units="weights/s", scale=1.0,
@@ -398,7 +462,8 @@ def pick(args):
 # The device sources each workload's kernel is compiled from: a recorded
 # traffic figure stays valid while these are unchanged.
 KERNEL_SOURCES = {
-    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer.h", "tq_common.h", "tq_decode.h"],
+    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer.h", "tq_tok.hip", "tq_tok.h", "tq_common.h",
+              "tq_decode.h"],
     "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
     "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],
 }
@@ -448,6 +513,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = hip.elapsed_ms(t0e, t1e)
+    # a wait that timed out in any call makes every result invalid (sticky status word)
+    status_error = None
+    if W.get("workspace") is not None:
+        status_error = int(W["workspace"][:8].view(torch.int32)[1].item())
+        if status_error:
+            raise SystemExit("bench.py: a wait timed out in the timed region (workspace status word set); "
+                             "the measurement is invalid")
     ms_per_step = total_ms / args.steps
     timed = range(args.warmup, args.warmup + args.steps)
     total_bytes = sum(W["bytes"](s) for s in timed)
@@ -472,7 +544,10 @@ def main():
                 traffic = None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": W["kernel"],
-                    "bytes_per_launch": per_launch}
+                    "bytes_per_launch": per_launch,
+                    "duration_us": round(float(d.mean() * 1e3), 3),
+                    "duration_source": f"mean of HIP event pairs around every {every}th launch of the timed "
+                                       "region, on the launch stream"}
         if W.get("traffic_bytes"):
             roofline["read_plus_write_GBs"] = round(W["traffic_bytes"] / (d.mean() * 1e-3) / 1e9, 1)
         if W.get("alu_flops"):
@@ -486,11 +561,51 @@ def main():
             roofline["matrix_core"] = {"useful_tflops": round(tf, 3), "fp4_dense_peak_tflops": FP4_PEAK_TFLOPS,
                                        "frac": round(tf / FP4_PEAK_TFLOPS, 6), "flops_per_launch": fl}
 
+    # interleaved rounds after the timed region (cold ring, warm = one copy
+    # repeated): A B B A ..., 50 steps each, with their spread
+    rounds = None
+    if args.rounds > 0 and W.get("ring"):
+        base = args.warmup + args.steps
+        vals = {"cold": [], "warm": []}
+        for r in range(args.rounds):
+            kind = "cold" if r % 4 in (0, 3) else "warm"
+            cs = [W["make"](base + 50 * r + i, copy=None if kind == "cold" else 0) for i in range(50)]
+            torch.cuda.synchronize()
+            hip.record(t0e, stream)
+            for c in cs:
+                c()
+            hip.record(t1e, stream)
+            torch.cuda.synchronize()
+            ms = hip.elapsed_ms(t0e, t1e)
+            vals[kind].append(sum(W["bytes"](base + 50 * r + i) for i in range(50)) / (ms * 1e-3) * scale)
+        rounds = {k: [round(v, 1) for v in vs] for k, vs in vals.items() if vs}
+        if vals["cold"]:
+            c = np.array(vals["cold"])
+            rounds["cold_median"] = round(float(np.median(c)), 1)
+            rounds["cold_spread_pct"] = round(100 * float((c.max() - c.min()) / np.median(c)), 2)
+            rounds["spread_over_5pct"] = bool(rounds["cold_spread_pct"] > 5.0)
+        if vals["warm"]:
+            rounds["warm_median"] = round(float(np.median(vals["warm"])), 1)
+        if W.get("status_check", True) and W.get("workspace") is not None:
+            if int(W["workspace"][:8].view(torch.int32)[1].item()):
+                raise SystemExit("bench.py: a wait timed out in the rounds (workspace status word set)")
+
+    # the practical read rate at this size: a plain device reduction over
+    # the same bytes per step, ring-walked like the steps
+    stream_peak = None
+    if "units" not in W and W.get("ring"):
+        gbs, us = stream_read_peak(int(np.mean([W["bytes"](s) for s in timed])), args.reuse_mb)
+        stream_peak = {"GBs": gbs, "us_per_step": us, "kernel": "torch.sum over the step's bytes (ring of copies)",
+                       "value_frac": round(value / gbs, 3)}
+
     cpu = None
     if not args.no_cpu_baseline:
-        v, sample = W["cpu"](args.cpu_seconds)
-        cpu = {"value": round(v, 6), "unit": W.get("units", "GB/s"), "cores": 1, "kind": "oracle",
-               "sample": sample}
+        n_cores, model = host_cpu()
+        v1, s1 = W["cpu"](args.cpu_seconds, 1)
+        vn, sn = W["cpu"](args.cpu_seconds, n_cores)
+        cpu = {"value": round(vn, 6), "unit": W.get("units", "GB/s"), "cores": n_cores, "kind": "oracle",
+               "sample": sn, "single_thread_value": round(v1, 6), "single_thread_sample": s1,
+               "cpu_model": model}
 
     if W.get("metric"):
         metric = W["metric"]
@@ -519,6 +634,9 @@ def main():
                        **{"wall_s": round(wall, 4)}),
         "launch": launch,
         "roofline": roofline,
+        "rounds": rounds,
+        "stream_read_peak": stream_peak,
+        "status_error": status_error,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

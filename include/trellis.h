@@ -109,6 +109,14 @@ size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols
                                        int32_t k);
 
 /*
+ * trellis_moe_gemv_workspace -- the same size for the matrix stack w itself
+ * (HEPH abstract, fused serving mode: one workspace per resident stack):
+ * trellis_moe_gemv_workspace_size(w->n_mat, w->rows, w->cols, T, k); 0 when
+ * w is NULL or describes no valid stack.
+ */
+size_t trellis_moe_gemv_workspace(const trellis_mat_t *w, int32_t T, int32_t k);
+
+/*
  * trellis_moe_gemv -- routed ("mixture-of-experts") GEMV / small-batch GEMM
  * with the weights decoded inside the kernel on every call (HEPH's fused
  * serving mode). Expert e's matrix is w[e] (n_mat experts).

@@ -41,5 +41,12 @@ def check_tol(y, y_ref, bound, what, tol=TOL):
     return ratio
 
 
+def sigmoid(z):
+    """1 / (1 + e^-z) without overflow for large |z|."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
 def silu(z):
-    return z / (1.0 + np.exp(-z))
+    return np.asarray(z, dtype=np.float64) * sigmoid(z)

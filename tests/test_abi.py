@@ -175,3 +175,27 @@ def test_router_argument_checks():
     assert call(wsb=16) == -3              # workspace too small
     assert lib.trellis_router_workspace_size(32, 1) == 256 + 32 * 8
     assert lib.trellis_router_workspace_size(0, 1) == 0
+
+
+def test_gemv_workspace_for_a_stack_matches_the_shape_query():
+    """trellis_moe_gemv_workspace(w, T, k) is the shape query for w's own shape."""
+    lib = tq.lib()
+    for n_mat, rows, cols, T, k in [(1, 256, 1024, 1, 1), (32, 5760, 2880, 1, 4), (128, 3072, 4096, 32, 8),
+                                    (3, 16, 32, 32, 8)]:
+        m = _mat(n_mat=n_mat, rows=rows, cols=cols)
+        assert lib.trellis_moe_gemv_workspace(ctypes.byref(m), T, k) == \
+            lib.trellis_moe_gemv_workspace_size(n_mat, rows, cols, T, k) > 0
+    assert lib.trellis_moe_gemv_workspace(None, 1, 1) == 0
+    assert lib.trellis_moe_gemv_workspace(ctypes.byref(_mat(cols=48)), 1, 1) == 0
+    assert lib.trellis_moe_gemv_workspace(ctypes.byref(_mat()), 0, 1) == 0
+
+
+def test_ffn_workspace_covers_the_single_token_region():
+    """The layer workspace holds the general kernel's layout and, after the
+    status words, the single-token kernel's region; larger for more tokens."""
+    lib = tq.lib()
+    one = lib.trellis_moe_ffn_workspace_size(32, 2880, 2880, 1, 4)
+    many = lib.trellis_moe_ffn_workspace_size(32, 2880, 2880, 8, 4)
+    # region: call counter line + tagged h of up to 32 experts + a tag per 16 rows of y
+    region = 256 + 32 * 2880 * 4 + (2880 // 16) * 4
+    assert one >= 256 + region and many > one

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import workloads
-from helpers import TOL, announce, check_tol, dev, silu, x_dev
+from helpers import TOL, announce, check_tol, dev, sigmoid, silu, x_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -111,7 +111,7 @@ def test_moe_gemv_repeat_is_deterministic(trellis_lib, orc):
 
 def _h_tolerance(g_ref, u_ref, bg, bu):
     """Bound on |h_gpu - silu(g)u| from the per-row GEMV bounds plus bf16 rounding."""
-    sig = 1.0 / (1.0 + np.exp(-g_ref))
+    sig = sigmoid(g_ref)
     dsilu = np.abs(sig * (1.0 + g_ref * (1.0 - sig)))
     tg, tu = TOL * bg, TOL * bu
     h = silu(g_ref) * u_ref

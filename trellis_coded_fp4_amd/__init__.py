@@ -25,7 +25,7 @@ ERRORS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_ENULL", -3: "TRELL
 
 # Every symbol include/trellis.h declares.
 EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
-           "trellis_moe_gemv_workspace_size", "trellis_moe_gemv",
+           "trellis_moe_gemv_workspace_size", "trellis_moe_gemv_workspace", "trellis_moe_gemv",
            "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
            "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn",
            "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_workspace_size",
@@ -71,6 +71,8 @@ def lib():
         L.trellis_decode_expand.restype = ctypes.c_int
         L.trellis_moe_gemv_workspace_size.argtypes = [I32] * 5
         L.trellis_moe_gemv_workspace_size.restype = SZ
+        L.trellis_moe_gemv_workspace.argtypes = [MP, I32, I32]
+        L.trellis_moe_gemv_workspace.restype = SZ
         L.trellis_moe_gemv.argtypes = [P, MP, P, I32, I32, P, P, I32, I32, P, P, SZ]
         L.trellis_moe_gemv.restype = ctypes.c_int
         L.trellis_moe_ffn_workspace_size.argtypes = [I32] * 5
@@ -119,6 +121,36 @@ def _stream(stream=None) -> int:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _on(stream):
+    """Context in which temporaries are allocated (and zero-filled) on the
+    stream the call is enqueued on, so that they are ordered before it and
+    the caching allocator keeps them for that stream."""
+    torch = _torch()
+    if stream is None:
+        import contextlib
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
+class WorkspaceError(RuntimeError):
+    """A call on this workspace found a wait that timed out (its status word
+    is set); its outputs are NaN until the workspace is zero-filled again."""
+
+
+def check_workspace(workspace, stream=None):
+    """Synchronise `stream` (default: current) and raise WorkspaceError if a
+    wait of a call on `workspace` timed out. Returns the number of routing
+    slots the last call skipped (expert id >= n_mat)."""
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    s.synchronize()
+    words = workspace[:8].view(torch.int32).cpu()
+    if int(words[1]) != 0:
+        raise WorkspaceError("a wait timed out in a call on this workspace (other work kept the kernel's "
+                             "workgroups from being resident); zero-fill the workspace before reusing it")
+    return int(words[0])
 
 
 def _check(t, dtype, name, shape=None):
@@ -180,10 +212,11 @@ def decode_expand(syms, scales, codes_out=None, scales_out=None, stream=None, pr
     """Expand to resident MXFP4: returns (codes [n_mat, rows, cols/2] uint8, scales copy)."""
     torch = _torch()
     m = mat(syms, scales)
-    if codes_out is None:
-        codes_out = torch.empty((m.n_mat, m.rows, m.cols // 2), dtype=torch.uint8, device=syms.device)
-    if scales_out is None:
-        scales_out = torch.empty((m.n_mat, m.rows, m.cols // 32), dtype=torch.uint8, device=syms.device)
+    with _on(stream):
+        if codes_out is None:
+            codes_out = torch.empty((m.n_mat, m.rows, m.cols // 2), dtype=torch.uint8, device=syms.device)
+        if scales_out is None:
+            scales_out = torch.empty((m.n_mat, m.rows, m.cols // 32), dtype=torch.uint8, device=syms.device)
     _check(codes_out, torch.uint8, "codes_out", (m.n_mat, m.rows, m.cols // 2))
     _check(scales_out, torch.uint8, "scales_out", (m.n_mat, m.rows, m.cols // 32))
     return _run(prepare, lib().trellis_decode_expand,
@@ -201,6 +234,7 @@ def _x_dtype(x):
 
 
 def gemv_workspace(n_mat, rows, cols, T, k, device="cuda"):
+    """A zero-filled workspace for trellis_moe_gemv (current stream)."""
     torch = _torch()
     n = lib().trellis_moe_gemv_workspace_size(n_mat, rows, cols, T, k)
     if n == 0:
@@ -209,6 +243,7 @@ def gemv_workspace(n_mat, rows, cols, T, k, device="cuda"):
 
 
 def ffn_workspace(n_exp, hidden, inter, T, k, device="cuda"):
+    """A zero-filled workspace for trellis_moe_ffn (current stream)."""
     torch = _torch()
     n = lib().trellis_moe_ffn_workspace_size(n_exp, hidden, inter, T, k)
     if n == 0:
@@ -227,11 +262,12 @@ def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, w
         _check(topk_w, torch.float32, "topk_w", (T, k))
     _check(x, x.dtype, "x", (T, k, m.cols) if x_per_slot else (T, m.cols))
     shape = (T, m.rows) if topk_w is not None else (T, k, m.rows)
-    if y is None:
-        y = torch.empty(shape, dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty(shape, dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
     _check(y, torch.float32, "y", shape)
-    if workspace is None:
-        workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
     return _run(prepare, lib().trellis_moe_gemv,
                 (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
@@ -242,8 +278,9 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
             workspace=None, stream=None, events=None, prepare=False):
     """Whole fused MoE layer; returns (y [T, hidden] fp32, h [T, k, inter] bf16).
 
-    ``events``: optional ctypes array of 4 hipEvent_t recorded at the stage
-    boundaries (see trellis_moe_ffn_timed)."""
+    ``events``: optional ctypes array of hipEvent_t; events[0] and events[1]
+    are recorded on the stream just before and just after the layer kernel
+    (see trellis_moe_ffn_timed)."""
     torch = _torch()
     mg = mat(gu_syms, gu_scales)
     md = mat(dn_syms, dn_scales)
@@ -253,14 +290,15 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
         _check(topk_w, torch.float32, "topk_w", (T, k))
     hidden, inter = mg.cols, mg.rows // 2
     _check(x, x.dtype, "x", (T, hidden))
-    if h is None:
-        h = torch.empty((T, k, inter), dtype=torch.bfloat16, device=x.device)
+    with _on(stream):
+        if h is None:
+            h = torch.empty((T, k, inter), dtype=torch.bfloat16, device=x.device)
+        if y is None:
+            y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
     _check(h, torch.bfloat16, "h", (T, k, inter))
-    if y is None:
-        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
     _check(y, torch.float32, "y", (T, hidden))
-    if workspace is None:
-        workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
     return _run(prepare, lib().trellis_moe_ffn_timed,
                 (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
@@ -295,11 +333,12 @@ def mxfp4_moe_gemv(codes, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=
         _check(topk_w, torch.float32, "topk_w", (T, k))
     _check(x, x.dtype, "x", (T, k, m.cols) if x_per_slot else (T, m.cols))
     shape = (T, m.rows) if topk_w is not None else (T, k, m.rows)
-    if y is None:
-        y = torch.empty(shape, dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty(shape, dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
     _check(y, torch.float32, "y", shape)
-    if workspace is None:
-        workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
     return _run(prepare, lib().trellis_mxfp4_moe_gemv,
                 (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
@@ -318,14 +357,15 @@ def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=
         _check(topk_w, torch.float32, "topk_w", (T, k))
     hidden, inter = mg.cols, mg.rows // 2
     _check(x, x.dtype, "x", (T, hidden))
-    if h is None:
-        h = torch.empty((T, k, inter), dtype=torch.bfloat16, device=x.device)
+    with _on(stream):
+        if h is None:
+            h = torch.empty((T, k, inter), dtype=torch.bfloat16, device=x.device)
+        if y is None:
+            y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
     _check(h, torch.bfloat16, "h", (T, k, inter))
-    if y is None:
-        y = torch.empty((T, hidden), dtype=torch.float32, device=x.device)
     _check(y, torch.float32, "y", (T, hidden))
-    if workspace is None:
-        workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
     return _run(prepare, lib().trellis_mxfp4_moe_ffn,
                 (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
@@ -351,14 +391,15 @@ def viterbi_encode(target, d=None, syms_out=None, cost_out=None, workspace=None,
     rows, n = target.shape
     if d is not None:
         _check(d, torch.float64, "d", (rows, n))
-    if syms_out is None:
-        syms_out = torch.empty((rows, n), dtype=torch.uint8, device=target.device)
-    if cost_out is None:
-        cost_out = torch.empty((rows,), dtype=torch.float64, device=target.device)
+    with _on(stream):
+        if syms_out is None:
+            syms_out = torch.empty((rows, n), dtype=torch.uint8, device=target.device)
+        if cost_out is None:
+            cost_out = torch.empty((rows,), dtype=torch.float64, device=target.device)
+        if workspace is None:
+            workspace = viterbi_workspace(rows, n, device=target.device)
     _check(syms_out, torch.uint8, "syms_out", (rows, n))
     _check(cost_out, torch.float64, "cost_out", (rows,))
-    if workspace is None:
-        workspace = viterbi_workspace(rows, n, device=target.device)
     return _run(prepare, lib().trellis_viterbi_encode,
                 (_stream(stream), target.data_ptr(), _ptr(d), rows, n, syms_out.data_ptr(), cost_out.data_ptr(),
                  workspace.data_ptr(), workspace.numel() * workspace.element_size()),
@@ -384,14 +425,15 @@ def router_topk(x, w_router, k, topk_ids=None, topk_w=None, workspace=None, stre
     E = w_router.shape[0]
     if w_router.shape[1] != H:
         raise ValueError("w_router must be [E, H] with the same H as x")
-    if topk_ids is None:
-        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-    if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if topk_ids is None:
+            topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        if topk_w is None:
+            topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = router_workspace(E, T, device=x.device)
     _check(topk_ids, torch.int32, "topk_ids", (T, k))
     _check(topk_w, torch.float32, "topk_w", (T, k))
-    if workspace is None:
-        workspace = router_workspace(E, T, device=x.device)
     return _run(prepare, lib().trellis_router_topk,
                 (_stream(stream), x.data_ptr(), _x_dtype(x), w_router.data_ptr(), E, H, T, k,
                  topk_ids.data_ptr(), topk_w.data_ptr(), workspace.data_ptr(),

@@ -21,10 +21,12 @@
 //   stage-2 items  a layer's down projection; its columns are the h splits
 //                  of the expert's slots, copied into LDS once every
 //                  stage-1 item of that expert has finished.
-// Combine: per-slot partial outputs go to the workspace; the item that
-// arrives last at a 64-row output tile (a counter per tile) sums them with
-// the gate weights, in slot order, into y. No atomics touch outputs and the
-// summation order is fixed, so results are deterministic.
+// Combine: in the routed GEMV with gate weights, per-slot partial outputs
+// go to the workspace and the item that arrives last at a 64-row output
+// tile (a counter per tile) sums them with the gate weights, in slot order,
+// into y (deterministic). In a layer, the down-projection items add their
+// gate-weighted rows into y with device-scope float atomics, so the order
+// of a token's k terms, and the last bits of y, can vary between calls.
 //
 // Synchronisation costs no grid-wide barrier: counters live one per
 // 128-byte line (device-scope atomics on one address serialise), each is

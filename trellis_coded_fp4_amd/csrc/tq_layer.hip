@@ -11,6 +11,11 @@ extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, i
   return make_layout<FmtTrellis>(0, (rows + 63) / 64, T * k, rows, 0, T, cols).total;
 }
 
+extern "C" size_t trellis_moe_gemv_workspace(const trellis_mat_t *w, int32_t T, int32_t k) {
+  if (!w) return 0;
+  return trellis_moe_gemv_workspace_size(w->n_mat, w->rows, w->cols, T, k);
+}
+
 extern "C" int trellis_moe_gemv(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
                                 int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w,
                                 int32_t T, int32_t k, float *y, void *workspace, size_t workspace_bytes) {

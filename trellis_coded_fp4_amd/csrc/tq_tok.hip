@@ -78,7 +78,7 @@ struct Args {
 // Timeline instrumentation, compiled in only with -DTQ_TRACE: thread 0 of
 // each workgroup stamps s_memrealtime at the phase boundaries.
 #ifdef TQ_TRACE
-#define TOK_MARK_T(k, t) do { if (threadIdx.x == (t) && a.trace) a.trace[blockIdx.x * 16 + (k)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define TOK_MARK_T(k, t) do { if (threadIdx.x == (t)) S.trace[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #define TOK_MARK(k) TOK_MARK_T(k, 0)
 static unsigned long long *g_tok_trace = nullptr;
 #else
@@ -100,6 +100,10 @@ struct Smem {
   int x_ready;      // the call tag is in LDS
   int up_issued;    // gate/up waves that have issued all their loads
   int up_done;      // gate/up waves that have stored their partial sums
+  int down_done;    // down waves that have stored theirs
+#ifdef TQ_TRACE
+  unsigned long long trace[16];   // phase stamps, copied out at the end
+#endif
 };
 
 __device__ __forceinline__ uint64_t ld_dc64(const uint64_t *p) {
@@ -150,12 +154,15 @@ __device__ __forceinline__ void split_block8(const float (&f)[8], int b, int j, 
 #pragma unroll
   for (int i = 0; i < 8; i += 2) lo[i / 2] = f32x2_to_e4m3(ldexpf(res[i], -El), ldexpf(res[i + 1], -El));
   if (!store) return;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int off = act_offset(b, 8 * j + i);
-    lq[off] = (uint8_t)(hi[i / 2] >> (8 * (i & 1)));
-    lq[(size_t)psteps * 128 + off] = (uint8_t)(lo[i / 2] >> (8 * (i & 1)));
-  }
+  // values 8j + 2m (m = 0..3) sit at four consecutive bytes of the chunk,
+  // values 8j + 2m + 1 eight bytes further on (the decoder's even/odd order)
+  const int off = act_offset(b, 8 * j);
+  const uint32_t h01 = hi[0] | hi[1] << 16, h23 = hi[2] | hi[3] << 16;
+  const uint32_t l01 = lo[0] | lo[1] << 16, l23 = lo[2] | lo[3] << 16;
+  *(uint32_t *)(lq + off) = __builtin_amdgcn_perm(h23, h01, 0x06040200u);
+  *(uint32_t *)(lq + off + 8) = __builtin_amdgcn_perm(h23, h01, 0x07050301u);
+  *(uint32_t *)(lq + (size_t)psteps * 128 + off) = __builtin_amdgcn_perm(l23, l01, 0x06040200u);
+  *(uint32_t *)(lq + (size_t)psteps * 128 + off + 8) = __builtin_amdgcn_perm(l23, l01, 0x07050301u);
   if (j == 0) {
     ls[act_scale_index(b)] = (uint8_t)(E + 127);
     ls[(size_t)psteps * 4 + act_scale_index(b)] = (uint8_t)(El + 127);
@@ -269,10 +276,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     S.x_ready = 0;
     S.up_issued = 0;
     S.up_done = 0;
+    S.down_done = 0;
   }
   __syncthreads();   // (nothing is in flight yet)
 #ifdef TQ_TRACE
-  if (tid == 0 && a.trace) a.trace[blockIdx.x * 16] = t_entry;
+  if (tid == 0) S.trace[0] = t_entry;
 #endif
 
   // ---- routing inputs (every wave), x and the call counter (down waves).
@@ -303,9 +311,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     err0 = __hip_atomic_load(&a.status[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- routing, in every wave's registers: lane s (< k) is slot s. Active
-  // experts in order of first occurrence; a duplicate slot shares its
-  // expert's units and adds its gate weight to it.
+  // ---- routing, in every wave's registers: lane s (< k; lanes 32-63
+  // mirror 0-31) is slot s. Active experts in order of first occurrence; a
+  // duplicate slot adds its gate weight to its expert's, in slot order.
   const bool valid = sl < a.k && idv >= 0 && idv < a.E;
   const int e_me = valid ? idv : -1;
   const float gw_me = a.gate_w ? gwr : 1.0f;
@@ -323,46 +331,31 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
       }
     }
   }
-  const uint64_t fm = __ballot(first) & 0xFFFFFFFFull;
-  const int n_skipped = __popcll(__ballot(sl < a.k && idv >= a.E) & 0xFFFFFFFFull);
-  const int n_act = __popcll(fm);
-  const int rank = __popcll(fm & ((1ull << dup_of) - 1ull));   // active index of this slot's expert
-  auto act_lane = [&](int r) {   // lane holding active expert r
-    uint64_t m = fm;
-    for (int i = 0; i < r; ++i) m &= m - 1ull;
-    return (int)__builtin_ctzll(m | (1ull << 63));
-  };
-  auto act_expert = [&](int r) { return __builtin_amdgcn_readlane(e_me, act_lane(r)); };
+  const uint32_t fm = (uint32_t)__ballot(first);
+  const int n_skipped = __popc((uint32_t)__ballot(sl < a.k && idv >= a.E));
+  const int n_act = __popc(fm);
+  const int rank = __popc(fm & ((1u << dup_of) - 1u));   // active index of this slot's expert
+  // lane r < n_act receives active expert r and its summed gate weight (a
+  // forward permutation: first occurrences to their rank, the other low
+  // lanes after them, the high lanes to themselves)
+  const int dst = lane >= 32 ? lane : first ? rank : n_act + __popc(~fm & ((1u << sl) - 1u));
+  const int act_e = __builtin_amdgcn_ds_permute(dst << 2, e_me);
+  const float act_g = __int_as_float(__builtin_amdgcn_ds_permute(dst << 2, __float_as_int(gsum)));
   TOK_MARK(1);
 
   // ---- this workgroup's units: pairs [p0, p0 + np), down tiles [d0, d0 + nd)
-  const int NP = n_act * pr_per, ND = n_act * rt_per;
-  const int p0 = (int)((long long)w * NP / G), np = (int)((long long)(w + 1) * NP / G) - p0;
+  const uint32_t NP = (uint32_t)n_act * pr_per, ND = (uint32_t)n_act * rt_per;
   const int wd = G - 1 - w;
-  const int d0 = (int)((long long)wd * ND / G), nd = (int)((long long)(wd + 1) * ND / G) - d0;
+  const int p0 = (int)((uint32_t)w * NP / (uint32_t)G), np = (int)((uint32_t)(w + 1) * NP / (uint32_t)G) - p0;
+  const int d0 = (int)((uint32_t)wd * ND / (uint32_t)G), nd = (int)((uint32_t)(wd + 1) * ND / (uint32_t)G) - d0;
   const int n1 = 2 * np;
-  // first matrix row of every tile (gate/up tiles: gate even, up odd; then
-  // down tiles); positions past the workgroup's tiles repeat a valid tile
-  size_t row[T1 + T2];
-#pragma unroll
-  for (int t = 0; t < T1; ++t) {
-    const int tc = n1 > 0 ? min(t, n1 - 1) : 0;
-    const int u = p0 + (tc >> 1), ai = u / pr_per, j = u - ai * pr_per;
-    row[t] = n1 > 0 ? (size_t)act_expert(ai) * 2 * I + (tc & 1 ? I : 0) + 16 * j : 0;
-  }
-#pragma unroll
-  for (int t = 0; t < T2; ++t) {
-    const int tc = nd > 0 ? min(t, nd - 1) : 0;
-    const int d = d0 + tc, ai = d / rt_per, rt = d - ai * rt_per;
-    row[T1 + t] = nd > 0 ? (size_t)act_expert(ai) * H + 16 * rt : 0;
-  }
   // this wave's pieces [pa, pa + c) of each of its role's tiles
   const int J = up_role ? J1 : J2;
   const int pa = min(rw * PPW, J), c = min(J - pa, PPW);
-  auto load_tile = [&](int t) -> TileLd<PPW> {   // tile position t (0 .. T1 + T2 - 1)
+  // loads of the tile whose first row is `r0` (gate/up matrix if s1)
+  auto load_tile = [&](size_t r0, bool s1) -> TileLd<PPW> {
     TileLd<PPW> L;
-    const bool s1 = t < T1;
-    const size_t r = row[t] + i16;
+    const size_t r = r0 + i16;
     const uint32_t *rp = s1 ? a.w1 + r * wpr1 : a.w2 + r * wpr2;
     const uint8_t *sp = s1 ? a.s1 + r * nb1 : a.s2 + r * nb2;
     const int wpr = s1 ? wpr1 : wpr2, nb = s1 ? nb1 : nb2;
@@ -381,14 +374,29 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   uint32_t tag;
   bool poisoned;
   if (up_role) {
-    // ---- gate/up tiles, AT loads ahead
+    // ---- gate/up tiles, AT loads ahead. Tile t: gate rows (t even) or up
+    // rows (t odd) of pair p0 + t/2 = (active expert ai0, 16-row group j0)
+    // advanced by t/2; positions past the workgroup's tiles repeat its last.
     __builtin_amdgcn_s_setprio(2);
+    const int ai0 = p0 / pr_per, j0 = p0 - ai0 * pr_per;
+    size_t row[T1];
+#pragma unroll
+    for (int t = 0; t < T1; ++t) {
+      const int tc = n1 > 0 ? min(t, n1 - 1) : 0;
+      int j = j0 + (tc >> 1), ai = ai0;
+      if (j >= pr_per) {   // t/2 < kMaxPairs <= pr_per: one wrap at most
+        j -= pr_per;
+        ++ai;
+      }
+      row[t] = n1 > 0 ? (size_t)__builtin_amdgcn_readlane(act_e, ai) * 2 * I + (tc & 1 ? I : 0) + 16 * j : 0;
+    }
     TileLd<PPW> R[AT];
 #pragma unroll
-    for (int t = 0; t < AT; ++t) R[t] = load_tile(t);
+    for (int t = 0; t < AT; ++t) R[t] = load_tile(row[t], true);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     if (AT >= T1 && lane == 0) __hip_atomic_fetch_add(&S.up_issued, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    TOK_MARK(3);
     // split this wave's blocks of x into LDS (blocks past K, up to the last
     // piece, get zero codes); the wave reads them back itself
 #pragma unroll
@@ -417,7 +425,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     for (int t = 0; t < T1; ++t) {
       const TileLd<PPW> cur = R[t % AT];
       if (t + AT < T1) {
-        R[t % AT] = load_tile(t + AT);
+        R[t % AT] = load_tile(row[t + AT], true);
         if (t + AT == T1 - 1 && lane == 0)
           __hip_atomic_fetch_add(&S.up_issued, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
@@ -462,12 +470,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
         float gs = 0.0f, us = 0.0f;
 #pragma unroll
         for (int v = 0; v < NR; ++v) {
-          gs += S.red1[2 * uo][v][r];
-          us += S.red1[2 * uo + 1][v][r];
+          if (v * PPW < J1) {
+            gs += S.red1[2 * uo][v][r];
+            us += S.red1[2 * uo + 1][v][r];
+          }
         }
         const float silu = gs / (1.0f + expf(-gs));
         const uint32_t hb = f32_to_bf16_rne(silu * us);
-        const int u = p0 + uo, ai = u / pr_per, j = u - ai * pr_per;
+        const int jj = j0 + uo, ai = jj >= pr_per ? ai0 + 1 : ai0, j = jj >= pr_per ? jj - pr_per : jj;
         const int col = 16 * j + r;
         // two values per tagged word: the even row's lane stores
         const uint32_t hb_next = __shfl_down(hb, 1, 64);
@@ -480,12 +490,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     }
     TOK_MARK(5);
   } else {
-    // clear this workgroup's tiles of y (tagged once the zeros are at the
-    // coherence point, after the down tiles are decoded)
-    if (rw == 0)
-      for (int rt = w; rt < rt_per; rt += G)
-        if (lane < 16) __hip_atomic_store(&a.y[16 * rt + lane], err0 ? __builtin_nanf("") : 0.0f,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     tag = epoch + 1u;   // 1 .. 2^32 - 1 (the counter skips 2^32 - 1)
     poisoned = err0 != 0;
     if (rtid == 0) {
@@ -495,13 +499,51 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     // the tag is in LDS before the flag goes up
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (rtid == 0) __hip_atomic_store(&S.x_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // clear this workgroup's tiles of y, tag them once the zeros are at the
+    // coherence point, and count the workgroup in; the last workgroup to
+    // count in advances the call counter (every workgroup read it first)
+    if (rw == 0) {
+      for (int rt = w; rt < rt_per; rt += G)
+        if (lane < 16) __hip_atomic_store(&a.y[16 * rt + lane], err0 ? __builtin_nanf("") : 0.0f,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      uint32_t seen_old = 0;
+      if (lane == 0) {
+        for (int rt = w; rt < rt_per; rt += G) st_dc32(a.yz + rt, tag);
+        seen_old = __hip_atomic_fetch_add(&a.sync[32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen_old == (uint32_t)(G - 1)) {
+          st_dc32(&a.sync[32], 0u);
+          st_dc32(&a.sync[0], epoch + 1u == 0xFFFFFFFFu ? 0u : epoch + 1u);
+        }
+      }
+    }
+    TOK_MARK_T(7, 256);
+    // down tile t: 16-row group rt[t] of active expert dai[t] (from d0,
+    // advanced by t; positions past the workgroup's tiles repeat its last)
+    int dai[T2], drt[T2];
+    {
+      const int ai0 = d0 / rt_per;
+      int ai = ai0, rt = d0 - ai0 * rt_per;
+#pragma unroll
+      for (int t = 0; t < T2; ++t) {
+        if (t > 0 && t < nd) {
+          if (++rt == rt_per) {
+            rt = 0;
+            ++ai;
+          }
+        }
+        dai[t] = ai;
+        drt[t] = rt;
+      }
+    }
     // ---- down tiles: loads once every gate/up load is issued, then the decode
     while (__hip_atomic_load(&S.up_issued, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NR)
       __builtin_amdgcn_s_sleep(2);
     asm volatile("" ::: "memory");
     TileLd<PPW> L2[T2];
 #pragma unroll
-    for (int t = 0; t < T2; ++t) L2[t] = load_tile(T1 + t);
+    for (int t = 0; t < T2; ++t)
+      L2[t] = load_tile(nd > 0 ? (size_t)__builtin_amdgcn_readlane(act_e, dai[t]) * H + 16 * drt[t] : 0, false);
 #pragma unroll
     for (int t = 0; t < T2; ++t) {
       if (!poisoned && t < nd && c > 0) {
@@ -519,110 +561,133 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
       }
     }
     TOK_MARK_T(6, 256);
-    // count the workgroup in and tag its tiles of y (the zeros were stored
-    // at entry; this wait also covers them)
-    if (rw == 0) {
-      uint32_t seen_old = 0;
-      if (lane == 0) seen_old = __hip_atomic_fetch_add(&a.sync[32], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-      for (int rt = w; rt < rt_per; rt += G)
-        if (lane == 0) st_dc32(a.yz + rt, tag);
-      // the last workgroup to count in advances the call counter (every
-      // workgroup read it before counting in)
-      if (lane == 0 && seen_old == (uint32_t)(G - 1)) {
-        st_dc32(&a.sync[32], 0u);
-        st_dc32(&a.sync[0], epoch + 1u == 0xFFFFFFFFu ? 0u : epoch + 1u);
-      }
-    }
-    TOK_MARK_T(7, 256);
-  }
-
-  // ---- h of the experts of this workgroup's down tiles, polled as tagged
-  // words (all waves) and split into LDS columns (2 ex, 2 ex + 1) for expert a_lo + ex
-  const int a_lo = nd > 0 ? d0 / rt_per : 0;
-  const int n_ex = nd > 0 ? (d0 + nd - 1) / rt_per - a_lo + 1 : 0;
-  constexpr int kHPass = (8 * kMaxJ + 16 * NW - 1) / (16 * NW);
-  for (int ex = 0; ex < n_ex && !poisoned; ++ex) {
-    const int ai = a_lo + ex;
-    uint64_t v[kHPass][4];
-    for (unsigned it = 0;; ++it) {
-      bool ok = true;
+    // ---- this wave's part of h (the K range of its pieces) for each expert
+    // of the workgroup's down tiles, polled as tagged words and split into
+    // LDS columns (2 ex, 2 ex + 1): blocks 8 pa .. 8 (pa + c) - 1, four lanes
+    // each, 16 per pass. No other wave reads them, so no barrier.
+    const int a_lo = dai[0];
+    const int n_ex = nd > 0 ? dai[T2 - 1] - a_lo + 1 : 0;
+    constexpr int kHPass = (8 * PPW + 15) / 16;
+    // the tags of this workgroup's tiles of y (stored at entry by the
+    // workgroups that cleared them): loaded here, checked once h is in
+    int rt_l = drt[0];
 #pragma unroll
-      for (int ps = 0; ps < kHPass; ++ps) {
-        const int hb = ps * 16 * NW + (tid >> 2), hj = tid & 3;
-        const uint64_t *hsrc = a.hx + ((size_t)ai * I + 32 * (hb < nb2 ? hb : 0) + 8 * hj) / 2;
+    for (int t = 1; t < T2; ++t)
+      if (lane == t) rt_l = drt[t];
+    uint32_t yzv = lane < nd ? ld_dc32(a.yz + rt_l) : tag;
+    for (int ex = 0; ex < n_ex && !poisoned && c > 0; ++ex) {
+      const int ai = a_lo + ex;
+      uint64_t v[kHPass][4];
+      for (unsigned it = 0;; ++it) {
+        bool ok = true;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[ps][q] = ld_dc64(hsrc + q);
-          ok = ok && (hb >= nb2 || (uint32_t)(v[ps][q] >> 32) == tag);
-        }
-      }
-      if (__syncthreads_and(ok)) break;
-      if (it >= kPolls) {
-        if (tid == 0) set_error(a.status);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
+        for (int ps = 0; ps < kHPass; ++ps) {
+          const int hb = 8 * pa + 16 * ps + (lane >> 2), hj = lane & 3;
+          const bool live = hb < min(nb2, 8 * (pa + c));
+          const uint64_t *hsrc = a.hx + ((size_t)ai * I + 32 * (live ? hb : 8 * pa) + 8 * hj) / 2;
 #pragma unroll
-    for (int ps = 0; ps < kHPass; ++ps) {
-      const int hb = ps * 16 * NW + (tid >> 2), hj = tid & 3;
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        f[i] = hb < nb2 ? __uint_as_float(((uint32_t)(v[ps][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16) : 0.0f;
-      split_block8(f, hb, hj, S.hq + (size_t)(2 * ex) * ps2 * 128, S.hs + (size_t)(2 * ex) * ps2 * 4, ps2,
-                   hb < 8 * J2);
-    }
-  }
-  __syncthreads();
-  TOK_MARK(8);
-
-  // ---- down projection (down waves): matrix-core steps on the pre-decoded pieces
-  if (!up_role) {
-#pragma unroll
-    for (int t = 0; t < T2; ++t) {
-      if (!poisoned && t < nd && c > 0) {
-        const int ex = (d0 + t) / rt_per - a_lo;
-        const int col = 2 * ex + (i16 & 1);
-        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < PPW; ++q) {
-          if (q < c) {
-            const BOp b0 = read_b(S.hq, S.hs, ps2, col, 2 * (pa + q), g);
-            const BOp b1 = read_b(S.hq, S.hs, ps2, col, 2 * (pa + q) + 1, g);
-            acc = mma2(D2[t][q], b0, b1, sc2[t][q], acc);
+          for (int q = 0; q < 4; ++q) {
+            v[ps][q] = ld_dc64(hsrc + q);
+            ok = ok && (!live || (uint32_t)(v[ps][q] >> 32) == tag);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = pair_sum(acc[r]);
-          if (i16 == 0) S.red2[t][rw][4 * g + r] = v;
+        if (__ballot(!ok) == 0ull) break;
+        if (it >= kPolls) {
+          if (lane == 0) set_error(a.status);
+          break;
         }
+        __builtin_amdgcn_s_sleep(2);
+      }
+#pragma unroll
+      for (int ps = 0; ps < kHPass; ++ps) {
+        const int hb = 8 * pa + 16 * ps + (lane >> 2), hj = lane & 3;
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          f[i] = hb < nb2 ? __uint_as_float(((uint32_t)(v[ps][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16) : 0.0f;
+        split_block8(f, hb, hj, S.hq + (size_t)(2 * ex) * ps2 * 128, S.hs + (size_t)(2 * ex) * ps2 * 4, ps2,
+                     hb < 8 * (pa + c));
       }
     }
-  }
-  __syncthreads();
-  TOK_MARK(9);
-
-  // ---- y += gate weight x row, once the tile is cleared in this call
-  for (int q = tid; q < 16 * nd && !poisoned; q += 64 * NW) {
-    const int t = q >> 4, r = q & 15;
-    float v = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < NR; ++wv) v += S.red2[t][wv][r];
-    const int d = d0 + t, ai = d / rt_per, rt = d - ai * rt_per;
-    const float gw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsum), act_lane(ai)));
-    for (unsigned it = 0; ld_dc32(a.yz + rt) != tag; ++it) {
+    for (unsigned it = 0; __ballot(yzv != tag) != 0ull; ++it) {
       if (it >= kPolls) {
-        set_error(a.status);
+        if (lane == 0) set_error(a.status);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
+      if (lane < nd) yzv = ld_dc32(a.yz + rt_l);
     }
-    __hip_atomic_fetch_add(a.y + 16 * rt + r, gw * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    TOK_MARK_T(8, 256);
+    // ---- down projection: matrix-core steps on the pre-decoded pieces, one
+    // accumulator chain per tile, a piece's h operands read once per expert
+    if (!poisoned && nd > 0 && c > 0) {
+      v4f acc[T2];
+#pragma unroll
+      for (int t = 0; t < T2; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) {
+        if (q < c) {
+          const int st = 2 * (pa + q);
+          const BOp b00 = read_b(S.hq, S.hs, ps2, i16 & 1, st, g);
+          const BOp b01 = read_b(S.hq, S.hs, ps2, i16 & 1, st + 1, g);
+          BOp b10 = b00, b11 = b01;
+          if (n_ex > 1) {
+            b10 = read_b(S.hq, S.hs, ps2, 2 + (i16 & 1), st, g);
+            b11 = read_b(S.hq, S.hs, ps2, 2 + (i16 & 1), st + 1, g);
+          }
+#pragma unroll
+          for (int t = 0; t < T2; ++t) {
+            if (t < nd) {
+              if (dai[t] == a_lo)
+                acc[t] = mma2(D2[t][q], b00, b01, sc2[t][q], acc[t]);
+              else
+                acc[t] = mma2(D2[t][q], b10, b11, sc2[t][q], acc[t]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < T2; ++t) {
+        if (t < nd) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = pair_sum(acc[t][r]);
+            if (i16 == 0) S.red2[t][rw][4 * g + r] = v;
+          }
+        }
+      }
+    }
+    TOK_MARK_T(9, 256);
+    // ---- the last down wave to finish adds the gate-weighted rows into y
+    // (every down wave saw the tiles cleared in this call; the partial sums
+    // of the other waves are in LDS: they were stored before those waves
+    // counted)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    int arrived = 0;
+    if (lane == 0) arrived = __hip_atomic_fetch_add(&S.down_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    arrived = __builtin_amdgcn_readfirstlane(arrived);
+    if (arrived == NR - 1 && !poisoned) {
+      asm volatile("" ::: "memory");
+      for (int q = lane; q < 16 * nd; q += 64) {
+        const int t = q >> 4, r = q & 15;
+        float v = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < NR; ++wv)
+          if (wv * PPW < J2) v += S.red2[t][wv][r];
+        int rt = drt[0];
+        float gw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(act_g), dai[0]));
+#pragma unroll
+        for (int tt = 1; tt < T2; ++tt)
+          if (t == tt) {
+            rt = drt[tt];
+            gw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(act_g), dai[tt]));
+          }
+        __hip_atomic_fetch_add(a.y + 16 * rt + r, gw * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    TOK_MARK_T(10, 256);
   }
-  TOK_MARK(10);
 
   // ---- once per call: skipped-slot count, h rows of dead slots
   if (w == 0) {
@@ -631,7 +696,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
       if (!__builtin_amdgcn_readlane((int)valid, s))
         for (int cc = tid; cc < I; cc += 64 * NW) a.h[(size_t)s * I + cc] = 0;
   }
-  TOK_MARK(11);
+  TOK_MARK_T(11, 256);
+#ifdef TQ_TRACE
+  __syncthreads();
+  if (tid < 12 && a.trace) a.trace[blockIdx.x * 16 + tid] = S.trace[tid];
+#endif
 }
 
 // Kernel instances: (pieces per wave, gate/up tiles, down tiles).
