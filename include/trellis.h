@@ -185,6 +185,35 @@ int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,
                           hipEvent_t *events);
 
 /*
+ * trellis_moe_ffn_noalloc -- trellis_moe_ffn for callers that cannot allocate
+ * device memory or hand over a workspace: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation. The
+ * workspace is the library's own device array of
+ * TRELLIS_NOALLOC_SCRATCH_BYTES bytes, one per device (the current device
+ * at the call; `stream` must belong to it), zero-filled when the library is
+ * loaded and held until the process ends. Since calls of every shape share
+ * it, each call first zeroes the counters and tagged words its shape uses,
+ * with a small fill kernel enqueued on `stream` ahead of the layer kernel
+ * (no memset node, so the pair can be captured into a graph). The call
+ * allocates and frees nothing and synchronises nothing.
+ *   Arguments, outputs (h, y), accuracy and the other errors: as for
+ *   trellis_moe_ffn.
+ *   TRELLIS_EWORKSPACE: the shape needs more than the array holds, i.e.
+ *   trellis_moe_ffn_workspace_size(n_exp, hidden, inter, T, k) >
+ *   TRELLIS_NOALLOC_SCRATCH_BYTES; nothing is enqueued.
+ *   TRELLIS_EHIP: the array's device address could not be obtained.
+ * Every call on a device uses that device's one array: calls that overlap in
+ * time on one device (on different streams, or from different threads
+ * without ordering) race and give wrong results. A wait that times out sets
+ * the array's sticky error word (see the workspace note above), after which
+ * every later call on that device writes NaN to y until the process ends.
+ */
+#define TRELLIS_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int trellis_moe_ffn_noalloc(hipStream_t stream, const trellis_mat_t *w_gate_up, const trellis_mat_t *w_down,
+                            const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,
+                            int32_t T, int32_t k, uint16_t *h, float *y);
+
+/*
  * Expand serving mode, second half (HEPH abstract: the expanded MXFP4 weights
  * feed a grouped mixture-of-experts kernel): the same routed GEMV / layer as
  * above, on weights that trellis_decode_expand has already turned into

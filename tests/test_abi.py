@@ -103,6 +103,21 @@ def test_ffn_argument_checks():
     assert call(wsb=100) == -3
 
 
+def test_ffn_noalloc_rejects_what_its_scratch_cannot_hold():
+    """trellis_moe_ffn_noalloc checks the shape's workspace need against its
+    fixed scratch before anything is enqueued."""
+    lib = tq.lib()
+    # 128 experts, hidden 4096, inter 4096, 128 tokens x top-8: ~9.8 MB
+    gu, dn = _mat(n_mat=128, rows=8192, cols=4096), _mat(n_mat=128, rows=4096, cols=4096)
+    assert lib.trellis_moe_ffn_workspace_size(128, 4096, 4096, 128, 8) > tq.NOALLOC_SCRATCH_BYTES
+    rc = lib.trellis_moe_ffn_noalloc(None, ctypes.byref(gu), ctypes.byref(dn), FAKE, 1, FAKE, None, 128, 8,
+                                     FAKE, FAKE)
+    assert rc == -3
+    assert lib.trellis_moe_ffn_noalloc(None, None, ctypes.byref(dn), FAKE, 1, FAKE, None, 1, 1, FAKE, FAKE) == -2
+    assert lib.trellis_moe_ffn_noalloc(None, ctypes.byref(gu), ctypes.byref(dn), FAKE, 1, FAKE, None, 1, 0,
+                                       FAKE, FAKE) == -1
+
+
 def test_workspace_sizes():
     lib = tq.lib()
     a = lib.trellis_moe_gemv_workspace_size(32, 5760, 2880, 1, 4)

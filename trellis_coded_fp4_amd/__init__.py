@@ -27,6 +27,7 @@ ERRORS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_ENULL", -3: "TRELL
 EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_gemv_workspace_size", "trellis_moe_gemv_workspace", "trellis_moe_gemv",
            "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
+           "trellis_moe_ffn_noalloc",
            "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn",
            "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_workspace_size",
            "trellis_router_topk"]
@@ -81,6 +82,8 @@ def lib():
         L.trellis_moe_ffn.restype = ctypes.c_int
         L.trellis_moe_ffn_timed.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P, P, SZ, P]
         L.trellis_moe_ffn_timed.restype = ctypes.c_int
+        L.trellis_moe_ffn_noalloc.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P]
+        L.trellis_moe_ffn_noalloc.restype = ctypes.c_int
         XP = ctypes.POINTER(MxMat)
         L.trellis_mxfp4_moe_gemv.argtypes = [P, XP, P, I32, I32, P, P, I32, I32, P, P, SZ]
         L.trellis_mxfp4_moe_gemv.restype = ctypes.c_int
@@ -304,6 +307,35 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
                  workspace.numel(), events),
                 "trellis_moe_ffn", (y, h), (mg, md, events))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # TRELLIS_NOALLOC_SCRATCH_BYTES
+
+
+def moe_ffn_noalloc(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w, h, y, stream=None,
+                    prepare=False):
+    """moe_ffn on the library's own per-device scratch (trellis_moe_ffn_noalloc):
+    the caller passes the outputs h [T, k, inter] bf16 and y [T, hidden] fp32,
+    and nothing is allocated. Returns (y, h)."""
+    torch = _torch()
+    mg = mat(gu_syms, gu_scales)
+    md = mat(dn_syms, dn_scales)
+    T, k = topk_ids.shape
+    _check(topk_ids, torch.int32, "topk_ids")
+    if topk_w is not None:
+        _check(topk_w, torch.float32, "topk_w", (T, k))
+    hidden, inter = mg.cols, mg.rows // 2
+    _check(x, x.dtype, "x", (T, hidden))
+    _check(h, torch.bfloat16, "h", (T, k, inter))
+    _check(y, torch.float32, "y", (T, hidden))
+    need = lib().trellis_moe_ffn_workspace_size(mg.n_mat, hidden, inter, T, k)
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise TrellisError(-3, f"trellis_moe_ffn_noalloc: this layer needs {need} bytes of "
+                           f"workspace, the library's scratch holds {NOALLOC_SCRATCH_BYTES}")
+    return _run(prepare, lib().trellis_moe_ffn_noalloc,
+                (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
+                 topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr()),
+                "trellis_moe_ffn_noalloc", (y, h), (mg, md))
 
 
 # ---------------------------------------------------------------- expanded (MXFP4) weights

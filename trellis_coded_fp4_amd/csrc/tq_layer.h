@@ -1738,10 +1738,20 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   return launch<F>(a, cus, stream);
 }
 
+// Zero the 16-byte words [0, n0) of p0 and [0, n1) of p1 (vector stores).
+static __global__ void __launch_bounds__(256) k_clear2(uint4 *p0, size_t n0, uint4 *p1, size_t n1) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n0 + n1; i += stride)
+    (i < n0 ? p0[i] : p1[i - n0]) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// clear_state: first zero the workspace's synchronisation state on the
+// stream (every counter and tagged word; the status words stay), so that a
+// workspace last used by a call of another shape serves this one.
 template <typename F>
 static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const void *x, int32_t x_dtype,
                     const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k, uint16_t *h, float *y,
-                    void *workspace, size_t workspace_bytes, hipEvent_t *events) {
+                    void *workspace, size_t workspace_bytes, hipEvent_t *events, bool clear_state = false) {
   int rc;
   if ((rc = check_mats(gu)) || (rc = check_mats(dn))) return rc;
   if (!x || !topk_ids || !h || !y || !workspace) return TRELLIS_ENULL;
@@ -1756,6 +1766,15 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
   char *ws = (char *)workspace;
+  if (clear_state) {
+    // [end of the status words, first data region) and [cntp, xq): the
+    // single-token region, the stage counters and the prep counters
+    const size_t n0 = (L.yslot - (L.status + 256)) / 16, n1 = (L.xq - L.cntp) / 16;
+    const int blocks = (int)std::min<size_t>((n0 + n1 + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_clear2, dim3(blocks), dim3(256), 0, stream, (uint4 *)(ws + L.status + 256), n0,
+                       (uint4 *)(ws + L.cntp), n1);
+    if (hipGetLastError() != hipSuccess) return TRELLIS_EHIP;
+  }
   if constexpr (F::kSteps == 2) {
     // one token of trellis-coded weights: the single-token layer kernel
     TokCall c{(const uint32_t *)gu.w, gu.scales, (const uint32_t *)dn.w, dn.scales, E, hidden, inter, k,

@@ -3,6 +3,8 @@
 // instantiates them for trellis-coded weights).
 #include "tq_layer.h"
 
+#include <mutex>
+
 using namespace tq;
 
 extern "C" size_t trellis_moe_gemv_workspace_size(int32_t n_mat, int32_t rows, int32_t cols, int32_t T,
@@ -52,3 +54,51 @@ extern "C" int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_u
 #ifdef TQ_TRACE
 extern "C" void tq_set_trace(void *p) { tq::g_trace = p; }
 #endif
+
+// ---------------------------------------------------------------- layer with the library's own scratch
+//
+// trellis_moe_ffn_noalloc runs trellis_moe_ffn on a workspace that lives in
+// the code object: `scratch` below, one copy per device, zero-filled when
+// the code object is loaded (a device global without an initializer). Calls
+// of every shape share it, so each call first zeroes the synchronisation
+// state its layout uses (a fill kernel on the call's stream, not a memset,
+// so that the call can be captured into a graph); the sticky error word is
+// kept. Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+namespace {
+constexpr size_t kScratchBytes = TRELLIS_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return TRELLIS_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TRELLIS_EHIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return TRELLIS_OK;
+}
+}  // namespace
+
+extern "C" int trellis_moe_ffn_noalloc(hipStream_t stream, const trellis_mat_t *w_gate_up,
+                                       const trellis_mat_t *w_down, const void *x, int32_t x_dtype,
+                                       const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t k,
+                                       uint16_t *h, float *y) {
+  if (!w_gate_up || !w_down) return TRELLIS_ENULL;
+  const size_t need = trellis_moe_ffn_workspace_size(w_gate_up->n_mat, w_gate_up->cols, w_gate_up->rows / 2, T, k);
+  if (need == 0) return TRELLIS_EINVAL;
+  if (need > kScratchBytes) return TRELLIS_EWORKSPACE;
+  void *ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != TRELLIS_OK) return rc;
+  return ffn_impl<FmtTrellis>(stream, trellis_mats(w_gate_up), trellis_mats(w_down), x, x_dtype, topk_ids, topk_w,
+                              T, k, h, y, ws, kScratchBytes, nullptr, true);
+}
