@@ -68,12 +68,13 @@ def test_expand_special_streams(trellis_lib, orc):
     assert (codes[0, 0] == 0xFF).all()       # zero stream: -6 everywhere
 
 
-def test_expand_full_128_experts_sampled(trellis_lib, orc):
+def test_expand_full_128_experts_every_row(trellis_lib, orc):
     """All 128 experts x 3 matrices of 4096 x 1536 expanded in one call (the
-    expand workload); scales compared in full on the device, codes on a
-    sample of rows against the oracle plus a full-size invariant."""
+    expand workload), every byte of codes and scales against the oracle's
+    expand (matrices checked in parallel host threads)."""
     import torch
-    announce("expand 128x3x4096x1536")
+    from concurrent.futures import ThreadPoolExecutor
+    announce("expand 128x3x4096x1536, every row")
     n_mat, rows, cols = 3 * 128, 4096, 1536
     g = workloads.rng(5, workloads.T_SYMS_UP)
     syms = workloads.symbols(g, n_mat, rows, cols)
@@ -82,18 +83,16 @@ def test_expand_full_128_experts_sampled(trellis_lib, orc):
     codes, sc2 = trellis_lib.decode_expand(ds, de)
     torch.cuda.synchronize()
     assert torch.equal(sc2, de)
-    rs = np.random.default_rng(3)
-    mats = rs.integers(0, n_mat, 24)
-    rws = rs.integers(0, rows, 24)
-    for m, r in zip(mats, rws):
-        ref, _ = orc.expand(syms[m:m + 1, r:r + 1], sc[m:m + 1, r:r + 1])
-        got = codes[m, r].cpu().numpy()
-        assert (got == ref[0, 0]).all(), f"matrix {m} row {r}"
-    # every row's first weight sees the reset state: its code depends only on
-    # the first symbol (s = b): b=0 -> P0[0] = -6 (0xF)
-    first_sym = torch.from_numpy((syms[..., 0] & 3).astype(np.int64)).cuda()
-    first_code = (codes[..., 0] & 0xF).to(torch.int64)
-    zero_rows = first_sym == 0
-    assert bool((first_code[zero_rows] == 0xF).all())
-    del ds, de, codes, sc2
+    del ds, de, sc2
+    got = codes.cpu().numpy()
+    del codes
     torch.cuda.empty_cache()
+
+    def differs(m):
+        ref, _ = orc.expand(syms[m:m + 1], sc[m:m + 1])
+        return not np.array_equal(ref[0], got[m])
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(threads) as ex:
+        bad = [m for m, d in enumerate(ex.map(differs, range(n_mat))) if d]
+    assert not bad, f"{len(bad)} of {n_mat} matrices differ, first {bad[:5]}"

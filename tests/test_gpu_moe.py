@@ -203,13 +203,11 @@ def test_ffn_expert_ffn_full(trellis_lib, orc):
     _check_layer(trellis_lib, orc, layer)
 
 
-def test_ffn_32_experts_sampled(trellis_lib, orc):
-    """Full MoE layer, 32 experts, top-4, batch 1 (sampled rows of both stages)."""
-    announce("ffn 32 experts top-4 batch 1")
+def test_ffn_32_experts_all_rows(trellis_lib, orc):
+    """Full MoE layer, 32 experts, top-4, batch 1: every row of both stages."""
+    announce("ffn 32 experts top-4 batch 1, all rows")
     layer = workloads.moe_layer(workloads.MOE_32E)
-    rs = np.random.default_rng(0)
-    _check_layer(trellis_lib, orc, layer, rows_gu=np.sort(rs.choice(2880, 160, replace=False)),
-                 rows_dn=np.sort(rs.choice(2880, 160, replace=False)))
+    _check_layer(trellis_lib, orc, layer)
 
 
 @pytest.mark.parametrize("T", [1, 4, 8, 16, 32, 64, 128])
@@ -328,3 +326,47 @@ def test_ffn_calls_share_a_workspace_varying_experts(trellis_lib, orc):
             if all(int(e) < 0 or int(e) >= cfg.n_exp for e in ids[t]):
                 assert (y[t] == 0).all(), f"call {i}: empty token {t} not zero"
         check_tol(y, yg, bg, f"shared workspace call {i}")
+
+
+def test_timed_out_workspace_is_sticky_and_raises(trellis_lib, orc):
+    """A workspace whose status word records a timed-out wait (written here
+    from the host, as such a call leaves it): every later call on it writes
+    NaN to y, the binding's check raises WorkspaceError, and once the
+    workspace is zero-filled again the calls are correct. Covers the
+    single-token layer kernel (T = 1), the general layer kernel (T = 2) and
+    the routed GEMV."""
+    announce("sticky timed-out status word: layer T=1, T=2, routed GEMV")
+    import torch
+    for T in (1, 2):
+        cfg = workloads.MoEConfig(94, f"sticky T={T}", 4, 256, 128, 2, T, True)
+        layer = workloads.moe_layer(cfg)
+        args = (dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales),
+                x_dev(layer.x, True), dev(layer.ids), dev(layer.gate_w))
+        ws = trellis_lib.ffn_workspace(cfg.n_exp, cfg.hidden, cfg.inter, T, cfg.k)
+        ws[:8].view(torch.int32)[1] = 1
+        y, _ = trellis_lib.moe_ffn(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(y).all(), f"T={T}: y not marked invalid"
+        with pytest.raises(trellis_lib.WorkspaceError):
+            trellis_lib.check_workspace(ws)
+        with pytest.raises(trellis_lib.WorkspaceError):
+            trellis_lib.moe_ffn(*args, workspace=ws, check=True)
+        assert int(ws[:8].view(torch.int32)[1]) == 1      # still set: sticky
+        ws.zero_()
+        _check_layer(trellis_lib, orc, layer,
+                     run=lambda L: trellis_lib.moe_ffn(*args, workspace=ws, check=True))
+    g = workloads.rng(606, 0)
+    E, rows, cols, T, k = 4, 32, 256, 2, 2
+    syms, sc = workloads.symbols(g, E, rows, cols), workloads.scales(g, E, rows, cols)
+    x = workloads.activations(g, T, cols, True)
+    ids, gw = workloads.routing_topk(g, T, E, k)
+    ws = trellis_lib.gemv_workspace(E, rows, cols, T, k)
+    ws[:8].view(torch.int32)[1] = 1
+    with pytest.raises(trellis_lib.WorkspaceError):
+        y = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(ids), dev(gw), workspace=ws, check=True)
+    y = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(ids), dev(gw), workspace=ws)
+    assert torch.isnan(y).all()
+    ws.zero_()
+    y = trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(x, True), dev(ids), dev(gw), workspace=ws, check=True)
+    y_ref, bound, _ = orc.moe_gemv(syms, sc, x, ids, gate_w=gw)
+    check_tol(y.cpu().numpy(), y_ref, bound, "gemv after re-zeroing")

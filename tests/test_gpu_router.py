@@ -41,7 +41,14 @@ def _check(orc, x, w, k, ids, gw):
             for j in range(k):
                 a, b = int(ids[t, j]), int(ref_ids[t, j])
                 assert abs(logits[t, a] - logits[t, b]) <= bound[t, a] + bound[t, b], (t, j, a, b)
-        else:
+        # gate weights of the ids the GPU picked: softmax over the oracle's
+        # float64 logits of those ids (equal to the oracle's own weights when
+        # the ids agree), so weights are checked whether or not a tie reordered
+        picked = logits[t, ids[t].astype(np.int64)]
+        e = np.exp(picked - picked.max())
+        want = (e / e.sum()).astype(np.float32)
+        np.testing.assert_allclose(gw[t], want, rtol=1e-6, atol=0)
+        if np.array_equal(ids[t], ref_ids[t]):
             np.testing.assert_allclose(gw[t], ref_gw[t], rtol=1e-6, atol=0)
 
 

@@ -191,9 +191,19 @@ class Call:
         return self.result
 
 
-def _run(prepare, fn, args, name, result, keep=()):
+def _run(prepare, fn, args, name, result, keep=(), check=None, stream=None):
+    """Enqueue the call (or return it prepared). ``check``: a workspace whose
+    status word is read after the call (synchronising ``stream``);
+    WorkspaceError is raised if a wait of the call timed out."""
     c = Call(fn, args, name, result, keep)
-    return c if prepare else c()
+    if prepare:
+        if check is not None:
+            raise ValueError("check=True needs an eager call (prepare=False)")
+        return c
+    out = c()
+    if check is not None:
+        check_workspace(check, stream)
+    return out
 
 
 def mat(syms, scales) -> Mat:
@@ -255,8 +265,11 @@ def ffn_workspace(n_exp, hidden, inter, T, k, device="cuda"):
 
 
 def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
-             stream=None, prepare=False):
-    """Routed fused-decode GEMV. y is [T, k, rows] without topk_w, [T, rows] with it."""
+             stream=None, prepare=False, check=False):
+    """Routed fused-decode GEMV. y is [T, k, rows] without topk_w, [T, rows] with it.
+
+    check=True synchronises the stream after the call and raises
+    WorkspaceError if a wait timed out (the workspace's sticky status word)."""
     torch = _torch()
     m = mat(syms, scales)
     T, k = topk_ids.shape
@@ -274,16 +287,16 @@ def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, w
     return _run(prepare, lib().trellis_moe_gemv,
                 (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
-                "trellis_moe_gemv", y, (m,))
+                "trellis_moe_gemv", y, (m,), workspace if check else None, stream)
 
 
 def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
-            workspace=None, stream=None, events=None, prepare=False):
+            workspace=None, stream=None, events=None, prepare=False, check=False):
     """Whole fused MoE layer; returns (y [T, hidden] fp32, h [T, k, inter] bf16).
 
     ``events``: optional ctypes array of hipEvent_t; events[0] and events[1]
     are recorded on the stream just before and just after the layer kernel
-    (see trellis_moe_ffn_timed)."""
+    (see trellis_moe_ffn_timed). check=True: as for moe_gemv."""
     torch = _torch()
     mg = mat(gu_syms, gu_scales)
     md = mat(dn_syms, dn_scales)
@@ -306,7 +319,7 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
                 (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
                  workspace.numel(), events),
-                "trellis_moe_ffn", (y, h), (mg, md, events))
+                "trellis_moe_ffn", (y, h), (mg, md, events), workspace if check else None, stream)
 
 
 NOALLOC_SCRATCH_BYTES = 8 << 20   # TRELLIS_NOALLOC_SCRATCH_BYTES
@@ -355,7 +368,7 @@ def mx_mat(codes, scales) -> MxMat:
 
 
 def mxfp4_moe_gemv(codes, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
-                   stream=None, prepare=False):
+                   stream=None, prepare=False, check=False):
     """moe_gemv on expanded MXFP4 weights (trellis_mxfp4_moe_gemv)."""
     torch = _torch()
     m = mx_mat(codes, scales)
@@ -374,11 +387,11 @@ def mxfp4_moe_gemv(codes, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=
     return _run(prepare, lib().trellis_mxfp4_moe_gemv,
                 (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
-                "trellis_mxfp4_moe_gemv", y, (m,))
+                "trellis_mxfp4_moe_gemv", y, (m,), workspace if check else None, stream)
 
 
 def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
-                  workspace=None, stream=None, prepare=False):
+                  workspace=None, stream=None, prepare=False, check=False):
     """moe_ffn on expanded MXFP4 weights (trellis_mxfp4_moe_ffn); returns (y, h)."""
     torch = _torch()
     mg = mx_mat(gu_codes, gu_scales)
@@ -402,7 +415,7 @@ def mxfp4_moe_ffn(gu_codes, gu_scales, dn_codes, dn_scales, x, topk_ids, topk_w=
                 (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
                  workspace.numel()),
-                "trellis_mxfp4_moe_ffn", (y, h), (mg, md))
+                "trellis_mxfp4_moe_ffn", (y, h), (mg, md), workspace if check else None, stream)
 
 
 def viterbi_workspace(rows, n, device="cuda"):
