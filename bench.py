@@ -55,6 +55,7 @@ MX_BPW = 0.5 + 1.0 / 32.0                 # E2M1 nibble + UE8M0 byte per 32 weig
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
 FP4_PEAK_TFLOPS = 10100.0                 # MI355X dense FP4 matrix cores, published
 FP64_PEAK_TFLOPS = 78.6                   # MI355X fp64 vector, published
+VALU_WAVE_INSTS_PER_S = 1024 * 2.4e9 / 4  # 256 CUs x 4 SIMDs, a wave64 VALU instruction every 4 cycles
 VIT_FLOPS_PER_EDGE = 4                    # err = t - v, (d * err) * err, cost + that
 VIT_EDGES_PER_POSITION = 4096 * 4         # histories x branches
 METRIC = "compressed-weight GB/s of fused trellis-decode MoE GEMV (batch 1) + % HBM peak"
@@ -211,20 +212,25 @@ def host_cpu():
 
 
 def stream_read_peak(nbytes, reuse_mb, steps=100):
-    """GB/s of a plain device reduction (torch.sum) over nbytes per step,
-    walking a ring of copies as the layer steps do: the practical read rate
-    at this size, launch gaps included, for comparison with the kernel."""
+    """GB/s of a plain streaming read (trellis_read_bandwidth: every byte read
+    once with 16-byte vector loads) over nbytes per step, walking a ring of
+    buffers as the layer steps do: the practical read rate at this size,
+    launch gaps included, for comparison with the layer."""
     import torch
+    import trellis_coded_fp4_amd as tq
     n = max(2, int(np.ceil(reuse_mb * (1 << 20) / nbytes)) + 1)
-    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(n)]
+    nbytes = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(n)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    calls = [tq.read_bandwidth(b, sink, prepare=True) for b in bufs]
     for i in range(10):
-        bufs[i % n].sum()
+        calls[i % n]()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        bufs[i % n].sum()
+        calls[i % n]()
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / steps
@@ -534,20 +540,31 @@ def main():
                   "event_release": args.event_release}
         per_launch = float(np.mean([W["bytes"](s) for s, e in zip(timed, evs) if e]))
         achieved = per_launch / (d.mean() * 1e-3) / 1e9
-        traffic = None
+        traffic, valu_insts = None, None
         if os.path.exists(PROFILE_TRAFFIC):
             try:
                 tr = json.load(open(PROFILE_TRAFFIC)).get(args.workload, {})
                 if tr.get("kernel_source_sha") == kernel_sha(args.workload):
                     traffic = tr.get("bytes_per_launch")
+                    valu_insts = tr.get("valu_insts_per_launch")
             except (OSError, ValueError):
-                traffic = None
+                traffic, valu_insts = None, None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": W["kernel"],
                     "bytes_per_launch": per_launch,
                     "duration_us": round(float(d.mean() * 1e3), 3),
                     "duration_source": f"mean of HIP event pairs around every {every}th launch of the timed "
                                        "region, on the launch stream"}
+        if valu_insts:
+            # the decode's vector-ALU bound: the kernel's VALU wave instructions
+            # (profiler count for these sources) at the chip's issue rate
+            issue_us = valu_insts / VALU_WAVE_INSTS_PER_S * 1e6
+            roofline["valu"] = {"insts_per_launch": valu_insts,
+                                "lane_ops_per_weight": round(valu_insts * 64 / (per_launch / TRELLIS_BPW), 3),
+                                "issue_us": round(issue_us, 3),
+                                "issue_bound_GBs": round(per_launch / (issue_us * 1e-6) / 1e9, 1),
+                                "issue_frac": round(issue_us / (d.mean() * 1e3), 4),
+                                "peak": "1024 SIMDs x 2.4 GHz / 4 cycles per wave64 instruction"}
         if W.get("traffic_bytes"):
             roofline["read_plus_write_GBs"] = round(W["traffic_bytes"] / (d.mean() * 1e-3) / 1e9, 1)
         if W.get("alu_flops"):
@@ -595,7 +612,8 @@ def main():
     stream_peak = None
     if "units" not in W and W.get("ring"):
         gbs, us = stream_read_peak(int(np.mean([W["bytes"](s) for s in timed])), args.reuse_mb)
-        stream_peak = {"GBs": gbs, "us_per_step": us, "kernel": "torch.sum over the step's bytes (ring of copies)",
+        stream_peak = {"GBs": gbs, "us_per_step": us,
+                       "kernel": "trellis_read_bandwidth over the step's bytes (ring of buffers, launch gaps included)",
                        "value_frac": round(value / gbs, 3)}
 
     cpu = None

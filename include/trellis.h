@@ -317,6 +317,22 @@ int trellis_viterbi_encode(hipStream_t stream, const double *target, const doubl
                            int32_t n, uint8_t *syms_out, double *cost_out, void *workspace,
                            size_t workspace_bytes);
 
+/*
+ * trellis_read_bandwidth -- a measurement reference, not part of the method:
+ * reads the `bytes` bytes at `buf` once (16-byte vector loads, every byte
+ * read exactly once) and XORs all their 32-bit words, per workgroup, into
+ * one of the 256 words of sink (atomically; the caller zero-fills sink to
+ * check the result: the XOR of the 256 words is the XOR of every word of
+ * buf). Timing it over the bytes one layer call reads gives the practical
+ * streaming-read rate of HBM at that size, which the layer's
+ * compressed-weight GB/s is compared with beside the 8 TB/s peak.
+ *   buf:  device, 16-byte aligned; bytes: a multiple of 4.
+ *   sink: device uint32[256].
+ * Errors: ENULL for a NULL pointer, EINVAL for misalignment, EHIP for a
+ * launch failure.
+ */
+int trellis_read_bandwidth(hipStream_t stream, const void *buf, size_t bytes, uint32_t *sink);
+
 #ifdef __cplusplus
 }
 #endif

@@ -214,3 +214,14 @@ def test_ffn_workspace_covers_the_single_token_region():
     # region: call counter line + tagged h of up to 32 experts + a tag per 16 rows of y
     region = 256 + 32 * 2880 * 4 + (2880 // 16) * 4
     assert one >= 256 + region and many > one
+
+
+def test_read_bandwidth_argument_checks():
+    """The streaming-read reference rejects NULL pointers, a misaligned buffer
+    and a byte count that is not a whole number of 32-bit words."""
+    lib = tq.lib()
+    buf, sink = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    assert lib.trellis_read_bandwidth(None, None, 64, sink) == -2
+    assert lib.trellis_read_bandwidth(None, buf, 64, None) == -2
+    assert lib.trellis_read_bandwidth(None, ctypes.c_void_p(0x10004), 64, sink) == -1
+    assert lib.trellis_read_bandwidth(None, buf, 66, sink) == -1

@@ -30,7 +30,7 @@ EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_ffn_noalloc",
            "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn",
            "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_workspace_size",
-           "trellis_router_topk"]
+           "trellis_router_topk", "trellis_read_bandwidth"]
 
 
 class TrellisError(RuntimeError):
@@ -97,6 +97,8 @@ def lib():
         L.trellis_router_workspace_size.restype = SZ
         L.trellis_router_topk.argtypes = [P, P, I32, P, I32, I32, I32, I32, P, P, P, SZ]
         L.trellis_router_topk.restype = ctypes.c_int
+        L.trellis_read_bandwidth.argtypes = [P, P, SZ, P]
+        L.trellis_read_bandwidth.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -484,3 +486,16 @@ def router_topk(x, w_router, k, topk_ids=None, topk_w=None, workspace=None, stre
                  topk_ids.data_ptr(), topk_w.data_ptr(), workspace.data_ptr(),
                  workspace.numel() * workspace.element_size()),
                 "trellis_router_topk", (topk_ids, topk_w), (workspace,))
+
+
+def read_bandwidth(buf, sink, stream=None, prepare=False):
+    """Read every byte of the device tensor `buf` once (trellis_read_bandwidth),
+    XOR-folding its 32-bit words into `sink` (int32 device tensor of 256
+    elements; the XOR of all of them is the checksum)."""
+    torch = _torch()
+    _check(sink, torch.int32, "sink", (256,))
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    return _run(prepare, lib().trellis_read_bandwidth,
+                (_stream(stream), buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr()),
+                "trellis_read_bandwidth", sink, (buf,))
