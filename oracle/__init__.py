@@ -76,6 +76,12 @@ def lib():
         L.oracle_moe_ffn.restype = I64
         L.oracle_viterbi.argtypes = [P, P, ctypes.c_int, P]
         L.oracle_viterbi.restype = ctypes.c_double
+        L.oracle_e5m3_scale.argtypes = [ctypes.c_int]
+        L.oracle_e5m3_scale.restype = ctypes.c_double
+        L.oracle_decode_values_fmt.argtypes = [P, P, I64, I64, ctypes.c_int, P]
+        L.oracle_decode_values_fmt.restype = None
+        L.oracle_moe_gemv_fmt.argtypes = [P, P, I64, I64, I64, ctypes.c_int, P, ctypes.c_int, P, P, I64, I64, P, P]
+        L.oracle_moe_gemv_fmt.restype = I64
         _lib = L
     return _lib
 
@@ -115,6 +121,14 @@ def ue8m0_scale(e: int) -> float:
     return lib().oracle_ue8m0_scale(int(e))
 
 
+SCALE_FORMATS = {"ue8m0": 0, "e5m3": 1}
+
+
+def e5m3_scale(byte: int) -> float:
+    """Value of an E5M3 block-scale byte (reading R14 in the C source)."""
+    return lib().oracle_e5m3_scale(int(byte))
+
+
 def state_value(s: int) -> float:
     return lib().oracle_state_value(int(s))
 
@@ -144,13 +158,17 @@ def decode_window(row_words: np.ndarray, k: int) -> int:
     return lib().oracle_decode_window(_p(w), int(k))
 
 
-def decode_values(syms: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Dense fp64 weights [..., rows, cols] from symbols and UE8M0 scales."""
+def decode_values(syms: np.ndarray, scales: np.ndarray, scale_fmt: str = "ue8m0") -> np.ndarray:
+    """Dense fp64 weights [..., rows, cols] from symbols and block scales
+    (UE8M0 bytes, or E5M3 bytes with scale_fmt="e5m3")."""
     s, e = _u32(syms), _u8(scales)
     cols = s.shape[-1] * 16
     rows = int(np.prod(s.shape[:-1]))
     out = np.empty(s.shape[:-1] + (cols,), dtype=np.float64)
-    lib().oracle_decode_values(_p(s), _p(e), rows, cols, _p(out))
+    if scale_fmt == "ue8m0":
+        lib().oracle_decode_values(_p(s), _p(e), rows, cols, _p(out))
+    else:
+        lib().oracle_decode_values_fmt(_p(s), _p(e), rows, cols, SCALE_FORMATS[scale_fmt], _p(out))
     return out
 
 
@@ -178,7 +196,7 @@ def gemv(syms: np.ndarray, scales: np.ndarray, x: np.ndarray):
     return y, b
 
 
-def moe_gemv(syms, scales, x, ids, gate_w=None, x_per_slot=False):
+def moe_gemv(syms, scales, x, ids, gate_w=None, x_per_slot=False, scale_fmt="ue8m0"):
     """Routed GEMV; returns (y, bound, skipped). See oracle_moe_gemv in the C source."""
     s, e = _u32(syms), _u8(scales)
     n_exp, rows, wpr = s.shape
@@ -190,8 +208,12 @@ def moe_gemv(syms, scales, x, ids, gate_w=None, x_per_slot=False):
     shape = (T, rows) if gw is not None else (T, k, rows)
     y = np.empty(shape)
     b = np.empty(shape)
-    skipped = lib().oracle_moe_gemv(_p(s), _p(e), n_exp, rows, cols, _p(xv), int(bool(x_per_slot)),
-                                    _p(idv), _p(gw), T, k, _p(y), _p(b))
+    if scale_fmt == "ue8m0":
+        skipped = lib().oracle_moe_gemv(_p(s), _p(e), n_exp, rows, cols, _p(xv), int(bool(x_per_slot)),
+                                        _p(idv), _p(gw), T, k, _p(y), _p(b))
+    else:
+        skipped = lib().oracle_moe_gemv_fmt(_p(s), _p(e), n_exp, rows, cols, SCALE_FORMATS[scale_fmt], _p(xv),
+                                            int(bool(x_per_slot)), _p(idv), _p(gw), T, k, _p(y), _p(b))
     return y, b, int(skipped)
 
 

@@ -37,6 +37,10 @@
  *  R7  SwiGLU between gate_up and down: gate = the first I rows of the
  *      gate_up output, up = the last I rows, h = silu(gate) * up rounded to
  *      bf16 (round to nearest even).
+ *  R14 E5M3 block scales (the XOR-Trellis article's grouping-format
+ *      paragraph names them, nothing more): an unsigned 8-bit float, the
+ *      upper byte of an IEEE binary16 number without its sign (bias 15,
+ *      subnormals at E = 0, E = 31 infinite or NaN). See oracle_e5m3_scale.
  *
  * Numbers: GEMV sums are accumulated in fp64, in column order. Inputs
  * (bf16 or fp32) are passed in as doubles, which holds them exactly.
@@ -103,6 +107,27 @@ double oracle_ue8m0_scale(int e) {
     return ldexp(1.0, e - 127);
 }
 
+/* ---- E5M3 block scales (XOR-Trellis article, "So what", the paragraph on
+ * the grouping format: E2M1 elements with E5M3 block scales) ----
+ *
+ * The article names the format only. Reading R14: an unsigned 8-bit float,
+ * 5 exponent bits (bias 15) above 3 mantissa bits, laid out and valued like
+ * the upper byte of an IEEE binary16 number without its sign: E = byte >> 3,
+ * m = byte & 7; E = 0 is subnormal, m/8 * 2^-14; E in 1..30 is normal,
+ * (1 + m/8) * 2^(E - 15); E = 31 is +infinity (m = 0) or NaN. */
+double oracle_e5m3_scale(int byte) {
+    const int E = (byte >> 3) & 31, m = byte & 7;
+    if (E == 31) return m == 0 ? INFINITY : NAN;
+    if (E == 0) return ldexp((double)m / 8.0, -14);
+    return ldexp(1.0 + (double)m / 8.0, E - 15);
+}
+
+enum { SCALE_UE8M0 = 0, SCALE_E5M3 = 1 };
+
+static double block_scale(int fmt, int byte) {
+    return fmt == SCALE_E5M3 ? oracle_e5m3_scale(byte) : oracle_ue8m0_scale(byte);
+}
+
 /* ---- the decoder ---- */
 
 static int masked_parity(uint32_t state, uint32_t mask) {
@@ -162,18 +187,24 @@ int oracle_decode_window(const uint32_t *row_words, int64_t k) {
     return oracle_state_code(s);
 }
 
-/* Dense decoded weights: w[r][k] = palette value * 2^(e - 127). */
-void oracle_decode_values(const uint32_t *syms, const uint8_t *scales,
-                          int64_t rows, int64_t cols, double *w) {
+/* Dense decoded weights: w[r][k] = palette value * block scale (UE8M0:
+ * 2^(e - 127); E5M3: reading R14). */
+void oracle_decode_values_fmt(const uint32_t *syms, const uint8_t *scales,
+                              int64_t rows, int64_t cols, int scale_fmt, double *w) {
     const int64_t wpr = cols / 16, spr = cols / 32;
     for (int64_t r = 0; r < rows; ++r) {
         const uint32_t *words = syms + r * wpr;
         uint32_t s = 0;
         for (int64_t k = 0; k < cols; ++k) {
             s = ((s << 2) | (uint32_t)row_symbol(words, k)) & 0xFFFFu;
-            w[r * cols + k] = oracle_state_value(s) * oracle_ue8m0_scale(scales[r * spr + k / 32]);
+            w[r * cols + k] = oracle_state_value(s) * block_scale(scale_fmt, scales[r * spr + k / 32]);
         }
     }
+}
+
+void oracle_decode_values(const uint32_t *syms, const uint8_t *scales,
+                          int64_t rows, int64_t cols, double *w) {
+    oracle_decode_values_fmt(syms, scales, rows, cols, SCALE_UE8M0, w);
 }
 
 /* Expand to resident MXFP4 (HEPH's second serving mode): packed E2M1 codes,
@@ -195,12 +226,12 @@ void oracle_expand(const uint32_t *syms, const uint8_t *scales, int64_t n_mat,
 /* One row's dot product with x, decoding as it goes, in fp64:
  * y = sum_k w[k] x[k] and bound = sum_k |w[k]| |x[k]|. */
 static void row_dot(const uint32_t *words, const uint8_t *row_scales, int64_t cols,
-                    const double *x, double *y, double *bound) {
+                    const double *x, double *y, double *bound, int scale_fmt) {
     uint32_t s = 0;
     double acc = 0.0, mag = 0.0;
     for (int64_t k = 0; k < cols; ++k) {
         s = ((s << 2) | (uint32_t)row_symbol(words, k)) & 0xFFFFu;
-        double w = oracle_state_value(s) * oracle_ue8m0_scale(row_scales[k / 32]);
+        double w = oracle_state_value(s) * block_scale(scale_fmt, row_scales[k / 32]);
         acc += w * x[k];
         mag += fabs(w) * fabs(x[k]);
     }
@@ -216,7 +247,7 @@ void oracle_gemv(const uint32_t *syms, const uint8_t *scales, int64_t rows, int6
     for (int64_t t = 0; t < nx; ++t)
         for (int64_t r = 0; r < rows; ++r)
             row_dot(syms + r * wpr, scales + r * spr, cols, x + t * cols,
-                    &y[t * rows + r], &bound[t * rows + r]);
+                    &y[t * rows + r], &bound[t * rows + r], SCALE_UE8M0);
 }
 
 /* Routed (mixture-of-experts) GEMV over n_exp matrices [rows][cols].
@@ -228,10 +259,10 @@ void oracle_gemv(const uint32_t *syms, const uint8_t *scales, int64_t rows, int6
  * slot (contributes zero); an id >= n_exp is skipped and counted. Returns the
  * number of skipped slots.  bound has the shape of y and holds
  * sum |gate_w| * sum_k |w| |x|. */
-int64_t oracle_moe_gemv(const uint32_t *syms, const uint8_t *scales, int64_t n_exp,
-                        int64_t rows, int64_t cols, const double *x, int x_per_slot,
-                        const int32_t *ids, const double *gate_w, int64_t T, int64_t k,
-                        double *y, double *bound) {
+int64_t oracle_moe_gemv_fmt(const uint32_t *syms, const uint8_t *scales, int64_t n_exp,
+                            int64_t rows, int64_t cols, int scale_fmt, const double *x, int x_per_slot,
+                            const int32_t *ids, const double *gate_w, int64_t T, int64_t k,
+                            double *y, double *bound) {
     const int64_t wpr = cols / 16, spr = cols / 32;
     int64_t skipped = 0;
     int64_t n_out = gate_w ? T * rows : T * k * rows;
@@ -247,13 +278,22 @@ int64_t oracle_moe_gemv(const uint32_t *syms, const uint8_t *scales, int64_t n_e
             double g = gate_w ? gate_w[t * k + j] : 1.0;
             for (int64_t r = 0; r < rows; ++r) {
                 double d, b;
-                row_dot(syms + (e * rows + r) * wpr, scales + (e * rows + r) * spr, cols, xv, &d, &b);
+                row_dot(syms + (e * rows + r) * wpr, scales + (e * rows + r) * spr, cols, xv, &d, &b,
+                        scale_fmt);
                 yo[r] += g * d;
                 bo[r] += fabs(g) * b;
             }
         }
     }
     return skipped;
+}
+
+int64_t oracle_moe_gemv(const uint32_t *syms, const uint8_t *scales, int64_t n_exp,
+                        int64_t rows, int64_t cols, const double *x, int x_per_slot,
+                        const int32_t *ids, const double *gate_w, int64_t T, int64_t k,
+                        double *y, double *bound) {
+    return oracle_moe_gemv_fmt(syms, scales, n_exp, rows, cols, SCALE_UE8M0, x, x_per_slot, ids, gate_w, T, k,
+                               y, bound);
 }
 
 /* Round a double to the nearest bf16 value (ties to even), as a double. */

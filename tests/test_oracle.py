@@ -438,3 +438,62 @@ def test_router_gate_weights_closed_form(orc):
         for i in range(3):
             for j in range(3):
                 assert math.isclose(gw[t, i] / gw[t, j], math.exp(l[i] - l[j]), rel_tol=1e-13)
+
+
+# ---------------------------------------------------------------- E5M3 block scales (reading R14)
+#
+# XOR-Trellis article, "So what", the paragraph on the grouping format: the
+# paper groups E2M1 elements under E5M3 block scales. The article gives no
+# encoding; the reading is an unsigned 8-bit float laid out like the upper
+# byte of an IEEE binary16 number without its sign. numpy's float16 is an
+# independent implementation of that number format.
+
+def _binary16_of_byte(c):
+    return float(np.array([int(c) << 7], dtype=np.uint16).view(np.float16)[0])
+
+
+def test_e5m3_scale_is_the_upper_byte_of_a_binary16(orc):
+    """All 256 bytes: bias 15, subnormals at exponent 0, infinity and NaN at 31."""
+    for c in range(256):
+        want, got = _binary16_of_byte(c), orc.e5m3_scale(c)
+        assert (np.isnan(want) and np.isnan(got)) or got == want, (c, got, want)
+    assert orc.e5m3_scale(0x78) == 1.0 and orc.e5m3_scale(0x01) == 2.0 ** -17
+
+
+def test_e5m3_powers_of_two_match_ue8m0(orc):
+    """An E5M3 byte with mantissa 0 and exponent E is 2^(E - 15): the same
+    weights as the UE8M0 byte E + 112 (the two decoders agree where the
+    formats overlap)."""
+    g = workloads.rng(99, 20)
+    syms = workloads.symbols(g, 1, 6, 256)[0]
+    E = g.integers(1, 31, size=(6, 8))
+    w5 = orc.decode_values(syms, (E << 3).astype(np.uint8), scale_fmt="e5m3")
+    w8 = orc.decode_values(syms, (E + 112).astype(np.uint8))
+    assert np.array_equal(w5, w8)
+
+
+def test_e5m3_moe_gemv_exact_rational(orc):
+    """Routed GEMV with E5M3 scales covering every mantissa, subnormals and
+    a wide exponent range: within cols * 2^-53 * sum|w||x| of the exact
+    Fraction sum of (E2M1 value x binary16 value of the scale byte) x x."""
+    g = workloads.rng(99, 21)
+    E, rows, cols, T, k = 3, 5, 96, 2, 2
+    syms = workloads.symbols(g, E, rows, cols)
+    sc = np.concatenate([g.integers(0, 8, size=(E, rows, 1)),           # subnormals
+                         g.integers(8, 248, size=(E, rows, cols // 32 - 1))], axis=2).astype(np.uint8)
+    x = workloads.activations(g, T, cols, bf16=True).astype(np.float64)
+    ids = np.array([[0, 2], [1, 0]], np.int32)
+    gw = np.array([[0.5, 0.25], [1.0, 2.0]])
+    y, bound, skipped = orc.moe_gemv(syms, sc, x, ids, gate_w=gw, scale_fmt="e5m3")
+    assert skipped == 0
+    codes = orc.decode_codes(syms.reshape(E * rows, cols // 16), cols).reshape(E, rows, cols)
+    for t in range(T):
+        for r in range(rows):
+            exact, mag = Fraction(0), Fraction(0)
+            for j in range(k):
+                e = int(ids[t, j])
+                for c in range(cols):
+                    v = Fraction(orc.e2m1_value(int(codes[e, r, c]))) * Fraction(_binary16_of_byte(sc[e, r, c // 32]))
+                    exact += Fraction(gw[t, j]) * v * Fraction(float(x[t, c]))
+                    mag += abs(Fraction(gw[t, j]) * v) * abs(Fraction(float(x[t, c])))
+            assert abs(Fraction(y[t, r]) - exact) <= Fraction(2 * cols) * Fraction(2) ** -53 * mag

@@ -32,6 +32,12 @@ MUTANTS = {
     "expand-nibble-order": ("(codes[2 * j] | (codes[2 * j + 1] << 4))", "(codes[2 * j + 1] | (codes[2 * j] << 4))"),
     "viterbi-drops-curvature": ("double c = cost[prev] + d[k] * err * err;", "double c = cost[prev] + err * err;"),
     "window-too-short": ("int64_t first = k - 7 < 0 ? 0 : k - 7;", "int64_t first = k - 5 < 0 ? 0 : k - 5;"),
+    "e5m3-bias": ("return ldexp(1.0 + (double)m / 8.0, E - 15);", "return ldexp(1.0 + (double)m / 8.0, E - 16);"),
+    "e5m3-no-subnormals": ("if (E == 0) return ldexp((double)m / 8.0, -14);",
+                           "if (E == 0) return ldexp(1.0 + (double)m / 8.0, -15);"),
+    "e5m3-mantissa-weight": ("return ldexp(1.0 + (double)m / 8.0, E - 15);", "return ldexp(1.0 + (double)m / 16.0, E - 15);"),
+    "e5m3-read-as-ue8m0": ("return fmt == SCALE_E5M3 ? oracle_e5m3_scale(byte) : oracle_ue8m0_scale(byte);",
+                           "return oracle_ue8m0_scale(byte);"),
 }
 
 
