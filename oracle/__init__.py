@@ -82,6 +82,8 @@ def lib():
         L.oracle_decode_values_fmt.restype = None
         L.oracle_moe_gemv_fmt.argtypes = [P, P, I64, I64, I64, ctypes.c_int, P, ctypes.c_int, P, P, I64, I64, P, P]
         L.oracle_moe_gemv_fmt.restype = I64
+        L.oracle_moe_ffn_fmt.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P, P, P, I64, I64, P, P, P]
+        L.oracle_moe_ffn_fmt.restype = I64
         _lib = L
     return _lib
 
@@ -224,8 +226,9 @@ def swiglu_bf16(y_gu: np.ndarray, inter: int) -> np.ndarray:
     return h.reshape(y_gu.shape[:-1] + (inter,))
 
 
-def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, ids, gate_w):
-    """Whole MoE layer; returns (y [T,H], bound [T,H], h [T,k,I], skipped)."""
+def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, ids, gate_w, scale_fmt="ue8m0"):
+    """Whole MoE layer; returns (y [T,H], bound [T,H], h [T,k,I], skipped).
+    scale_fmt: both stacks' scale bytes as "ue8m0" or "e5m3"."""
     gs, ge, ds, de = _u32(gu_syms), _u8(gu_scales), _u32(dn_syms), _u8(dn_scales)
     n_exp, two_i, wpr = gs.shape
     hidden = wpr * 16
@@ -237,8 +240,8 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, ids, gate_w):
     h = np.empty((T, k, inter))
     y = np.empty((T, hidden))
     b = np.empty((T, hidden))
-    skipped = lib().oracle_moe_ffn(_p(gs), _p(ge), _p(ds), _p(de), n_exp, hidden, inter, _p(xv),
-                                   _p(idv), _p(gw), T, k, _p(h), _p(y), _p(b))
+    skipped = lib().oracle_moe_ffn_fmt(_p(gs), _p(ge), _p(ds), _p(de), n_exp, hidden, inter,
+                                       SCALE_FORMATS[scale_fmt], _p(xv), _p(idv), _p(gw), T, k, _p(h), _p(y), _p(b))
     return y, b, h, int(skipped)
 
 

@@ -325,21 +325,32 @@ void oracle_swiglu_bf16(const double *y_gu, int64_t n, int64_t inter, double *h)
  * gate-weighted combine.  gate_up is [n_exp][2I][H], down is [n_exp][H][I].
  * h[T][k][I] receives the bf16 activations between the two GEMVs (slots that
  * are empty or skipped hold zero); y[T][H] and bound[T][H] as in
- * oracle_moe_gemv.  Returns the number of skipped slots. */
+ * oracle_moe_gemv.  Returns the number of skipped slots.  scale_fmt: both
+ * stacks' scale bytes as UE8M0 or E5M3 (reading R14). */
+int64_t oracle_moe_ffn_fmt(const uint32_t *gu_syms, const uint8_t *gu_scales,
+                           const uint32_t *dn_syms, const uint8_t *dn_scales,
+                           int64_t n_exp, int64_t hidden, int64_t inter, int scale_fmt,
+                           const double *x, const int32_t *ids, const double *gate_w,
+                           int64_t T, int64_t k, double *h, double *y, double *bound) {
+    double *ygu = (double *)malloc(sizeof(double) * (size_t)(T * k * 2 * inter));
+    double *bgu = (double *)malloc(sizeof(double) * (size_t)(T * k * 2 * inter));
+    int64_t skipped = oracle_moe_gemv_fmt(gu_syms, gu_scales, n_exp, 2 * inter, hidden, scale_fmt,
+                                          x, 0, ids, NULL, T, k, ygu, bgu);
+    oracle_swiglu_bf16(ygu, T * k, inter, h);
+    oracle_moe_gemv_fmt(dn_syms, dn_scales, n_exp, hidden, inter, scale_fmt, h, 1, ids, gate_w,
+                        T, k, y, bound);
+    free(ygu);
+    free(bgu);
+    return skipped;
+}
+
 int64_t oracle_moe_ffn(const uint32_t *gu_syms, const uint8_t *gu_scales,
                        const uint32_t *dn_syms, const uint8_t *dn_scales,
                        int64_t n_exp, int64_t hidden, int64_t inter,
                        const double *x, const int32_t *ids, const double *gate_w,
                        int64_t T, int64_t k, double *h, double *y, double *bound) {
-    double *ygu = (double *)malloc(sizeof(double) * (size_t)(T * k * 2 * inter));
-    double *bgu = (double *)malloc(sizeof(double) * (size_t)(T * k * 2 * inter));
-    int64_t skipped = oracle_moe_gemv(gu_syms, gu_scales, n_exp, 2 * inter, hidden, x, 0,
-                                      ids, NULL, T, k, ygu, bgu);
-    oracle_swiglu_bf16(ygu, T * k, inter, h);
-    oracle_moe_gemv(dn_syms, dn_scales, n_exp, hidden, inter, h, 1, ids, gate_w, T, k, y, bound);
-    free(ygu);
-    free(bgu);
-    return skipped;
+    return oracle_moe_ffn_fmt(gu_syms, gu_scales, dn_syms, dn_scales, n_exp, hidden, inter,
+                              SCALE_UE8M0, x, ids, gate_w, T, k, h, y, bound);
 }
 
 /* ---- test-only encoder: Viterbi search over the trellis ----

@@ -497,3 +497,42 @@ def test_e5m3_moe_gemv_exact_rational(orc):
                     exact += Fraction(gw[t, j]) * v * Fraction(float(x[t, c]))
                     mag += abs(Fraction(gw[t, j]) * v) * abs(Fraction(float(x[t, c])))
             assert abs(Fraction(y[t, r]) - exact) <= Fraction(2 * cols) * Fraction(2) ** -53 * mag
+
+
+def _dense_e5m3(orc, syms, sc):
+    """Weights rebuilt from the decoded E2M1 codes and numpy's binary16 value
+    of each scale byte (independent of the oracle's E5M3 decoder)."""
+    E, rows, wpr = syms.shape
+    cols = wpr * 16
+    codes = orc.decode_codes(syms.reshape(E * rows, wpr), cols).reshape(E, rows, cols)
+    val = np.array([orc.e2m1_value(c) for c in range(16)])[codes]
+    s16 = np.array([_binary16_of_byte(c) for c in range(256)])[sc]
+    return val * np.repeat(s16, 32, axis=2)
+
+
+def test_ffn_e5m3_matches_numpy(orc):
+    """The layer with E5M3 scales (subnormal and normal blocks) against numpy
+    on weights rebuilt with binary16 scale values."""
+    g = workloads.rng(99, 22)
+    E, H, I, T, k = 3, 64, 32, 2, 2
+    gs = workloads.symbols(g, E, 2 * I, H)
+    ge = g.integers(0, 0xF0, size=(E, 2 * I, H // 32)).astype(np.uint8)
+    ds = workloads.symbols(g, E, H, I)
+    de = g.integers(0x60, 0x88, size=(E, H, I // 32)).astype(np.uint8)
+    ge[0, :4, 0] = np.arange(4)   # subnormal and zero scales
+    x = workloads.activations(g, T, H, bf16=True).astype(np.float64)
+    ids = np.array([[2, 0], [1, 2]], dtype=np.int32)
+    gw = np.array([[0.6, 0.4], [0.3, 0.7]])
+    y, b, h, skipped = orc.moe_ffn(gs, ge, ds, de, x, ids, gw, scale_fmt="e5m3")
+    assert skipped == 0
+    Wg, Wd = _dense_e5m3(orc, gs, ge), _dense_e5m3(orc, ds, de)
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            e = ids[t, j]
+            z = Wg[e] @ x[t]
+            hh = z[:I] / (1 + np.exp(-z[:I])) * z[I:]
+            hb = np.array([orc.round_bf16(v) for v in hh])
+            np.testing.assert_allclose(h[t, j], hb, rtol=0, atol=0)
+            acc += gw[t, j] * (Wd[e] @ hb)
+        np.testing.assert_allclose(y[t], acc, rtol=1e-11, atol=1e-11)
