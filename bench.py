@@ -68,7 +68,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="moe32",
-                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | moe32r | viterbi")
+                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | moe32r | e5m3_32 | "
+                        "e5m3_128:T | viterbi")
     p.add_argument("--ring-gb", type=float, default=1.0,
                    help="minimum total size of the ring of weight copies (GiB)")
     p.add_argument("--reuse-mb", type=float, default=512.0,
@@ -245,11 +246,16 @@ def stream_read_peak(nbytes, reuse_mb, steps=100):
 # given) with its arguments already checked and marshalled, per-step
 # algorithmic bytes, and optionally flops and a CPU-oracle sample.
 
-def layer_workload(args, cfg, mx=False, router=False):
+def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
     import torch
     import trellis_coded_fp4_amd as tq
     E, H, I = cfg.n_exp, cfg.hidden, cfg.inter
     L0 = workloads.moe_layer(cfg)
+    if e5m3:
+        # the same streams under E5M3 block scales (same byte count)
+        L0.gu_scales = workloads.scales_e5m3(workloads.rng(cfg.config_id, workloads.T_SCALES_GATE_UP), E,
+                                             2 * I, H)
+        L0.dn_scales = workloads.scales_e5m3(workloads.rng(cfg.config_id, workloads.T_SCALES_DOWN), E, H, I)
     w0 = (dev(L0.gu_syms), dev(L0.gu_scales), dev(L0.dn_syms), dev(L0.dn_scales))
     bpw = MX_BPW if mx else TRELLIS_BPW
     if mx:
@@ -305,13 +311,17 @@ def layer_workload(args, cfg, mx=False, router=False):
         if mx:
             return hip.bracket(tq.mxfp4_moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True),
                                events, stream)
+        if e5m3:
+            return hip.bracket(tq.moe_ffn_e5m3(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True),
+                               events, stream)
         return tq.moe_ffn(a, b, c, d, xs, ids, gw, h=h, y=y, workspace=ws, prepare=True,
                           events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
 
     def cpu_sample(seconds, threads=1):
         import oracle
         done, dt = cpu_run(lambda: oracle.moe_ffn(L0.gu_syms, L0.gu_scales, L0.dn_syms, L0.dn_scales, L0.x,
-                                                  L0.ids, L0.gate_w), seconds, threads)
+                                                  L0.ids, L0.gate_w, scale_fmt="e5m3" if e5m3 else "ue8m0"),
+                           seconds, threads)
         return done * uniq[0] * expert_weights * TRELLIS_BPW / dt / 1e9, \
             f"{done} full layer step(s) of the same workload (routing of step 0" + \
             ("; the router itself is not part of the sample" if router else "") + \
@@ -319,6 +329,9 @@ def layer_workload(args, cfg, mx=False, router=False):
 
     if mx:
         kernel = "k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)"
+    elif e5m3:
+        kernel = ("k_layer<FmtTrellisE5M3> (whole MoE layer, E5M3 block scales: each matrix-core step issued "
+                  "once per power-of-two term of its scale, four terms)")
     elif T == 1:
         kernel = ("k_tok (single-token MoE layer: routing, fused decode + FP4 matrix-core gate_up + SwiGLU, "
                   "tagged h hand-off, down + gate-weighted atomic combine)")
@@ -328,13 +341,15 @@ def layer_workload(args, cfg, mx=False, router=False):
     if router:
         kernel += "; each step is k_router then k_layer, the events bracket k_layer"
     return dict(
-        name=("router + " if router else "") + cfg.name + (" [expanded MXFP4]" if mx else ""), make=make, hip=hip,
+        name=("router + " if router else "") + cfg.name + (" [expanded MXFP4]" if mx else "")
+        + (" [E5M3 scales]" if e5m3 else ""), make=make, hip=hip,
         stream=stream,
         bytes=lambda s: uniq[s] * expert_weights * bpw,
         flops=lambda s: 2.0 * slots[s] * expert_weights,
         tokens=T, kernel=kernel, cpu=cpu_sample, workspace=ws, ring=len(ring),
         config={"n_experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
-                "bytes_per_weight": bpw, "weights": "expanded MXFP4" if mx else "trellis-coded",
+                "bytes_per_weight": bpw,
+                "weights": "expanded MXFP4" if mx else "trellis-coded" + (", E5M3 scales" if e5m3 else ""),
                 "ring_copies": len(ring), "reuse_distance_mb": round(reuse / (1 << 20), 1)})
 
 
@@ -460,6 +475,10 @@ def pick(args):
         return viterbi_workload(args)
     if w.startswith("moe128:"):
         return layer_workload(args, workloads.moe_128e(int(w.split(":")[1])))
+    if w == "e5m3_32":
+        return layer_workload(args, workloads.MOE_32E, e5m3=True)
+    if w.startswith("e5m3_128:"):
+        return layer_workload(args, workloads.moe_128e(int(w.split(":")[1])), e5m3=True)
     if w.startswith("mx128:"):
         return layer_workload(args, workloads.moe_128e(int(w.split(":")[1])), mx=True)
     raise SystemExit(f"unknown workload {w}")
@@ -468,7 +487,7 @@ def pick(args):
 # The device sources each workload's kernel is compiled from: a recorded
 # traffic figure stays valid while these are unchanged.
 KERNEL_SOURCES = {
-    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer.h", "tq_tok.hip", "tq_tok.h", "tq_common.h",
+    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer_e5m3.hip", "tq_layer.h", "tq_tok.hip", "tq_tok.h", "tq_common.h",
               "tq_decode.h"],
     "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
     "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],

@@ -251,6 +251,36 @@ int trellis_mxfp4_moe_ffn(hipStream_t stream, const trellis_mx_t *w_gate_up, con
                           size_t workspace_bytes);
 
 /*
+ * E5M3 block scales (XOR-Trellis article, the paragraph on the grouping
+ * format: the paper puts E2M1 elements under E5M3 block scales; it gives no
+ * encoding). Reading taken: each scale byte is an unsigned 8-bit float laid
+ * out as the upper byte of an IEEE binary16 number without its sign,
+ * exponent bits 7..3 with bias 15, mantissa bits 2..0, subnormal
+ * (m/8 * 2^-14) at exponent 0, infinity (m = 0) or NaN at exponent 31.
+ *
+ * trellis_moe_gemv_e5m3 -- trellis_moe_gemv with w->scales read as E5M3
+ * instead of UE8M0: same arguments, layout, outputs, workspace
+ * (trellis_moe_gemv_workspace_size) and errors. Accuracy: the same bound as
+ * trellis_moe_gemv (each scale enters the matrix cores as four exact
+ * power-of-two terms). A block whose scale has exponent 31 makes its
+ * outputs NaN (the oracle's infinity times a nonzero value is +-inf there).
+ */
+int trellis_moe_gemv_e5m3(hipStream_t stream, const trellis_mat_t *w, const void *x, int32_t x_dtype,
+                          int32_t x_per_slot, const int32_t *topk_ids, const float *topk_w, int32_t T,
+                          int32_t k, float *y, void *workspace, size_t workspace_bytes);
+
+/*
+ * trellis_moe_ffn_e5m3 -- trellis_moe_ffn with both matrix stacks' scales read
+ * as E5M3 (the reading above): same arguments, outputs, workspace
+ * (trellis_moe_ffn_workspace_size), accuracy and errors. It runs the general
+ * layer kernel at every T.
+ */
+int trellis_moe_ffn_e5m3(hipStream_t stream, const trellis_mat_t *w_gate_up, const trellis_mat_t *w_down,
+                         const void *x, int32_t x_dtype, const int32_t *topk_ids, const float *topk_w,
+                         int32_t T, int32_t k, uint16_t *h, float *y, void *workspace,
+                         size_t workspace_bytes);
+
+/*
  * Workspace bytes needed by trellis_router_topk: T counters and T * E
  * float64 logits. 0 for E outside 1..1024 or T < 1. Like the layer's
  * workspaces it is zero-filled once before first use; every call leaves

@@ -29,6 +29,8 @@ def bc():
         getattr(L, f).restype = ctypes.c_int
     L.tq_bitcheck_canonical_k.argtypes = [ctypes.c_int, ctypes.c_int]
     L.tq_bitcheck_canonical_k.restype = ctypes.c_int
+    L.tq_bitcheck_e5m3_terms.argtypes = [U]
+    L.tq_bitcheck_e5m3_terms.restype = U
     return L
 
 
@@ -113,3 +115,20 @@ def test_activation_column_layout(bc):
                 got = sorted(bc.tq_bitcheck_act_offset(b, p) - 128 * step for p in range(32))
                 assert got == list(range(16 * g, 16 * g + 16)) + list(range(64 + 16 * g, 64 + 16 * g + 16)) or \
                     got == sorted(bc.tq_bitcheck_bchunk_offset(32 * g + n) for n in range(32))
+
+
+def test_e5m3_terms_sum_to_the_oracle_scale(bc, orc):
+    """The matrix-core path writes each E5M3 block scale as four UE8M0
+    terms; their values sum to the oracle's E5M3 value for every byte, with
+    0 marking the zero scale and four NaN bytes for exponent 31."""
+    for c in range(256):
+        t = bc.tq_bitcheck_e5m3_terms(c)
+        want = orc.e5m3_scale(c)
+        if not np.isfinite(want):
+            assert t == 0xFFFFFFFF, c
+        elif want == 0.0:
+            assert t == 0, c
+        else:
+            b = [(t >> (8 * i)) & 0xFF for i in range(4)]
+            assert all(1 <= x <= 254 for x in b), (c, b)
+            assert sum(np.ldexp(1.0, x - 127) for x in b) == want, (c, b)

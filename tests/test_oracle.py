@@ -516,7 +516,7 @@ def test_ffn_e5m3_matches_numpy(orc):
     g = workloads.rng(99, 22)
     E, H, I, T, k = 3, 64, 32, 2, 2
     gs = workloads.symbols(g, E, 2 * I, H)
-    ge = g.integers(0, 0xF0, size=(E, 2 * I, H // 32)).astype(np.uint8)
+    ge = g.integers(0x40, 0x90, size=(E, 2 * I, H // 32)).astype(np.uint8)
     ds = workloads.symbols(g, E, H, I)
     de = g.integers(0x60, 0x88, size=(E, H, I // 32)).astype(np.uint8)
     ge[0, :4, 0] = np.arange(4)   # subnormal and zero scales

@@ -28,7 +28,7 @@ EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_gemv_workspace_size", "trellis_moe_gemv_workspace", "trellis_moe_gemv",
            "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
            "trellis_moe_ffn_noalloc",
-           "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn",
+           "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn", "trellis_moe_gemv_e5m3", "trellis_moe_ffn_e5m3",
            "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_workspace_size",
            "trellis_router_topk", "trellis_read_bandwidth"]
 
@@ -84,6 +84,10 @@ def lib():
         L.trellis_moe_ffn_timed.restype = ctypes.c_int
         L.trellis_moe_ffn_noalloc.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P]
         L.trellis_moe_ffn_noalloc.restype = ctypes.c_int
+        L.trellis_moe_gemv_e5m3.argtypes = [P, MP, P, I32, I32, P, P, I32, I32, P, P, SZ]
+        L.trellis_moe_gemv_e5m3.restype = ctypes.c_int
+        L.trellis_moe_ffn_e5m3.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P, P, SZ]
+        L.trellis_moe_ffn_e5m3.restype = ctypes.c_int
         XP = ctypes.POINTER(MxMat)
         L.trellis_mxfp4_moe_gemv.argtypes = [P, XP, P, I32, I32, P, P, I32, I32, P, P, SZ]
         L.trellis_mxfp4_moe_gemv.restype = ctypes.c_int
@@ -272,6 +276,18 @@ def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, w
 
     check=True synchronises the stream after the call and raises
     WorkspaceError if a wait timed out (the workspace's sticky status word)."""
+    return _moe_gemv("trellis_moe_gemv", syms, scales, x, topk_ids, topk_w, x_per_slot, y, workspace, stream,
+                     prepare, check)
+
+
+def moe_gemv_e5m3(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, workspace=None,
+                  stream=None, prepare=False, check=False):
+    """moe_gemv with the scale bytes read as E5M3 (trellis_moe_gemv_e5m3)."""
+    return _moe_gemv("trellis_moe_gemv_e5m3", syms, scales, x, topk_ids, topk_w, x_per_slot, y, workspace,
+                     stream, prepare, check)
+
+
+def _moe_gemv(entry, syms, scales, x, topk_ids, topk_w, x_per_slot, y, workspace, stream, prepare, check):
     torch = _torch()
     m = mat(syms, scales)
     T, k = topk_ids.shape
@@ -286,10 +302,10 @@ def moe_gemv(syms, scales, x, topk_ids, topk_w=None, x_per_slot=False, y=None, w
         if workspace is None:
             workspace = gemv_workspace(m.n_mat, m.rows, m.cols, T, k, x.device)
     _check(y, torch.float32, "y", shape)
-    return _run(prepare, lib().trellis_moe_gemv,
+    return _run(prepare, getattr(lib(), entry),
                 (_stream(stream), ctypes.byref(m), x.data_ptr(), _x_dtype(x), int(bool(x_per_slot)),
                  topk_ids.data_ptr(), _ptr(topk_w), T, k, y.data_ptr(), workspace.data_ptr(), workspace.numel()),
-                "trellis_moe_gemv", y, (m,), workspace if check else None, stream)
+                entry, y, (m,), workspace if check else None, stream)
 
 
 def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
@@ -299,6 +315,19 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
     ``events``: optional ctypes array of hipEvent_t; events[0] and events[1]
     are recorded on the stream just before and just after the layer kernel
     (see trellis_moe_ffn_timed). check=True: as for moe_gemv."""
+    return _moe_ffn(None, gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w, h, y, workspace, stream,
+                    events, prepare, check)
+
+
+def moe_ffn_e5m3(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=None, y=None,
+                 workspace=None, stream=None, prepare=False, check=False):
+    """moe_ffn with both stacks' scale bytes read as E5M3 (trellis_moe_ffn_e5m3)."""
+    return _moe_ffn("trellis_moe_ffn_e5m3", gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w, h, y,
+                    workspace, stream, None, prepare, check)
+
+
+def _moe_ffn(entry, gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w, h, y, workspace, stream, events,
+             prepare, check):
     torch = _torch()
     mg = mat(gu_syms, gu_scales)
     md = mat(dn_syms, dn_scales)
@@ -317,11 +346,14 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
             workspace = ffn_workspace(mg.n_mat, hidden, inter, T, k, x.device)
     _check(h, torch.bfloat16, "h", (T, k, inter))
     _check(y, torch.float32, "y", (T, hidden))
-    return _run(prepare, lib().trellis_moe_ffn_timed,
-                (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
-                 topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
-                 workspace.numel(), events),
-                "trellis_moe_ffn", (y, h), (mg, md, events), workspace if check else None, stream)
+    args = (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x),
+            topk_ids.data_ptr(), _ptr(topk_w), T, k, h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+            workspace.numel())
+    if entry is None:   # the UE8M0 layer, through the timed entry point (events may be None)
+        return _run(prepare, lib().trellis_moe_ffn_timed, args + (events,), "trellis_moe_ffn", (y, h),
+                    (mg, md, events), workspace if check else None, stream)
+    return _run(prepare, getattr(lib(), entry), args, entry, (y, h), (mg, md), workspace if check else None,
+                stream)
 
 
 NOALLOC_SCRATCH_BYTES = 8 << 20   # TRELLIS_NOALLOC_SCRATCH_BYTES

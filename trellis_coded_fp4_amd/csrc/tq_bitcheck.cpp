@@ -21,3 +21,4 @@ extern "C" int tq_bitcheck_canonical_k(int beta, int pos) { return tq::canonical
 extern "C" int tq_bitcheck_bchunk_offset(int k) { return tq::bchunk_offset(k); }
 extern "C" int tq_bitcheck_act_offset(int b, int pos) { return tq::act_offset(b, pos); }
 extern "C" int tq_bitcheck_act_scale_index(int b) { return tq::act_scale_index(b); }
+extern "C" uint32_t tq_bitcheck_e5m3_terms(uint32_t s) { return tq::e5m3_terms(s); }

@@ -115,6 +115,43 @@ TQ_HD int nibble_position(int n) {
   return 16 * (r >> 1) + 2 * m + (r & 1);
 }
 
+// ---- E5M3 block scales
+//
+// The XOR-Trellis article's paragraph on the grouping format puts E2M1
+// elements under E5M3 block scales without giving the encoding. Reading
+// taken: an unsigned 8-bit float laid out as the upper byte of an IEEE
+// binary16 number without its sign: exponent E in bits 7..3 (bias 15),
+// mantissa m in bits 2..0, subnormal at E = 0, infinity / NaN at E = 31.
+//
+// The matrix cores take UE8M0 (power-of-two) A scales only. A finite,
+// nonzero E5M3 value is n units of 2^(max(E,1) - 18) with significand
+// n = 8 + m (or m when subnormal), which has at most four binary digits;
+// halving the largest term until there are four writes it as a sum of
+// exactly four powers of two. e5m3_terms returns those four as UE8M0
+// bytes (byte i of the result); a step issued once per term with that
+// term as its A scale sums to the E5M3-scaled product exactly (each term's
+// products are exact). Returns 0 for the zero scale (no UE8M0 sum is zero:
+// the caller zeroes the A operand) and 0xFFFFFFFF (four NaN bytes) for
+// E = 31.
+TQ_HD uint32_t e5m3_terms(uint32_t s) {
+  const int E = (int)((s >> 3) & 31u), m = (int)(s & 7u);
+  if (E == 31) return 0xFFFFFFFFu;
+  const int n = E ? 8 + m : m;
+  if (n == 0) return 0u;
+  const int unit = (E ? E : 1) - 18 + 127;   // UE8M0 byte of one unit
+  int t[4], cnt = 0;
+  for (int j = 3; j >= 0; --j)
+    if ((n >> j) & 1) t[cnt++] = unit + j;
+  while (cnt < 4) {   // halve the largest term into two
+    int big = 0;
+    for (int i = 1; i < cnt; ++i)
+      if (t[i] > t[big]) big = i;
+    t[big] -= 1;
+    t[cnt++] = t[big];
+  }
+  return (uint32_t)t[0] | (uint32_t)t[1] << 8 | (uint32_t)t[2] << 16 | (uint32_t)t[3] << 24;
+}
+
 // ---- activation layout for the matrix cores (see tq_common.h for the operand layout)
 
 // Byte offset, inside one 128-K chunk of a B column (128 bytes laid out as the

@@ -79,6 +79,7 @@ __device__ __forceinline__ int tidx() {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+static_assert(kThreads == 256, "one E5M3 term-table entry per thread");
 constexpr int kMaxT = 128;
 constexpr int kMaxK = 32;
 constexpr int kMaxSlots = 1024;
@@ -100,6 +101,7 @@ enum { MODE_FFN = 0, MODE_SLOTS = 1, MODE_COMBINE = 2 };
 // activation layout: block b of a column goes to byte offset(b, pos) of the
 // step-chunk layout, its UE8M0 byte to scale_index(b).
 struct FmtTrellis {
+  static constexpr bool kE5M3 = false;   // UE8M0 block scales
   static constexpr int kSteps = 2;    // matrix-core steps per piece
   static constexpr int kBlocks = 8;   // 32-weight blocks per piece
   static constexpr int kWords = 2;    // 32-bit words per block
@@ -109,12 +111,19 @@ struct FmtTrellis {
   __device__ __host__ static int block_of(int st, int beta) { return 8 * (st >> 1) + 2 * beta + (st & 1); }
 };
 struct FmtMx {
+  static constexpr bool kE5M3 = false;
   static constexpr int kSteps = 1;
   static constexpr int kBlocks = 4;
   static constexpr int kWords = 4;
   __device__ __host__ static int offset(int b, int pos) { return (b >> 2) * 128 + bchunk_offset(32 * (b & 3) + pos); }
   __device__ __host__ static int scale_index(int b) { return b; }
   __device__ __host__ static int block_of(int st, int beta) { return 4 * st + beta; }
+};
+// Trellis-coded weights under E5M3 block scales: the same streams and
+// layout; each matrix-core step is issued once per UE8M0 term of its A
+// scale (e5m3_terms, four terms) against one accumulator.
+struct FmtTrellisE5M3 : FmtTrellis {
+  static constexpr bool kE5M3 = true;
 };
 template <typename F>
 __host__ __device__ inline int fmt_steps(int nb) { return F::kSteps * ((nb + F::kBlocks - 1) / F::kBlocks); }
@@ -224,6 +233,41 @@ struct Shared {
   uint8_t as[kWaves][kAScaleBytes] __attribute__((aligned(16)));
 };
 static_assert(kWaves * 4 * 256 * sizeof(float) <= kBBytes / 2, "accumulator dump must fit the column area");
+
+// ---------------------------------------------------------------- A scales
+
+// e5m3_terms of every byte, filled by each E5M3 workgroup at entry (LDS;
+// allocated only in the kernels that use it).
+__shared__ uint32_t g_e5m3_terms[256];
+
+// A-scale operand of K-block HH of a step: `sa` holds the raw scale bytes of
+// the piece's two steps (byte HH is this step's). UE8M0: sa as it is (the
+// matrix-core op selects byte HH). E5M3: the byte's four terms; a zero
+// scale zeroes A (no UE8M0 sum is zero).
+template <typename F, int HH>
+__device__ __forceinline__ uint32_t a_scale(uint32_t sa, v8i &A) {
+  if constexpr (!F::kE5M3) {
+    return sa;
+  } else {
+    const uint32_t t = g_e5m3_terms[(sa >> (8 * HH)) & 0xFFu];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[i] = t ? A[i] : 0;
+    return t;
+  }
+}
+
+// One matrix-core step, with the A scale from a_scale<F, HH>.
+template <typename F, int HH>
+__device__ __forceinline__ v4f mma_a(const v8i &A, const v8i &B, v4f c, uint32_t sx, uint32_t sb) {
+  if constexpr (!F::kE5M3) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, HH, (int)sx, 0, (int)sb);
+  } else {
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 0, (int)sx, 0, (int)sb);
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 1, (int)sx, 0, (int)sb);
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 2, (int)sx, 0, (int)sb);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 3, (int)sx, 0, (int)sb);
+  }
+}
 
 // ---------------------------------------------------------------- helpers
 
@@ -800,15 +844,15 @@ __device__ __forceinline__ void mma_tile(const Tile &t, int p0, int np, bool til
         const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
         const nib2 d0 = decode_word(w0, hw);
         const nib2 d1 = decode_word(w1, w0);
-        const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        if (hh == 0) {
+          const uint32_t sx = a_scale<F, 0>(sa, A);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (hh == 0)
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 0, (int)sa, 0,
-                                                                     (int)sb[n]);
-          else
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[n], acc[n], 4, 0, 1, (int)sa, 0,
-                                                                     (int)sb[n]);
+          for (int n = 0; n < NT; ++n) acc[n] = mma_a<F, 0>(A, B[n], acc[n], sx, sb[n]);
+        } else {
+          const uint32_t sx = a_scale<F, 1>(sa, A);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[n] = mma_a<F, 1>(A, B[n], acc[n], sx, sb[n]);
         }
       }
     }
@@ -856,7 +900,7 @@ __device__ __forceinline__ uint32_t pre_sa(const PreCtx<NT> &x, int q) {
   return x.tile_ok && 8 * q + 2 * x.g < x.nb ? (uint32_t)*(const uint16_t *)(x.as_row + 8 * q) : 0x7F7Fu;
 }
 
-template <int NT, int S>
+template <typename F, int NT, int S>
 __device__ __forceinline__ void pre_step(const PreCtx<NT> &x, const PreDec &pd, BStep<NT> (&ring)[NT == 1 ? 3 : 1],
                                          uint32_t (&sa)[2], v4f (&acc)[NT], v4f (&acc2)[NT]) {
   constexpr int kD = NT == 1 ? 2 : 0;
@@ -866,22 +910,21 @@ __device__ __forceinline__ void pre_step(const PreCtx<NT> &x, const PreDec &pd, 
     if (S + kD < x.ns) read_bstep<NT>(ring[(S + kD) % (kD + 1)], x.lq, x.ls, x.psteps, S + kD, x.c, x.g);
     if (hh == 0 && S + 2 < x.ns) sa[(q + 1) & 1] = pre_sa(x, q + 1);
     const uint4 w = pd.s[q][hh];
-    const v8i A = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    v8i A = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     const BStep<NT> &cur = ring[S % (kD + 1)];
+    const uint32_t sx = a_scale<F, hh>(sa[q & 1], A);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if (hh == 0)
-        acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, cur.b[n], acc[n], 4, 0, 0, (int)sa[q & 1], 0,
-                                                                 (int)cur.s[n]);
+        acc[n] = mma_a<F, 0>(A, cur.b[n], acc[n], sx, cur.s[n]);
       else
-        acc2[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, cur.b[n], acc2[n], 4, 0, 1, (int)sa[q & 1], 0,
-                                                                  (int)cur.s[n]);
+        acc2[n] = mma_a<F, 1>(A, cur.b[n], acc2[n], sx, cur.s[n]);
     }
-    pre_step<NT, S + 1>(x, pd, ring, sa, acc, acc2);
+    pre_step<F, NT, S + 1>(x, pd, ring, sa, acc, acc2);
   }
 }
 
-template <int NT>
+template <typename F, int NT>
 __device__ __forceinline__ void mma_pre(const PreDec &pd, int np, bool tile_ok, const uint8_t *as_w, int astride,
                                         int nb, const uint8_t *lq, const uint8_t *ls, int psteps,
                                         const int (&col)[NT], const bool (&on)[NT], v4f (&acc)[NT], int lane) {
@@ -908,7 +951,7 @@ __device__ __forceinline__ void mma_pre(const PreDec &pd, int np, bool tile_ok, 
   for (int d = 0; d < kD; ++d) read_bstep<NT>(ring[d], lq, ls, psteps, d < x.ns ? d : 0, x.c, x.g);
   sa[0] = pre_sa(x, 0);
   sa[1] = 0x7F7Fu;
-  pre_step<NT, 0>(x, pd, ring, sa, acc, acc2);
+  pre_step<F, NT, 0>(x, pd, ring, sa, acc, acc2);
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] += acc2[n];
 }
@@ -1018,15 +1061,15 @@ __device__ __forceinline__ void stream_piece(StreamCtx<NT> &c, Ring &R, v4f (&ac
         const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
         const nib2 d0 = decode_word(w0, hw);
         const nib2 d1 = decode_word(w1, w0);
-        const v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+        if (hh == 0) {
+          const uint32_t sx = a_scale<F, 0>(sa, A);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (hh == 0)
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[0][n], acc[n], 4, 0, 0, (int)sa, 0,
-                                                                     (int)sb[0][n]);
-          else
-            acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[1][n], acc[n], 4, 0, 1, (int)sa, 0,
-                                                                     (int)sb[1][n]);
+          for (int n = 0; n < NT; ++n) acc[n] = mma_a<F, 0>(A, B[0][n], acc[n], sx, sb[0][n]);
+        } else {
+          const uint32_t sx = a_scale<F, 1>(sa, A);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[n] = mma_a<F, 1>(A, B[1][n], acc[n], sx, sb[1][n]);
         }
       }
     }
@@ -1212,7 +1255,7 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
       TQ_MARK(S, 5);
       lds_barrier();
       TQ_MARK(S, 6);
-      mma_pre<NT>(pd, J, tile_ok, as_w, astride, nb, S.bq, S.bs, F::kSteps * J, col, on, acc, lane);
+      mma_pre<F, NT>(pd, J, tile_ok, as_w, astride, nb, S.bq, S.bs, F::kSteps * J, col, on, acc, lane);
     } else {
       // Streamed (see mma_stream). fetch_ahead first (a resident token's
       // split, on a workgroup's first stage-1 item: it waits for the split
@@ -1531,6 +1574,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) S.trp = nullptr;
 #endif
+  if constexpr (F::kE5M3) g_e5m3_terms[tid] = e5m3_terms((uint32_t)tid);   // kThreads == 256
   if (tid == 0) {
     S.x_done = 0;
     // a wait of an earlier call on this workspace timed out: its counters
@@ -1775,7 +1819,7 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
                        (uint4 *)(ws + L.cntp), n1);
     if (hipGetLastError() != hipSuccess) return TRELLIS_EHIP;
   }
-  if constexpr (F::kSteps == 2) {
+  if constexpr (F::kSteps == 2 && !F::kE5M3) {
     // one token of trellis-coded weights: the single-token layer kernel
     TokCall c{(const uint32_t *)gu.w, gu.scales, (const uint32_t *)dn.w, dn.scales, E, hidden, inter, k,
               topk_ids, topk_w, x, x_dtype == TRELLIS_BF16, h, y, ws, L.reserve};

@@ -61,6 +61,19 @@ def scales(g: np.random.Generator, n_mat: int, rows: int, cols: int,
     return g.integers(lo, hi + 1, size=(n_mat, rows, cols // 32), dtype=np.int64).astype(np.uint8)
 
 
+# E5M3 block-scale bytes (exponent bits 7..3, mantissa 2..0): exponents 12..18
+# with every mantissa, the UE8M0 range above at eight steps per octave.
+E5M3_LO = 0x60
+E5M3_HI = 0x97
+
+
+def scales_e5m3(g: np.random.Generator, n_mat: int, rows: int, cols: int,
+                lo: int = E5M3_LO, hi: int = E5M3_HI) -> np.ndarray:
+    """E5M3 scale bytes, one per 32 weights, uniform in [lo, hi]: shape [n_mat, rows, cols // 32]."""
+    assert cols % 32 == 0
+    return g.integers(lo, hi + 1, size=(n_mat, rows, cols // 32), dtype=np.int64).astype(np.uint8)
+
+
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bf16 (round-to-nearest-even); return the raw uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
