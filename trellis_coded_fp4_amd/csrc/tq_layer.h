@@ -136,8 +136,8 @@ enum { ST_SKIPPED = 0, ST_ERROR = 1 };
 #define TQ_INLINE __attribute__((always_inline))
 
 // Timeline instrumentation, compiled in only with -DTQ_TRACE: per workgroup
-// 64 u64 slots of s_memrealtime stamps (entry, routing done, then ten per
-// item: id, start, marks 2..8, end).
+// 512 u64 slots of s_memrealtime stamps (entry, routing done, then ten per
+// item for its first 51 items: id, start, marks 2..8, end).
 #ifdef TQ_TRACE
 #define TQ_MARK(S, k) do { if (tix() == 0 && (S).trp) (S).trp[k] = __builtin_amdgcn_s_memrealtime(); } while (0)
 static void *g_trace = nullptr;
@@ -605,6 +605,43 @@ template <typename F, int NT, typename ColMap>
 __device__ __forceinline__ void copy_pass(uint8_t *lq, uint8_t *ls, const uint8_t *gq, const uint8_t *gs,
                                           int gsteps, int kp, int np, int nb, int ncols, ColMap src_col) {
   constexpr int kBatch = 8;
+  if (F::kSteps == 2 && ncols <= 128 && np <= kPieceMax) {
+    // Trellis windows (32 eight-byte units per column and piece): the same
+    // copy with multiply-shift quotients (exact: every dividend times the
+    // divisor stays below 2^20) in place of the general case's divisions.
+    // (tix: the per-unit addresses are recomputed per window, not hoisted
+    // out of the caller's window loop into registers)
+    const uint32_t m_np = ((1u << 20) + np - 1) / np, m_ps = ((1u << 20) + 2 * np - 1) / (2 * np);
+    const int per_col = 32 * np, total = ncols * per_col;
+    for (int base = tix(); base < total; base += kBatch * kThreads) {
+      uint64_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int idx = min(base + u * kThreads, total - 1);
+        const int c = (int)(((uint32_t)(idx >> 5) * m_np) >> 20), p = idx - c * per_col;
+        v[u] = ld_dc64(gq + ((size_t)src_col(c) * gsteps + 2 * kp + (p >> 4)) * 128 + (p & 15) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int idx = base + u * kThreads;
+        if (idx < total) {
+          const int c = (int)(((uint32_t)(idx >> 5) * m_np) >> 20), p = idx - c * per_col;
+          const bool pad = F::kBlocks * kp + chunk_block<F>(p >> 4, (p & 15) * 8) >= nb;
+          *(uint64_t *)(lq + (size_t)idx * 8) = pad ? 0ull : v[u];
+        }
+      }
+    }
+    const int stotal = ncols * 2 * np;
+    for (int idx = tix(); idx < stotal; idx += kThreads) {
+      const int c = (int)(((uint32_t)idx * m_ps) >> 20), st = idx - c * 2 * np;
+      uint32_t w = ld_dc32(gs + ((size_t)src_col(c) * gsteps + 2 * kp + st) * 4);
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta)
+        if (F::kBlocks * kp + F::block_of(st, beta) >= nb) w = (w & ~(0xFFu << (8 * beta))) | (127u << (8 * beta));
+      *(uint32_t *)(ls + (size_t)idx * 4) = w;
+    }
+    return;
+  }
   const int psteps = F::kSteps * np, per_col = psteps * 16;   // 8-byte pieces per column
   const int total = ncols * per_col;
   for (int base = tidx<NT>(); base < total; base += kBatch * kThreads) {
@@ -1168,6 +1205,117 @@ __device__ __forceinline__ void arrive_and_combine(const LayerArgs &a, Shared &S
   if (S.last) combine_rows(a, S, rt);
 }
 
+// ---------------------------------------------------------------- many slots per expert
+
+// One piece of a many-slot pass: decode piece Q of the tile (history from
+// lane-group g-1 of the same piece, or the previous piece's last word) and
+// multiply it into the accumulators of the pass's up to 64 slots: N-tiles
+// 0..3 (LDS columns 0..63) in acc0, 4..7 (columns 64..127) in acc1. The LDS
+// holds the slots' activation columns of the window's pieces (psteps steps
+// per column); the piece's steps are st0 and st0 + 1 there.
+template <typename F, int Q>
+__device__ __forceinline__ void pf_piece(const Tile &tl, int psteps, int st0, const uint8_t *as_w, int astride,
+                                         int nb, bool tile_ok, uint32_t &carry, const uint8_t *lq, const uint8_t *ls,
+                                         int ncol, v4f (&acc0)[4], v4f (&acc1)[4]) {
+  // (tix: the lane-derived LDS addresses are recomputed here, per piece;
+  // hoisted out of the window loop they would outlive it in registers)
+  const int lane = tix() & 63, g = lane >> 4, i16 = lane & 15;
+  const uint4 a = tl.a[Q];
+  const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(((lane - 16) & 63) << 2, (int)a.w);
+  const uint32_t hist = g == 0 ? carry : rot;
+  carry = rot;
+  // (A scales past the row's blocks, and of tiles past the matrix: finite
+  // bytes that meet zero codes or unused rows)
+  const uint32_t sa = tile_ok && 8 * Q + 2 * g < nb
+                          ? (uint32_t)*(const uint16_t *)(as_w + i16 * astride + 2 * g + 8 * Q) : 0x7F7Fu;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint32_t w0 = hh ? a.z : a.x, w1 = hh ? a.w : a.y, hw = hh ? a.y : hist;
+    const nib2 d0 = decode_word(w0, hw);
+    const nib2 d1 = decode_word(w1, w0);
+    v8i A = v8i{(int)d0.even, (int)d0.odd, (int)d1.even, (int)d1.odd, 0, 0, 0, 0};
+    const uint32_t sx = hh ? a_scale<F, 1>(sa, A) : a_scale<F, 0>(sa, A);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if (n >= 4 && ncol <= 32) break;   // uniform
+      // unused N-tile lanes read column 0 or 1 (their outputs are never stored)
+      const int c = n * 8 + (i16 >> 1) < ncol ? n * 16 + i16 : (i16 & 1);
+      const int cs = c * psteps + st0 + hh;
+      const uint4 *p = (const uint4 *)(lq + cs * 128 + g * 32);
+      const uint4 u0 = p[0], u1 = p[1];
+      const v8i B = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      const uint32_t sb = ls[cs * 4 + g];
+      v4f &d = n < 4 ? acc0[n & 3] : acc1[n & 3];
+      d = hh ? mma_a<F, 1>(A, B, d, sx, sb) : mma_a<F, 0>(A, B, d, sx, sb);
+    }
+  }
+}
+
+// The window's pieces [p0, p0 + np), by compile-time recursion over the
+// tile's piece index (the tile stays in registers).
+template <typename F, int Q>
+__device__ __forceinline__ void pf_window(int p0, int np, const Tile &tl, const uint8_t *as_w, int astride, int nb,
+                                          bool tile_ok, uint32_t &carry, const uint8_t *lq, const uint8_t *ls,
+                                          int ncol, v4f (&acc0)[4], v4f (&acc1)[4]) {
+  if constexpr (Q < kPieceMax) {
+    if (Q >= p0 + np) return;
+    if (Q >= p0) pf_piece<F, Q>(tl, 2 * np, 2 * (Q - p0), as_w, astride, nb, tile_ok, carry, lq, ls, ncol, acc0, acc1);
+    pf_window<F, Q + 1>(p0, np, tl, as_w, astride, nb, tile_ok, carry, lq, ls, ncol, acc0, acc1);
+  }
+}
+
+// An item whose expert has more slots than one window pass of the general
+// loop holds (at K = 4096 that is 4): each pass of up to 64 slots loads the
+// tile (<= 16 pieces) once, all of it in flight at once, and decodes it
+// once. The pass's activation columns come into LDS a window of pieces at a
+// time, as many pieces as the 32 KB column area holds for its slots (one
+// piece for 64 slots, eight for 8). The pass's two halves of 32 slots go to
+// the epilogue one after the other.
+template <typename F, bool ALIGNED, typename Stage, typename Epi>
+__device__ __forceinline__ void pf_item(Shared &S, Tile &tl, const uint32_t *rowp, const uint8_t *srow,
+                                        const uint8_t *stile, int wpr, int nb, int J, int fast, bool tile_ok, int ne,
+                                        Stage &stage, Epi &epilogue) {
+  const int lane = tix() & 63, wave = tix() >> 6, g = lane >> 4;
+  uint8_t *as_w = S.as[wave];
+  if (fast) {
+    AScalePre sp;
+    ascale_prefetch(sp, stile, nb);
+    ascale_store(as_w, sp, nb);
+    // the last row's last piece may read a byte past the tile's scales: a finite one
+    if (lane == 0 && 16 * nb + 8 <= kAScaleBytes) *(uint64_t *)(as_w + 16 * nb) = 0x7F7F7F7F7F7F7F7Full;
+  } else {
+    ascale_generic<F>(as_w, srow, nb, 0, J, tile_ok);
+  }
+  const int astride = fast ? nb : 128;
+  for (int c0 = 0; c0 < ne; c0 += 64) {
+    const int ncol = min(ne - c0, 64);
+    const int W = max(1, min(J, kBBytes / (ncol * 2 * F::kSteps * 128)));   // pieces per window
+    v4f acc0[4], acc1[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc0[n] = acc1[n] = v4f{0.f, 0.f, 0.f, 0.f};
+    uint32_t carry = 0u;
+    load_tile_full<ALIGNED, kPieceMax>(tl, rowp, wpr, J, g);
+    TQ_MARK(S, 3);
+    for (int p0 = 0; p0 < J; p0 += W) {
+      const int np = min(W, J - p0);
+      stage(c0, ncol, p0, np);   // the window's activation columns of the pass's slots
+      __syncthreads();
+      if (p0 == 0) TQ_MARK(S, 4);
+      pf_window<F, 0>(p0, np, tl, as_w, astride, nb, tile_ok, carry, S.bq, S.bs, ncol, acc0, acc1);
+      __syncthreads();   // everyone is done with the window's columns
+      if (p0 == 0) TQ_MARK(S, 5);
+    }
+    TQ_MARK(S, 6);
+    epilogue(c0, min(ncol, 32), acc0);
+    if (ncol > 32) {
+      __syncthreads();
+      epilogue(c0 + 32, ncol - 32, acc1);
+    }
+    __syncthreads();
+    TQ_MARK(S, 7);
+  }
+}
+
 // ---------------------------------------------------------------- work items
 
 // The grouped GEMM of one item: expert e, 16 rows per wave starting at r0
@@ -1195,6 +1343,12 @@ __device__ __forceinline__ void gemm_item(Shared &S, const uint32_t *w, const ui
   const int astride = fast ? nb : 128;
   const int gsz = min(NT * 8, kBBytes / (min(J, kPieceMax) * F::kSteps * 256));
   Tile tl;
+  if constexpr (NT == 4 && F::kSteps == 2) {
+    if (J <= kPieceMax && ne > gsz) {
+      pf_item<F, ALIGNED>(S, tl, rowp, srow, sc + row0 * nb, wpr, nb, J, fast, tile_ok, ne, stage, epilogue);
+      return;
+    }
+  }
   if (J <= kPieceMax && ne <= gsz) {
     // The common case, one window and one slot group, as straight-line code.
     // Load order: activations, the tile's pieces, whatever the stage loads,
@@ -1550,15 +1704,23 @@ __device__ __forceinline__ void bookkeeping(const LayerArgs &a, Shared &S) {
 // call: hi and lo E4M3 columns with their UE8M0 scales, in the step-chunk
 // layout the stage-1 items copy into LDS. Splitting per item instead redid
 // the same work for every item of every expert the token is routed to.
+// The split goes to LDS first and leaves in 16-byte stores (the split's own
+// byte-scattered stores, straight to global memory, took ~30 us per token).
 template <typename F, int NT>
-__device__ __forceinline__ void run_prep(const LayerArgs &a, int t) {
+__device__ __forceinline__ void run_prep(const LayerArgs &a, Shared &S, int t) {
   const int K = a.cols1, nb = K / 32;
   const size_t el = (size_t)t * K;
   const void *xt = a.x_bf16 ? (const void *)((const uint16_t *)a.x + el) : (const void *)((const float *)a.x + el);
   TokRaw tok;
   tok_load_at(tok, xt, a.x_bf16, nb);
-  tok_split<F>(tok, a.xq + (size_t)t * 2 * a.x_steps * 128, a.xs + (size_t)t * 2 * a.x_steps * 4, a.x_steps, nb,
-               a.x_bf16);
+  tok_split<F>(tok, S.bq, S.bs, a.x_steps, nb, a.x_bf16);   // every byte of both columns (K padding: zeros)
+  __syncthreads();
+  {
+    uint4 *dq = (uint4 *)(a.xq + (size_t)t * 2 * a.x_steps * 128);
+    for (int i = tidx<NT>(); i < a.x_steps * 16; i += kThreads) dq[i] = ((const uint4 *)S.bq)[i];
+    uint32_t *ds = (uint32_t *)(a.xs + (size_t)t * 2 * a.x_steps * 4);
+    for (int i = tidx<NT>(); i < a.x_steps * 2; i += kThreads) ds[i] = ((const uint32_t *)S.bs)[i];
+  }
   // visible device-wide before it is counted
   __threadfence();
   __syncthreads();
@@ -1570,7 +1732,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   __shared__ Shared S;
   const int tid = tidx<NT>();
 #ifdef TQ_TRACE
-  unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 64 : nullptr;
+  unsigned long long *TR = a.trace ? a.trace + (size_t)blockIdx.x * 512 : nullptr;
   if (TR && tid == 0) TR[0] = __builtin_amdgcn_s_memrealtime();
   if (tid == 0) S.trp = nullptr;
 #endif
@@ -1630,14 +1792,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   for (int item = blockIdx.x; item < n_items; item += a.grid) {
 #ifdef TQ_TRACE
     if (tid == 0) {
-      S.trp = (TR && it_no < 6) ? TR + 2 + 10 * it_no : nullptr;
+      S.trp = (TR && it_no < 51) ? TR + 2 + 10 * it_no : nullptr;
       if (S.trp) S.trp[0] = (unsigned long long)item;
     }
     __syncthreads();
     TQ_MARK(S, 1);
     ++it_no;
 #endif
-    if (item < a.n_prep) run_prep<F, NT>(a, item);
+    if (item < a.n_prep) run_prep<F, NT>(a, S, item);
     else run_item<F, NT, ALIGNED>(a, S, item - a.n_prep);
     // nothing of this item stays in flight into the next one (the
     // compiler's waits in the next item then count only its own loads)
