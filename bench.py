@@ -327,7 +327,10 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
             ("; the router itself is not part of the sample" if router else "") + \
             f"), C oracle on {threads} thread(s), {dt:.1f} s"
 
-    if mx:
+    if mx and T == 1:
+        kernel = ("k_tok<MX> (single-token MoE layer on expanded MXFP4 weights: routing, FP4 matrix-core gate_up "
+                  "+ SwiGLU, tagged h hand-off, down + gate-weighted atomic combine)")
+    elif mx:
         kernel = "k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)"
     elif e5m3:
         kernel = ("k_layer<FmtTrellisE5M3> (whole MoE layer, E5M3 block scales: each matrix-core step issued "

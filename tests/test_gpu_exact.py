@@ -171,11 +171,19 @@ def _candidate_gap(orc):
     return gap
 
 
-def _ffn_dev(tq, L):
-    return [dev(L.gu_syms), dev(L.gu_scales), dev(L.dn_syms), dev(L.dn_scales)]
+def _ffn_dev(tq, L, orc=None, mx_experts=None):
+    """The layer's weights on the device: trellis streams, or (mx_experts
+    given) the MXFP4 codes and scales the oracle expands for those experts
+    (the other experts are never read)."""
+    if mx_experts is None:
+        return [dev(L.gu_syms), dev(L.gu_scales), dev(L.dn_syms), dev(L.dn_scales)]
+    from test_gpu_mxfp4 import _expand
+    gc, gs = _expand(orc, L.gu_syms, L.gu_scales, mx_experts)
+    dc, ds = _expand(orc, L.dn_syms, L.dn_scales, mx_experts)
+    return [dev(gc), dev(gs), dev(dc), dev(ds)]
 
 
-def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws):
+def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws, mx=False):
     """One layer call per list of probe columns (one token each); returns h, y."""
     import torch
     n, T = len(col_lists), len(col_lists[0])
@@ -183,8 +191,9 @@ def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws):
     Hh = torch.empty((n, T, k, I), dtype=torch.bfloat16, device="cuda")
     Yy = torch.empty((n, T, H), dtype=torch.float32, device="cuda")
     dids, dgw = dev(ids), dev(gw)
+    fn = tq.mxfp4_moe_ffn if mx else tq.moe_ffn
     for i, cs in enumerate(col_lists):
-        tq.moe_ffn(*wd, _rows_of(eye, cs), dids, dgw, h=Hh[i], y=Yy[i], workspace=ws)
+        fn(*wd, _rows_of(eye, cs), dids, dgw, h=Hh[i], y=Yy[i], workspace=ws)
     h = Hh.float().cpu().numpy()
     y = Yy.cpu().numpy()
     assert int(ws[:8].view(torch.int32)[1].item()) == 0, "a wait timed out"
@@ -199,9 +208,11 @@ def _layer_setup(cfg, T, seed):
     return L, act, ids, gw
 
 
-def _stage1_probe(tq, orc, cfg, T, which, seed=0):
+def _stage1_probe(tq, orc, cfg, T, which, seed=0, mx=False):
     """which = 'gate': up rows of the active experts are the all-zero stream;
-    'up': gate rows are. h at every column identifies the other weight."""
+    'up': gate rows are. h at every column identifies the other weight.
+    mx: the same weights expanded to MXFP4 by the oracle, through the
+    layer on expanded weights."""
     import torch
     H, I, k = cfg.hidden, cfg.inter, cfg.k
     L, act, ids, gw = _layer_setup(cfg, T, seed)
@@ -210,11 +221,11 @@ def _stage1_probe(tq, orc, cfg, T, which, seed=0):
         L.gu_syms[e, zero_rows] = 0
     if which == "gate":
         assert _candidate_gap(orc) > 2.0 ** -7   # > 2^-8 (accepted) + 2^-9 (bf16 rounding) + margin
-    wd = _ffn_dev(tq, L)
+    wd = _ffn_dev(tq, L, orc, act if mx else None)
     eye = _eye(H)
     ws = tq.ffn_workspace(cfg.n_exp, H, I, T, k)
     lists = [(c0 + np.arange(T)) % H for c0 in range(0, H, T)]
-    h, _ = _run_layer(tq, wd, eye, lists, ids, gw, I, H, ws)
+    h, _ = _run_layer(tq, wd, eye, lists, ids, gw, I, H, ws, mx)
     probe = np.concatenate(lists)                       # column of each (call, token)
     h = h.reshape(-1, k, I)
     worst = 0.0
@@ -239,9 +250,10 @@ def _stage1_probe(tq, orc, cfg, T, which, seed=0):
     print(f"{which}: {len(probe)} columns x {I} rows x {k} experts, worst relative h error {worst:.2e}")
 
 
-def _down_probe(tq, orc, cfg, T, seed=0):
+def _down_probe(tq, orc, cfg, T, seed=0, mx=False):
     """Crafted gate rows make h one-hot at one row r per token; y then exposes
-    column r of every active down matrix exactly."""
+    column r of every active down matrix exactly (mx: on the weights
+    expanded to MXFP4 by the oracle)."""
     import torch
     H, I, k = cfg.hidden, cfg.inter, cfg.k
     L, act, ids, gw = _layer_setup(cfg, T, seed)
@@ -253,7 +265,7 @@ def _down_probe(tq, orc, cfg, T, seed=0):
     for e in act:
         L.gu_syms[e, I:] = 0                            # up rows: -6 everywhere
         L.gu_scales[e] = 127
-    wd = _ffn_dev(tq, L)
+    wd = _ffn_dev(tq, L, orc, act if mx else None)
     eye = _eye(H)
     ws = tq.ffn_workspace(cfg.n_exp, H, I, T, k)
     Wdn = [orc.decode_values(L.dn_syms[e], L.dn_scales[e]) for e in act]   # [H, I] each
@@ -269,10 +281,11 @@ def _down_probe(tq, orc, cfg, T, seed=0):
         want_nz = np.zeros_like(dec, bool)
         want_nz[r_all[mine], r_all[mine] // n_st] = True
         assert np.array_equal(dec != 0, want_nz) and (dec[want_nz] == 2.0).all()
+        g_dev = dev(orc.expand(gate[None], np.full((1, I, H // 32), 127, np.uint8))[0][0]) if mx else dev(gate)
         for e in act:
-            wd[0][int(e), :I] = dev(gate)
+            wd[0][int(e), :I] = g_dev
         lists = [(p0 + np.arange(T)) % P for p0 in range(0, P, T)]
-        h, y = _run_layer(tq, wd, eye, [8 * p + 7 for p in lists], ids, gw, I, H, ws)
+        h, y = _run_layer(tq, wd, eye, [8 * p + 7 for p in lists], ids, gw, I, H, ws, mx)
         n_of = np.concatenate(lists)
         r_of = n_of * n_st + sigma
         h = h.reshape(-1, k, I)
@@ -310,10 +323,13 @@ LAYERS = {
     # hidden and inter not multiples of 64: the general layer kernel's single-token path
     # (unaligned rows, pre-decoded down projection)
     "odd": workloads.MoEConfig(95, "8 experts top-4 H=2912 I=1440", 8, 2912, 1440, 4, 1, True),
+    # one piece per row: waves of the single-token kernel without pieces of their own
+    "small": workloads.MoEConfig(96, "8 experts top-4 H=256 I=128", 8, 256, 128, 4, 1, True),
 }
 
 
-@pytest.mark.parametrize("layer,T", [("moe32", 1), ("moe32", 128), ("moe128", 1), ("moe128", 32), ("odd", 1)])
+@pytest.mark.parametrize("layer,T", [("moe32", 1), ("moe32", 128), ("moe128", 1), ("moe128", 32), ("odd", 1),
+                                     ("small", 1)])
 @pytest.mark.parametrize("which", ["gate", "up"])
 def test_layer_gate_up_decode_exact(trellis_lib, orc, layer, T, which):
     cfg = LAYERS[layer]
@@ -321,8 +337,28 @@ def test_layer_gate_up_decode_exact(trellis_lib, orc, layer, T, which):
     _stage1_probe(trellis_lib, orc, cfg, T, which)
 
 
-@pytest.mark.parametrize("layer,T", [("moe32", 1), ("moe32", 128), ("moe128", 1), ("moe128", 32), ("odd", 1)])
+@pytest.mark.parametrize("layer,T", [("moe32", 1), ("moe32", 128), ("moe128", 1), ("moe128", 32), ("odd", 1),
+                                     ("small", 1)])
 def test_layer_down_decode_exact(trellis_lib, orc, layer, T):
     cfg = LAYERS[layer]
     announce(f"exact layer down probe {cfg.name} T={T}")
     _down_probe(trellis_lib, orc, cfg, T)
+
+
+# Expanded MXFP4 weights (expand mode): the same probes through
+# trellis_mxfp4_moe_ffn, on codes the oracle expands. One token runs the
+# single-token kernel where it takes the shape (moe32, small), the general
+# layer kernel otherwise (moe128 at eight slots, odd widths).
+@pytest.mark.parametrize("layer,T", [("moe32", 1), ("small", 1), ("moe128", 1), ("odd", 1), ("moe32", 8)])
+@pytest.mark.parametrize("which", ["gate", "up"])
+def test_mxfp4_layer_gate_up_exact(trellis_lib, orc, layer, T, which):
+    cfg = LAYERS[layer]
+    announce(f"exact mxfp4 layer stage-1 probe ({which}) {cfg.name} T={T}")
+    _stage1_probe(trellis_lib, orc, cfg, T, which, mx=True)
+
+
+@pytest.mark.parametrize("layer,T", [("moe32", 1), ("small", 1), ("moe128", 1), ("odd", 1), ("moe32", 8)])
+def test_mxfp4_layer_down_exact(trellis_lib, orc, layer, T):
+    cfg = LAYERS[layer]
+    announce(f"exact mxfp4 layer down probe {cfg.name} T={T}")
+    _down_probe(trellis_lib, orc, cfg, T, mx=True)

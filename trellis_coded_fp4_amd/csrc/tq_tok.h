@@ -1,5 +1,6 @@
 // tq_tok.h -- host interface of the single-token mixture-of-experts layer
-// kernel (tq_tok.hip), which trellis_moe_ffn uses for one token.
+// kernel (tq_tok.hip), which trellis_moe_ffn and trellis_mxfp4_moe_ffn use
+// for one token.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -19,12 +20,14 @@ TokRegion tok_region(int n_exp, int hidden, int inter);
 struct TokCall {
   const uint32_t *w1; const uint8_t *s1;   // gate_up [E][2I][H]
   const uint32_t *w2; const uint8_t *s2;   // down    [E][H][I]
+  // (trellis symbols, or with mx set expanded MXFP4 codes, cols / 2 bytes a row)
   int E, H, I, k;
   const int32_t *ids; const float *gate_w;
   const void *x; int x_bf16;
   uint16_t *h; float *y;
   char *ws;                                // layer workspace (status words at 0)
   size_t region_off;                       // offset of the TokRegion
+  bool mx = false;                         // weights are expanded MXFP4
 };
 
 // True when the kernel takes this shape (otherwise the general layer kernel

@@ -7,6 +7,8 @@
 // "XOR-Trellis FP4 decoder"), bit-sliced in tq_decode.h; the decoded E2M1
 // nibbles and the weights' UE8M0 bytes feed the block-scaled FP4 x FP8
 // matrix cores, the token's activations entering as a two-term FP8 split.
+// The same kernel serves expand mode (HEPH abstract): weights already
+// expanded to MXFP4 go to the matrix cores as loaded, with no decode.
 //
 // Why a kernel of its own for one token: the layer moves ~28 MB at the
 // 32-expert shape and every weight costs ~1.5 VALU operations to decode, so
@@ -134,7 +136,10 @@ __device__ __forceinline__ float quad_max4(float v) {
 // Two-term FP8 split of one 32-value block held by a quad (lane j of the
 // quad: values 8j .. 8j+7): hi = E4M3(v / 2^E), lo = E4M3((v - hi 2^E) / 2^El),
 // each with its UE8M0 exponent, written into column pair (lq, lq + psteps*128)
-// at block b's place in the step-chunk layout. `store` is uniform per quad.
+// at block b's place in the step-chunk layout of the weight format (MX:
+// expanded MXFP4, natural order, block b in step b / 4 as K-block b % 4;
+// otherwise the trellis decoder's order). `store` is uniform per quad.
+template <bool MX>
 __device__ __forceinline__ void split_block8(const float (&f)[8], int b, int j, uint8_t *lq, uint8_t *ls,
                                              int psteps, bool store) {
   float m = 0.0f;
@@ -154,11 +159,22 @@ __device__ __forceinline__ void split_block8(const float (&f)[8], int b, int j, 
 #pragma unroll
   for (int i = 0; i < 8; i += 2) lo[i / 2] = f32x2_to_e4m3(ldexpf(res[i], -El), ldexpf(res[i + 1], -El));
   if (!store) return;
+  const uint32_t h01 = hi[0] | hi[1] << 16, h23 = hi[2] | hi[3] << 16;
+  const uint32_t l01 = lo[0] | lo[1] << 16, l23 = lo[2] | lo[3] << 16;
+  if (MX) {
+    // values 8j .. 8j+7 are eight consecutive bytes of the chunk
+    const int off = (b >> 2) * 128 + bchunk_offset(32 * (b & 3) + 8 * j);
+    *(uint2 *)(lq + off) = make_uint2(h01, h23);
+    *(uint2 *)(lq + (size_t)psteps * 128 + off) = make_uint2(l01, l23);
+    if (j == 0) {
+      ls[b] = (uint8_t)(E + 127);
+      ls[(size_t)psteps * 4 + b] = (uint8_t)(El + 127);
+    }
+    return;
+  }
   // values 8j + 2m (m = 0..3) sit at four consecutive bytes of the chunk,
   // values 8j + 2m + 1 eight bytes further on (the decoder's even/odd order)
   const int off = act_offset(b, 8 * j);
-  const uint32_t h01 = hi[0] | hi[1] << 16, h23 = hi[2] | hi[3] << 16;
-  const uint32_t l01 = lo[0] | lo[1] << 16, l23 = lo[2] | lo[3] << 16;
   *(uint32_t *)(lq + off) = __builtin_amdgcn_perm(h23, h01, 0x06040200u);
   *(uint32_t *)(lq + off + 8) = __builtin_amdgcn_perm(h23, h01, 0x07050301u);
   *(uint32_t *)(lq + (size_t)psteps * 128 + off) = __builtin_amdgcn_perm(l23, l01, 0x06040200u);
@@ -222,13 +238,17 @@ __device__ __forceinline__ void pin(DecA &d) {
                "+v"(d.s1.z), "+v"(d.s1.w));
 }
 
-// One wave's loads of one tile: its PPW pieces (16 bytes per lane each) and
-// the word before its first piece (decoder history of lane-group 0).
-template <int PPW>
+// One wave's loads of one tile: its PPW pieces and, for trellis streams,
+// the word before its first piece (decoder history of lane-group 0). A
+// piece is 8 blocks of 32 weights of each of the 16 rows, two matrix-core
+// steps. Trellis: 16 bytes of symbols per lane (blocks 8p+2g, 8p+2g+1),
+// decoded into the two steps' A operands. Expanded MXFP4 (MX): the two A
+// operands as stored, 16 bytes each (blocks 8p+g and 8p+4+g).
+template <int PPW, bool MX>
 struct TileLd {
-  uint4 w[PPW];
+  uint4 w[MX ? 2 * PPW : PPW];
   uint32_t hist;
-  uint32_t sc[PPW];   // UE8M0 bytes of blocks 8p+2g, 8p+2g+1 of each piece p
+  uint32_t sc[PPW];   // the UE8M0 bytes of the piece's two blocks (byte 0: first step)
 };
 
 // Decode piece words `a` whose history is `hist` (lane-group 0: the word
@@ -242,6 +262,19 @@ __device__ __forceinline__ DecA decode_words(const uint4 &a, uint32_t hist) {
   return d;
 }
 
+// A operands of piece q of a tile (trellis: decoded, history `hist`).
+template <int PPW, bool MX>
+__device__ __forceinline__ DecA piece_a(const TileLd<PPW, MX> &L, int q, uint32_t hist) {
+  if constexpr (MX) {
+    DecA d;
+    d.s0 = L.w[2 * q];
+    d.s1 = L.w[2 * q + 1];
+    return d;
+  } else {
+    return decode_words(L.w[q], hist);
+  }
+}
+
 // Eight waves, two per SIMD, in two roles. Waves 0-3 ("gate/up waves")
 // each own PPW consecutive pieces of every gate/up tile of the workgroup
 // (T1 tiles at most), streamed through a register ring AT tiles deep (a
@@ -253,8 +286,11 @@ __device__ __forceinline__ DecA decode_words(const uint4 &a, uint32_t hist) {
 // and decode them while the gate/up waves work and h is on its way; after
 // h arrives they run the down projection's matrix-core steps. The roles
 // meet through LDS flags until the gate/up work is done, so neither waits
-// at a barrier for the other's loads.
-template <int PPW, int T1, int T2, int AT>
+// at a barrier for the other's loads. MX: the weights are expanded MXFP4
+// (codes [rows][cols / 2], even column in the low nibble, same scales),
+// fed to the matrix cores as loaded; the activations take that format's
+// layout.
+template <int PPW, int T1, int T2, int AT, bool MX>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k_tok(Args a) {
   constexpr int NW = 8, NR = 4;   // waves, waves per role
   __shared__ Smem S;
@@ -353,21 +389,42 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   const int J = up_role ? J1 : J2;
   const int pa = min(rw * PPW, J), c = min(J - pa, PPW);
   // loads of the tile whose first row is `r0` (gate/up matrix if s1)
-  auto load_tile = [&](size_t r0, bool s1) -> TileLd<PPW> {
-    TileLd<PPW> L;
+  auto load_tile = [&](size_t r0, bool s1) -> TileLd<PPW, MX> {
+    TileLd<PPW, MX> L;
     const size_t r = r0 + i16;
-    const uint32_t *rp = s1 ? a.w1 + r * wpr1 : a.w2 + r * wpr2;
     const uint8_t *sp = s1 ? a.s1 + r * nb1 : a.s2 + r * nb2;
-    const int wpr = s1 ? wpr1 : wpr2, nb = s1 ? nb1 : nb2;
+    const int nb = s1 ? nb1 : nb2;
+    if constexpr (MX) {
+      // 16 bytes per block; the row's last block stands in for blocks past it
+      const uint8_t *rp = (const uint8_t *)(s1 ? a.w1 : a.w2) + r * (size_t)nb * 16;
 #pragma unroll
-    for (int q = 0; q < PPW; ++q) L.sc[q] = *(const uint16_t *)(sp + min(8 * (pa + q) + 2 * g, nb - 2));
+      for (int q = 0; q < PPW; ++q)
+        L.sc[q] = (uint32_t)sp[min(8 * (pa + q) + g, nb - 1)] | (uint32_t)sp[min(8 * (pa + q) + 4 + g, nb - 1)] << 8;
 #pragma unroll
-    for (int q = 0; q < PPW; ++q) L.w[q] = *(const uint4 *)(rp + min(16 * (pa + q) + 4 * g, wpr - 4));
-    L.hist = rp[min(max(16 * pa - 1, 0), wpr - 1)];
+      for (int q = 0; q < PPW; ++q) {
+        L.w[2 * q] = *(const uint4 *)(rp + 16 * min(8 * (pa + q) + g, nb - 1));
+        L.w[2 * q + 1] = *(const uint4 *)(rp + 16 * min(8 * (pa + q) + 4 + g, nb - 1));
+      }
+      L.hist = 0;
+    } else {
+      const uint32_t *rp = s1 ? a.w1 + r * wpr1 : a.w2 + r * wpr2;
+      const int wpr = s1 ? wpr1 : wpr2;
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) L.sc[q] = *(const uint16_t *)(sp + min(8 * (pa + q) + 2 * g, nb - 2));
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) L.w[q] = *(const uint4 *)(rp + min(16 * (pa + q) + 4 * g, wpr - 4));
+      L.hist = rp[min(max(16 * pa - 1, 0), wpr - 1)];
+    }
     return L;
   };
-  // A-scale pair of piece p (blocks past the row: 2^0, meeting zero codes)
-  auto a_scale = [&](uint32_t sc, int nb, int p) -> uint32_t { return 8 * p + 2 * g < nb ? sc : 0x7F7Fu; };
+  // A-scale pair of piece p (blocks past the row: 2^0, meeting zero
+  // activations; the codes there are the row's own, finite)
+  auto a_scale = [&](uint32_t sc, int nb, int p) -> uint32_t {
+    if constexpr (MX)
+      return (8 * p + g < nb ? sc & 0xFFu : 0x7Fu) | (8 * p + 4 + g < nb ? sc & 0xFF00u : 0x7F00u);
+    else
+      return 8 * p + 2 * g < nb ? sc : 0x7F7Fu;
+  };
 
   DecA D2[T2][PPW];
   uint32_t sc2[T2][PPW];
@@ -390,7 +447,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
       }
       row[t] = n1 > 0 ? (size_t)__builtin_amdgcn_readlane(act_e, ai) * 2 * I + (tc & 1 ? I : 0) + 16 * j : 0;
     }
-    TileLd<PPW> R[AT];
+    TileLd<PPW, MX> R[AT];
 #pragma unroll
     for (int t = 0; t < AT; ++t) R[t] = load_tile(row[t], true);
     asm volatile("" ::: "memory");
@@ -410,7 +467,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
         const uint32_t bits = a.x_bf16 ? (wv[i >> 1] >> (16 * (i & 1))) << 16 : wv[i];
         f[i] = xb < nb1 ? __uint_as_float(bits) : 0.0f;
       }
-      split_block8(f, xb, xj, S.xq, S.xs, ps1, xb < 8 * (pa + c));
+      split_block8<MX>(f, xb, xj, S.xq, S.xs, ps1, xb < 8 * (pa + c));
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     TOK_MARK(2);
@@ -423,7 +480,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
         bx[q][hh] = read_b(S.xq, S.xs, ps1, i16 & 1, min(2 * (pa + q) + hh, ps1 - 1), g);
 #pragma unroll
     for (int t = 0; t < T1; ++t) {
-      const TileLd<PPW> cur = R[t % AT];
+      const TileLd<PPW, MX> cur = R[t % AT];
       if (t + AT < T1) {
         R[t % AT] = load_tile(row[t + AT], true);
         if (t + AT == T1 - 1 && lane == 0)
@@ -435,8 +492,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
         for (int q = 0; q < PPW; ++q) {
           if (q < c) {
-            const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
-            const DecA d = decode_words(cur.w[q], g == 0 ? carry : rot);
+            const uint32_t rot = MX ? 0u : (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
+            const DecA d = piece_a<PPW, MX>(cur, q, g == 0 ? carry : rot);
             carry = rot;
             acc = mma2(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], nb1, pa + q), acc);
           }
@@ -540,7 +597,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     while (__hip_atomic_load(&S.up_issued, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NR)
       __builtin_amdgcn_s_sleep(2);
     asm volatile("" ::: "memory");
-    TileLd<PPW> L2[T2];
+    TileLd<PPW, MX> L2[T2];
 #pragma unroll
     for (int t = 0; t < T2; ++t)
       L2[t] = load_tile(nd > 0 ? (size_t)__builtin_amdgcn_readlane(act_e, dai[t]) * H + 16 * drt[t] : 0, false);
@@ -551,8 +608,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
         for (int q = 0; q < PPW; ++q) {
           if (q < c) {
-            const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)L2[t].w[q].w);
-            D2[t][q] = decode_words(L2[t].w[q], g == 0 ? carry : rot);
+            const uint32_t rot = MX ? 0u : (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)L2[t].w[q].w);
+            D2[t][q] = piece_a<PPW, MX>(L2[t], q, g == 0 ? carry : rot);
             carry = rot;
             sc2[t][q] = a_scale(L2[t].sc[q], nb2, pa + q);
             pin(D2[t][q]);
@@ -605,8 +662,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           f[i] = hb < nb2 ? __uint_as_float(((uint32_t)(v[ps][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16) : 0.0f;
-        split_block8(f, hb, hj, S.hq + (size_t)(2 * ex) * ps2 * 128, S.hs + (size_t)(2 * ex) * ps2 * 4, ps2,
-                     hb < 8 * (pa + c));
+        split_block8<MX>(f, hb, hj, S.hq + (size_t)(2 * ex) * ps2 * 128, S.hs + (size_t)(2 * ex) * ps2 * 4, ps2,
+                         hb < 8 * (pa + c));
       }
     }
     for (unsigned it = 0; __ballot(yzv != tag) != 0ull; ++it) {
@@ -703,17 +760,23 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 #endif
 }
 
-// Kernel instances: (pieces per wave, gate/up tiles, down tiles).
+// Kernel instances: (pieces per wave, gate/up tiles, down tiles, format).
 struct Inst {
   int ppw, t1, t2;
+  bool mx;
   const void *fn;
 };
 #ifndef TQ_TOK_AT
 #define TQ_TOK_AT 2
 #endif
-#define TQ_TOK_INST(PPW, T1, T2) {PPW, T1, T2, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT>}
+#ifndef TQ_TOK_AT_MX
+#define TQ_TOK_AT_MX 2
+#endif
+#define TQ_TOK_INST(PPW, T1, T2) {PPW, T1, T2, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false>}
+#define TQ_TOK_INST_MX(PPW, T1, T2) {PPW, T1, T2, true, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT_MX, true>}
 const Inst kInsts[] = {
     TQ_TOK_INST(3, 6, 3), TQ_TOK_INST(4, 6, 3), TQ_TOK_INST(3, 6, 4), TQ_TOK_INST(4, 6, 4),
+    TQ_TOK_INST_MX(3, 6, 3), TQ_TOK_INST_MX(4, 6, 3), TQ_TOK_INST_MX(3, 6, 4), TQ_TOK_INST_MX(4, 6, 4),
 };
 
 // Worst-case work of a workgroup (every slot a distinct expert).
@@ -736,10 +799,10 @@ Plan plan(const TokCall &c, int cus) {
   return p;
 }
 
-const Inst *pick(const Plan &p) {
+const Inst *pick(const Plan &p, bool mx) {
   const Inst *best = nullptr;
   for (const Inst &i : kInsts)
-    if (i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
+    if (i.mx == mx && i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
         (!best || i.ppw * (i.t1 + i.t2) < best->ppw * (best->t1 + best->t2)))
       best = &i;
   return best;
@@ -762,12 +825,12 @@ bool tok_supported(const TokCall &c, int cus) {
   if (((uintptr_t)c.w1 & 15) || ((uintptr_t)c.w2 & 15) || ((uintptr_t)c.x & 15)) return false;
   if (((uintptr_t)c.s1 & 15) || ((uintptr_t)c.s2 & 15)) return false;
   const Plan p = plan(c, cus);
-  return p.ok && pick(p) != nullptr;
+  return p.ok && pick(p, c.mx) != nullptr;
 }
 
 int tok_launch(const TokCall &c, int cus, hipStream_t s) {
   const Plan p = plan(c, cus);
-  const Inst *inst = p.ok ? pick(p) : nullptr;
+  const Inst *inst = p.ok ? pick(p, c.mx) : nullptr;
   if (!inst) return TRELLIS_EINVAL;
   const TokRegion R = tok_region(c.E, c.H, c.I);
   char *base = c.ws + c.region_off;
