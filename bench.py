@@ -29,9 +29,10 @@ keep the 256 MB Infinity Cache from serving repeated weights, steps walk a
 ring of distinct copies of the weights totalling >= --ring-gb GiB.
 
 Printed: one JSON line with the whole-job throughput, a roofline entry for
-the kernel (its average duration from HIP events recorded around each launch
-in the timed region, on the stream it runs on), and the CPU oracle's rate on
-a bounded sample as a reported baseline.
+the kernel (its average duration over launches of the timed region, from HIP
+events on the stream it runs on: stamped by the kernel's dispatch for the
+UE8M0 layer, recorded around the call otherwise), and the CPU oracle's rate
+on a bounded sample as a reported baseline.
 """
 from __future__ import annotations
 
@@ -54,10 +55,12 @@ TRELLIS_BPW = 0.25 + 1.0 / 32.0           # 2-bit symbol + one UE8M0 byte per 32
 MX_BPW = 0.5 + 1.0 / 32.0                 # E2M1 nibble + UE8M0 byte per 32 weights
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
 FP4_PEAK_TFLOPS = 10100.0                 # MI355X dense FP4 matrix cores, published
-FP64_PEAK_TFLOPS = 78.6                   # MI355X fp64 vector, published
+FP64_PEAK_TFLOPS = 78.6                   # MI355X fp64 vector, published (an FMA counted as two)
+FP64_OPS_PEAK_T = FP64_PEAK_TFLOPS / 2    # fp64 vector instructions of one operation each (add, min): 39.3 T/s
 VALU_WAVE_INSTS_PER_S = 1024 * 2.4e9 / 4  # 256 CUs x 4 SIMDs, a wave64 VALU instruction every 4 cycles
-VIT_FLOPS_PER_EDGE = 4                    # err = t - v, (d * err) * err, cost + that
-VIT_EDGES_PER_POSITION = 4096 * 4         # histories x branches
+# encoder search, per position and row: one add per candidate (4096 histories
+# x 4 branches) and three minimums per history (the best of four)
+VIT_OPS_PER_POSITION = 4096 * 4 + 4096 * 3
 METRIC = "compressed-weight GB/s of fused trellis-decode MoE GEMV (batch 1) + % HBM peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -342,7 +345,7 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
         kernel = ("k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 "
                   "matrix-core gate_up + SwiGLU, down + combine)")
     if router:
-        kernel += "; each step is k_router then k_layer, the events bracket k_layer"
+        kernel += "; each step is k_router then k_layer, the events time k_layer"
     return dict(
         name=("router + " if router else "") + cfg.name + (" [expanded MXFP4]" if mx else "")
         + (" [E5M3 scales]" if e5m3 else ""), make=make, hip=hip,
@@ -350,6 +353,9 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
         bytes=lambda s: uniq[s] * expert_weights * bpw,
         flops=lambda s: 2.0 * slots[s] * expert_weights,
         tokens=T, kernel=kernel, cpu=cpu_sample, workspace=ws, ring=len(ring),
+        # the UE8M0 layer's events are stamped by the kernel's dispatch
+        # (trellis_moe_ffn_timed); the other calls are bracketed by events
+        dispatch_events=not (mx or e5m3),
         config={"n_experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
                 "bytes_per_weight": bpw,
                 "weights": "expanded MXFP4" if mx else "trellis-coded" + (", E5M3 scales" if e5m3 else ""),
@@ -454,7 +460,7 @@ def viterbi_workload(args):
     return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: rows * n,
                 units="weights/s", scale=1.0,
                 metric="Viterbi-encoded weights/s (curvature-aware search, 4096 histories x 4 branches, fp64)",
-                alu_flops=rows * n * VIT_EDGES_PER_POSITION * VIT_FLOPS_PER_EDGE,
+                alu_ops=rows * n * VIT_OPS_PER_POSITION,
                 flops=None, tokens=None, cpu=cpu_sample,
                 kernel="k_viterbi (one workgroup per row, fp64 add-compare-select in LDS)",
                 config={"rows": rows, "positions": n, "histories": 4096, "branches": 4})
@@ -488,17 +494,21 @@ def pick(args):
 
 
 # The device sources each workload's kernel is compiled from: a recorded
-# traffic figure stays valid while these are unchanged.
+# traffic figure stays valid while these are unchanged. One token of the
+# 32-expert shape (trellis or expanded) runs the single-token kernel
+# (tq_tok.hip); the other layer and GEMV workloads the general layer kernel.
 KERNEL_SOURCES = {
-    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer_e5m3.hip", "tq_layer.h", "tq_tok.hip", "tq_tok.h", "tq_common.h",
+    "tok": ["tq_tok.hip", "tq_tok.h", "tq_common.h", "tq_decode.h"],
+    "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer_e5m3.hip", "tq_layer.h", "tq_tok.h", "tq_common.h",
               "tq_decode.h"],
     "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
     "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],
 }
+TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "ffn1")
 
 
 def kernel_sha(workload="moe32"):
-    kind = workload if workload in KERNEL_SOURCES else "layer"
+    kind = workload if workload in KERNEL_SOURCES else "tok" if workload in TOK_WORKLOADS else "layer"
     h = hashlib.sha256()
     d = os.path.join(ROOT, "trellis_coded_fp4_amd", "csrc")
     for f in sorted(KERNEL_SOURCES[kind]):
@@ -575,8 +585,11 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": W["kernel"],
                     "bytes_per_launch": per_launch,
                     "duration_us": round(float(d.mean() * 1e3), 3),
-                    "duration_source": f"mean of HIP event pairs around every {every}th launch of the timed "
-                                       "region, on the launch stream"}
+                    "duration_source": (f"mean over every {every}th launch of the timed region of HIP events "
+                                        "stamped with the kernel's start and end by its dispatch "
+                                        "(trellis_moe_ffn_timed)") if W.get("dispatch_events") else
+                                       (f"mean of HIP event pairs recorded around every {every}th launch of the "
+                                        "timed region, on the launch stream")}
         if valu_insts:
             # the decode's vector-ALU bound: the kernel's VALU wave instructions
             # (profiler count for these sources) at the chip's issue rate
@@ -589,11 +602,17 @@ def main():
                                 "peak": "1024 SIMDs x 2.4 GHz / 4 cycles per wave64 instruction"}
         if W.get("traffic_bytes"):
             roofline["read_plus_write_GBs"] = round(W["traffic_bytes"] / (d.mean() * 1e-3) / 1e9, 1)
-        if W.get("alu_flops"):
-            tf = W["alu_flops"] / (d.mean() * 1e-3) / 1e12
-            roofline = {"bound": "alu", "achieved": round(tf, 3), "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tf / FP64_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": W["kernel"],
-                        "flops_per_launch": W["alu_flops"]}
+        if W.get("alu_ops"):
+            # adds and minimums, one fp64 vector operation each, against the
+            # chip's fp64 vector issue rate for such operations (half the
+            # FMA-counted 78.6 TFLOP/s)
+            tf = W["alu_ops"] / (d.mean() * 1e-3) / 1e12
+            roofline = {"bound": "alu", "achieved": round(tf, 3), "peak": FP64_OPS_PEAK_T,
+                        "unit": "T fp64 ops/s (add, min)",
+                        "frac": round(tf / FP64_OPS_PEAK_T, 4), "traffic": traffic, "kernel": W["kernel"],
+                        "ops_per_launch": W["alu_ops"],
+                        "peak_note": "78.6 TFLOP/s fp64 vector counts an FMA as two operations; adds and "
+                                     "minimums issue at half that"}
         if W.get("flops"):
             fl = float(np.mean([W["flops"](s) for s, e in zip(timed, evs) if e]))
             tf = fl / (d.mean() * 1e-3) / 1e12

@@ -168,14 +168,17 @@ int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_up, const tr
                     size_t workspace_bytes);
 
 /*
- * trellis_moe_ffn_timed -- trellis_moe_ffn that also records HIP events on
- * `stream` around its work, for timing the layer kernel in place:
- *   events[0] just before the layer kernel is enqueued,
- *   events[1] just after it.
- * (The whole layer -- routing, activation split, gate_up + SwiGLU, down +
- * combine -- is one persistent kernel.) `events` (caller-created hipEvent_t
- * handles) may be NULL, as may either entry. Same arguments, results and
- * errors as trellis_moe_ffn otherwise.
+ * trellis_moe_ffn_timed -- trellis_moe_ffn that also stamps HIP events with
+ * the layer kernel's execution, for timing it in place:
+ *   events[0] when the kernel starts,
+ *   events[1] when it ends
+ * (the events are attached to the kernel's dispatch, hipExtLaunchKernel,
+ * rather than recorded as separate commands around it, so hipEventElapsedTime
+ * between them is the kernel's duration). The whole layer -- routing,
+ * activation split, gate_up + SwiGLU, down + combine -- is one persistent
+ * kernel. `events` (caller-created hipEvent_t handles) may be NULL, as may
+ * either entry. Same arguments, results and errors as trellis_moe_ffn
+ * otherwise.
  */
 typedef struct ihipEvent_t *hipEvent_t;
 int trellis_moe_ffn_timed(hipStream_t stream, const trellis_mat_t *w_gate_up,

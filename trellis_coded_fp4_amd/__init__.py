@@ -313,7 +313,7 @@ def moe_ffn(gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w=None, h=
     """Whole fused MoE layer; returns (y [T, hidden] fp32, h [T, k, inter] bf16).
 
     ``events``: optional ctypes array of hipEvent_t; events[0] and events[1]
-    are recorded on the stream just before and just after the layer kernel
+    are stamped with the start and the end of the layer kernel's execution
     (see trellis_moe_ffn_timed). check=True: as for moe_gemv."""
     return _moe_ffn(None, gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w, h, y, workspace, stream,
                     events, prepare, check)

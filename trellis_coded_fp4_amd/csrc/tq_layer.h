@@ -49,6 +49,7 @@
 // it: from the neighbouring lane-group's piece via ds_bpermute, or the
 // previous piece.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1861,7 +1862,7 @@ static int check_routing(int T, int k) {
 }
 
 template <typename F, int NT, bool ALIGNED>
-static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
+static int launch_nt(LayerArgs &a, int cus, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int n_items = a.n_prep + a.n_s1 + a.n_s2;
   a.grid = std::max(1, std::min(n_items, cus * resident_blocks<F, NT, ALIGNED>()));
   // A single resident token whose items about fit one round of workgroups:
@@ -1871,17 +1872,20 @@ static int launch_nt(LayerArgs &a, int cus, hipStream_t s) {
   // system). With many rounds of items (several tokens, or many experts'
   // down projections) expert order is faster.
   a.s1_ilv = a.mode == MODE_FFN && a.x_resident && 4 * n_items <= 5 * a.grid;
-  hipLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
+  if (e0 || e1)   // events stamped by the dispatch itself (start and end of the kernel's execution)
+    hipExtLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((k_layer<F, NT, ALIGNED>), dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
 }
 
 template <typename F, bool ALIGNED>
-static int launch_al(LayerArgs &a, int cus, hipStream_t s) {
+static int launch_al(LayerArgs &a, int cus, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch ((a.T + 7) / 8) {
-    case 1: return launch_nt<F, 1, ALIGNED>(a, cus, s);
-    case 2: return launch_nt<F, 2, ALIGNED>(a, cus, s);
-    case 3: return launch_nt<F, 3, ALIGNED>(a, cus, s);
-    default: return launch_nt<F, 4, ALIGNED>(a, cus, s);
+    case 1: return launch_nt<F, 1, ALIGNED>(a, cus, s, e0, e1);
+    case 2: return launch_nt<F, 2, ALIGNED>(a, cus, s, e0, e1);
+    case 3: return launch_nt<F, 3, ALIGNED>(a, cus, s, e0, e1);
+    default: return launch_nt<F, 4, ALIGNED>(a, cus, s, e0, e1);
   }
 }
 
@@ -1889,12 +1893,12 @@ static int launch_al(LayerArgs &a, int cus, hipStream_t s) {
 // pieces per row (words per row % 4 == 0) and a 16-byte aligned base. The
 // fast scale path needs a 16-byte aligned scale base and cols <= 4096.
 template <typename F>
-static int launch(LayerArgs &a, int cus, hipStream_t s) {
+static int launch(LayerArgs &a, int cus, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const bool aligned = (a.cols1 / 32 * F::kWords) % 4 == 0 && (a.cols2 / 32 * F::kWords) % 4 == 0 &&
                        ((uintptr_t)a.w1 & 15) == 0 && ((uintptr_t)a.w2 & 15) == 0;
   a.fast1 = aligned && ((uintptr_t)a.s1 & 15) == 0 && a.cols1 / 32 <= kAScaleBytes / 16;
   a.fast2 = aligned && ((uintptr_t)a.s2 & 15) == 0 && a.cols2 / 32 <= kAScaleBytes / 16;
-  return aligned ? launch_al<F, true>(a, cus, s) : launch_al<F, false>(a, cus, s);
+  return aligned ? launch_al<F, true>(a, cus, s, e0, e1) : launch_al<F, false>(a, cus, s, e0, e1);
 }
 
 // Tokens split once per call (see run_prep) when the token is not resident,
@@ -1986,13 +1990,8 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
     // single-token layer kernel
     TokCall c{(const uint32_t *)gu.w, gu.scales, (const uint32_t *)dn.w, dn.scales, E, hidden, inter, k,
               topk_ids, topk_w, x, x_dtype == TRELLIS_BF16, h, y, ws, L.reserve, F::kSteps == 1};
-    if (T == 1 && tok_supported(c, cus)) {
-      if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
-      rc = tok_launch(c, cus, stream);
-      if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess)
-        rc = TRELLIS_EHIP;
-      return rc;
-    }
+    if (T == 1 && tok_supported(c, cus))
+      return tok_launch(c, cus, stream, events ? events[0] : nullptr, events ? events[1] : nullptr);
   }
   LayerArgs a{};
   a.mode = MODE_FFN;
@@ -2016,10 +2015,7 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
   const int J = (hidden / 32 + F::kBlocks - 1) / F::kBlocks;
   a.x_resident = T == 1 && J <= kPieceMax && ((uintptr_t)x & 15) == 0;
   set_prep<F>(a, L, ws, !a.x_resident && hidden / 32 <= 64 * kTokRounds && ((uintptr_t)x & 15) == 0);
-  if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return TRELLIS_EHIP;
-  rc = launch<F>(a, cus, stream);
-  if (rc == TRELLIS_OK && events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) rc = TRELLIS_EHIP;
-  return rc;
+  return launch<F>(a, cus, stream, events ? events[0] : nullptr, events ? events[1] : nullptr);
 }
 
 static Mats trellis_mats(const trellis_mat_t *w) {

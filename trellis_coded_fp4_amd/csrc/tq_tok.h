@@ -36,7 +36,9 @@ struct TokCall {
 // that fits the kernel's register arrays on this device.
 bool tok_supported(const TokCall &c, int cus);
 
-// Enqueue the kernel on `s` (argument checks already done by the caller).
-int tok_launch(const TokCall &c, int cus, hipStream_t s);
+// Enqueue the kernel on `s` (argument checks already done by the caller);
+// e0 / e1, when given, are stamped with the start and end of the kernel's
+// execution by the dispatch itself.
+int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 }  // namespace tq

@@ -45,6 +45,8 @@
 // that finds it set writes NaN to y and does nothing else.
 #include "tq_tok.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "tq_common.h"
@@ -828,7 +830,7 @@ bool tok_supported(const TokCall &c, int cus) {
   return p.ok && pick(p, c.mx) != nullptr;
 }
 
-int tok_launch(const TokCall &c, int cus, hipStream_t s) {
+int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const Plan p = plan(c, cus);
   const Inst *inst = p.ok ? pick(p, c.mx) : nullptr;
   if (!inst) return TRELLIS_EINVAL;
@@ -858,8 +860,9 @@ int tok_launch(const TokCall &c, int cus, hipStream_t s) {
     pad[ii] = std::max<size_t>(kCuLds / 2 + 1024 - std::min<size_t>(fa.sharedSizeBytes, kCuLds / 2), 1);
   }
   void *args[] = {&a};
-  if (hipLaunchKernel(inst->fn, dim3(cus), dim3(512), args, pad[ii], s) != hipSuccess)
-    return TRELLIS_EHIP;
+  const hipError_t e = e0 || e1 ? hipExtLaunchKernel(inst->fn, dim3(cus), dim3(512), args, pad[ii], s, e0, e1, 0)
+                               : hipLaunchKernel(inst->fn, dim3(cus), dim3(512), args, pad[ii], s);
+  if (e != hipSuccess) return TRELLIS_EHIP;
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
 }
 
