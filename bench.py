@@ -335,6 +335,9 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
                   "+ SwiGLU, tagged h hand-off, down + gate-weighted atomic combine)")
     elif mx:
         kernel = "k_layer<FmtMx> (whole MoE layer on expanded MXFP4 weights)"
+    elif e5m3 and T == 1:
+        kernel = ("k_tok<E5M3> (single-token MoE layer, E5M3 block scales: each matrix-core step issued once per "
+                  "power-of-two term of its scale, four terms)")
     elif e5m3:
         kernel = ("k_layer<FmtTrellisE5M3> (whole MoE layer, E5M3 block scales: each matrix-core step issued "
                   "once per power-of-two term of its scale, four terms)")
@@ -504,7 +507,7 @@ KERNEL_SOURCES = {
     "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
     "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],
 }
-TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "ffn1")
+TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "ffn1", "e5m3_32")
 
 
 def kernel_sha(workload="moe32"):

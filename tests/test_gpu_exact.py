@@ -183,7 +183,7 @@ def _ffn_dev(tq, L, orc=None, mx_experts=None):
     return [dev(gc), dev(gs), dev(dc), dev(ds)]
 
 
-def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws, mx=False):
+def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws, mx=False, fmt="ue8m0"):
     """One layer call per list of probe columns (one token each); returns h, y."""
     import torch
     n, T = len(col_lists), len(col_lists[0])
@@ -191,7 +191,7 @@ def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws, mx=False):
     Hh = torch.empty((n, T, k, I), dtype=torch.bfloat16, device="cuda")
     Yy = torch.empty((n, T, H), dtype=torch.float32, device="cuda")
     dids, dgw = dev(ids), dev(gw)
-    fn = tq.mxfp4_moe_ffn if mx else tq.moe_ffn
+    fn = tq.mxfp4_moe_ffn if mx else tq.moe_ffn_e5m3 if fmt == "e5m3" else tq.moe_ffn
     for i, cs in enumerate(col_lists):
         fn(*wd, _rows_of(eye, cs), dids, dgw, h=Hh[i], y=Yy[i], workspace=ws)
     h = Hh.float().cpu().numpy()
@@ -200,37 +200,52 @@ def _run_layer(tq, wd, eye, col_lists, ids, gw, I, H, ws, mx=False):
     return h, y
 
 
-def _layer_setup(cfg, T, seed):
+# the scale byte whose value is 1 in each format (E5M3: exponent 15, mantissa 0)
+ONE = {"ue8m0": 127, "e5m3": 15 << 3}
+
+
+def _layer_setup(cfg, T, seed, fmt="ue8m0"):
     L = workloads.moe_layer(cfg, layer_id=seed)
+    if fmt == "e5m3":
+        g = workloads.rng(616, cfg.config_id, seed)
+        E = L.gu_syms.shape[0]
+        L.gu_scales = workloads.scales_e5m3(g, E, 2 * cfg.inter, cfg.hidden)
+        L.dn_scales = workloads.scales_e5m3(g, E, cfg.hidden, cfg.inter)
     act = np.array(L.ids[0][:cfg.k], np.int32)           # k distinct experts
     ids = np.tile(act, (T, 1)).astype(np.int32)
     gw = np.full((T, cfg.k), 1.0 / cfg.k, np.float32)    # a power of two for k = 4, 8
     return L, act, ids, gw
 
 
-def _stage1_probe(tq, orc, cfg, T, which, seed=0, mx=False):
+def _stage1_probe(tq, orc, cfg, T, which, seed=0, mx=False, fmt="ue8m0"):
     """which = 'gate': up rows of the active experts are the all-zero stream;
     'up': gate rows are. h at every column identifies the other weight.
     mx: the same weights expanded to MXFP4 by the oracle, through the
     layer on expanded weights."""
     import torch
     H, I, k = cfg.hidden, cfg.inter, cfg.k
-    L, act, ids, gw = _layer_setup(cfg, T, seed)
+    L, act, ids, gw = _layer_setup(cfg, T, seed, fmt)
     zero_rows = slice(I, 2 * I) if which == "gate" else slice(0, I)
     for e in act:
         L.gu_syms[e, zero_rows] = 0
+        if fmt == "e5m3":
+            # E5M3 scales reach ~15: a zero-stream gate row would decode to
+            # about -90, where silu's exp leaves the fp32 range; at scale 1
+            # the constant gate is -6
+            L.gu_scales[e, zero_rows] = ONE[fmt]
     if which == "gate":
+        assert fmt == "ue8m0", "the gate probe's gap bound is derived for UE8M0 scales"
         assert _candidate_gap(orc) > 2.0 ** -7   # > 2^-8 (accepted) + 2^-9 (bf16 rounding) + margin
     wd = _ffn_dev(tq, L, orc, act if mx else None)
     eye = _eye(H)
     ws = tq.ffn_workspace(cfg.n_exp, H, I, T, k)
     lists = [(c0 + np.arange(T)) % H for c0 in range(0, H, T)]
-    h, _ = _run_layer(tq, wd, eye, lists, ids, gw, I, H, ws, mx)
+    h, _ = _run_layer(tq, wd, eye, lists, ids, gw, I, H, ws, mx, fmt)
     probe = np.concatenate(lists)                       # column of each (call, token)
     h = h.reshape(-1, k, I)
     worst = 0.0
     for j, e in enumerate(act):
-        Wgu = orc.decode_values(L.gu_syms[e], L.gu_scales[e])       # [2I, H]
+        Wgu = orc.decode_values(L.gu_syms[e], L.gu_scales[e], scale_fmt=fmt)   # [2I, H]
         g = Wgu[:I][:, probe].T                                     # [probes, I]
         u = Wgu[I:][:, probe].T
         ref = silu(g) * u
@@ -250,13 +265,13 @@ def _stage1_probe(tq, orc, cfg, T, which, seed=0, mx=False):
     print(f"{which}: {len(probe)} columns x {I} rows x {k} experts, worst relative h error {worst:.2e}")
 
 
-def _down_probe(tq, orc, cfg, T, seed=0, mx=False):
+def _down_probe(tq, orc, cfg, T, seed=0, mx=False, fmt="ue8m0"):
     """Crafted gate rows make h one-hot at one row r per token; y then exposes
     column r of every active down matrix exactly (mx: on the weights
     expanded to MXFP4 by the oracle)."""
     import torch
     H, I, k = cfg.hidden, cfg.inter, cfg.k
-    L, act, ids, gw = _layer_setup(cfg, T, seed)
+    L, act, ids, gw = _layer_setup(cfg, T, seed, fmt)
     s_zero, s_two = _states(orc)
     hw_zero, hw_two = _state_halfword(s_zero), _state_halfword(s_two)
     n_probe_cols = H // 8                               # windows of 8 symbols end at 8n + 7
@@ -264,11 +279,11 @@ def _down_probe(tq, orc, cfg, T, seed=0, mx=False):
     P = -(-I // n_st)                                   # probes per stack
     for e in act:
         L.gu_syms[e, I:] = 0                            # up rows: -6 everywhere
-        L.gu_scales[e] = 127
+        L.gu_scales[e] = ONE[fmt]
     wd = _ffn_dev(tq, L, orc, act if mx else None)
     eye = _eye(H)
     ws = tq.ffn_workspace(cfg.n_exp, H, I, T, k)
-    Wdn = [orc.decode_values(L.dn_syms[e], L.dn_scales[e]) for e in act]   # [H, I] each
+    Wdn = [orc.decode_values(L.dn_syms[e], L.dn_scales[e], scale_fmt=fmt) for e in act]   # [H, I] each
     h_two = orc.round_bf16(float(silu(2.0) * -6.0))
     r_all = np.arange(I)
     for sigma in range(n_st):
@@ -277,7 +292,7 @@ def _down_probe(tq, orc, cfg, T, seed=0, mx=False):
         half[r_all[mine], r_all[mine] // n_st] = hw_two
         gate = half.view(np.uint32)                     # [I, H/16], little-endian halves
         # the crafting itself, checked on the oracle: at column 8n+7 only row n*n_st+sigma is non-zero
-        dec = orc.decode_values(gate[None], np.full((1, I, H // 32), 127, np.uint8))[0][:, 7::8]
+        dec = orc.decode_values(gate[None], np.full((1, I, H // 32), ONE[fmt], np.uint8), scale_fmt=fmt)[0][:, 7::8]
         want_nz = np.zeros_like(dec, bool)
         want_nz[r_all[mine], r_all[mine] // n_st] = True
         assert np.array_equal(dec != 0, want_nz) and (dec[want_nz] == 2.0).all()
@@ -285,7 +300,7 @@ def _down_probe(tq, orc, cfg, T, seed=0, mx=False):
         for e in act:
             wd[0][int(e), :I] = g_dev
         lists = [(p0 + np.arange(T)) % P for p0 in range(0, P, T)]
-        h, y = _run_layer(tq, wd, eye, [8 * p + 7 for p in lists], ids, gw, I, H, ws, mx)
+        h, y = _run_layer(tq, wd, eye, [8 * p + 7 for p in lists], ids, gw, I, H, ws, mx, fmt)
         n_of = np.concatenate(lists)
         r_of = n_of * n_st + sigma
         h = h.reshape(-1, k, I)
@@ -362,3 +377,21 @@ def test_mxfp4_layer_down_exact(trellis_lib, orc, layer, T):
     cfg = LAYERS[layer]
     announce(f"exact mxfp4 layer down probe {cfg.name} T={T}")
     _down_probe(trellis_lib, orc, cfg, T, mx=True)
+
+
+# E5M3 block scales (the XOR-Trellis article's grouping format, read as an
+# unsigned binary16 upper byte): the up and down probes through
+# trellis_moe_ffn_e5m3. One token runs the single-token kernel (moe32,
+# small), eight tokens the general layer kernel.
+@pytest.mark.parametrize("layer,T", [("moe32", 1), ("small", 1), ("moe32", 8)])
+def test_e5m3_layer_up_exact(trellis_lib, orc, layer, T):
+    cfg = LAYERS[layer]
+    announce(f"exact e5m3 layer stage-1 probe (up) {cfg.name} T={T}")
+    _stage1_probe(trellis_lib, orc, cfg, T, "up", fmt="e5m3")
+
+
+@pytest.mark.parametrize("layer,T", [("moe32", 1), ("small", 1), ("moe32", 8)])
+def test_e5m3_layer_down_exact(trellis_lib, orc, layer, T):
+    cfg = LAYERS[layer]
+    announce(f"exact e5m3 layer down probe {cfg.name} T={T}")
+    _down_probe(trellis_lib, orc, cfg, T, fmt="e5m3")

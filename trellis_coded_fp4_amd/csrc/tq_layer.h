@@ -1985,11 +1985,11 @@ static int ffn_impl(hipStream_t stream, const Mats &gu, const Mats &dn, const vo
                        (uint4 *)(ws + L.cntp), n1);
     if (hipGetLastError() != hipSuccess) return TRELLIS_EHIP;
   }
-  if constexpr (!F::kE5M3) {
-    // one token of trellis-coded or expanded MXFP4 weights: the
-    // single-token layer kernel
+  {
+    // one token (trellis-coded under either scale format, or expanded
+    // MXFP4): the single-token layer kernel
     TokCall c{(const uint32_t *)gu.w, gu.scales, (const uint32_t *)dn.w, dn.scales, E, hidden, inter, k,
-              topk_ids, topk_w, x, x_dtype == TRELLIS_BF16, h, y, ws, L.reserve, F::kSteps == 1};
+              topk_ids, topk_w, x, x_dtype == TRELLIS_BF16, h, y, ws, L.reserve, F::kSteps == 1, F::kE5M3};
     if (T == 1 && tok_supported(c, cus))
       return tok_launch(c, cus, stream, events ? events[0] : nullptr, events ? events[1] : nullptr);
   }

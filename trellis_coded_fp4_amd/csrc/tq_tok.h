@@ -1,6 +1,6 @@
 // tq_tok.h -- host interface of the single-token mixture-of-experts layer
-// kernel (tq_tok.hip), which trellis_moe_ffn and trellis_mxfp4_moe_ffn use
-// for one token.
+// kernel (tq_tok.hip), which trellis_moe_ffn, trellis_moe_ffn_e5m3 and
+// trellis_mxfp4_moe_ffn use for one token.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -28,6 +28,7 @@ struct TokCall {
   char *ws;                                // layer workspace (status words at 0)
   size_t region_off;                       // offset of the TokRegion
   bool mx = false;                         // weights are expanded MXFP4
+  bool e5m3 = false;                       // scale bytes are E5M3 (trellis streams)
 };
 
 // True when the kernel takes this shape (otherwise the general layer kernel

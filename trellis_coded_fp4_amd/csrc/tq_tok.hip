@@ -8,7 +8,9 @@
 // nibbles and the weights' UE8M0 bytes feed the block-scaled FP4 x FP8
 // matrix cores, the token's activations entering as a two-term FP8 split.
 // The same kernel serves expand mode (HEPH abstract): weights already
-// expanded to MXFP4 go to the matrix cores as loaded, with no decode.
+// expanded to MXFP4 go to the matrix cores as loaded, with no decode; and
+// trellis streams under E5M3 block scales (each matrix-core step issued
+// once per power-of-two term of its scale).
 //
 // Why a kernel of its own for one token: the layer moves ~28 MB at the
 // 32-expert shape and every weight costs ~1.5 VALU operations to decode, so
@@ -105,6 +107,7 @@ struct Smem {
   int up_issued;    // gate/up waves that have issued all their loads
   int up_done;      // gate/up waves that have stored their partial sums
   int down_done;    // down waves that have stored theirs
+  uint32_t e5t[256];   // E5M3 instances: e5m3_terms of every scale byte
 #ifdef TQ_TRACE
   unsigned long long trace[16];   // phase stamps, copied out at the end
 #endif
@@ -202,7 +205,8 @@ __device__ __forceinline__ BOp read_b(const uint8_t *lq, const uint8_t *ls, int 
   return o;
 }
 
-// Matrix-core steps 2p and 2p+1 of a decoded piece (A), x or h operands (B).
+// Matrix-core steps 2p and 2p+1 of a decoded piece (A), x or h operands (B);
+// byte 0 / 1 of `sa` is the A scale of step 2p / 2p+1.
 struct DecA {
   uint4 s0, s1;
 };
@@ -212,6 +216,27 @@ __device__ __forceinline__ v4f mma2(const DecA &d, const BOp &b0, const BOp &b1,
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, b0.b, acc, 4, 0, 0, (int)sa, 0, (int)b0.s);
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, b1.b, acc, 4, 0, 1, (int)sa, 0, (int)b1.s);
   return acc;
+}
+
+// The same two steps under E5M3 block scales (XOR-Trellis article, the
+// paragraph on the grouping format; reading: unsigned binary16 upper byte).
+// The matrix cores take power-of-two A scales only, so each scale byte is
+// looked up in `terms` (e5m3_terms of every byte: four UE8M0 terms that sum
+// to it exactly) and the step is issued once per term, byte select i, on
+// one accumulator; a zero scale has no such sum and zeroes A instead.
+__device__ __forceinline__ v4f mma2_e5m3(const DecA &d, const BOp &b0, const BOp &b1, uint32_t sa, v4f acc,
+                                         const uint32_t *terms) {
+  const uint32_t t0 = terms[sa & 0xFFu], t1 = terms[(sa >> 8) & 0xFFu];
+  const v8i A0 = t0 ? v8i{(int)d.s0.x, (int)d.s0.y, (int)d.s0.z, (int)d.s0.w, 0, 0, 0, 0} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  const v8i A1 = t1 ? v8i{(int)d.s1.x, (int)d.s1.y, (int)d.s1.z, (int)d.s1.w, 0, 0, 0, 0} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, b0.b, acc, 4, 0, 0, (int)t0, 0, (int)b0.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, b0.b, acc, 4, 0, 1, (int)t0, 0, (int)b0.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, b0.b, acc, 4, 0, 2, (int)t0, 0, (int)b0.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, b0.b, acc, 4, 0, 3, (int)t0, 0, (int)b0.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, b1.b, acc, 4, 0, 0, (int)t1, 0, (int)b1.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, b1.b, acc, 4, 0, 1, (int)t1, 0, (int)b1.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, b1.b, acc, 4, 0, 2, (int)t1, 0, (int)b1.s);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, b1.b, acc, 4, 0, 3, (int)t1, 0, (int)b1.s);
 }
 
 // Wait until at most N of this wave's vector-memory operations are
@@ -291,9 +316,10 @@ __device__ __forceinline__ DecA piece_a(const TileLd<PPW, MX> &L, int q, uint32_
 // at a barrier for the other's loads. MX: the weights are expanded MXFP4
 // (codes [rows][cols / 2], even column in the low nibble, same scales),
 // fed to the matrix cores as loaded; the activations take that format's
-// layout.
-template <int PPW, int T1, int T2, int AT, bool MX>
+// layout. E5: the scale bytes are E5M3 (trellis streams only).
+template <int PPW, int T1, int T2, int AT, bool MX, bool E5>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k_tok(Args a) {
+  static_assert(!(MX && E5), "E5M3 scales are served on trellis streams");
   constexpr int NW = 8, NR = 4;   // waves, waves per role
   __shared__ Smem S;
 #ifdef TQ_TRACE
@@ -310,6 +336,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   const int rt_per = H >> 4, pr_per = I >> 4;   // down tiles / pairs per expert
   const int src = ((lane - 16) & 63) << 2;       // lane-group g-1, same row (ds_bpermute address)
   const int rtid = tid & (64 * NR - 1);          // thread index within the role
+  if (E5 && tid < 256) S.e5t[tid] = e5m3_terms((uint32_t)tid);
   if (tid == 0) {
     S.x_ready = 0;
     S.up_issued = 0;
@@ -497,7 +524,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
             const uint32_t rot = MX ? 0u : (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
             const DecA d = piece_a<PPW, MX>(cur, q, g == 0 ? carry : rot);
             carry = rot;
-            acc = mma2(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], nb1, pa + q), acc);
+            if constexpr (E5)
+              acc = mma2_e5m3(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], nb1, pa + q), acc, S.e5t);
+            else
+              acc = mma2(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], nb1, pa + q), acc);
           }
         }
 #pragma unroll
@@ -698,10 +728,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
           for (int t = 0; t < T2; ++t) {
             if (t < nd) {
-              if (dai[t] == a_lo)
-                acc[t] = mma2(D2[t][q], b00, b01, sc2[t][q], acc[t]);
-              else
-                acc[t] = mma2(D2[t][q], b10, b11, sc2[t][q], acc[t]);
+              if constexpr (E5) {
+                if (dai[t] == a_lo)
+                  acc[t] = mma2_e5m3(D2[t][q], b00, b01, sc2[t][q], acc[t], S.e5t);
+                else
+                  acc[t] = mma2_e5m3(D2[t][q], b10, b11, sc2[t][q], acc[t], S.e5t);
+              } else {
+                if (dai[t] == a_lo)
+                  acc[t] = mma2(D2[t][q], b00, b01, sc2[t][q], acc[t]);
+                else
+                  acc[t] = mma2(D2[t][q], b10, b11, sc2[t][q], acc[t]);
+              }
             }
           }
         }
@@ -765,7 +802,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 // Kernel instances: (pieces per wave, gate/up tiles, down tiles, format).
 struct Inst {
   int ppw, t1, t2;
-  bool mx;
+  bool mx, e5m3;
   const void *fn;
 };
 #ifndef TQ_TOK_AT
@@ -774,11 +811,16 @@ struct Inst {
 #ifndef TQ_TOK_AT_MX
 #define TQ_TOK_AT_MX 2
 #endif
-#define TQ_TOK_INST(PPW, T1, T2) {PPW, T1, T2, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false>}
-#define TQ_TOK_INST_MX(PPW, T1, T2) {PPW, T1, T2, true, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT_MX, true>}
+#define TQ_TOK_INST(PPW, T1, T2) \
+  {PPW, T1, T2, false, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, false>}
+#define TQ_TOK_INST_MX(PPW, T1, T2) \
+  {PPW, T1, T2, true, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT_MX, true, false>}
+#define TQ_TOK_INST_E5(PPW, T1, T2) \
+  {PPW, T1, T2, false, true, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, true>}
 const Inst kInsts[] = {
     TQ_TOK_INST(3, 6, 3), TQ_TOK_INST(4, 6, 3), TQ_TOK_INST(3, 6, 4), TQ_TOK_INST(4, 6, 4),
     TQ_TOK_INST_MX(3, 6, 3), TQ_TOK_INST_MX(4, 6, 3), TQ_TOK_INST_MX(3, 6, 4), TQ_TOK_INST_MX(4, 6, 4),
+    TQ_TOK_INST_E5(3, 6, 3), TQ_TOK_INST_E5(4, 6, 3), TQ_TOK_INST_E5(3, 6, 4), TQ_TOK_INST_E5(4, 6, 4),
 };
 
 // Worst-case work of a workgroup (every slot a distinct expert).
@@ -801,10 +843,10 @@ Plan plan(const TokCall &c, int cus) {
   return p;
 }
 
-const Inst *pick(const Plan &p, bool mx) {
+const Inst *pick(const Plan &p, bool mx, bool e5m3) {
   const Inst *best = nullptr;
   for (const Inst &i : kInsts)
-    if (i.mx == mx && i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
+    if (i.mx == mx && i.e5m3 == e5m3 && i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
         (!best || i.ppw * (i.t1 + i.t2) < best->ppw * (best->t1 + best->t2)))
       best = &i;
   return best;
@@ -827,12 +869,12 @@ bool tok_supported(const TokCall &c, int cus) {
   if (((uintptr_t)c.w1 & 15) || ((uintptr_t)c.w2 & 15) || ((uintptr_t)c.x & 15)) return false;
   if (((uintptr_t)c.s1 & 15) || ((uintptr_t)c.s2 & 15)) return false;
   const Plan p = plan(c, cus);
-  return p.ok && pick(p, c.mx) != nullptr;
+  return p.ok && !(c.mx && c.e5m3) && pick(p, c.mx, c.e5m3) != nullptr;
 }
 
 int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const Plan p = plan(c, cus);
-  const Inst *inst = p.ok ? pick(p, c.mx) : nullptr;
+  const Inst *inst = p.ok ? pick(p, c.mx, c.e5m3) : nullptr;
   if (!inst) return TRELLIS_EINVAL;
   const TokRegion R = tok_region(c.E, c.H, c.I);
   char *base = c.ws + c.region_off;
