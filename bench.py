@@ -26,7 +26,11 @@ Other workloads (--workload):
 
 All data is synthetic (workloads.py) and resident in HBM before timing. To
 keep the 256 MB Infinity Cache from serving repeated weights, steps walk a
-ring of distinct copies of the weights totalling >= --ring-gb GiB.
+ring of distinct copies of the weights totalling >= --ring-gb GiB, with at
+least --reuse-mb MiB of other weights read between two reads of a copy.
+Each step's activations, ids and gate weights are consecutive slices of one
+device tensor each (--step-buffers packed), as a serving loop reuses its
+buffers from layer to layer.
 
 Printed: one JSON line with the whole-job throughput, a roofline entry for
 the kernel (its average duration over launches of the timed region, from HIP
@@ -81,6 +85,10 @@ def parse():
     p.add_argument("--rounds", type=int, default=4,
                    help="after the timed region: this many interleaved rounds, cold ring / warm (one copy "
                         "repeated) / warm / cold ..., 50 steps each, reported as a spread check")
+    p.add_argument("--step-buffers", choices=("packed", "separate"), default="packed",
+                   help="layer workloads: each step's activations, ids and gate weights as consecutive slices of "
+                        "one device tensor each (packed, as a serving loop reuses its buffers) or as tensors of "
+                        "their own (separate)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="seconds of oracle work for each CPU-baseline leg (one thread, then all cores)")
@@ -269,10 +277,20 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
     expert_weights = 3 * H * I
     routes, uniq, slots = [], [], []
     n_steps = args.warmup + args.steps + 50 * max(args.rounds, 0)
-    for s in range(n_steps):
-        x, ids, gw = (L0.x, L0.ids, L0.gate_w) if s == 0 else workloads.moe_batch(cfg, 0, 1000 + s)
-        xs = dev(x).to(torch.bfloat16) if cfg.x_bf16 else dev(x)
-        routes.append((xs, dev(ids), dev(gw)))
+    batches = [(L0.x, L0.ids, L0.gate_w) if s == 0 else workloads.moe_batch(cfg, 0, 1000 + s)
+               for s in range(n_steps)]
+    if args.step_buffers == "packed":
+        # every step's activations, ids and gate weights are consecutive
+        # slices of one tensor each, as a serving loop reuses its buffers
+        X = dev(np.stack([b[0] for b in batches]))
+        X = X.to(torch.bfloat16) if cfg.x_bf16 else X
+        IDS, GW = dev(np.stack([b[1] for b in batches])), dev(np.stack([b[2] for b in batches]))
+    for s, (x, ids, gw) in enumerate(batches):
+        if args.step_buffers == "packed":
+            routes.append((X[s], IDS[s], GW[s]))
+        else:
+            xs = dev(x).to(torch.bfloat16) if cfg.x_bf16 else dev(x)
+            routes.append((xs, dev(ids), dev(gw)))
         live = ids[(ids >= 0) & (ids < E)]
         uniq.append(len(np.unique(live)))
         slots.append(len(live))
