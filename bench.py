@@ -411,7 +411,7 @@ def gemv_workload(args):
 
     return dict(name=c["name"], make=make, hip=hip, stream=stream, bytes=lambda s: rows * cols * TRELLIS_BPW,
                 flops=lambda s: 2.0 * rows * cols, tokens=1, cpu=cpu_sample, workspace=ws, ring=len(ring),
-                kernel="k_layer<FmtTrellis> (routed GEMV, one slot)",
+                kernel="k_tok_gemv (single-token routed GEMV: one 16-row tile per workgroup, K split over its waves)",
                 config={"rows": rows, "cols": cols, "tokens": 1, "x": "fp32", "ring_copies": len(ring),
                         "reuse_distance_mb": round(reuse / (1 << 20), 3)})
 
@@ -516,8 +516,9 @@ def pick(args):
 
 # The device sources each workload's kernel is compiled from: a recorded
 # traffic figure stays valid while these are unchanged. One token of the
-# 32-expert shape (trellis or expanded) runs the single-token kernel
-# (tq_tok.hip); the other layer and GEMV workloads the general layer kernel.
+# 32-expert shape (trellis, expanded or E5M3) and the single-matrix GEMV run
+# the single-token kernels (tq_tok.hip); the other layer workloads the
+# general layer kernel.
 KERNEL_SOURCES = {
     "tok": ["tq_tok.hip", "tq_tok.h", "tq_common.h", "tq_decode.h"],
     "layer": ["tq_layer.hip", "tq_layer_mx.hip", "tq_layer_e5m3.hip", "tq_layer.h", "tq_tok.h", "tq_common.h",
@@ -525,7 +526,7 @@ KERNEL_SOURCES = {
     "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
     "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],
 }
-TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "ffn1", "e5m3_32")
+TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "ffn1", "e5m3_32", "gemv1")
 
 
 def kernel_sha(workload="moe32"):

@@ -62,6 +62,10 @@ def test_single_matrix_fp32(trellis_lib, orc):
     (16, 32, 512, 32, 4, True, True, False),
     (16, 32, 512, 32, 4, True, False, False),
     (3, 16, 32, 32, 8, False, True, True),      # one block per row; T*k = 256 slots over 3 experts
+    # one token, shared x, per-slot outputs: the single-token GEMV kernel
+    (5, 48, 192, 1, 3, True, False, False),     # three row tiles, one piece per row
+    (40, 1024, 256, 1, 32, False, False, False),   # 32 slots: eight tiles per workgroup
+    (1, 256, 1024, 1, 1, False, False, False),  # the single-matrix benchmark shape
 ])
 def test_moe_gemv(trellis_lib, orc, E, rows, cols, T, k, bf16, weighted, per_slot):
     announce(f"gemv E={E} {rows}x{cols} T={T} k={k} bf16={bf16} w={weighted} per_slot={per_slot}")
@@ -90,6 +94,30 @@ def test_moe_gemv_dead_and_duplicate_slots(trellis_lib, orc):
     trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(workloads.activations(g, 3, cols, True), True), dev(ids),
                          workspace=ws)
     torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0]) == 1
+
+
+def test_moe_gemv_one_token_dead_duplicate_and_empty(trellis_lib, orc):
+    """One token through the single-token GEMV kernel: a skipped id, an empty
+    slot, a duplicated expert; then a call where no slot routes anywhere
+    (every output row zero, y starting as garbage)."""
+    announce("gemv one token: dead, duplicate and all-empty slots")
+    import torch
+    E, rows, cols = 4, 64, 512
+    ids = np.array([[7, -1, 2, 2]], dtype=np.int32)
+    y, y_ref, bound, skipped = _gemv_case(trellis_lib, orc, E, rows, cols, 1, 4, True, False, False, ids=ids,
+                                          seed=3)
+    assert skipped == 1
+    check_tol(y, y_ref, bound, "one token dead/dup")
+    assert (y[0, 0] == 0).all() and (y[0, 1] == 0).all() and np.array_equal(y[0, 2], y[0, 3])
+    g = workloads.rng(604, 0)
+    syms, sc = workloads.symbols(g, E, rows, cols), workloads.scales(g, E, rows, cols)
+    ws = trellis_lib.gemv_workspace(E, rows, cols, 1, 2)
+    yd = torch.full((1, 2, rows), 3.0, dtype=torch.float32, device="cuda")
+    trellis_lib.moe_gemv(dev(syms), dev(sc), x_dev(workloads.activations(g, 1, cols, True), True),
+                         dev(np.array([[-1, 9]], np.int32)), y=yd, workspace=ws)
+    torch.cuda.synchronize()
+    assert (yd.cpu().numpy() == 0).all()
     assert int(ws[:4].view(torch.int32)[0]) == 1
 
 

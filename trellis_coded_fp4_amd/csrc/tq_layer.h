@@ -1929,6 +1929,12 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
   char *ws = (char *)workspace;
+  if constexpr (F::kSteps == 2 && !F::kE5M3) {
+    // one token, shared x, every slot's output: the single-token GEMV kernel
+    TokGemvCall c{(const uint32_t *)w.w, w.scales, w.n_mat, w.rows, w.cols, k, topk_ids, x,
+                  x_dtype == TRELLIS_BF16, y, (int *)(ws + L.status)};
+    if (T == 1 && !combine && !x_per_slot && tok_gemv_supported(c, cus)) return tok_gemv_launch(c, cus, stream);
+  }
   LayerArgs a{};
   a.mode = combine ? MODE_COMBINE : MODE_SLOTS;
   a.w1 = (const uint32_t *)w.w; a.s1 = w.scales; a.rows1 = w.rows; a.cols1 = w.cols;

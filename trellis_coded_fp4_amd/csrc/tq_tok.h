@@ -42,4 +42,21 @@ bool tok_supported(const TokCall &c, int cus);
 // execution by the dispatch itself.
 int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
+// One token through a routed matrix stack of trellis streams under UE8M0
+// scales, every slot's output kept (trellis_moe_gemv with T = 1, shared x,
+// no gate weights): y[k][rows], zeros for slots routed nowhere.
+struct TokGemvCall {
+  const uint32_t *w; const uint8_t *s;   // [E][rows][K / 16], [E][rows][K / 32]
+  int E, rows, K, k;
+  const int32_t *ids;
+  const void *x; int x_bf16;
+  float *y;
+  int *status;                           // the workspace's status words
+};
+// True when the kernel takes this shape: rows % 16 == 0, K % 64 == 0, K <=
+// 4096, k <= 32, 16-byte aligned streams, scales and x, and at most eight
+// tiles per workgroup for the worst-case routing.
+bool tok_gemv_supported(const TokGemvCall &c, int cus);
+int tok_gemv_launch(const TokGemvCall &c, int cus, hipStream_t s);
+
 }  // namespace tq

@@ -289,6 +289,50 @@ __device__ __forceinline__ DecA decode_words(const uint4 &a, uint32_t hist) {
   return d;
 }
 
+// One token's routing, in every lane of a wave: lane s (< k; lanes 32-63
+// mirror 0-31) holds slot s's expert id `idv` and gate weight `gwr`. The
+// active experts are taken in order of first occurrence; a duplicate slot
+// adds its gate weight to its expert's, in slot order. Lane r < n_act
+// receives active expert r (act_e) and its summed gate weight (act_g) by a
+// forward permutation: first occurrences to their rank, the other low lanes
+// after them, the high lanes to themselves.
+struct TokRoute {
+  bool valid;      // this lane's slot routes to an expert of the stack
+  int rank;        // active index of this slot's expert
+  int n_act, n_skipped;
+  int act_e;
+  float act_g;
+};
+__device__ __forceinline__ TokRoute tok_route(int lane, int k, int E, int idv, float gwr, bool weighted) {
+  TokRoute R;
+  const int sl = lane & 31;
+  R.valid = sl < k && idv >= 0 && idv < E;
+  const int e_me = R.valid ? idv : -1;
+  const float gw_me = weighted ? gwr : 1.0f;
+  bool first = R.valid;
+  int dup_of = sl;
+  float gsum = 0.0f;
+  for (int s2 = 0; s2 < k; ++s2) {
+    const int e2 = __builtin_amdgcn_readlane(e_me, s2);
+    const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gw_me), s2));
+    if (R.valid && e2 == e_me) {
+      gsum += w2;
+      if (s2 < sl && first) {
+        first = false;
+        dup_of = s2;
+      }
+    }
+  }
+  const uint32_t fm = (uint32_t)__ballot(first);
+  R.n_skipped = __popc((uint32_t)__ballot(sl < k && idv >= E));
+  R.n_act = __popc(fm);
+  R.rank = __popc(fm & ((1u << dup_of) - 1u));
+  const int dst = lane >= 32 ? lane : first ? R.rank : R.n_act + __popc(~fm & ((1u << sl) - 1u));
+  R.act_e = __builtin_amdgcn_ds_permute(dst << 2, e_me);
+  R.act_g = __int_as_float(__builtin_amdgcn_ds_permute(dst << 2, __float_as_int(gsum)));
+  return R;
+}
+
 // A operands of piece q of a tile (trellis: decoded, history `hist`).
 template <int PPW, bool MX>
 __device__ __forceinline__ DecA piece_a(const TileLd<PPW, MX> &L, int q, uint32_t hist) {
@@ -376,36 +420,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
     err0 = __hip_atomic_load(&a.status[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- routing, in every wave's registers: lane s (< k; lanes 32-63
-  // mirror 0-31) is slot s. Active experts in order of first occurrence; a
-  // duplicate slot adds its gate weight to its expert's, in slot order.
-  const bool valid = sl < a.k && idv >= 0 && idv < a.E;
-  const int e_me = valid ? idv : -1;
-  const float gw_me = a.gate_w ? gwr : 1.0f;
-  bool first = valid;
-  int dup_of = sl;
-  float gsum = 0.0f;
-  for (int s2 = 0; s2 < a.k; ++s2) {
-    const int e2 = __builtin_amdgcn_readlane(e_me, s2);
-    const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gw_me), s2));
-    if (valid && e2 == e_me) {
-      gsum += w2;
-      if (s2 < sl && first) {
-        first = false;
-        dup_of = s2;
-      }
-    }
-  }
-  const uint32_t fm = (uint32_t)__ballot(first);
-  const int n_skipped = __popc((uint32_t)__ballot(sl < a.k && idv >= a.E));
-  const int n_act = __popc(fm);
-  const int rank = __popc(fm & ((1u << dup_of) - 1u));   // active index of this slot's expert
-  // lane r < n_act receives active expert r and its summed gate weight (a
-  // forward permutation: first occurrences to their rank, the other low
-  // lanes after them, the high lanes to themselves)
-  const int dst = lane >= 32 ? lane : first ? rank : n_act + __popc(~fm & ((1u << sl) - 1u));
-  const int act_e = __builtin_amdgcn_ds_permute(dst << 2, e_me);
-  const float act_g = __int_as_float(__builtin_amdgcn_ds_permute(dst << 2, __float_as_int(gsum)));
+  // ---- routing, in every wave's registers (tok_route)
+  const TokRoute route = tok_route(lane, a.k, a.E, idv, gwr, a.gate_w != nullptr);
+  const bool valid = route.valid;
+  const int n_skipped = route.n_skipped, n_act = route.n_act, rank = route.rank;
+  const int act_e = route.act_e;
+  const float act_g = route.act_g;
   TOK_MARK(1);
 
   // ---- this workgroup's units: pairs [p0, p0 + np), down tiles [d0, d0 + nd)
@@ -823,6 +843,165 @@ const Inst kInsts[] = {
     TQ_TOK_INST_E5(3, 6, 3), TQ_TOK_INST_E5(4, 6, 3), TQ_TOK_INST_E5(3, 6, 4), TQ_TOK_INST_E5(4, 6, 4),
 };
 
+// ---------------------------------------------------------------- single-token routed GEMV
+//
+// One token through one routed matrix stack, each slot's output kept
+// (trellis_moe_gemv with T = 1, shared x and no gate weights; HEPH abstract,
+// fused serving mode). A unit is one 16-row tile of one active expert;
+// workgroup w takes units [w NU / G, (w + 1) NU / G), at most T1 of them,
+// streamed through a register ring two tiles deep. Its four waves split
+// every tile along K (wave v: pieces [v PPW, (v+1) PPW), x split by the wave
+// for its own range, as in the layer kernel), meet in LDS, and the tile's 16
+// rows go to every slot routed to its expert. A tile's rows are final in one
+// workgroup, so nothing waits on another workgroup. Slots that route to no
+// expert get zeros from the tiles of active expert 0, which cover every row
+// once (or from workgroup 0 when no slot is active). A set sticky error word
+// makes the call write NaN to y and nothing else.
+struct GemvArgs {
+  const uint32_t *w; const uint8_t *s;   // [E][rows][K / 16] symbols, [E][rows][K / 32] scales
+  int E, rows, K, k;
+  const int32_t *ids;
+  const void *x; int x_bf16;
+  float *y;                              // [k][rows]
+  int *status;
+  int G;
+};
+
+template <int PPW, int T1>
+__global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
+  constexpr int NR = 4, AT = T1 < 2 ? T1 : 2;
+  __shared__ uint8_t xq[2 * 2 * kMaxJ * 128], xs[2 * 2 * kMaxJ * 4];
+  __shared__ float red[T1][NR][16];
+  const int tid = threadIdx.x, lane = tid & 63, rw = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int w = blockIdx.x, G = a.G;
+  const int nb = a.K >> 5, J = (nb + 7) >> 3, wpr = a.K >> 4, ps = 2 * J;
+  const int rpe = a.rows >> 4;                 // tiles per expert
+  const int src = ((lane - 16) & 63) << 2;     // lane-group g-1, same row (ds_bpermute address)
+  const int pa = min(rw * PPW, J), c = min(J - pa, PPW);
+
+  const int sl = lane & 31, slc = sl < a.k ? sl : 0;
+  const int idv = a.ids[slc];
+  const int err = __hip_atomic_load(&a.status[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  constexpr int kXPass = (8 * PPW + 15) / 16;
+  uint4 xr[kXPass][2];
+#pragma unroll
+  for (int p = 0; p < kXPass; ++p) {
+    const int xb = 8 * pa + 16 * p + (lane >> 2), xj = lane & 3;
+    const char *xp = (const char *)a.x + (size_t)(32 * (xb < nb ? xb : 0) + 8 * xj) * (a.x_bf16 ? 2 : 4);
+    xr[p][0] = *(const uint4 *)xp;
+    xr[p][1] = *(const uint4 *)(a.x_bf16 ? xp : xp + 16);
+  }
+  const TokRoute route = tok_route(lane, a.k, a.E, idv, 0.0f, false);
+  if (err) {
+    const size_t n = (size_t)a.k * a.rows;
+    for (size_t i = (size_t)w * 256 + tid; i < n; i += (size_t)G * 256) a.y[i] = __builtin_nanf("");
+    return;
+  }
+  const uint32_t NU = (uint32_t)route.n_act * rpe;
+  const int u0 = (int)((uint32_t)w * NU / (uint32_t)G), nu = (int)((uint32_t)(w + 1) * NU / (uint32_t)G) - u0;
+  // tile t: unit u0 + t (positions past the workgroup's units repeat its last)
+  int tai[T1], trt[T1];
+  {
+    int ai = u0 / max(rpe, 1), rt = u0 - ai * rpe;
+#pragma unroll
+    for (int t = 0; t < T1; ++t) {
+      if (t > 0 && t < nu && ++rt == rpe) {
+        rt = 0;
+        ++ai;
+      }
+      tai[t] = ai;
+      trt[t] = rt;
+    }
+  }
+  auto load_tile = [&](int t) -> TileLd<PPW, false> {
+    TileLd<PPW, false> L;
+    const size_t r = (nu > 0 ? (size_t)__builtin_amdgcn_readlane(route.act_e, tai[t]) * a.rows + 16 * trt[t] : 0) + i16;
+    const uint32_t *rp = a.w + r * wpr;
+    const uint8_t *sp = a.s + r * nb;
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) L.sc[q] = *(const uint16_t *)(sp + min(8 * (pa + q) + 2 * g, nb - 2));
+#pragma unroll
+    for (int q = 0; q < PPW; ++q) L.w[q] = *(const uint4 *)(rp + min(16 * (pa + q) + 4 * g, wpr - 4));
+    L.hist = rp[min(max(16 * pa - 1, 0), wpr - 1)];
+    return L;
+  };
+  TileLd<PPW, false> R[AT > 0 ? AT : 1];
+#pragma unroll
+  for (int t = 0; t < AT; ++t) R[t] = load_tile(t);
+  // this wave's blocks of x, split into LDS (blocks past K, up to the last
+  // piece, get zero codes); the wave reads them back itself
+#pragma unroll
+  for (int p = 0; p < kXPass; ++p) {
+    const int xb = 8 * pa + 16 * p + (lane >> 2), xj = lane & 3;
+    float f[8];
+    const uint32_t wv[8] = {xr[p][0].x, xr[p][0].y, xr[p][0].z, xr[p][0].w,
+                            xr[p][1].x, xr[p][1].y, xr[p][1].z, xr[p][1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = a.x_bf16 ? (wv[i >> 1] >> (16 * (i & 1))) << 16 : wv[i];
+      f[i] = xb < nb ? __uint_as_float(bits) : 0.0f;
+    }
+    split_block8<false>(f, xb, xj, xq, xs, ps, xb < 8 * (pa + c));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  BOp bx[PPW][2];
+#pragma unroll
+  for (int q = 0; q < PPW; ++q)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) bx[q][hh] = read_b(xq, xs, ps, i16 & 1, min(2 * (pa + q) + hh, ps - 1), g);
+#pragma unroll
+  for (int t = 0; t < T1; ++t) {
+    const TileLd<PPW, false> cur = R[t % AT];
+    if (t + AT < T1) R[t % AT] = load_tile(t + AT);
+    if (t < nu && c > 0) {
+      uint32_t carry = pa == 0 ? 0u : cur.hist;
+      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) {
+        if (q < c) {
+          const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
+          const DecA d = decode_words(cur.w[q], g == 0 ? carry : rot);
+          carry = rot;
+          acc = mma2(d, bx[q][0], bx[q][1], 8 * (pa + q) + 2 * g < nb ? cur.sc[q] : 0x7F7Fu, acc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = pair_sum(acc[r]);
+        if (i16 == 0) red[t][rw][4 * g + r] = v;
+      }
+    }
+  }
+  __syncthreads();
+  // row r of tile t to every slot of its expert (zeros to the slots that
+  // route nowhere, from active expert 0's tiles)
+  for (int q = tid; q < 16 * nu; q += 256) {
+    const int t = q >> 4, r = q & 15;
+    float v = 0.0f;
+#pragma unroll
+    for (int v4 = 0; v4 < NR; ++v4)
+      if (v4 * PPW < J) v += red[t][v4][r];
+    int ai = tai[0], rt = trt[0];
+#pragma unroll
+    for (int tt = 1; tt < T1; ++tt)
+      if (t == tt) {
+        ai = tai[tt];
+        rt = trt[tt];
+      }
+    for (int sidx = 0; sidx < a.k; ++sidx) {
+      const bool vs = __builtin_amdgcn_readlane((int)route.valid, sidx) != 0;
+      if (vs ? __builtin_amdgcn_readlane(route.rank, sidx) == ai : ai == 0)
+        a.y[(size_t)sidx * a.rows + 16 * rt + r] = vs ? v : 0.0f;
+    }
+  }
+  if (w == 0) {
+    if (tid == 0) __hip_atomic_store(&a.status[0], route.n_skipped, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (route.n_act == 0)
+      for (int i = tid; i < a.k * a.rows; i += 256) a.y[i] = 0.0f;
+  }
+}
+
 // Worst-case work of a workgroup (every slot a distinct expert).
 struct Plan {
   int nw, ppw, t1, t2;
@@ -905,6 +1084,54 @@ int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0, hipEvent
   const hipError_t e = e0 || e1 ? hipExtLaunchKernel(inst->fn, dim3(cus), dim3(512), args, pad[ii], s, e0, e1, 0)
                                : hipLaunchKernel(inst->fn, dim3(cus), dim3(512), args, pad[ii], s);
   if (e != hipSuccess) return TRELLIS_EHIP;
+  return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
+}
+
+// ---------------------------------------------------------------- single-token routed GEMV (host)
+
+namespace {
+struct GemvInst {
+  int ppw, t1;
+  const void *fn;
+};
+#define TQ_TOKV_INST(PPW, T1) {PPW, T1, (const void *)k_tok_gemv<PPW, T1>}
+const GemvInst kGemvInsts[] = {
+    TQ_TOKV_INST(1, 1), TQ_TOKV_INST(2, 1), TQ_TOKV_INST(3, 1), TQ_TOKV_INST(4, 1),
+    TQ_TOKV_INST(1, 8), TQ_TOKV_INST(2, 8), TQ_TOKV_INST(3, 8), TQ_TOKV_INST(4, 8),
+};
+
+// The instance and grid for the worst case (every slot a distinct expert).
+const GemvInst *gemv_pick(const TokGemvCall &c, int cus, int *grid) {
+  if (c.k < 1 || c.k > kMaxSlots || c.rows < 16 || c.rows % 16 || c.K < 64 || c.K % 64 || c.K > 32 * 8 * kMaxJ)
+    return nullptr;
+  if (((uintptr_t)c.w & 15) || ((uintptr_t)c.s & 15) || ((uintptr_t)c.x & 15)) return nullptr;
+  const int J = (c.K / 32 + 7) / 8, ppw = (J + 3) / 4;
+  const long nu = (long)std::min(c.E, c.k) * (c.rows / 16);
+  const int G = (int)std::min<long>(nu, cus);
+  const long t1 = (nu + G - 1) / G;
+  for (const GemvInst &i : kGemvInsts)
+    if (i.ppw == ppw && i.t1 >= t1) {
+      *grid = G;
+      return &i;
+    }
+  return nullptr;
+}
+}  // namespace
+
+bool tok_gemv_supported(const TokGemvCall &c, int cus) {
+  int grid = 0;
+  return gemv_pick(c, cus, &grid) != nullptr;
+}
+
+int tok_gemv_launch(const TokGemvCall &c, int cus, hipStream_t s) {
+  int grid = 0;
+  const GemvInst *inst = gemv_pick(c, cus, &grid);
+  if (!inst) return TRELLIS_EINVAL;
+  GemvArgs a;
+  a.w = c.w; a.s = c.s; a.E = c.E; a.rows = c.rows; a.K = c.K; a.k = c.k;
+  a.ids = c.ids; a.x = c.x; a.x_bf16 = c.x_bf16; a.y = c.y; a.status = c.status; a.G = grid;
+  void *args[] = {&a};
+  if (hipLaunchKernel(inst->fn, dim3(grid), dim3(256), args, 0, s) != hipSuccess) return TRELLIS_EHIP;
   return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_EHIP;
 }
 
