@@ -20,6 +20,8 @@ Other workloads (--workload):
   moe32r    the default layer with the device-side router in front of it
             (trellis_router_topk then trellis_moe_ffn, one stream): the
             per-layer latency from activations to output
+  moe32rf   the same in one launch (trellis_moe_ffn_routed: every workgroup
+            computes the router, then the layer)
   viterbi   the encoder's curvature-aware Viterbi search: 512 rows x 2880
             positions per call (trellis_viterbi_encode), float64; reported
             in encoded weights/s against the fp64 vector ALU roofline
@@ -75,7 +77,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="moe32",
-                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | moe32r | e5m3_32 | "
+                   help="moe32 (default) | ffn1 | gemv1 | moe128:T | expand | mx128:T | mx32 | moe32r | moe32rf | e5m3_32 | "
                         "e5m3_128:T | viterbi")
     p.add_argument("--ring-gb", type=float, default=1.0,
                    help="minimum total size of the ring of weight copies (GiB)")
@@ -257,7 +259,7 @@ def stream_read_peak(nbytes, reuse_mb, steps=100):
 # given) with its arguments already checked and marshalled, per-step
 # algorithmic bytes, and optionally flops and a CPU-oracle sample.
 
-def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
+def layer_workload(args, cfg, mx=False, router=False, e5m3=False, fused_router=False):
     import torch
     import trellis_coded_fp4_amd as tq
     E, H, I = cfg.n_exp, cfg.hidden, cfg.inter
@@ -320,6 +322,10 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
     def make(s, events=None, copy=None):
         a, b, c, d = ring[s % len(ring) if copy is None else copy]
         xs, ids, gw = routes[s]
+        if router and fused_router:
+            return tq.moe_ffn_routed(a, b, c, d, xs, wr, k, topk_ids=r_ids, topk_w=r_gw, h=h, y=y, workspace=ws,
+                                     prepare=True,
+                                     events=(ctypes.c_void_p * 4)(events[0], events[1], None, None) if events else None)
         if router:
             rcall = tq.router_topk(xs, wr, k, topk_ids=r_ids, topk_w=r_gw, workspace=r_ws, prepare=True)
             lcall = tq.moe_ffn(a, b, c, d, xs, r_ids, r_gw, h=h, y=y, workspace=ws, prepare=True,
@@ -365,10 +371,13 @@ def layer_workload(args, cfg, mx=False, router=False, e5m3=False):
     else:
         kernel = ("k_layer<FmtTrellis> (whole MoE layer: routing, activation split, fused decode + FP4 "
                   "matrix-core gate_up + SwiGLU, down + combine)")
-    if router:
+    if router and fused_router:
+        kernel = ("k_tok<routed> (router computed by every workgroup, then the single-token MoE layer, one launch "
+                  "per step)")
+    elif router:
         kernel += "; each step is k_router then k_layer, the events time k_layer"
     return dict(
-        name=("router + " if router else "") + cfg.name + (" [expanded MXFP4]" if mx else "")
+        name=("router + " if router else "") + ("(one launch) " if fused_router else "") + cfg.name + (" [expanded MXFP4]" if mx else "")
         + (" [E5M3 scales]" if e5m3 else ""), make=make, hip=hip,
         stream=stream,
         bytes=lambda s: uniq[s] * expert_weights * bpw,
@@ -495,6 +504,8 @@ def pick(args):
         return layer_workload(args, workloads.MOE_32E, mx=True)
     if w == "moe32r":
         return layer_workload(args, workloads.MOE_32E, router=True)
+    if w == "moe32rf":
+        return layer_workload(args, workloads.MOE_32E, router=True, fused_router=True)
     if w == "ffn1":
         return layer_workload(args, workloads.EXPERT_FFN)
     if w == "gemv1":
@@ -526,7 +537,7 @@ KERNEL_SOURCES = {
     "expand": ["tq_expand.hip", "tq_common.h", "tq_decode.h"],
     "viterbi": ["tq_viterbi.hip", "tq_common.h", "tq_decode.h"],
 }
-TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "ffn1", "e5m3_32", "gemv1")
+TOK_WORKLOADS = ("moe32", "mx32", "moe32r", "moe32rf", "ffn1", "e5m3_32", "gemv1")
 
 
 def kernel_sha(workload="moe32"):

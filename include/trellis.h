@@ -316,6 +316,29 @@ int trellis_router_topk(hipStream_t stream, const void *x, int32_t x_dtype, cons
                         void *workspace, size_t workspace_bytes);
 
 /*
+ * trellis_moe_ffn_routed -- trellis_router_topk and trellis_moe_ffn for one
+ * token (T = 1) in one launch: every workgroup of the single-token layer
+ * kernel computes the router itself (the same arithmetic as
+ * trellis_router_topk, so the same ids and gate weights bit for bit), then
+ * runs the layer (HEPH abstract, fused serving mode; the routing is the
+ * usual router, which the pages leave unspecified).
+ *   x:           device [1][hidden], fp32 or bf16 (x_dtype), 16-byte aligned.
+ *   w_router:    device [E][hidden] bf16, 16-byte aligned (E = w_gate_up->n_mat).
+ *   topk_ids_out, topk_w_out: device [1][k] (written): the routing used.
+ *   h, y, workspace: as for trellis_moe_ffn (its workspace size for T = 1).
+ *   events:      as for trellis_moe_ffn_timed (may be NULL).
+ * Limits: the single-token kernel's shapes (hidden and inter multiples of
+ * 64, at most 4096, 16-byte aligned streams), E <= 32, 1 <= k <= E,
+ * trellis streams under UE8M0 scales. Other shapes get TRELLIS_EINVAL before
+ * anything is enqueued: chain trellis_router_topk and trellis_moe_ffn there.
+ * Errors otherwise as trellis_moe_ffn.
+ */
+int trellis_moe_ffn_routed(hipStream_t stream, const trellis_mat_t *w_gate_up, const trellis_mat_t *w_down,
+                           const void *x, int32_t x_dtype, const uint16_t *w_router, int32_t k,
+                           int32_t *topk_ids_out, float *topk_w_out, uint16_t *h, float *y, void *workspace,
+                           size_t workspace_bytes, hipEvent_t *events);
+
+/*
  * Workspace bytes needed by trellis_viterbi_encode for `rows` rows of n
  * positions on the current device: 1 KB per position for each row searched
  * at once (at most 2 per compute unit). 0 for rows < 1 or n < 1, or when

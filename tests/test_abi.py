@@ -103,6 +103,22 @@ def test_ffn_argument_checks():
     assert call(wsb=100) == -3
 
 
+def test_ffn_routed_argument_checks():
+    lib = tq.lib()
+    gu, dn = _mat(n_mat=4, rows=128, cols=64), _mat(n_mat=4, rows=64, cols=64)
+
+    def call(gu=gu, dn=dn, x=FAKE, w=FAKE, k=2, ids=FAKE, gw=FAKE, h=FAKE, y=FAKE, ws=0x10000, wsb=1 << 30):
+        return lib.trellis_moe_ffn_routed(None, ctypes.byref(gu), ctypes.byref(dn), x, 1, w, k, ids, gw, h, y,
+                                          ws, wsb, None)
+    assert call(w=None) == -2
+    assert call(ids=None) == -2
+    assert call(gw=None) == -2
+    assert call(k=5) == -1                                    # k > number of experts
+    assert call(k=0) == -1
+    assert call(dn=_mat(n_mat=3, rows=64, cols=64)) == -1     # expert counts differ
+    assert call(wsb=100) == -3
+
+
 def test_ffn_noalloc_rejects_what_its_scratch_cannot_hold():
     """trellis_moe_ffn_noalloc checks the shape's workspace need against its
     fixed scratch before anything is enqueued."""

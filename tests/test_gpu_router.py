@@ -103,3 +103,51 @@ def test_router_calls_share_a_workspace(trellis_lib, orc):
         x, w = _router_inputs(20 + i, T, E, H, False)
         ids, gw = trellis_lib.router_topk(_x_dev(x, False), _w_dev(w), k, workspace=ws)
         _check(orc, x, w, k, ids.cpu().numpy(), gw.cpu().numpy())
+
+
+@pytest.mark.parametrize("cfg,bf16", [
+    (workloads.MOE_32E, True),   # the 32-expert layer, bf16 x
+    (workloads.MoEConfig(98, "routed: 16 experts top-4 H=512 I=256 batch-1", 16, 512, 256, 4, 1, False), False),
+    (workloads.MoEConfig(99, "routed: 6 experts top-6 H=256 I=128 batch-1", 6, 256, 128, 6, 1, True), True),
+])
+def test_routed_layer_in_one_launch(trellis_lib, orc, cfg, bf16):
+    """trellis_moe_ffn_routed: the routing the kernel computes equals the
+    standalone router's bit for bit (and the oracle's, as the router tests
+    check it); h equals the unrouted layer's fed that routing, bit for bit;
+    the layer is checked against the oracle with that routing; a second call
+    on the same workspace gives the same routing and h."""
+    import torch
+    from test_gpu_moe import _check_layer
+    announce(f"routed layer in one launch: {cfg.name}")
+    cfg = dataclasses.replace(cfg, x_bf16=bf16)
+    layer = workloads.moe_layer(cfg)
+    _, w = _router_inputs(cfg.config_id, 1, cfg.n_exp, cfg.hidden, bf16)
+    xd, wd = _x_dev(layer.x, bf16), _w_dev(w)
+    W = [dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales)]
+    ws = trellis_lib.ffn_workspace(cfg.n_exp, cfg.hidden, cfg.inter, 1, cfg.k)
+    y, h, ids, gw = trellis_lib.moe_ffn_routed(*W, xd, wd, cfg.k, workspace=ws, check=True)
+    ids2, gw2 = trellis_lib.router_topk(xd, wd, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(gw, gw2), "fused routing differs from trellis_router_topk"
+    ids_h, gw_h = ids.cpu().numpy(), gw.cpu().numpy()
+    _check(orc, layer.x, w, cfg.k, ids_h, gw_h)
+    y_u, h_u = trellis_lib.moe_ffn(*W, xd, ids, gw)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_u), "h differs from the unrouted layer fed the same routing"
+    routed = dataclasses.replace(layer, ids=ids_h, gate_w=gw_h)
+    _check_layer(trellis_lib, orc, routed, run=lambda L: (y, h))
+    y3, h3, ids3, gw3 = trellis_lib.moe_ffn_routed(*W, xd, wd, cfg.k, workspace=ws, check=True)
+    assert torch.equal(ids3, ids) and torch.equal(gw3, gw) and torch.equal(h3, h)
+
+
+def test_routed_layer_rejects_other_shapes(trellis_lib):
+    """Shapes the single-token kernel does not take are refused before
+    anything is enqueued (more than 32 experts here)."""
+    import torch
+    cfg = workloads.MoEConfig(100, "routed: 40 experts", 40, 256, 128, 4, 1, True)
+    layer = workloads.moe_layer(cfg)
+    _, w = _router_inputs(5, 1, 40, 256, True)
+    W = [dev(layer.gu_syms), dev(layer.gu_scales), dev(layer.dn_syms), dev(layer.dn_scales)]
+    with pytest.raises(trellis_lib.TrellisError):
+        trellis_lib.moe_ffn_routed(*W, _x_dev(layer.x, True), _w_dev(w), 4)
+    torch.cuda.synchronize()

@@ -27,7 +27,7 @@ ERRORS = {0: "TRELLIS_OK", -1: "TRELLIS_EINVAL", -2: "TRELLIS_ENULL", -3: "TRELL
 EXPORTS = ["trellis_version", "trellis_strerror", "trellis_decode_expand",
            "trellis_moe_gemv_workspace_size", "trellis_moe_gemv_workspace", "trellis_moe_gemv",
            "trellis_moe_ffn_workspace_size", "trellis_moe_ffn", "trellis_moe_ffn_timed",
-           "trellis_moe_ffn_noalloc",
+           "trellis_moe_ffn_noalloc", "trellis_moe_ffn_routed",
            "trellis_mxfp4_moe_gemv", "trellis_mxfp4_moe_ffn", "trellis_moe_gemv_e5m3", "trellis_moe_ffn_e5m3",
            "trellis_viterbi_workspace_size", "trellis_viterbi_encode", "trellis_router_workspace_size",
            "trellis_router_topk", "trellis_read_bandwidth"]
@@ -82,6 +82,8 @@ def lib():
         L.trellis_moe_ffn.restype = ctypes.c_int
         L.trellis_moe_ffn_timed.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P, P, SZ, P]
         L.trellis_moe_ffn_timed.restype = ctypes.c_int
+        L.trellis_moe_ffn_routed.argtypes = [P, MP, MP, P, I32, P, I32, P, P, P, P, P, SZ, P]
+        L.trellis_moe_ffn_routed.restype = ctypes.c_int
         L.trellis_moe_ffn_noalloc.argtypes = [P, MP, MP, P, I32, P, P, I32, I32, P, P]
         L.trellis_moe_ffn_noalloc.restype = ctypes.c_int
         L.trellis_moe_gemv_e5m3.argtypes = [P, MP, P, I32, I32, P, P, I32, I32, P, P, SZ]
@@ -354,6 +356,39 @@ def _moe_ffn(entry, gu_syms, gu_scales, dn_syms, dn_scales, x, topk_ids, topk_w,
                     (mg, md, events), workspace if check else None, stream)
     return _run(prepare, getattr(lib(), entry), args, entry, (y, h), (mg, md), workspace if check else None,
                 stream)
+
+
+def moe_ffn_routed(gu_syms, gu_scales, dn_syms, dn_scales, x, w_router, k, topk_ids=None, topk_w=None, h=None,
+                   y=None, workspace=None, stream=None, events=None, prepare=False, check=False):
+    """Router and layer for one token in one launch (trellis_moe_ffn_routed):
+    x [1, hidden], w_router bf16 [E, hidden]; returns (y, h, topk_ids, topk_w),
+    the last two the routing the kernel computed."""
+    torch = _torch()
+    mg = mat(gu_syms, gu_scales)
+    md = mat(dn_syms, dn_scales)
+    hidden, inter = mg.cols, mg.rows // 2
+    _check(x, x.dtype, "x", (1, hidden))
+    _check(w_router, torch.bfloat16, "w_router", (mg.n_mat, hidden))
+    with _on(stream):
+        if topk_ids is None:
+            topk_ids = torch.empty((1, k), dtype=torch.int32, device=x.device)
+        if topk_w is None:
+            topk_w = torch.empty((1, k), dtype=torch.float32, device=x.device)
+        if h is None:
+            h = torch.empty((1, k, inter), dtype=torch.bfloat16, device=x.device)
+        if y is None:
+            y = torch.empty((1, hidden), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = ffn_workspace(mg.n_mat, hidden, inter, 1, k, x.device)
+    _check(topk_ids, torch.int32, "topk_ids", (1, k))
+    _check(topk_w, torch.float32, "topk_w", (1, k))
+    _check(h, torch.bfloat16, "h", (1, k, inter))
+    _check(y, torch.float32, "y", (1, hidden))
+    args = (_stream(stream), ctypes.byref(mg), ctypes.byref(md), x.data_ptr(), _x_dtype(x), w_router.data_ptr(),
+            k, topk_ids.data_ptr(), topk_w.data_ptr(), h.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), events)
+    return _run(prepare, lib().trellis_moe_ffn_routed, args, "trellis_moe_ffn_routed", (y, h, topk_ids, topk_w),
+                (mg, md, events), workspace if check else None, stream)
 
 
 NOALLOC_SCRATCH_BYTES = 8 << 20   # TRELLIS_NOALLOC_SCRATCH_BYTES

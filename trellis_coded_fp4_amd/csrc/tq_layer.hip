@@ -51,6 +51,34 @@ extern "C" int trellis_moe_ffn(hipStream_t stream, const trellis_mat_t *w_gate_u
                                workspace_bytes, nullptr);
 }
 
+extern "C" int trellis_moe_ffn_routed(hipStream_t stream, const trellis_mat_t *w_gate_up,
+                                      const trellis_mat_t *w_down, const void *x, int32_t x_dtype,
+                                      const uint16_t *w_router, int32_t k, int32_t *topk_ids_out,
+                                      float *topk_w_out, uint16_t *h, float *y, void *workspace,
+                                      size_t workspace_bytes, hipEvent_t *events) {
+  if (!w_gate_up || !w_down) return TRELLIS_ENULL;
+  const Mats gu = trellis_mats(w_gate_up), dn = trellis_mats(w_down);
+  int rc;
+  if ((rc = check_mats(gu)) || (rc = check_mats(dn))) return rc;
+  if (!x || !w_router || !topk_ids_out || !topk_w_out || !h || !y || !workspace) return TRELLIS_ENULL;
+  if (x_dtype != TRELLIS_F32 && x_dtype != TRELLIS_BF16) return TRELLIS_EINVAL;
+  if ((rc = check_routing(1, k))) return rc;
+  const int E = gu.n_mat, hidden = gu.cols, inter = gu.rows / 2;
+  if (gu.rows % 64 || dn.n_mat != E || dn.rows != hidden || dn.cols != inter || k > E) return TRELLIS_EINVAL;
+  const Layout L = make_layout<FmtTrellis>(std::min(E, k), 0, k, 0, inter, 1, hidden,
+                                           tok_region(E, hidden, inter).total);
+  if (((uintptr_t)workspace & 255) || workspace_bytes < L.total) return TRELLIS_EWORKSPACE;
+  int cus = 0;
+  if ((rc = device_check(&cus))) return rc;
+  TokCall c{(const uint32_t *)gu.w, gu.scales, (const uint32_t *)dn.w, dn.scales, E, hidden, inter, k, nullptr,
+            nullptr, x, x_dtype == TRELLIS_BF16, h, y, (char *)workspace, L.reserve};
+  c.w_router = w_router;
+  c.ids_out = topk_ids_out;
+  c.gw_out = topk_w_out;
+  if (!tok_supported(c, cus)) return TRELLIS_EINVAL;
+  return tok_launch(c, cus, stream, events ? events[0] : nullptr, events ? events[1] : nullptr);
+}
+
 #ifdef TQ_TRACE
 extern "C" void tq_set_trace(void *p) { tq::g_trace = p; }
 #endif

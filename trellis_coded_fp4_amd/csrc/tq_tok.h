@@ -29,6 +29,11 @@ struct TokCall {
   size_t region_off;                       // offset of the TokRegion
   bool mx = false;                         // weights are expanded MXFP4
   bool e5m3 = false;                       // scale bytes are E5M3 (trellis streams)
+  // routed calls: the kernel computes the routing from these router rows
+  // (bf16 [E][H]) and writes it to ids_out / gw_out ([k] each); ids and
+  // gate_w are then not read
+  const uint16_t *w_router = nullptr;
+  int32_t *ids_out = nullptr; float *gw_out = nullptr;
 };
 
 // True when the kernel takes this shape (otherwise the general layer kernel

@@ -49,6 +49,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <math.h>
+
 #include <algorithm>
 
 #include "tq_common.h"
@@ -76,6 +78,10 @@ struct Args {
   uint64_t *hx;         // [n_exp <= 32][I / 2]: tag << 32 | bf16 pair
   uint32_t *yz;         // [H / 16]: tag of the call that cleared the tile
   int G;
+  // routed instances: the router rows, and where workgroup 0 writes the
+  // routing it computed (ids and gate_w above are then unused)
+  const uint16_t *w_router;   // [E][H] bf16
+  int32_t *ids_out; float *gw_out;
 #ifdef TQ_TRACE
   unsigned long long *trace;   // [G][16] s_memrealtime stamps
 #endif
@@ -346,6 +352,116 @@ __device__ __forceinline__ DecA piece_a(const TileLd<PPW, MX> &L, int q, uint32_
   }
 }
 
+// The router in front of the layer, computed by every workgroup for the one
+// token (routed instances): logits[e] = sum_h x[h] w_router[e][h], the k
+// largest in descending order (ties to the lower id), gate weights = softmax
+// over them. The arithmetic is the standalone router's (trellis_router_topk)
+// step for step -- fp64 sums of exact products, lane-sequential over 16-byte
+// chunks and then an xor butterfly; k rounds of a wave-wide argmax; an fp64
+// softmax rounded to fp32 -- so both give the same bits. Wave v takes the
+// experts v, v + 8, v + 16, v + 24, issuing every load of their router rows
+// before anything waits, and sums them as independent chains; x goes
+// through LDS as fp32. Lane j < k returns pick j (id, gate weight); lanes
+// 32..63 mirror 0..31. E <= 32, H <= 4096.
+constexpr int kRtMaxE = 32, kRtMaxH = 4096;
+__device__ __forceinline__ void tok_router(const Args &a, int tid, int *idv, float *gwr) {
+  __shared__ float rx[kRtMaxH];
+  __shared__ double rlg[kRtMaxE];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, nq = H / 8;
+  constexpr int kLd = kRtMaxH / 8 / 64;   // 16-byte loads per lane and expert, at most
+  constexpr int kPer = kRtMaxE / 8;       // experts per wave, at most
+  uint4 r[kPer][kLd];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const uint4 *row = (const uint4 *)(a.w_router + (size_t)min(wave + 8 * m, a.E - 1) * H);
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) r[m][i] = row[min(lane + 64 * i, nq - 1)];
+  }
+  {
+    const int nx = H * (a.x_bf16 ? 2 : 4) / 16;   // 16-byte loads of x
+    for (int c = tid; c < nx; c += 512) {
+      const uint4 v = ((const uint4 *)a.x)[c];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      if (a.x_bf16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rx[8 * c + 2 * j] = bf16_to_f32((uint16_t)(u[j] & 0xFFFFu));
+          rx[8 * c + 2 * j + 1] = bf16_to_f32((uint16_t)(u[j] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rx[4 * c + j] = __uint_as_float(u[j]);
+      }
+    }
+  }
+  __syncthreads();
+  double sum[kPer];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) sum[m] = 0.0;
+#pragma unroll
+  for (int i = 0; i < kLd; ++i) {
+    const int q = lane + 64 * i;
+    if (q < nq) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const uint32_t wv[4] = {r[m][i].x, r[m][i].y, r[m][i].z, r[m][i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sum[m] += (double)rx[8 * q + 2 * j] * (double)bf16_to_f32((uint16_t)(wv[j] & 0xFFFFu));
+          sum[m] += (double)rx[8 * q + 2 * j + 1] * (double)bf16_to_f32((uint16_t)(wv[j] >> 16));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum[m] += __shfl_xor(sum[m], off);
+    if (lane == 0 && wave + 8 * m < a.E) rlg[wave + 8 * m] = sum[m];
+  }
+  __syncthreads();
+  // every wave picks the top k itself (lane l owns expert l)
+  const double lv = rlg[min(lane, a.E - 1)];
+  bool taken = false;
+  int my_pick = 0;
+  double my_val = 0.0, top = 0.0;
+  for (int j = 0; j < a.k; ++j) {
+    double bv = -INFINITY;
+    int be = -1;
+    if (lane < a.E && !taken) {
+      bv = lv;
+      be = lane;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be == lane) taken = true;
+    if (lane == j) {
+      my_pick = be;
+      my_val = bv;
+    }
+    if (j == 0) top = bv;
+  }
+  const double ex = lane < a.k ? exp(my_val - top) : 0.0;
+  double den = ex;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  const float g = (float)(ex / den);
+  if (blockIdx.x == 0 && wave == 0 && lane < a.k) {
+    a.ids_out[lane] = my_pick;
+    a.gw_out[lane] = g;
+  }
+  *idv = __shfl(my_pick, lane & 31);
+  *gwr = __shfl(g, lane & 31);
+}
+
 // Eight waves, two per SIMD, in two roles. Waves 0-3 ("gate/up waves")
 // each own PPW consecutive pieces of every gate/up tile of the workgroup
 // (T1 tiles at most), streamed through a register ring AT tiles deep (a
@@ -360,8 +476,9 @@ __device__ __forceinline__ DecA piece_a(const TileLd<PPW, MX> &L, int q, uint32_
 // at a barrier for the other's loads. MX: the weights are expanded MXFP4
 // (codes [rows][cols / 2], even column in the low nibble, same scales),
 // fed to the matrix cores as loaded; the activations take that format's
-// layout. E5: the scale bytes are E5M3 (trellis streams only).
-template <int PPW, int T1, int T2, int AT, bool MX, bool E5>
+// layout. E5: the scale bytes are E5M3 (trellis streams only). RT: the
+// kernel computes the routing itself (tok_router) instead of reading it.
+template <int PPW, int T1, int T2, int AT, bool MX, bool E5, bool RT = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k_tok(Args a) {
   static_assert(!(MX && E5), "E5M3 scales are served on trellis streams");
   constexpr int NW = 8, NR = 4;   // waves, waves per role
@@ -397,8 +514,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   // role (clamped addresses), so the compiler's waits count exactly the
   // loads issued after each one.
   const int sl = lane & 31, slc = sl < a.k ? sl : 0;
-  const int idv = a.ids[slc];
-  const float gwr = *(a.gate_w ? a.gate_w + slc : (const float *)(a.ids + slc));
+  int idv;
+  float gwr;
+  if constexpr (RT) {
+    tok_router(a, tid, &idv, &gwr);
+  } else {
+    idv = a.ids[slc];
+    gwr = *(a.gate_w ? a.gate_w + slc : (const float *)(a.ids + slc));
+  }
   // x: a gate/up wave splits the 32-value blocks of its own pieces
   // (8 PPW of them, four lanes each, 16 per pass), loaded ahead of its tiles
   constexpr int kXPass = (8 * PPW + 15) / 16;
@@ -421,7 +544,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
   }
 
   // ---- routing, in every wave's registers (tok_route)
-  const TokRoute route = tok_route(lane, a.k, a.E, idv, gwr, a.gate_w != nullptr);
+  const TokRoute route = tok_route(lane, a.k, a.E, idv, gwr, RT || a.gate_w != nullptr);
   const bool valid = route.valid;
   const int n_skipped = route.n_skipped, n_act = route.n_act, rank = route.rank;
   const int act_e = route.act_e;
@@ -822,7 +945,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) k
 // Kernel instances: (pieces per wave, gate/up tiles, down tiles, format).
 struct Inst {
   int ppw, t1, t2;
-  bool mx, e5m3;
+  bool mx, e5m3, routed;
   const void *fn;
 };
 #ifndef TQ_TOK_AT
@@ -832,13 +955,16 @@ struct Inst {
 #define TQ_TOK_AT_MX 2
 #endif
 #define TQ_TOK_INST(PPW, T1, T2) \
-  {PPW, T1, T2, false, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, false>}
+  {PPW, T1, T2, false, false, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, false>}
 #define TQ_TOK_INST_MX(PPW, T1, T2) \
-  {PPW, T1, T2, true, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT_MX, true, false>}
+  {PPW, T1, T2, true, false, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT_MX, true, false>}
 #define TQ_TOK_INST_E5(PPW, T1, T2) \
-  {PPW, T1, T2, false, true, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, true>}
+  {PPW, T1, T2, false, true, false, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, true>}
+#define TQ_TOK_INST_RT(PPW, T1, T2) \
+  {PPW, T1, T2, false, false, true, (const void *)k_tok<PPW, T1, T2, TQ_TOK_AT, false, false, true>}
 const Inst kInsts[] = {
     TQ_TOK_INST(3, 6, 3), TQ_TOK_INST(4, 6, 3), TQ_TOK_INST(3, 6, 4), TQ_TOK_INST(4, 6, 4),
+    TQ_TOK_INST_RT(3, 6, 3), TQ_TOK_INST_RT(4, 6, 3), TQ_TOK_INST_RT(3, 6, 4), TQ_TOK_INST_RT(4, 6, 4),
     TQ_TOK_INST_MX(3, 6, 3), TQ_TOK_INST_MX(4, 6, 3), TQ_TOK_INST_MX(3, 6, 4), TQ_TOK_INST_MX(4, 6, 4),
     TQ_TOK_INST_E5(3, 6, 3), TQ_TOK_INST_E5(4, 6, 3), TQ_TOK_INST_E5(3, 6, 4), TQ_TOK_INST_E5(4, 6, 4),
 };
@@ -1022,10 +1148,10 @@ Plan plan(const TokCall &c, int cus) {
   return p;
 }
 
-const Inst *pick(const Plan &p, bool mx, bool e5m3) {
+const Inst *pick(const Plan &p, bool mx, bool e5m3, bool routed) {
   const Inst *best = nullptr;
   for (const Inst &i : kInsts)
-    if (i.mx == mx && i.e5m3 == e5m3 && i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
+    if (i.mx == mx && i.e5m3 == e5m3 && i.routed == routed && i.ppw >= p.ppw && i.t1 >= p.t1 && i.t2 >= p.t2 &&
         (!best || i.ppw * (i.t1 + i.t2) < best->ppw * (best->t1 + best->t2)))
       best = &i;
   return best;
@@ -1048,12 +1174,15 @@ bool tok_supported(const TokCall &c, int cus) {
   if (((uintptr_t)c.w1 & 15) || ((uintptr_t)c.w2 & 15) || ((uintptr_t)c.x & 15)) return false;
   if (((uintptr_t)c.s1 & 15) || ((uintptr_t)c.s2 & 15)) return false;
   const Plan p = plan(c, cus);
-  return p.ok && !(c.mx && c.e5m3) && pick(p, c.mx, c.e5m3) != nullptr;
+  if (c.w_router && (c.mx || c.e5m3 || c.E > kRtMaxE || c.H > kRtMaxH || c.k > c.E || !c.ids_out || !c.gw_out ||
+                    ((uintptr_t)c.w_router & 15)))
+    return false;
+  return p.ok && !(c.mx && c.e5m3) && pick(p, c.mx, c.e5m3, c.w_router != nullptr) != nullptr;
 }
 
 int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const Plan p = plan(c, cus);
-  const Inst *inst = p.ok ? pick(p, c.mx, c.e5m3) : nullptr;
+  const Inst *inst = p.ok ? pick(p, c.mx, c.e5m3, c.w_router != nullptr) : nullptr;
   if (!inst) return TRELLIS_EINVAL;
   const TokRegion R = tok_region(c.E, c.H, c.I);
   char *base = c.ws + c.region_off;
@@ -1068,6 +1197,7 @@ int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0, hipEvent
   a.hx = (uint64_t *)(base + R.hx);
   a.yz = (uint32_t *)(base + R.yz);
   a.G = cus;
+  a.w_router = c.w_router; a.ids_out = c.ids_out; a.gw_out = c.gw_out;
 #ifdef TQ_TRACE
   a.trace = g_tok_trace;
 #endif
