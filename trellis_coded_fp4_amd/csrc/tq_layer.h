@@ -1929,10 +1929,10 @@ static int gemv_impl(hipStream_t stream, const Mats &w, const void *x, int32_t x
   int cus = 0;
   if ((rc = device_check(&cus))) return rc;
   char *ws = (char *)workspace;
-  if constexpr (F::kSteps == 2 && !F::kE5M3) {
+  {
     // one token, shared x, every slot's output: the single-token GEMV kernel
     TokGemvCall c{(const uint32_t *)w.w, w.scales, w.n_mat, w.rows, w.cols, k, topk_ids, x,
-                  x_dtype == TRELLIS_BF16, y, (int *)(ws + L.status)};
+                  x_dtype == TRELLIS_BF16, y, (int *)(ws + L.status), F::kSteps == 1, F::kE5M3};
     if (T == 1 && !combine && !x_per_slot && tok_gemv_supported(c, cus)) return tok_gemv_launch(c, cus, stream);
   }
   LayerArgs a{};

@@ -47,16 +47,18 @@ bool tok_supported(const TokCall &c, int cus);
 // execution by the dispatch itself.
 int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-// One token through a routed matrix stack of trellis streams under UE8M0
-// scales, every slot's output kept (trellis_moe_gemv with T = 1, shared x,
-// no gate weights): y[k][rows], zeros for slots routed nowhere.
+// One token through a routed matrix stack (trellis streams under UE8M0 or
+// E5M3 scales, or expanded MXFP4 codes), every slot's output kept
+// (trellis_moe_gemv and its variants with T = 1, shared x, no gate
+// weights): y[k][rows], zeros for slots routed nowhere.
 struct TokGemvCall {
-  const uint32_t *w; const uint8_t *s;   // [E][rows][K / 16], [E][rows][K / 32]
+  const uint32_t *w; const uint8_t *s;   // [E][rows][K / 16] (MXFP4: K / 2 bytes a row), [E][rows][K / 32]
   int E, rows, K, k;
   const int32_t *ids;
   const void *x; int x_bf16;
   float *y;
   int *status;                           // the workspace's status words
+  bool mx = false, e5m3 = false;
 };
 // True when the kernel takes this shape: rows % 16 == 0, K % 64 == 0, K <=
 // 4096, k <= 32, 16-byte aligned streams, scales and x, and at most eight

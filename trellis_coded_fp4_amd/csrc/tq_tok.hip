@@ -982,7 +982,9 @@ const Inst kInsts[] = {
 // workgroup, so nothing waits on another workgroup. Slots that route to no
 // expert get zeros from the tiles of active expert 0, which cover every row
 // once (or from workgroup 0 when no slot is active). A set sticky error word
-// makes the call write NaN to y and nothing else.
+// makes the call write NaN to y and nothing else. MX: expanded MXFP4 codes;
+// E5: trellis streams under E5M3 scales (each matrix-core step once per
+// power-of-two term of its scale), as in the layer kernel.
 struct GemvArgs {
   const uint32_t *w; const uint8_t *s;   // [E][rows][K / 16] symbols, [E][rows][K / 32] scales
   int E, rows, K, k;
@@ -993,11 +995,13 @@ struct GemvArgs {
   int G;
 };
 
-template <int PPW, int T1>
+template <int PPW, int T1, bool MX, bool E5>
 __global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
+  static_assert(!(MX && E5), "E5M3 scales are served on trellis streams");
   constexpr int NR = 4, AT = T1 < 2 ? T1 : 2;
   __shared__ uint8_t xq[2 * 2 * kMaxJ * 128], xs[2 * 2 * kMaxJ * 4];
   __shared__ float red[T1][NR][16];
+  __shared__ uint32_t e5t[E5 ? 256 : 1];
   const int tid = threadIdx.x, lane = tid & 63, rw = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int w = blockIdx.x, G = a.G;
@@ -1006,6 +1010,7 @@ __global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
   const int src = ((lane - 16) & 63) << 2;     // lane-group g-1, same row (ds_bpermute address)
   const int pa = min(rw * PPW, J), c = min(J - pa, PPW);
 
+  if constexpr (E5) e5t[tid] = e5m3_terms((uint32_t)tid);   // 256 threads
   const int sl = lane & 31, slc = sl < a.k ? sl : 0;
   const int idv = a.ids[slc];
   const int err = __hip_atomic_load(&a.status[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1040,19 +1045,41 @@ __global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
       trt[t] = rt;
     }
   }
-  auto load_tile = [&](int t) -> TileLd<PPW, false> {
-    TileLd<PPW, false> L;
+  auto load_tile = [&](int t) -> TileLd<PPW, MX> {
+    TileLd<PPW, MX> L;
     const size_t r = (nu > 0 ? (size_t)__builtin_amdgcn_readlane(route.act_e, tai[t]) * a.rows + 16 * trt[t] : 0) + i16;
-    const uint32_t *rp = a.w + r * wpr;
     const uint8_t *sp = a.s + r * nb;
+    if constexpr (MX) {
+      // 16 bytes per block; the row's last block stands in for blocks past it
+      const uint8_t *rp = (const uint8_t *)a.w + r * (size_t)nb * 16;
 #pragma unroll
-    for (int q = 0; q < PPW; ++q) L.sc[q] = *(const uint16_t *)(sp + min(8 * (pa + q) + 2 * g, nb - 2));
+      for (int q = 0; q < PPW; ++q)
+        L.sc[q] = (uint32_t)sp[min(8 * (pa + q) + g, nb - 1)] | (uint32_t)sp[min(8 * (pa + q) + 4 + g, nb - 1)] << 8;
 #pragma unroll
-    for (int q = 0; q < PPW; ++q) L.w[q] = *(const uint4 *)(rp + min(16 * (pa + q) + 4 * g, wpr - 4));
-    L.hist = rp[min(max(16 * pa - 1, 0), wpr - 1)];
+      for (int q = 0; q < PPW; ++q) {
+        L.w[2 * q] = *(const uint4 *)(rp + 16 * min(8 * (pa + q) + g, nb - 1));
+        L.w[2 * q + 1] = *(const uint4 *)(rp + 16 * min(8 * (pa + q) + 4 + g, nb - 1));
+      }
+      L.hist = 0;
+    } else {
+      const uint32_t *rp = a.w + r * wpr;
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) L.sc[q] = *(const uint16_t *)(sp + min(8 * (pa + q) + 2 * g, nb - 2));
+#pragma unroll
+      for (int q = 0; q < PPW; ++q) L.w[q] = *(const uint4 *)(rp + min(16 * (pa + q) + 4 * g, wpr - 4));
+      L.hist = rp[min(max(16 * pa - 1, 0), wpr - 1)];
+    }
     return L;
   };
-  TileLd<PPW, false> R[AT > 0 ? AT : 1];
+  // A-scale pair of piece p (blocks past the row: 2^0 or E5M3 1.875,
+  // meeting zero activations; the codes there are the row's own, finite)
+  auto a_scale = [&](uint32_t sc, int p) -> uint32_t {
+    if constexpr (MX)
+      return (8 * p + g < nb ? sc & 0xFFu : 0x7Fu) | (8 * p + 4 + g < nb ? sc & 0xFF00u : 0x7F00u);
+    else
+      return 8 * p + 2 * g < nb ? sc : 0x7F7Fu;
+  };
+  TileLd<PPW, MX> R[AT > 0 ? AT : 1];
 #pragma unroll
   for (int t = 0; t < AT; ++t) R[t] = load_tile(t);
   // this wave's blocks of x, split into LDS (blocks past K, up to the last
@@ -1068,8 +1095,9 @@ __global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
       const uint32_t bits = a.x_bf16 ? (wv[i >> 1] >> (16 * (i & 1))) << 16 : wv[i];
       f[i] = xb < nb ? __uint_as_float(bits) : 0.0f;
     }
-    split_block8<false>(f, xb, xj, xq, xs, ps, xb < 8 * (pa + c));
+    split_block8<MX>(f, xb, xj, xq, xs, ps, xb < 8 * (pa + c));
   }
+  if constexpr (E5) __syncthreads();   // the term table is complete
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   BOp bx[PPW][2];
 #pragma unroll
@@ -1078,7 +1106,7 @@ __global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
     for (int hh = 0; hh < 2; ++hh) bx[q][hh] = read_b(xq, xs, ps, i16 & 1, min(2 * (pa + q) + hh, ps - 1), g);
 #pragma unroll
   for (int t = 0; t < T1; ++t) {
-    const TileLd<PPW, false> cur = R[t % AT];
+    const TileLd<PPW, MX> cur = R[t % AT];
     if (t + AT < T1) R[t % AT] = load_tile(t + AT);
     if (t < nu && c > 0) {
       uint32_t carry = pa == 0 ? 0u : cur.hist;
@@ -1086,10 +1114,13 @@ __global__ void __launch_bounds__(256) k_tok_gemv(GemvArgs a) {
 #pragma unroll
       for (int q = 0; q < PPW; ++q) {
         if (q < c) {
-          const uint32_t rot = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
-          const DecA d = decode_words(cur.w[q], g == 0 ? carry : rot);
+          const uint32_t rot = MX ? 0u : (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)cur.w[q].w);
+          const DecA d = piece_a<PPW, MX>(cur, q, g == 0 ? carry : rot);
           carry = rot;
-          acc = mma2(d, bx[q][0], bx[q][1], 8 * (pa + q) + 2 * g < nb ? cur.sc[q] : 0x7F7Fu, acc);
+          if constexpr (E5)
+            acc = mma2_e5m3(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], pa + q), acc, e5t);
+          else
+            acc = mma2(d, bx[q][0], bx[q][1], a_scale(cur.sc[q], pa + q), acc);
         }
       }
 #pragma unroll
@@ -1222,17 +1253,19 @@ int tok_launch(const TokCall &c, int cus, hipStream_t s, hipEvent_t e0, hipEvent
 namespace {
 struct GemvInst {
   int ppw, t1;
+  bool mx, e5m3;
   const void *fn;
 };
-#define TQ_TOKV_INST(PPW, T1) {PPW, T1, (const void *)k_tok_gemv<PPW, T1>}
-const GemvInst kGemvInsts[] = {
-    TQ_TOKV_INST(1, 1), TQ_TOKV_INST(2, 1), TQ_TOKV_INST(3, 1), TQ_TOKV_INST(4, 1),
-    TQ_TOKV_INST(1, 8), TQ_TOKV_INST(2, 8), TQ_TOKV_INST(3, 8), TQ_TOKV_INST(4, 8),
-};
+#define TQ_TOKV_INST(PPW, T1, MX, E5) {PPW, T1, MX, E5, (const void *)k_tok_gemv<PPW, T1, MX, E5>}
+#define TQ_TOKV_FMT(MX, E5)                                                                             \
+  TQ_TOKV_INST(1, 1, MX, E5), TQ_TOKV_INST(2, 1, MX, E5), TQ_TOKV_INST(3, 1, MX, E5), TQ_TOKV_INST(4, 1, MX, E5), \
+      TQ_TOKV_INST(1, 8, MX, E5), TQ_TOKV_INST(2, 8, MX, E5), TQ_TOKV_INST(3, 8, MX, E5), TQ_TOKV_INST(4, 8, MX, E5)
+const GemvInst kGemvInsts[] = {TQ_TOKV_FMT(false, false), TQ_TOKV_FMT(true, false), TQ_TOKV_FMT(false, true)};
 
 // The instance and grid for the worst case (every slot a distinct expert).
 const GemvInst *gemv_pick(const TokGemvCall &c, int cus, int *grid) {
-  if (c.k < 1 || c.k > kMaxSlots || c.rows < 16 || c.rows % 16 || c.K < 64 || c.K % 64 || c.K > 32 * 8 * kMaxJ)
+  if (c.k < 1 || c.k > kMaxSlots || c.rows < 16 || c.rows % 16 || c.K < 64 || c.K % 64 || c.K > 32 * 8 * kMaxJ ||
+      (c.mx && c.e5m3))
     return nullptr;
   if (((uintptr_t)c.w & 15) || ((uintptr_t)c.s & 15) || ((uintptr_t)c.x & 15)) return nullptr;
   const int J = (c.K / 32 + 7) / 8, ppw = (J + 3) / 4;
@@ -1240,7 +1273,7 @@ const GemvInst *gemv_pick(const TokGemvCall &c, int cus, int *grid) {
   const int G = (int)std::min<long>(nu, cus);
   const long t1 = (nu + G - 1) / G;
   for (const GemvInst &i : kGemvInsts)
-    if (i.ppw == ppw && i.t1 >= t1) {
+    if (i.mx == c.mx && i.e5m3 == c.e5m3 && i.ppw == ppw && i.t1 >= t1) {
       *grid = G;
       return &i;
     }
